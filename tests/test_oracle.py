@@ -1,0 +1,313 @@
+"""Pins of the CPU oracle against facts other than itself (no GPU).
+
+Each test names the passage it follows.  Pins used: exact rational closed
+forms, brute force over every subset, float64 BLAS / torch float64 library
+routines for the special cases that reduce to plain products and textbook
+attention, and identities that must hold exactly.
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+
+# --------------------------------------------------------------------------- keep count
+# Paper abstract: a single retention ratio r; kept count ceil(r*K).
+
+def _exact_keep(K, r: Fraction):
+    p = r * K
+    n = math.floor(p + Fraction(1, 2))
+    if abs(p - n) <= Fraction(1, 10**9) * max(1, p):
+        k = n
+    else:
+        k = math.ceil(p)
+    return max(1, min(K, k))
+
+
+@pytest.mark.parametrize("K", list(range(1, 21)) + [127, 128, 4096, 14336, 131072])
+def test_keep_count_closed_form(K):
+    decimals = ["0.07", "0.1", "0.3", "0.25", "0.5", "0.75", "1", "0.001", "0.999"]
+    for s in decimals:
+        assert oracle.keep_count(K, float(s)) == _exact_keep(K, Fraction(s)), (K, s)
+        # away from the snap band the closed form is the plain ceiling
+        if (Fraction(s) * K).denominator == 1 or abs(Fraction(s) * K - round(Fraction(s) * K)) > Fraction(1, 1000):
+            assert oracle.keep_count(K, float(s)) == max(1, min(K, math.ceil(Fraction(s) * K)))
+    assert oracle.keep_count(K, 1.0 / 3.0) == _exact_keep(K, Fraction(1, 3))
+    if K <= 20:
+        for k in range(1, K + 1):
+            assert oracle.keep_count(K, k / K) == k
+    for bad in (0.0, -0.25, 1.5, float("nan"), float("inf")):
+        assert oracle.keep_count(K, bad) == -1
+
+
+def test_keep_count_configs():
+    # the decode shapes keep 3584/7168/10752/14336 of 14336; head_dim 32/64 of 128
+    assert [oracle.keep_count(14336, r) for r in (0.25, 0.5, 0.75, 1.0)] == [3584, 7168, 10752, 14336]
+    assert [oracle.keep_count(128, r) for r in (0.25, 0.5)] == [32, 64]
+    assert oracle.keep_count(32768, 0.25) == 8192 and oracle.keep_count(131072, 0.25) == 32768
+    assert oracle.keep_count(100, 0.07) == 7  # 0.07*100 is 7.000000000000001 in binary
+
+
+# --------------------------------------------------------------------------- scorer
+# Blog section 5.1: a cheap score per slice from the current input.
+
+def test_scorer_tile1_unit_weight_is_abs():
+    cs = W.linear_random(6, 300, 8, 1, "f32", seed=3)
+    s = oracle.scores(cs.x, np.ones(300, np.float32), 1)
+    assert np.array_equal(s, np.abs(cs.x))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scorer_max_then_scale_equals_scale_then_max(dtype):
+    # rounding is monotone and c >= 0, so fl(max|x| * c) == max fl(|x| * c) (numpy float32 ops)
+    cs = W.linear_random(10, 257, 8, 4, dtype, seed=5)
+    s = oracle.scores(cs.x, cs.c, 4)
+    xf = W.bf16_bits_to_f32(cs.x) if dtype == "bf16" else cs.x
+    for tau in range(3):
+        blk = np.abs(xf[4 * tau:4 * tau + 4]) * cs.c[None, :]
+        assert np.array_equal(s[tau], blk.max(axis=0))
+
+
+def test_scorer_is_token_order_independent():
+    cs = W.linear_random(8, 100, 8, 8, "bf16", seed=7)
+    perm = np.random.default_rng(1).permutation(8)
+    assert np.array_equal(oracle.scores(cs.x, cs.c, 8), oracle.scores(cs.x[perm], cs.c, 8))
+
+
+def test_scorer_single_token_column():
+    # only one token of the tile is non-zero in column j: the score is exactly |x|*c
+    x = np.zeros((4, 5), np.float32)
+    x[2, 0], x[0, 1], x[3, 2], x[1, 4] = -3.0, 0.5, 1e-30, 7.25
+    c = np.array([2.0, 0.1, 3.0, 5.0, 0.0], np.float32)
+    s = oracle.scores(x, c, 4)[0]
+    exp = np.array([6.0, np.float32(0.5) * np.float32(0.1), np.float32(1e-30) * np.float32(3.0), 0.0, 0.0],
+                   np.float32)
+    assert np.array_equal(s, exp)
+
+
+# --------------------------------------------------------------------------- selector
+# Blog sections 5.2 / 6.1: top-k, kept indices sorted ascending.  Brute force:
+# the kept set maximises the score sum; among maximisers, the lexicographically
+# smallest ascending index list (ties go to the lower index).
+
+def _exact_ints(vals):
+    fr = [Fraction(float(v)) for v in vals]
+    den = math.lcm(*[f.denominator for f in fr])
+    return [int(f * den) for f in fr]
+
+
+def _brute_topk(scores, k):
+    ints = _exact_ints(scores)
+    best, best_set = None, None
+    for comb in itertools.combinations(range(len(scores)), k):  # lexicographic order
+        tot = sum(ints[i] for i in comb)
+        if best is None or tot > best:
+            best, best_set = tot, comb
+    return list(best_set)
+
+
+def _tie_case(seed, T=4, K=12):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-3, 4, size=(T, K)).astype(np.float32)
+    return x, np.ones(K, np.float32)
+
+
+@pytest.mark.parametrize("tile", [4, 2, 3])
+def test_select_brute_force_random(tile):
+    for seed in range(40):
+        cs = W.linear_random(4, 12, 8, tile, "f32", seed=seed, wsigma=0.05)
+        s = oracle.scores(cs.x, cs.c, tile)
+        for k in range(1, 13):
+            idx = oracle.select(cs.x, cs.c, tile, k / 12)
+            assert idx.shape == (s.shape[0], k)
+            for tau in range(s.shape[0]):
+                assert list(idx[tau]) == _brute_topk(s[tau], k), (seed, k, tau)
+
+
+def test_select_brute_force_ties():
+    for seed in range(120):
+        x, c = _tie_case(seed)
+        s = oracle.scores(x, c, 4)
+        for k in range(1, 13):
+            idx = oracle.select(x, c, 4, k / 12)
+            assert list(idx[0]) == _brute_topk(s[0], k), (seed, k)
+
+
+def test_select_all_equal_keeps_lowest():
+    x = np.ones((1, 50), np.float32)
+    c = np.ones(50, np.float32)
+    assert list(oracle.select(x, c, 1, 0.2)[0]) == list(range(10))
+    # negative zero ranks with +0: zero scores keep the lowest indices
+    x = np.zeros((1, 8), np.float32)
+    c = np.array([0, 0, 0, 0, 1, 1, 1, 1], np.float32)
+    x[0, 4:] = 1.0
+    x[0, 0] = -0.0
+    assert list(oracle.select(x, c, 1, 6 / 8)[0]) == [0, 1, 4, 5, 6, 7]
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged"])
+def test_select_count_and_order(case):
+    cs = W.linear_tiny() if case == "tiny" else W.linear_random(37, 300, 16, 8, "bf16", seed=2)
+    for r in (0.1, 0.25, 0.5, 1 / 3, 0.75, 1.0):
+        idx = oracle.select(cs.x, cs.c, cs.tile, r)
+        k = oracle.keep_count(cs.K, r)
+        assert idx.shape == (-(-cs.T // cs.tile), k)
+        assert np.all(np.diff(idx, axis=1) > 0) and idx.min() >= 0 and idx.max() < cs.K
+
+
+# --------------------------------------------------------------------------- products
+# Blog section 2 (Y = X @ W^T) and 6.1 (keep ratio 1.0 equals the full result).
+
+def _f64(a, dtype):
+    return (W.bf16_bits_to_f32(a) if dtype == "bf16" else a).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_linear_r1_equals_dense(dtype):
+    cs = W.linear_random(5, 96, 40, 2, dtype, seed=11)
+    idx = oracle.select(cs.x, cs.c, 2, 1.0)
+    y, yd = oracle.linear(cs.x, cs.wt, idx, 2, want_double=True)
+    yf, yfd = oracle.dense_linear(cs.x, cs.wt, want_double=True)
+    assert np.array_equal(y, yf) and np.array_equal(yd, yfd)  # same order, bitwise
+    ref = _f64(cs.x, dtype) @ _f64(cs.wt, dtype)  # float64 BLAS (different summation order)
+    assert np.max(np.abs(yfd - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("dtype,tile", [("f32", 4), ("f32", 2), ("bf16", 3)])
+def test_linear_dropped_slice_identity(dtype, tile):
+    # Y_full - Y_red = X[:, dropped] @ W^T[dropped, :]   (per tile's own dropped set)
+    cs = W.linear_random(7, 64, 24, tile, dtype, seed=13)
+    xd, wd = _f64(cs.x, dtype), _f64(cs.wt, dtype)
+    _, yfull = oracle.dense_linear(cs.x, cs.wt, want_double=True)
+    for r in (0.25, 0.5, 0.75):
+        idx = oracle.select(cs.x, cs.c, tile, r)
+        _, yred = oracle.linear(cs.x, cs.wt, idx, tile, want_double=True)
+        for t in range(cs.T):
+            keep = set(idx[t // tile].tolist())
+            drop = [j for j in range(cs.K) if j not in keep]
+            rhs = xd[t, drop] @ wd[drop, :]
+            assert np.max(np.abs((yfull[t] - yred[t]) - rhs)) <= 1e-12 * np.max(np.abs(yfull)), (r, t)
+
+
+def test_linear_row_subset_matches_full():
+    cs = W.linear_random(9, 80, 30, 4, "bf16", seed=17)
+    idx = oracle.select(cs.x, cs.c, 4, 0.5)
+    full = oracle.linear(cs.x, cs.wt, idx, 4)
+    part = oracle.linear(cs.x, cs.wt, idx, 4, rows=(3, 7))
+    assert np.array_equal(full[3:7], part[3:7]) and not part[:3].any() and not part[7:].any()
+
+
+# --------------------------------------------------------------------------- attention
+# Blog sections 3.1 / 3.3; GEMM notes section 1 (scores = Q K^T, softmax, @ V).
+
+def _qkv_f64(cs):
+    q = W.bf16_bits_to_f32(cs.q).astype(np.float64)
+    kt = W.bf16_bits_to_f32(cs.kt).astype(np.float64)
+    v = W.bf16_bits_to_f32(cs.v).astype(np.float64)
+    return q, kt, v
+
+
+def _sdpa64(q, k, v, scale):
+    # q [Hq, d], k [S, d], v [S, D] float64 -> torch's float64 SDPA
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None, :], torch.from_numpy(np.ascontiguousarray(k))[None, None].expand(1, q.shape[0], *k.shape),
+        torch.from_numpy(np.ascontiguousarray(v))[None, None].expand(1, q.shape[0], *v.shape), scale=scale)
+    return out[0, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_attn_full_ratios_equal_textbook(mode):
+    cs = W.attn_case(2, 40, Hq=4, Hkv=2, D=16, seed=1, n_hot=3)
+    res = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 1.0, 1.0, mode, want=("out_d", "p"))
+    dense = oracle.dense_attn(cs.q, cs.kt, cs.v, cs.scale)
+    q, kt, v = _qkv_f64(cs)
+    for b in range(2):
+        for g in range(2):
+            ref = _sdpa64(q[b, 2 * g:2 * g + 2], kt[b, g].T, v[b, g], cs.scale)
+            assert np.max(np.abs(res["out_d"][b, 2 * g:2 * g + 2] - ref)) <= 1e-12 * np.max(np.abs(ref))
+            assert np.max(np.abs(dense[b, 2 * g:2 * g + 2] - ref)) <= 1e-12 * np.max(np.abs(ref))
+    assert np.max(np.abs(res["p"].sum(axis=2) - 1.0)) <= 1e-12
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_attn_reduced_dims_equal_sliced_textbook(mode):
+    # with every position kept, the result is textbook attention over the kept head_dim slices
+    # (scale stays 1/sqrt(full D)); lse matches torch.logsumexp of the sliced logits
+    cs = W.attn_case(1, 64, Hq=4, Hkv=1, D=32, seed=2, n_hot=4)
+    res = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.25, 1.0, mode, want=("out_d",))
+    q, kt, v = _qkv_f64(cs)
+    for h in range(4):
+        sel = res["dim_idx"][0, 0 if mode == 0 else h]
+        ref = _sdpa64(q[0][h:h + 1][:, sel], kt[0, 0][sel].T, v[0, 0], cs.scale)
+        assert np.max(np.abs(res["out_d"][0, h] - ref[0])) <= 1e-12 * np.max(np.abs(ref))
+        logits = torch.from_numpy(cs.scale * (q[0, h, sel] @ kt[0, 0][sel]))
+        assert abs(float(torch.logsumexp(logits, 0)) - float(res["lse"][0, h])) <= 2e-6 * abs(float(res["lse"][0, h]))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_attn_dropped_position_identity(mode):
+    cs = W.attn_case(2, 50, Hq=8, Hkv=2, D=16, seed=3, n_hot=5)
+    _, _, v = _qkv_f64(cs)
+    full = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.5, 1.0, mode, want=("out_d", "p"))
+    for r_pos in (0.1, 0.25, 0.5, 0.9):
+        red = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.5, r_pos, mode, want=("out_d", "p"))
+        assert np.array_equal(red["dim_idx"], full["dim_idx"])
+        G = 4
+        for b in range(2):
+            for h in range(8):
+                sg = h // G if mode == 0 else h
+                keep = set(red["pos_idx"][b, sg].tolist())
+                drop = [s for s in range(50) if s not in keep]
+                rhs = full["p"][b, h, drop] @ v[b, h // G][drop]
+                lhs = full["out_d"][b, h] - red["out_d"][b, h]
+                assert np.max(np.abs(lhs - rhs)) <= 1e-12 * np.max(np.abs(full["out_d"][b, h]))
+                assert full["p"][b, h, sorted(keep)].sum() <= 1.0 + 1e-12
+
+
+def _dim_scores(cs, b, heads, g):
+    qa = np.abs(W.bf16_bits_to_f32(cs.q[b, heads])).max(axis=0)
+    return qa * cs.kn[b, g]  # float32 multiply, as the definition
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_attn_selections_brute_force(mode):
+    for seed in range(12):
+        cs = W.attn_case(1, 12, Hq=4, Hkv=1, D=12, seed=seed, n_hot=2)
+        for kd in range(1, 13, 3):
+            for ks in range(1, 13):
+                res = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, kd / 12, ks / 12, mode,
+                                         want=("pi", "p"))
+                groups = [[0, 1, 2, 3]] if mode == 0 else [[h] for h in range(4)]
+                for sg, heads in enumerate(groups):
+                    sig = _dim_scores(cs, 0, heads, 0)
+                    assert list(res["dim_idx"][0, sg]) == _brute_topk(sig, kd)
+                    pi = res["pi"][0, sg]
+                    assert np.array_equal(pi, res["p"][0, heads].max(axis=0))
+                    assert list(res["pos_idx"][0, sg]) == _brute_topk(pi, ks)
+
+
+def test_attn_mode1_equals_mode0_without_grouping():
+    cs = W.attn_case(1, 30, Hq=2, Hkv=2, D=16, seed=4, n_hot=2)
+    a = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.5, 0.5, 0)
+    b = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.5, 0.5, 1)
+    for key in ("out", "dim_idx", "pos_idx", "lse"):
+        assert np.array_equal(a[key], b[key])
+
+
+def test_attn_strided_cache_equals_packed():
+    # ldk/ldv larger than S (a cache with spare capacity) gives the same result as packed buffers
+    cs = W.attn_case(1, 40, Hq=4, Hkv=2, D=16, seed=6, n_hot=3)
+    ktp = np.zeros((1, 2, 16, 64), np.uint16)
+    ktp[..., :40] = cs.kt
+    vp = np.zeros((1, 2, 56, 16), np.uint16)
+    vp[:, :, :40] = cs.v
+    a = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.5, 0.25, 0)
+    b = oracle.attn_decode(cs.q, ktp, vp, cs.kn, cs.scale, 0.5, 0.25, 0, S=40)
+    for key in ("out", "dim_idx", "pos_idx", "lse"):
+        assert np.array_equal(a[key], b[key])
