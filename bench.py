@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Benchmark of the RMM (Reduced Matrix Multiplication) hot path on one MI355X.
+
+Headline (the JSON line's `value`): retained-work HBM throughput of one decode
+step of a Llama-3-8B-shaped MLP down projection, X[1,14336] bf16 times
+W^T[14336,4096] bf16, at retention ratio r = 0.5: rmm_select (scorer + top-k)
+followed by rmm_linear (reduced streaming GEMV).  Retained bytes per step are
+the bytes the method must move (x and c for the scorer, the index list written
+and read, the kept W^T rows, y).  Every step reads a different copy of the
+inputs, cycling through copies totalling more than twice the 256 MB Infinity
+Cache, so the figures are HBM figures, not cache figures.
+
+The same line carries, under "sweep", every r of the decode shape, the prefill
+shape (bf16 MFMA, TFLOP/s on retained FLOPs) and the GQA attention-decode
+shapes (microseconds per call), each next to the dense r = 1 kernels; the
+roofline of the dominant kernel (the reduced GEMV) measured with HIP events on
+the launch stream; and the CPU oracle timed on this host as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--headline-only]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MALL_BYTES = 256 * 2**20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-sweep", action="store_true", help="headline shape only (all four r)")
+    p.add_argument("--headline-only", action="store_true", help="only r = 0.5 of the decode shape (profiling)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def n_copies(bytes_per_copy: int, touched_per_step: int) -> int:
+    """Copies to cycle through so that one full cycle touches > 2x the MALL."""
+    n = math.ceil(2 * MALL_BYTES / max(1, touched_per_step)) + 1
+    cap = max(2, int(6e9 // max(1, bytes_per_copy)))
+    return max(2, min(n, cap, 64))
+
+
+def time_loop(fn, steps, warmup, torch):
+    """Seconds per step of `fn(i)`: `warmup` eager steps, then `steps` steps
+    captured into one HIP graph and replayed once between two synchronizations
+    (device time of back-to-back steps, free of Python launch overhead)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def event_avg(fn, steps, torch, warmup=3):
+    """Average duration per launch of the work `fn(i)` enqueues, from HIP events
+    recorded on the launch stream around a graph of `steps` back-to-back launches."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps * 1e-3
+
+
+def eager_event_avg(fn, steps, torch, warmup=3):
+    """Average duration per call of `fn(i)` launched eagerly back to back (for
+    library calls kept out of graphs), from HIP events around the whole loop."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps * 1e-3
+
+
+def eager_loop(fn, steps, torch):
+    """Seconds per step with one Python call per step (host launch overhead included)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def src_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, sha: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported (see DESIGN.md for how "
+              f"it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import input_adaptive_reduced_score_amd as rmm
+    from input_adaptive_reduced_score_amd import accounting as A
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rmm.lib()
+    steps, warmup = args.steps, args.warmup
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    sweep = []
+
+    # ------------------------------------------------------------------ decode down_proj
+    log("[bench] decode down_proj: generating inputs")
+    dc = W.linear_decode()
+    K, M = dc.K, dc.M
+    x0, w0, c0 = bf(dc.x), bf(dc.wt), torch.from_numpy(dc.c).to(dev)
+    ncp = n_copies(w0.numel() * 2, 2 * rmm.keep_count(K, 0.25) * M)
+    xs = [x0.clone() for _ in range(ncp)]
+    ws_ = [w0 if i == 0 else w0.clone() for i in range(ncp)]
+    cs_ = [c0.clone() for _ in range(ncp)]
+    del w0
+    log(f"[bench] decode: {ncp} input copies ({ncp * K * M * 2 / 1e9:.2f} GB) rotate per step")
+    rs = (0.5,) if args.headline_only else (0.25, 0.5, 0.75, 1.0)
+    head = None
+    for r in rs:
+        k = rmm.keep_count(K, r)
+        idxb = [torch.empty((1, k), dtype=torch.int32, device=dev) for _ in range(ncp)]
+        yb = torch.empty((1, M), dtype=torch.float32, device=dev)
+        for i in range(ncp):
+            rmm.select(xs[i], cs_[i], 1, r, idx=idxb[i])
+
+        def step(i):
+            j = i % ncp
+            rmm.select(xs[j], cs_[j], 1, r, idx=idxb[j])
+            rmm.linear(xs[j], ws_[j], idxb[j], 1, out=yb)
+
+        t_step = time_loop(step, steps, warmup, torch)
+        t_eager = eager_loop(step, min(steps, 50), torch)
+        t_gemv = event_avg(lambda i: rmm.linear(xs[i % ncp], ws_[i % ncp], idxb[i % ncp], 1, out=yb), steps, torch)
+        t_sel = event_avg(lambda i: rmm.select(xs[i % ncp], cs_[i % ncp], 1, r, idx=idxb[i % ncp]), steps, torch)
+        rec = {"workload": "decode_down_proj", "r": r, "k": k,
+               "step_us": t_step * 1e6, "eager_step_us": t_eager * 1e6, "select_us": t_sel * 1e6,
+               "gemv_us": t_gemv * 1e6,
+               "retained_bytes": A.decode_step_bytes(K, M, k),
+               "step_GBps": A.decode_step_bytes(K, M, k) / t_step / 1e9,
+               "gemv_GBps": A.gemv_launch_bytes(k, M) / t_gemv / 1e9}
+        rec["gemv_frac_hbm"] = rec["gemv_GBps"] / A.HBM_PEAK_GBS
+        sweep.append(rec)
+        log(f"[bench] decode r={r}: step {rec['step_us']:.2f} us ({rec['step_GBps']:.0f} GB/s), gemv "
+            f"{rec['gemv_us']:.2f} us ({rec['gemv_GBps']:.0f} GB/s), select {rec['select_us']:.2f} us")
+        if r == 0.5:
+            head = rec
+    if not args.headline_only:
+        t_dense = event_avg(lambda i: rmm.linear_dense(xs[i % ncp], ws_[i % ncp], out=yb), steps, torch)
+        t_blas = eager_event_avg(lambda i: torch.matmul(xs[i % ncp], ws_[i % ncp]), min(steps, 50), torch)
+        sweep.append({"workload": "decode_down_proj_dense", "r": 1.0, "gemv_us": t_dense * 1e6,
+                      "gemv_GBps": A.gemv_launch_bytes(K, M) / t_dense / 1e9, "torch_matmul_us": t_blas * 1e6})
+        log(f"[bench] decode dense GEMV {t_dense * 1e6:.2f} us, torch.matmul (hipBLASLt) {t_blas * 1e6:.2f} us")
+    del xs, ws_, cs_
+
+    # ------------------------------------------------------------------ prefill (MFMA)
+    if not args.no_sweep and not args.headline_only:
+        log("[bench] prefill: generating inputs")
+        pc = W.linear_prefill()
+        T, K2, M2, tile = pc.T, pc.K, pc.M, pc.tile
+        xp0, wp0, cp0 = bf(pc.x), bf(pc.wt), torch.from_numpy(pc.c).to(dev)
+        npc = n_copies(xp0.numel() * 2 + wp0.numel() * 2, xp0.numel() * 2 + wp0.numel() * 2 + T * M2 * 4)
+        xps = [xp0 if i == 0 else xp0.clone() for i in range(npc)]
+        wps = [wp0 if i == 0 else wp0.clone() for i in range(npc)]
+        cps = [cp0.clone() for _ in range(npc)]
+        yp = torch.empty((T, M2), dtype=torch.float32, device=dev)
+        ps = max(10, steps // 4)
+        for r in (0.25, 0.5, 0.75, 1.0):
+            k = rmm.keep_count(K2, r)
+            idxp = [rmm.select(xps[i], cps[i], tile, r) for i in range(npc)]
+
+            def pstep(i):
+                j = i % npc
+                rmm.select(xps[j], cps[j], tile, r, idx=idxp[j])
+                rmm.linear(xps[j], wps[j], idxp[j], tile, out=yp)
+
+            t_step = time_loop(pstep, ps, max(3, warmup // 4), torch)
+            t_lin = event_avg(lambda i: rmm.linear(xps[i % npc], wps[i % npc], idxp[i % npc], tile, out=yp), ps,
+                              torch)
+            fl = A.linear_flops(T, k, M2)
+            rec = {"workload": "prefill", "r": r, "k": k, "step_us": t_step * 1e6, "linear_us": t_lin * 1e6,
+                   "retained_flops": fl, "step_TFLOPs": fl / t_step / 1e12, "linear_TFLOPs": fl / t_lin / 1e12}
+            rec["linear_frac_mfma"] = rec["linear_TFLOPs"] / A.BF16_MFMA_PEAK_TFLOPS
+            sweep.append(rec)
+            log(f"[bench] prefill r={r}: step {rec['step_us']:.1f} us, linear (gather+MFMA) {rec['linear_us']:.1f} "
+                f"us = {rec['linear_TFLOPs']:.0f} TFLOP/s ({100 * rec['linear_frac_mfma']:.1f}% of bf16 peak)")
+        t_dense = event_avg(lambda i: rmm.linear_dense(xps[i % npc], wps[i % npc], out=yp), ps, torch)
+        t_blas = eager_event_avg(lambda i: torch.matmul(xps[i % npc], wps[i % npc]), ps, torch)
+        fl = A.linear_flops(T, K2, M2)
+        sweep.append({"workload": "prefill_dense", "r": 1.0, "linear_us": t_dense * 1e6,
+                      "linear_TFLOPs": fl / t_dense / 1e12, "torch_matmul_us": t_blas * 1e6,
+                      "torch_matmul_TFLOPs": fl / t_blas / 1e12})
+        log(f"[bench] prefill dense MFMA {t_dense * 1e6:.1f} us ({fl / t_dense / 1e12:.0f} TFLOP/s), torch.matmul "
+            f"{t_blas * 1e6:.1f} us ({fl / t_blas / 1e12:.0f} TFLOP/s)")
+        del xps, wps, cps, yp
+
+    # ------------------------------------------------------------------ attention decode
+    if not args.no_sweep and not args.headline_only:
+        for name, mk, pairs in (("attn_gqa_32k", W.attn_32k, ((0.25, 0.25), (0.5, 0.5), (1.0, 1.0))),
+                                ("attn_gqa_128k_b4", W.attn_128k, ((0.5, 0.25),))):
+            log(f"[bench] {name}: generating inputs")
+            ac = mk()
+            B, Hq, Hkv, D, S = ac.B, ac.Hq, ac.Hkv, ac.D, ac.S
+            q0, k0, v0, kn0 = bf(ac.q), bf(ac.kt), bf(ac.v), torch.from_numpy(ac.kn).to(dev)
+            kvbytes = (k0.numel() + v0.numel()) * 2
+            nac = n_copies(kvbytes, kvbytes // 3)
+            qs = [q0.clone() for _ in range(nac)]
+            ks_ = [k0 if i == 0 else k0.clone() for i in range(nac)]
+            vs_ = [v0 if i == 0 else v0.clone() for i in range(nac)]
+            kns = [kn0.clone() for _ in range(nac)]
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+            asteps = max(10, steps // 4) if S <= 32768 else max(5, steps // 20)
+            for rd, rp in pairs:
+                kd, kss = rmm.keep_count(D, rd), rmm.keep_count(S, rp)
+
+                def astep(i):
+                    j = i % nac
+                    rmm.attn_decode(qs[j], ks_[j], vs_[j], kns[j], rd, rp, scale=ac.scale, out=out, want_idx=False)
+
+                t = time_loop(astep, asteps, 3, torch)
+                by = A.attn_step_bytes(B, Hq, Hkv, D, S, kd, kss)
+                rec = {"workload": name, "r_dim": rd, "r_pos": rp, "kd": kd, "ks": kss, "call_us": t * 1e6,
+                       "retained_bytes": by, "GBps": by / t / 1e9, "frac_hbm": by / t / 1e9 / A.HBM_PEAK_GBS}
+                sweep.append(rec)
+                log(f"[bench] {name} r=({rd},{rp}): {rec['call_us']:.1f} us, {rec['GBps']:.0f} GB/s retained")
+            t = time_loop(lambda i: rmm.attn_decode_dense(qs[i % nac], ks_[i % nac], vs_[i % nac], scale=ac.scale,
+                                                          out=out), asteps, 3, torch)
+            by = A.attn_dense_bytes(B, Hq, Hkv, D, S)
+            sweep.append({"workload": name + "_dense", "call_us": t * 1e6, "bytes": by, "GBps": by / t / 1e9})
+            log(f"[bench] {name} dense flash-decode: {t * 1e6:.1f} us ({by / t / 1e9:.0f} GB/s)")
+            del qs, ks_, vs_, kns, q0, k0, v0
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        k = oracle.keep_count(dc.K, 0.5)
+        n, t0 = 0, time.perf_counter()
+        while True:
+            idx = oracle.select(dc.x, dc.c, 1, 0.5)
+            oracle.linear(dc.x, dc.wt, idx, 1)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds and n >= 3:
+                break
+        cpu = {"value": A.decode_step_bytes(dc.K, dc.M, k) * n / el / 1e9, "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{n} full decode steps (select + reduced product, r=0.5, X[1,14336] x W^T[14336,4096] "
+                         f"bf16) of the single-threaded C oracle, {el:.1f} s"}
+        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s retained ({n} steps in {el:.1f} s)")
+
+    k_head = head["k"]
+    sha = src_hash(["input_adaptive_reduced_score_amd/csrc/linear.hip", "input_adaptive_reduced_score_amd/csrc/device.h",
+                    "input_adaptive_reduced_score_amd/csrc/kernels.h"])
+    roofline = {"kernel": "gemv_kernel<bf16,NT=1> (reduced streaming GEMV)", "bound": "hbm",
+                "achieved": head["gemv_GBps"], "peak": A.HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": head["gemv_GBps"] / A.HBM_PEAK_GBS,
+                "algorithmic_bytes_per_launch": A.gemv_launch_bytes(k_head, M),
+                "avg_launch_us": head["gemv_us"],
+                "traffic": load_traffic("gemv_decode_r0.5", sha), "source_sha": sha}
+    line = {
+        "metric": "retained-work HBM GB/s & MFMA TFLOP/s vs r; reduced attn-decode us at S=32K",
+        "value": head["step_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": head["step_us"] * 1e-3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_down_proj: select + reduced GEMV, X[1,14336] bf16 = silu(a)*b, "
+                               "W^T[14336,4096] bf16 ~N(0,0.02), r=0.5 (k=7168), cold-cache input rotation",
+                   "r": 0.5, "K": K, "M": M, "T": 1, "accumulate": "fp32", "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

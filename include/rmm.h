@@ -1,0 +1,171 @@
+/*
+ * rmm.h -- C ABI of librmm.so, the MI355X (gfx950) hot path of Reduced Matrix
+ * Multiplication (RMM).
+ *
+ * RMM ("Reduced Matrix Multiplication: Input-Adaptive Matrix-Product Reduction
+ * for LLM Inference", paper abstract) scores the slices of a matrix product's
+ * contraction dimension from the current input, keeps the ceil(r*K) best under
+ * a retention ratio r, and multiplies over those slices only; weights are not
+ * modified.  The cf-1.com blog on input-adaptive matrix-product reduction gives
+ * the problem statement (section 2: Y = X @ W^T, X [T,H], W [M,H]), the flow
+ * (sections 5.1-5.3: cheap score, top-k, gather, compact product) and a code
+ * sketch (section 6.1: inputs and a keep ratio in, the product and the kept
+ * index list out, output shape equal to the dense one).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) owned
+ *    by the caller; the library never allocates or frees memory and keeps no
+ *    per-call state between calls.
+ *  - Matrices are row-major with a leading dimension (elements between rows);
+ *    a [rows][ld] matrix spans rows*ld elements.  Input matrices (x, W^T, keys,
+ *    values, q) must be 16-byte aligned and their leading dimensions a multiple
+ *    of 8 elements for bf16 / 4 for fp32; fp32 outputs need only 4-byte
+ *    alignment and any leading dimension.
+ *  - bf16 data are raw bfloat16 bit patterns (uint16).  fp32 is IEEE binary32.
+ *  - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
+ *    results are valid once the stream reaches this point; inputs must stay
+ *    unchanged until then.
+ *  - Workspace: `ws` is caller-owned device memory of at least the size the
+ *    matching *_workspace_size query returns.  Its first RMM_WS_HEADER_BYTES
+ *    bytes hold completion counters: they must be zero before a workspace is
+ *    used for the first time (e.g. allocate it zero-filled); every call leaves
+ *    them zero again when it completes.  The same workspace may serve all entry
+ *    points, but two calls must not use one workspace concurrently.
+ *  - Errors: arguments are validated on the host before anything is enqueued;
+ *    on any non-OK status nothing has been written.  RMM_EHIP reports a launch
+ *    failure (text in rmm_last_error()).  No exception crosses the ABI, and the
+ *    library never aborts.  Non-finite inputs give unspecified results.
+ */
+#ifndef RMM_H
+#define RMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RMM_WS_HEADER_BYTES 4096
+
+typedef enum {
+    RMM_OK = 0,
+    RMM_EINVAL = 1,        /* bad argument: null pointer, size, ratio, stride */
+    RMM_EUNSUPPORTED = 2,  /* valid, but no kernel for this shape / dtype / alignment */
+    RMM_EWORKSPACE = 3,    /* workspace missing or smaller than the size query */
+    RMM_EHIP = 4           /* a HIP launch failed */
+} rmm_status_t;
+
+typedef enum { RMM_F32 = 0, RMM_BF16 = 1 } rmm_dtype_t;
+
+/* Selection groups for grouped-query attention.  PER_KV_GROUP: the G = Hq/Hkv
+ * query heads sharing one KV head share one head_dim selection and one key
+ * position selection (scores take the max over those heads).  PER_Q_HEAD:
+ * each query head selects alone (the KV rows of a group are then read once per
+ * query head). */
+typedef enum { RMM_SEL_PER_KV_GROUP = 0, RMM_SEL_PER_Q_HEAD = 1 } rmm_sel_mode_t;
+
+/* ------------------------------------------------------------------ keep count
+ * Paper abstract ("retention-ratio control"): k = ceil(r*n) slices are kept.
+ * r*n is snapped to the nearest integer when within 1e-9 relative of it, then
+ * clamped to [1, n].  Host-only, pure.  Returns -1 if n < 1 or r is not in (0,1]. */
+int64_t rmm_keep_count(int64_t n, double r);
+
+/* ------------------------------------------------------------------ select
+ * Scorer + top-k selector (blog sections 5.1-5.2; paper abstract).
+ * Tokens are grouped into tiles of `tile` consecutive rows, tile tau covering
+ * rows [tau*tile, min(T, (tau+1)*tile)); all tokens of a tile share one kept
+ * set.  For each tile and slice j < K:
+ *     s[j] = fl32( max_{t in tile} |x[t,j]| * c[j] )        (one fp32 multiply)
+ * The k = rmm_keep_count(K, r) slices of largest s are kept (equal scores: the
+ * lower index wins; -0 ranks as +0) and written in ASCENDING index order.
+ *   x    [T][ldx] fp32 or bf16 activations (xt), ldx >= K
+ *   c    [K] fp32 per-slice weights, c[j] >= 0 (the norm of W^T row j)
+ *   idx  out, int32 [ceil(T/tile)][k]
+ * Limits: K <= 32768.  Deterministic: equal inputs give equal outputs. */
+size_t rmm_select_workspace_size(int64_t T, int64_t K, int64_t tile, rmm_dtype_t xt);
+rmm_status_t rmm_select(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int64_t ldx,
+                        const float *c, int64_t tile, double r,
+                        int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ linear
+ * Reduced product (blog sections 2 and 5.3; paper abstract):
+ *     y[t,m] = sum_{j in idx[t/tile]} x[t,j] * wt[j,m]      (fp32 accumulation)
+ * W^T is stored K-major ([K][ldw], row j = the weights slice j multiplies), so
+ * every kept slice is one contiguous row; nothing is gathered into a copy of W.
+ * Output shape equals the dense one (blog section 6.1).
+ *   x   [T][ldx] activations, dtype xt;  wt [K][ldw], dtype must equal xt
+ *   idx [ceil(T/tile)][k] int32, strictly ascending, each < K (as rmm_select
+ *       writes it; contents are trusted)
+ *   y   out, fp32 [T][ldy], ldy >= M
+ * bf16 with >= 32 tokens per tile runs on MFMA tiles; otherwise a streaming
+ * kernel (any T) runs.  Deterministic. */
+size_t rmm_linear_workspace_size(int64_t T, int64_t K, int64_t M, int64_t k, int64_t tile,
+                                 rmm_dtype_t xt);
+rmm_status_t rmm_linear(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int64_t ldx,
+                        const void *wt, rmm_dtype_t wt_t, int64_t M, int64_t ldw,
+                        const int32_t *idx, int64_t k, int64_t tile,
+                        float *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dense product y = x @ wt over all K slices, by the same kernels without the
+ * index list (the r = 1 baseline; blog section 8 asks for a full path next to
+ * the compact one).  Same arguments and rules as rmm_linear. */
+size_t rmm_linear_dense_workspace_size(int64_t T, int64_t K, int64_t M, rmm_dtype_t xt);
+rmm_status_t rmm_linear_dense(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int64_t ldx,
+                              const void *wt, rmm_dtype_t wt_t, int64_t M, int64_t ldw,
+                              float *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ attention decode
+ * Reduced grouped-query attention for one decode step (blog sections 3.1 and
+ * 3.3; GEMM notes section 1: scores = Q K^T, out = softmax(scores) V).
+ * Query head h reads KV head g = h / G, G = Hq / Hkv.  Per batch element b and
+ * selection group (mode above):
+ *  1. head_dim slices: sigma_j = fl32( max_{h in group} |q[b,h,j]| * kn[b,g,j] );
+ *     the k_d = rmm_keep_count(D, r_dim) best are kept (ties: lower index);
+ *  2. logits l_h[s] = scale * sum_{j kept} q[b,h,j] * K[b,g,s,j], every s < S;
+ *  3. full softmax over all S positions: p_h[s] = exp(l_h[s] - lse_h);
+ *  4. key positions: pi_s = max_{h in group} p_h[s]; the k_s = rmm_keep_count(S,
+ *     r_pos) best are kept (ranked by max_h (l_h[s] - lse_h) held as a fixed-point
+ *     log-probability with 2^-25 resolution clamped at -128; ties: lower index);
+ *  5. out[b,h,:] = sum_{s kept} p_h[s] * V[b,g,s,:]  -- no renormalisation.
+ *   q   bf16 [B][Hq][D]
+ *   kt  bf16 [B][Hkv][D][ldk]  keys stored dim-major: row j holds dim j of every position
+ *   v   bf16 [B][Hkv][ldv][D]  values position-major
+ *   kn  fp32 [B][Hkv][D]       kn[b,g,j] = L2 norm of K[b,g,0:S,j] (kept by the cache owner)
+ *   scale  logit scale (1/sqrt(D) for standard attention; not rescaled by k_d)
+ *   out     out, fp32 [B][Hq][D]
+ *   dim_idx optional out (NULL ok), int32 [B][Hsel][k_d] ascending
+ *   pos_idx optional out (NULL ok), int32 [B][Hsel][k_s] ascending
+ *   lse     optional out (NULL ok), fp32 [B][Hq] = log sum_s exp(l_h[s])
+ *   Hsel = Hkv (PER_KV_GROUP) or Hq (PER_Q_HEAD).
+ * Limits: D == 128, Hq/Hkv in {1,2,4,8}, S <= 2^24, ldk/ldv multiples of 8.
+ * Deterministic. */
+size_t rmm_attn_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,
+                                      double r_dim, double r_pos, rmm_sel_mode_t mode);
+rmm_status_t rmm_attn_decode(const void *q, const void *kt, const void *v, const float *kn,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,
+                             int64_t ldk, int64_t ldv, float scale,
+                             double r_dim, double r_pos, rmm_sel_mode_t mode,
+                             float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dense decode attention (all D dims, all S positions, online softmax) -- the
+ * r = 1 baseline.  Same layouts; lse optional. */
+size_t rmm_attn_decode_dense_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S);
+rmm_status_t rmm_attn_decode_dense(const void *q, const void *kt, const void *v,
+                                   int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,
+                                   int64_t ldk, int64_t ldv, float scale,
+                                   float *out, float *lse, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------ errors */
+const char *rmm_status_string(rmm_status_t s);
+/* detail of the last non-OK status returned on the calling thread */
+const char *rmm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RMM_H */

@@ -1,0 +1,274 @@
+"""Python binding of librmm.so, the MI355X (gfx950) hot path of Reduced Matrix
+Multiplication (RMM).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``librmm.so`` (see ``include/rmm.h`` for the semantics of each call).  PyTorch
+provides device memory and the current stream.  There is no CPU or PyTorch
+fallback: if the library is missing or the device is not a GPU, calls raise.
+
+Names follow the C ABI: ``keep_count``, ``select``, ``linear``,
+``linear_dense``, ``attn_decode``, ``attn_decode_dense``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_PATH = os.path.join(HERE, "librmm.so")
+SOURCES = ["select.hip", "linear.hip", "attn.hip", "api.hip"]
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+RMM_F32, RMM_BF16 = 0, 1
+PER_KV_GROUP, PER_Q_HEAD = 0, 1
+STATUS = {0: "RMM_OK", 1: "RMM_EINVAL", 2: "RMM_EUNSUPPORTED", 3: "RMM_EWORKSPACE", 4: "RMM_EHIP"}
+WS_HEADER_BYTES = 4096
+
+
+class RmmError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+def build(out: str = LIB_PATH, extra_flags=(), jobs: int = 4) -> str:
+    """Compile every HIP source for gfx950 and link librmm.so (in-tree)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = os.path.join(ROOT, "include")
+    procs, objs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, f"-I{inc}", "-c", os.path.join(HERE, "csrc", src), "-o", obj]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        if len(procs) >= jobs:
+            _wait(procs.pop(0))
+    for p in procs:
+        _wait(p)
+    tmp = out + ".tmp"
+    subprocess.run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], check=True,
+                   stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    os.replace(tmp, out)
+    return out
+
+
+def _wait(item):
+    cmd, p = item
+    txt, _ = p.communicate()
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({p.returncode}): {' '.join(cmd)}\n{txt.decode(errors='replace')}")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load librmm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() (hipcc, gfx950) first")
+            L = C.CDLL(LIB_PATH)
+            vp, i64, i32, dbl, sz, flt = C.c_void_p, C.c_int64, C.c_int, C.c_double, C.c_size_t, C.c_float
+            sig = {
+                "rmm_keep_count": (i64, [i64, dbl]),
+                "rmm_select_workspace_size": (sz, [i64, i64, i64, i32]),
+                "rmm_select": (i32, [vp, i32, i64, i64, i64, vp, i64, dbl, vp, vp, sz, vp]),
+                "rmm_linear_workspace_size": (sz, [i64, i64, i64, i64, i64, i32]),
+                "rmm_linear": (i32, [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, i64, i64, vp, i64, vp, sz, vp]),
+                "rmm_linear_dense_workspace_size": (sz, [i64, i64, i64, i32]),
+                "rmm_linear_dense": (i32, [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, i64, vp, sz, vp]),
+                "rmm_attn_decode_workspace_size": (sz, [i64, i64, i64, i64, i64, dbl, dbl, i32]),
+                "rmm_attn_decode": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, flt, dbl, dbl, i32,
+                                          vp, vp, vp, vp, vp, sz, vp]),
+                "rmm_attn_decode_dense_workspace_size": (sz, [i64, i64, i64, i64, i64]),
+                "rmm_attn_decode_dense": (i32, [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, flt, vp, vp, vp, sz,
+                                                vp]),
+                "rmm_status_string": (C.c_char_p, [i32]),
+                "rmm_last_error": (C.c_char_p, []),
+            }
+            for name, (res, args) in sig.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+    return _lib
+
+
+EXPORTS = ("rmm_keep_count", "rmm_select_workspace_size", "rmm_select", "rmm_linear_workspace_size", "rmm_linear",
+           "rmm_linear_dense_workspace_size", "rmm_linear_dense", "rmm_attn_decode_workspace_size",
+           "rmm_attn_decode", "rmm_attn_decode_dense_workspace_size", "rmm_attn_decode_dense", "rmm_status_string",
+           "rmm_last_error")
+
+
+def _check(st: int):
+    if st != 0:
+        raise RmmError(st, lib().rmm_last_error().decode(errors="replace"))
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RMM_F32
+    if t.dtype == torch.bfloat16:
+        return RMM_BF16
+    raise TypeError(f"tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise RuntimeError(f"{name} must be a GPU tensor (the RMM path has no CPU fallback)")
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("matrices must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Workspace:
+    """A zero-initialised device workspace, grown on demand (per device)."""
+
+    def __init__(self):
+        self._bufs = {}
+
+    def get(self, nbytes: int, device) -> torch.Tensor:
+        key = torch.device(device).index
+        buf = self._bufs.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+            self._bufs[key] = buf
+        return buf
+
+
+_WS = Workspace()
+
+
+def keep_count(n: int, r: float) -> int:
+    return int(lib().rmm_keep_count(int(n), float(r)))
+
+
+def select(x: torch.Tensor, c: torch.Tensor, tile: int, r: float, idx: torch.Tensor | None = None, ws=None):
+    """Scorer + top-k: returns idx int32 [ceil(T/tile), keep_count(K, r)], ascending per tile."""
+    L = lib()
+    _dev(x, "x")
+    T, K = x.shape
+    k = keep_count(K, r)
+    if k < 0:
+        raise RmmError(1, f"retention ratio {r} not in (0, 1]")
+    nt = -(-T // tile)
+    if idx is None:
+        idx = torch.empty((nt, k), dtype=torch.int32, device=x.device)
+    need = L.rmm_select_workspace_size(T, K, tile, _dtype(x))
+    w = ws if ws is not None else _WS.get(need, x.device)
+    _check(L.rmm_select(_ptr(x), _dtype(x), T, K, _ld(x), _ptr(c), tile, float(r), _ptr(idx), _ptr(w),
+                        w.numel() * w.element_size(), _stream()))
+    return idx
+
+
+def linear(x: torch.Tensor, wt: torch.Tensor, idx: torch.Tensor, tile: int, out: torch.Tensor | None = None,
+           ws=None):
+    """Reduced product y = sum over kept slices of x[t, j] * wt[j, :]  (fp32 [T, M])."""
+    L = lib()
+    _dev(x, "x")
+    T, K = x.shape
+    M = wt.shape[1]
+    k = idx.shape[1]
+    if out is None:
+        out = torch.empty((T, M), dtype=torch.float32, device=x.device)
+    need = L.rmm_linear_workspace_size(T, K, M, k, tile, _dtype(x))
+    w = ws if ws is not None else _WS.get(need, x.device)
+    _check(L.rmm_linear(_ptr(x), _dtype(x), T, K, _ld(x), _ptr(wt), _dtype(wt), M, _ld(wt), _ptr(idx), k, tile,
+                        _ptr(out), _ld(out), _ptr(w), w.numel() * w.element_size(), _stream()))
+    return out
+
+
+def linear_dense(x: torch.Tensor, wt: torch.Tensor, out: torch.Tensor | None = None, ws=None):
+    """Dense product y = x @ wt over all slices by the same kernels (r = 1 baseline)."""
+    L = lib()
+    _dev(x, "x")
+    T, K = x.shape
+    M = wt.shape[1]
+    if out is None:
+        out = torch.empty((T, M), dtype=torch.float32, device=x.device)
+    need = L.rmm_linear_dense_workspace_size(T, K, M, _dtype(x))
+    w = ws if ws is not None else _WS.get(need, x.device)
+    _check(L.rmm_linear_dense(_ptr(x), _dtype(x), T, K, _ld(x), _ptr(wt), _dtype(wt), M, _ld(wt), _ptr(out),
+                              _ld(out), _ptr(w), w.numel() * w.element_size(), _stream()))
+    return out
+
+
+def attn_decode(q, kt, v, kn, r_dim: float, r_pos: float, scale: float | None = None, mode: int = PER_KV_GROUP,
+                S: int | None = None, out=None, dim_idx=None, pos_idx=None, lse=None, want_idx: bool = True,
+                ws=None):
+    """Reduced GQA decode attention.  q [B,Hq,D] bf16; kt [B,Hkv,D,ldk] bf16 (dim-major keys);
+    v [B,Hkv,ldv,D] bf16; kn [B,Hkv,D] fp32.  Returns (out, dim_idx, pos_idx, lse)."""
+    L = lib()
+    _dev(q, "q")
+    B, Hq, D = q.shape
+    Hkv, ldk = kt.shape[1], kt.shape[3]
+    ldv = v.shape[2]
+    S = ldk if S is None else S
+    for t, n in ((q, "q"), (kt, "kt"), (v, "v"), (kn, "kn")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    Hsel = Hkv if mode == PER_KV_GROUP else Hq
+    kd, ks = keep_count(D, r_dim), keep_count(S, r_pos)
+    if kd < 0 or ks < 0:
+        raise RmmError(1, "ratios must be in (0, 1]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    if want_idx:
+        if dim_idx is None:
+            dim_idx = torch.empty((B, Hsel, kd), dtype=torch.int32, device=dev)
+        if pos_idx is None:
+            pos_idx = torch.empty((B, Hsel, ks), dtype=torch.int32, device=dev)
+        if lse is None:
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = L.rmm_attn_decode_workspace_size(B, Hq, Hkv, D, S, float(r_dim), float(r_pos), mode)
+    w = ws if ws is not None else _WS.get(need, dev)
+    _check(L.rmm_attn_decode(_ptr(q), _ptr(kt), _ptr(v), _ptr(kn), B, Hq, Hkv, D, S, ldk, ldv, scale, float(r_dim),
+                             float(r_pos), mode, _ptr(out), _ptr(dim_idx), _ptr(pos_idx), _ptr(lse), _ptr(w),
+                             w.numel() * w.element_size(), _stream()))
+    return out, dim_idx, pos_idx, lse
+
+
+def attn_decode_dense(q, kt, v, scale: float | None = None, S: int | None = None, out=None, lse=None, ws=None):
+    """Dense decode attention over all dims and positions (r = 1 baseline).  Returns (out, lse)."""
+    L = lib()
+    _dev(q, "q")
+    B, Hq, D = q.shape
+    Hkv, ldk = kt.shape[1], kt.shape[3]
+    ldv = v.shape[2]
+    S = ldk if S is None else S
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    need = L.rmm_attn_decode_dense_workspace_size(B, Hq, Hkv, D, S)
+    w = ws if ws is not None else _WS.get(need, dev)
+    _check(L.rmm_attn_decode_dense(_ptr(q), _ptr(kt), _ptr(v), B, Hq, Hkv, D, S, ldk, ldv, scale, _ptr(out),
+                                   _ptr(lse), _ptr(w), w.numel() * w.element_size(), _stream()))
+    return out, lse

@@ -1,0 +1,891 @@
+// Reduced grouped-query attention decode.
+//
+// Blog on input-adaptive matrix-product reduction: section 3.1 (most past keys
+// matter little to the current query: skip low-contribution work along the
+// sequence), section 3.3 (reduce inside each head, never drop a head);
+// paper abstract (keep informative slices of each product's contraction
+// dimension: head_dim for Q K^T, key positions for P V).  GEMM notes section 1:
+// scores = Q K^T, out = softmax(scores) V.
+//
+// Pipeline per (batch element, selection group), four launches on one stream:
+//  qk    : head_dim selection (one wave, bitwise search over ballots), then
+//          unscaled logits over the kept dims for 8 positions per lane from
+//          dim-major keys (a kept dim is one contiguous row), per-chunk
+//          softmax statistics; the last workgroup of the group merges them into
+//          lse (double) and clears the group's key histogram.
+//  keys  : position score max_h (scale*a_h[s] - lse_h) in double, stored as a
+//          fixed-point log-probability key; 4096-bin histogram of the top bits.
+//  select: one workgroup per group: threshold bin from the histogram, two
+//          radix passes over the keys, then kept/tie counts per PV chunk.
+//  pv    : each workgroup takes a chunk of positions, keeps the selected ones
+//          (order-preserving), streams their V rows and accumulates p*V; the
+//          last workgroup sums the chunk partials in a fixed order.
+#include "device.h"
+#include "kernels.h"
+#include "radix.h"
+
+namespace rmm {
+
+constexpr int D = ATTN_D;
+constexpr int QK_U = 16;      // kept key rows in flight per lane
+constexpr int PV_SUB = 512;   // positions examined per PV sub-chunk
+constexpr int PV_MAX_CHUNKS = 32;
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, WAVE));
+    return v;
+}
+template <typename F> __device__ __forceinline__ F wave_sum(F v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, WAVE);
+    return v;
+}
+
+// Keeps the kd largest of 128 keys held two per lane (j = lane, lane + 64),
+// ties to the lower index, and writes the kept indices in ascending order.
+__device__ __forceinline__ void wave_select128(uint32_t key0, uint32_t key1, int kd, int *jd)
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+    // largest v with #(key >= v) >= kd: the kd-th largest key
+    uint32_t v = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = v | (1u << bit);
+        const int c = __popcll(__ballot(key0 >= cand)) + __popcll(__ballot(key1 >= cand));
+        if (c >= kd)
+            v = cand;
+    }
+    const int gt = __popcll(__ballot(key0 > v)) + __popcll(__ballot(key1 > v));
+    const int quota = kd - gt;
+    const uint64_t e0 = __ballot(key0 == v), e1 = __ballot(key1 == v);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int r0 = __popcll(e0 & lt), r1 = __popcll(e0) + __popcll(e1 & lt);
+    const bool keep0 = key0 > v || (key0 == v && r0 < quota);
+    const bool keep1 = key1 > v || (key1 == v && r1 < quota);
+    const uint64_t k0 = __ballot(keep0), k1 = __ballot(keep1);
+    if (keep0)
+        jd[__popcll(k0 & lt)] = lane;
+    if (keep1)
+        jd[__popcll(k0) + __popcll(k1 & lt)] = lane + WAVE;
+}
+
+// ------------------------------------------------------------------ qk
+template <int GS>
+__global__ __launch_bounds__(WAVE) void attn_qk_kernel(AttnShape s, int Sp, const uint16_t *__restrict__ q,
+                                                       const uint16_t *__restrict__ kt, const float *__restrict__ kn,
+                                                       float *__restrict__ logit, float2 *__restrict__ pstat,
+                                                       double *__restrict__ lse_ws, float *__restrict__ lse_out,
+                                                       int32_t *__restrict__ dim_idx_out, uint32_t *__restrict__ hist,
+                                                       uint32_t *__restrict__ cnt)
+{
+    __shared__ int jd[D];
+    __shared__ float qs[GS][D];
+    __shared__ uint32_t last;
+    const int lane = threadIdx.x;
+    const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel;
+    const int h0 = sg * s.GS, g = h0 / s.G;
+    const int chunk = blockIdx.x, nchunk = gridDim.x;
+    const uint16_t *qb = q + ((int64_t)b * s.Hq + h0) * D;
+
+    // 1. head_dim selection: sigma_j = fl32(max_h |q_h[j]| * kn[j])
+    {
+        uint32_t key[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int j = lane + WAVE * half;
+            float a = 0.0f;
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+                a = fmaxf(a, fabsf(bf16_to_f32(qb[hh * D + j])));
+            key[half] = nonneg_key(__fmul_rn(a, kn[((int64_t)b * s.Hkv + g) * D + j]));
+        }
+        wave_select128(key[0], key[1], s.kd, jd);
+    }
+    __syncthreads();
+    for (int i = lane; i < s.kd; i += WAVE) {
+        const int j = jd[i];
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh)
+            qs[hh][i] = bf16_to_f32(qb[hh * D + j]);
+        if (chunk == 0 && dim_idx_out)
+            dim_idx_out[(int64_t)grp * s.kd + i] = j;
+    }
+    __syncthreads();
+
+    // 2. unscaled dot products over the kept dims (ascending), 8 positions per lane
+    const int sp = chunk * ATTN_QK_CHUNK + lane * 8;
+    const bool act = sp < s.S;
+    float acc[GS][8];
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[hh][e] = 0.0f;
+    if (act) {
+        const uint16_t *kbase = kt + ((int64_t)b * s.Hkv + g) * D * s.ldk + sp;
+        for (int i0 = 0; i0 < s.kd; i0 += QK_U) {
+            uint4 u[QK_U];
+#pragma unroll
+            for (int qq = 0; qq < QK_U; ++qq)
+                if (i0 + qq < s.kd)
+                    u[qq] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)jd[i0 + qq] * s.ldk);
+#pragma unroll
+            for (int qq = 0; qq < QK_U; ++qq) {
+                if (i0 + qq < s.kd) {
+                    float v[8];
+                    Vec16<uint16_t>::unpack(u[qq], v);
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh) {
+                        const float qv = qs[hh][i0 + qq];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[hh][e] = fmaf(qv, v[e], acc[hh][e]);
+                    }
+                }
+            }
+        }
+    }
+
+    // 3. logits and per-chunk softmax statistics (max, sum exp) per head
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+        if (act) {
+            float *dst = logit + ((int64_t)b * s.Hq + h0 + hh) * Sp + sp;
+            reinterpret_cast<f32x4_t *>(dst)[0] = f32x4_t{acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]};
+            reinterpret_cast<f32x4_t *>(dst)[1] = f32x4_t{acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]};
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (sp + e < s.S)
+                mx = fmaxf(mx, acc[hh][e]);
+        mx = wave_max(mx);
+        float z = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (sp + e < s.S)
+                z += expf(s.scale * (acc[hh][e] - mx));
+        z = wave_sum(z);
+        if (lane == 0)
+            pstat[((int64_t)b * s.Hq + h0 + hh) * nchunk + chunk] = make_float2(mx, z);
+    }
+
+    // 4. the last workgroup of this group merges the statistics into lse
+    __threadfence();
+    __syncthreads();
+    if (lane == 0)
+        last = atomicInc(&cnt[grp], (uint32_t)(nchunk - 1)) == (uint32_t)(nchunk - 1);
+    __syncthreads();
+    if (!last)
+        return;
+    __threadfence();
+#pragma unroll 1
+    for (int hh = 0; hh < GS; ++hh) {
+        const float2 *ps = pstat + ((int64_t)b * s.Hq + h0 + hh) * nchunk;
+        float M = -INFINITY;
+        for (int i = lane; i < nchunk; i += WAVE)
+            M = fmaxf(M, ps[i].x);
+        M = wave_max(M);
+        double zs = 0.0;
+        for (int i = lane; i < nchunk; i += WAVE) {
+            const float2 st = ps[i];
+            zs += (double)st.y * exp((double)s.scale * ((double)st.x - (double)M));
+        }
+        zs = wave_sum(zs);
+        if (lane == 0) {
+            const double l = (double)s.scale * (double)M + log(zs);
+            lse_ws[(int64_t)b * s.Hq + h0 + hh] = l;
+            if (lse_out)
+                lse_out[(int64_t)b * s.Hq + h0 + hh] = (float)l;
+        }
+    }
+    for (int i = lane; i < ATTN_HIST_BINS; i += WAVE)
+        hist[(int64_t)grp * ATTN_HIST_BINS + i] = 0;
+}
+
+// ------------------------------------------------------------------ keys
+// Position key: max over the group's heads of the log-probability
+// scale*a_h[s] - lse_h (double), as fixed point floor((L + 128) * 2^25), clamped.
+__device__ __forceinline__ uint32_t logprob_key(double L)
+{
+    const double t = (L + 128.0) * 33554432.0;
+    if (!(t > 0.0))
+        return 0u;
+    if (t >= 4294967295.0)
+        return 0xffffffffu;
+    return (uint32_t)t;
+}
+
+template <int GS>
+__global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, const float *__restrict__ logit,
+                                                       const double *__restrict__ lse_ws, uint32_t *__restrict__ keys,
+                                                       uint32_t *__restrict__ hist)
+{
+    __shared__ uint32_t lh[ATTN_HIST_BINS];
+    const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS;
+    for (int i = threadIdx.x; i < ATTN_HIST_BINS; i += 256)
+        lh[i] = 0;
+    double lse[GS];
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+        lse[hh] = lse_ws[(int64_t)b * s.Hq + h0 + hh];
+    __syncthreads();
+    const int sp = blockIdx.x * ATTN_KEY_CHUNK + threadIdx.x * 8;
+    if (sp < s.S) {
+        f32x4_t a[GS][2];
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh) {
+            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(logit + ((int64_t)b * s.Hq + h0 + hh) * Sp + sp);
+            a[hh][0] = src[0];
+            a[hh][1] = src[1];
+        }
+        uint32_t kk[8];
+        const double sc = (double)s.scale;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            double m = sc * (double)a[0][e >> 2][e & 3] - lse[0];
+#pragma unroll
+            for (int hh = 1; hh < GS; ++hh)
+                m = fmax(m, sc * (double)a[hh][e >> 2][e & 3] - lse[hh]);
+            kk[e] = logprob_key(m);
+            if (sp + e < s.S)
+                atomicAdd(&lh[kk[e] >> 20], 1u);
+        }
+        uint4 *dst = reinterpret_cast<uint4 *>(keys + (int64_t)grp * Sp + sp);
+        dst[0] = uint4{kk[0], kk[1], kk[2], kk[3]};
+        dst[1] = uint4{kk[4], kk[5], kk[6], kk[7]};
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < ATTN_HIST_BINS; i += 256)
+        if (lh[i])
+            atomicAdd(&hist[(int64_t)grp * ATTN_HIST_BINS + i], lh[i]);
+}
+
+// ------------------------------------------------------------------ select
+// Threshold key thr and tie quota of the group, then per PV chunk c (P
+// positions): info[c] = (kept before the chunk, ties at thr before the chunk).
+// Fast path: the 4096-bin histogram names the bin holding the k-th key; one
+// pass over the keys counts, per chunk, the keys in higher bins and collects
+// the bin's keys (candidates) into LDS, where the last 20 bits are resolved.
+// If the bin holds more than CAND_CAP keys, two radix passes over all keys and
+// a counting pass run instead.
+struct SelInfo {
+    uint32_t thr, quota;
+};
+constexpr int CAND_CAP = 8192;
+
+__global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, int P, int npv,
+                                                           const uint32_t *__restrict__ keys,
+                                                           const uint32_t *__restrict__ hist, SelInfo *__restrict__ sel,
+                                                           uint2 *__restrict__ info)
+{
+    __shared__ uint32_t h2[SEL_BINS];
+    __shared__ uint32_t tmp[64];
+    __shared__ uint32_t cgt[PV_MAX_CHUNKS], ceq[PV_MAX_CHUNKS];
+    __shared__ uint32_t ckey[CAND_CAP];
+    __shared__ int cpos[CAND_CAP];
+    __shared__ uint32_t ncand;
+    const int grp = blockIdx.x;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const uint32_t *K = keys + (int64_t)grp * Sp;
+    const uint32_t *H = hist + (int64_t)grp * ATTN_HIST_BINS;
+    uint32_t krem = (uint32_t)s.ks;
+    const uint32_t d = hist_crossing(H, ATTN_HIST_BINS, krem, tmp);
+    const uint32_t nbin = H[d];
+    if (threadIdx.x < PV_MAX_CHUNKS) {
+        cgt[threadIdx.x] = 0;
+        ceq[threadIdx.x] = 0;
+    }
+    if (threadIdx.x == 0)
+        ncand = 0;
+    __syncthreads();
+    const uint4 *k4 = reinterpret_cast<const uint4 *>(K);
+    const int n4 = (int)((s.S + 3) / 4), step = 1024;
+    uint32_t thr, quota;
+    if (nbin <= (uint32_t)CAND_CAP) {
+        for (int i0 = threadIdx.x; i0 < n4; i0 += 8 * step) {
+            uint4 u[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (i0 + q * step < n4)
+                    u[q] = k4[i0 + q * step];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int i = i0 + q * step; // a wave covers 256 consecutive positions: one chunk
+                if (i0 + q * step - lane >= n4)
+                    break;
+                const uint32_t kk[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+                int ngt = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * i + e;
+                    const bool ok = i < n4 && j < s.S;
+                    const uint32_t top = kk[e] >> 20;
+                    ngt += __popcll(__ballot(ok && top > d));
+                    if (ok && top == d) {
+                        const uint32_t slot = atomicAdd(&ncand, 1u);
+                        ckey[slot] = kk[e];
+                        cpos[slot] = j;
+                    }
+                }
+                if (lane == 0 && ngt)
+                    atomicAdd(&cgt[(4 * (i - lane)) / P], (uint32_t)ngt);
+            }
+        }
+        __syncthreads();
+        uint32_t prefix = d << 20, pmask = 0xfff00000u;
+        radix_pass(ckey, (int)nbin, prefix, pmask, 10, 10, krem, h2, tmp);
+        radix_pass(ckey, (int)nbin, prefix, pmask, 0, 10, krem, h2, tmp);
+        thr = prefix;
+        quota = krem;
+        for (int i = threadIdx.x; i < (int)nbin; i += 1024) {
+            if (ckey[i] > thr)
+                atomicAdd(&cgt[cpos[i] / P], 1u);
+            else if (ckey[i] == thr)
+                atomicAdd(&ceq[cpos[i] / P], 1u);
+        }
+    } else {
+        uint32_t prefix = d << 20, pmask = 0xfff00000u;
+        radix_pass_v4(K, (int)s.S, prefix, pmask, 10, 10, krem, h2, tmp);
+        radix_pass_v4(K, (int)s.S, prefix, pmask, 0, 10, krem, h2, tmp);
+        thr = prefix;
+        quota = krem;
+        for (int i0 = threadIdx.x; i0 < n4; i0 += 8 * step) {
+            uint4 u[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (i0 + q * step < n4)
+                    u[q] = k4[i0 + q * step];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int i = i0 + q * step;
+                if (i0 + q * step - lane >= n4)
+                    break;
+                const uint32_t kk[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+                int ngt = 0, neq = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * i + e;
+                    const bool ok = i < n4 && j < s.S;
+                    ngt += __popcll(__ballot(ok && kk[e] > thr));
+                    neq += __popcll(__ballot(ok && kk[e] == thr));
+                }
+                if (lane == 0) {
+                    if (ngt)
+                        atomicAdd(&cgt[(4 * (i - lane)) / P], (uint32_t)ngt);
+                    if (neq)
+                        atomicAdd(&ceq[(4 * (i - lane)) / P], (uint32_t)neq);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t gacc = 0, eacc = 0;
+        uint2 *o = info + (int64_t)grp * npv;
+        for (int c = 0; c < npv; ++c) {
+            o[c] = make_uint2(gacc + min(eacc, quota), eacc);
+            gacc += cgt[c];
+            eacc += ceq[c];
+        }
+        sel[grp].thr = thr;
+        sel[grp].quota = quota;
+    }
+}
+
+// ------------------------------------------------------------------ pv
+// One workgroup per (chunk of P positions, group).  4 waves; each wave
+// quarter (16 lanes) holds one 256-byte V row, 8 dims per lane.
+template <int GS>
+__global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P, const uint16_t *__restrict__ v,
+                                                      const float *__restrict__ logit, const double *__restrict__ lse_ws,
+                                                      const uint32_t *__restrict__ keys, const SelInfo *__restrict__ sel,
+                                                      const uint2 *__restrict__ info, int32_t *__restrict__ pos_out,
+                                                      float *__restrict__ part, float *__restrict__ out,
+                                                      uint32_t *__restrict__ cnt)
+{
+    __shared__ int rows[PV_SUB];
+    __shared__ float pr[GS][PV_SUB];
+    __shared__ uint32_t wtot[2][4];
+    __shared__ float red[4][GS][D];
+    __shared__ uint32_t last;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS, g = h0 / s.G;
+    const int c = blockIdx.x, npv = gridDim.x;
+    const uint32_t thr = sel[grp].thr, quota = sel[grp].quota;
+    const uint2 inf = info[(int64_t)grp * npv + c];
+    uint32_t kept_before = inf.x, ties_before = inf.y;
+    float lsef[GS];
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+        lsef[hh] = (float)lse_ws[(int64_t)b * s.Hq + h0 + hh];
+    const uint32_t *K = keys + (int64_t)grp * Sp;
+    const uint16_t *vb = v + ((int64_t)b * s.Hkv + g) * s.ldv * D;
+    const int quarter = lane >> 4, dl = lane & 15;
+
+    float acc[GS][8];
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[hh][e] = 0.0f;
+
+    const int p0 = c * P, p1 = min((int)s.S, p0 + P);
+    for (int sb = p0; sb < p1; sb += PV_SUB) {
+        // order-preserving selection of this sub-chunk: thread tid covers positions sb + 2*tid, +1
+        const int j0 = sb + 2 * tid;
+        uint32_t ka = j0 < p1 ? K[j0] : 0u, kb = j0 + 1 < p1 ? K[j0 + 1] : 0u;
+        const bool va = j0 < p1, vbb = j0 + 1 < p1;
+        const bool ea = va && ka == thr, eb = vbb && kb == thr;
+        // tie ranks (index order) across the block
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const uint64_t ma = __ballot(ea), mb = __ballot(eb);
+        // positions are interleaved a,b per thread: ties before (tid, a) = ties of lower lanes (both) + none
+        uint32_t tie_lane = __popcll(ma & lt) + __popcll(mb & lt);
+        if (lane == 0)
+            wtot[0][w] = __popcll(ma) + __popcll(mb);
+        __syncthreads();
+        uint32_t tie_w = 0;
+        for (int i = 0; i < w; ++i)
+            tie_w += wtot[0][i];
+        const uint32_t ra = ties_before + tie_w + tie_lane;
+        const uint32_t rb = ra + (ea ? 1u : 0u);
+        const bool keepa = va && (ka > thr || (ea && ra < quota));
+        const bool keepb = vbb && (kb > thr || (eb && rb < quota));
+        uint32_t sub_ties = 0;
+        for (int i = 0; i < 4; ++i)
+            sub_ties += wtot[0][i];
+        const uint64_t qa = __ballot(keepa), qb = __ballot(keepb);
+        const uint32_t kept_lane = __popcll(qa & lt) + __popcll(qb & lt);
+        if (lane == 0)
+            wtot[1][w] = __popcll(qa) + __popcll(qb);
+        __syncthreads();
+        uint32_t kept_w = 0, nkept = 0;
+        for (int i = 0; i < 4; ++i) {
+            if (i < w)
+                kept_w += wtot[1][i];
+            nkept += wtot[1][i];
+        }
+        const uint32_t oa = kept_w + kept_lane, ob = oa + (keepa ? 1u : 0u);
+        if (keepa)
+            rows[oa] = j0;
+        if (keepb)
+            rows[ob] = j0 + 1;
+        __syncthreads();
+        // probabilities of the kept rows, and the optional index output
+        for (int r = tid; r < (int)nkept; r += 256) {
+            const int sidx = rows[r];
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+                pr[hh][r] = expf(fmaf(s.scale, logit[((int64_t)b * s.Hq + h0 + hh) * Sp + sidx], -lsef[hh]));
+            if (pos_out)
+                pos_out[(int64_t)grp * s.ks + kept_before + r] = sidx;
+        }
+        __syncthreads();
+        // stream kept V rows: wave w, quarter q handles rows w*4 + q, +16, ...
+        for (int r0 = w * 4 + quarter; r0 < (int)nkept; r0 += 16 * 4) {
+            uint4 u[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int r = r0 + 16 * qq;
+                if (r < (int)nkept)
+                    u[qq] = *reinterpret_cast<const uint4 *>(vb + (int64_t)rows[r] * D + dl * 8);
+            }
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int r = r0 + 16 * qq;
+                if (r < (int)nkept) {
+                    float vv[8];
+                    Vec16<uint16_t>::unpack(u[qq], vv);
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh) {
+                        const float p = pr[hh][r];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[hh][e] = fmaf(p, vv[e], acc[hh][e]);
+                    }
+                }
+            }
+        }
+        kept_before += nkept;
+        ties_before += sub_ties;
+        __syncthreads();
+    }
+
+    // reduce the four quarters of each wave, then the four waves (fixed order)
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = acc[hh][e];
+            x += __shfl_xor(x, 16, WAVE);
+            x += __shfl_xor(x, 32, WAVE);
+            acc[hh][e] = x;
+        }
+    if (quarter == 0) {
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                red[w][hh][dl * 8 + e] = acc[hh][e];
+    }
+    __syncthreads();
+    float *mine = part + ((int64_t)grp * npv + c) * GS * D;
+    for (int i = tid; i < GS * D; i += 256) {
+        const int hh = i / D, dd = i % D;
+        mine[i] = ((red[0][hh][dd] + red[1][hh][dd]) + red[2][hh][dd]) + red[3][hh][dd];
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0)
+        last = atomicInc(&cnt[ATTN_MAX_GROUPS + grp], (uint32_t)(npv - 1)) == (uint32_t)(npv - 1);
+    __syncthreads();
+    if (!last)
+        return;
+    __threadfence();
+    const float *pb = part + (int64_t)grp * npv * GS * D;
+    for (int i = tid; i < GS * D; i += 256) {
+        float vals[PV_MAX_CHUNKS];
+#pragma unroll
+        for (int cc = 0; cc < PV_MAX_CHUNKS; ++cc)
+            vals[cc] = cc < npv ? pb[(int64_t)cc * GS * D + i] : 0.0f;
+        float acc2 = 0.0f;
+#pragma unroll
+        for (int cc = 0; cc < PV_MAX_CHUNKS; ++cc)
+            acc2 += vals[cc];
+        const int hh = i / D, dd = i % D;
+        out[((int64_t)b * s.Hq + h0 + hh) * D + dd] = acc2;
+    }
+}
+
+// ------------------------------------------------------------------ host side
+static void pv_chunks(int64_t S, int *P, int *npv)
+{
+    int64_t n = (S + PV_SUB - 1) / PV_SUB;
+    if (n > PV_MAX_CHUNKS)
+        n = PV_MAX_CHUNKS;
+    int64_t per = (S + n - 1) / n;
+    per = (per + PV_SUB - 1) / PV_SUB * PV_SUB;
+    *P = (int)per;
+    *npv = (int)((S + per - 1) / per);
+}
+
+static inline char *align256(char *p) { return (char *)(((uintptr_t)p + 255) & ~(uintptr_t)255); }
+
+size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base)
+{
+    const int64_t Sp = (s.S + 7) / 8 * 8;
+    const int64_t nqk = (s.S + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK;
+    const int64_t G = s.B * s.Hsel;
+    int P, npv;
+    pv_chunks(s.S, &P, &npv);
+    char *p = base + RMM_WS_HEADER_BYTES_INTERNAL;
+    AttnWs w;
+    w.cnt = (uint32_t *)base;
+    w.logit = (float *)p;
+    p = align256(p + (size_t)(s.B * s.Hq * Sp) * 4);
+    w.pstat = (float2 *)p;
+    p = align256(p + (size_t)(s.B * s.Hq * nqk) * 8);
+    w.lse = (double *)p;
+    p = align256(p + (size_t)(s.B * s.Hq) * 8);
+    w.keys = (uint32_t *)p;
+    p = align256(p + (size_t)(G * Sp) * 4);
+    w.hist = (uint32_t *)p;
+    p = align256(p + (size_t)(G * ATTN_HIST_BINS) * 4);
+    w.pos = (int32_t *)p; // SelInfo [G] then chunk info [G][npv]
+    p = align256(p + (size_t)G * sizeof(SelInfo) + (size_t)(G * npv) * sizeof(uint2) + 256);
+    w.pvpart = (float *)p;
+    p = align256(p + (size_t)(G * npv * s.GS * D) * 4);
+    if (ws)
+        *ws = w;
+    return (size_t)(p - base);
+}
+
+template <int GS>
+static hipError_t attn_run(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v,
+                           const float *kn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
+                           const AttnWs &ws, hipStream_t st)
+{
+    const int Sp = (int)((s.S + 7) / 8 * 8);
+    const int G = (int)(s.B * s.Hsel);
+    const int nqk = (int)((s.S + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK);
+    int P, npv;
+    pv_chunks(s.S, &P, &npv);
+    SelInfo *sel = reinterpret_cast<SelInfo *>(ws.pos);
+    uint2 *info = reinterpret_cast<uint2 *>(align256((char *)(sel + G)));
+    attn_qk_kernel<GS><<<dim3(nqk, G), WAVE, 0, st>>>(s, Sp, q, kt, kn, ws.logit, ws.pstat, ws.lse, lse, dim_idx,
+                                                      ws.hist, ws.cnt);
+    attn_key_kernel<GS><<<dim3((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK, G), 256, 0, st>>>(s, Sp, ws.logit, ws.lse,
+                                                                                              ws.keys, ws.hist);
+    attn_select_kernel<<<G, 1024, 0, st>>>(s, Sp, P, npv, ws.keys, ws.hist, sel, info);
+    attn_pv_kernel<GS><<<dim3(npv, G), 256, 0, st>>>(s, Sp, P, v, ws.logit, ws.lse, ws.keys, sel, info, pos_idx,
+                                                     ws.pvpart, out, ws.cnt);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v, const float *kn,
+                       float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse, const AttnWs &ws, hipStream_t st)
+{
+    switch (s.GS) {
+    case 1:
+        return attn_run<1>(s, q, kt, v, kn, out, dim_idx, pos_idx, lse, ws, st);
+    case 2:
+        return attn_run<2>(s, q, kt, v, kn, out, dim_idx, pos_idx, lse, ws, st);
+    case 4:
+        return attn_run<4>(s, q, kt, v, kn, out, dim_idx, pos_idx, lse, ws, st);
+    case 8:
+        return attn_run<8>(s, q, kt, v, kn, out, dim_idx, pos_idx, lse, ws, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+// ------------------------------------------------------------------ dense flash decode (r = 1 baseline)
+// One workgroup per (span of positions, KV head): QK over all D dims (waves
+// split the dims), online softmax over 512-position sub-chunks, P V; partial
+// (max, sum, o) per span; the last workgroup rescales and sums in a fixed order.
+constexpr int DN_SUB = 512;
+constexpr int DN_MAX_SPANS = 64;
+
+template <int G>
+__global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, int span, const uint16_t *__restrict__ q,
+                                                         const uint16_t *__restrict__ kt, const uint16_t *__restrict__ v,
+                                                         float *__restrict__ part, float2 *__restrict__ stat,
+                                                         float *__restrict__ out, float *__restrict__ lse_out,
+                                                         uint32_t *__restrict__ cnt)
+{
+    __shared__ float qs[G][D];
+    __shared__ float lg[4][G][DN_SUB]; // per-wave partial dots, then wave 0's slot holds the sums
+    __shared__ float red[4][G][D];
+    __shared__ float mrun[G], zrun[G], fac[G];
+    __shared__ uint32_t last;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    const int grp = blockIdx.y, b = grp / s.Hkv, g = grp % s.Hkv, h0 = g * G;
+    const int c = blockIdx.x, nspan = gridDim.x;
+    for (int i = tid; i < G * D; i += 256)
+        qs[i / D][i % D] = bf16_to_f32(q[((int64_t)b * s.Hq + h0) * D + i]);
+    if (tid < G) {
+        mrun[tid] = -INFINITY;
+        zrun[tid] = 0.0f;
+    }
+    const uint16_t *kb = kt + ((int64_t)b * s.Hkv + g) * D * s.ldk;
+    const uint16_t *vb = v + ((int64_t)b * s.Hkv + g) * s.ldv * D;
+    const int quarter = lane >> 4, dl = lane & 15;
+    float o[G][8];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            o[hh][e] = 0.0f;
+    __syncthreads();
+    const int p0 = c * span, p1 = min((int)s.S, p0 + span);
+    for (int sb = p0; sb < p1; sb += DN_SUB) {
+        // QK: wave w takes dims [32w, 32w+32) for 8 positions per lane
+        const int sp = sb + lane * 8;
+        float a[G][8];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                a[hh][e] = 0.0f;
+        if (sp < p1) {
+            for (int j0 = 32 * w; j0 < 32 * w + 32; j0 += 16) {
+                uint4 u[16];
+#pragma unroll
+                for (int qq = 0; qq < 16; ++qq)
+                    u[qq] = *reinterpret_cast<const uint4 *>(kb + (int64_t)(j0 + qq) * s.ldk + sp);
+#pragma unroll
+                for (int qq = 0; qq < 16; ++qq) {
+                    float kv[8];
+                    Vec16<uint16_t>::unpack(u[qq], kv);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) {
+                        const float qv = qs[hh][j0 + qq];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            a[hh][e] = fmaf(qv, kv[e], a[hh][e]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                lg[w][hh][lane * 8 + e] = a[hh][e];
+        __syncthreads();
+        // logits (scaled), sub-chunk max per head, new running max
+        for (int i = tid; i < G * DN_SUB; i += 256) {
+            const int hh = i / DN_SUB, r = i % DN_SUB;
+            const float l = ((lg[0][hh][r] + lg[1][hh][r]) + lg[2][hh][r]) + lg[3][hh][r];
+            lg[0][hh][r] = sb + r < p1 ? s.scale * l : -INFINITY;
+        }
+        __syncthreads();
+        for (int hh = w; hh < G; hh += 4) {
+            float m = -INFINITY;
+            for (int r = lane; r < DN_SUB; r += WAVE)
+                m = fmaxf(m, lg[0][hh][r]);
+            m = wave_max(m);
+            if (lane == 0) {
+                const float mn = fmaxf(mrun[hh], m);
+                fac[hh] = expf(mrun[hh] - mn);
+                mrun[hh] = mn;
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < G * DN_SUB; i += 256) {
+            const int hh = i / DN_SUB, r = i % DN_SUB;
+            lg[1][hh][r] = expf(lg[0][hh][r] - mrun[hh]);
+        }
+        __syncthreads();
+        for (int hh = w; hh < G; hh += 4) {
+            float z = 0.0f;
+            for (int r = lane; r < DN_SUB; r += WAVE)
+                z += lg[1][hh][r];
+            z = wave_sum(z);
+            if (lane == 0)
+                zrun[hh] = zrun[hh] * fac[hh] + z;
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                o[hh][e] *= fac[hh];
+        // P V over this sub-chunk's rows
+        const int nr = min(DN_SUB, p1 - sb);
+        for (int r0 = w * 4 + quarter; r0 < nr; r0 += 64) {
+            uint4 u[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int r = r0 + 16 * qq;
+                if (r < nr)
+                    u[qq] = *reinterpret_cast<const uint4 *>(vb + (int64_t)(sb + r) * D + dl * 8);
+            }
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int r = r0 + 16 * qq;
+                if (r < nr) {
+                    float vv[8];
+                    Vec16<uint16_t>::unpack(u[qq], vv);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) {
+                        const float p = lg[1][hh][r];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            o[hh][e] = fmaf(p, vv[e], o[hh][e]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = o[hh][e];
+            x += __shfl_xor(x, 16, WAVE);
+            x += __shfl_xor(x, 32, WAVE);
+            o[hh][e] = x;
+        }
+    if (quarter == 0) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                red[w][hh][dl * 8 + e] = o[hh][e];
+    }
+    __syncthreads();
+    float *mine = part + ((int64_t)grp * nspan + c) * G * D;
+    for (int i = tid; i < G * D; i += 256) {
+        const int hh = i / D, dd = i % D;
+        mine[i] = ((red[0][hh][dd] + red[1][hh][dd]) + red[2][hh][dd]) + red[3][hh][dd];
+    }
+    if (tid < G)
+        stat[((int64_t)grp * nspan + c) * G + tid] = make_float2(mrun[tid], zrun[tid]);
+    __threadfence();
+    __syncthreads();
+    if (tid == 0)
+        last = atomicInc(&cnt[grp], (uint32_t)(nspan - 1)) == (uint32_t)(nspan - 1);
+    __syncthreads();
+    if (!last)
+        return;
+    __threadfence();
+    for (int i = tid; i < G * D; i += 256) {
+        const int hh = i / D, dd = i % D;
+        float M = -INFINITY;
+        for (int cc = 0; cc < nspan; ++cc)
+            M = fmaxf(M, stat[((int64_t)grp * nspan + cc) * G + hh].x);
+        float num = 0.0f, den = 0.0f;
+        for (int cc = 0; cc < nspan; ++cc) {
+            const float2 st2 = stat[((int64_t)grp * nspan + cc) * G + hh];
+            const float f = expf(st2.x - M);
+            num += f * part[((int64_t)grp * nspan + cc) * G * D + i];
+            den += f * st2.y;
+        }
+        out[((int64_t)b * s.Hq + h0 + hh) * D + dd] = num / den;
+        if (lse_out && dd == 0)
+            lse_out[(int64_t)b * s.Hq + h0 + hh] = M + logf(den);
+    }
+}
+
+static void dense_spans(int64_t S, int *span, int *nspan)
+{
+    int64_t n = (S + DN_SUB - 1) / DN_SUB;
+    if (n > DN_MAX_SPANS)
+        n = DN_MAX_SPANS;
+    int64_t per = (S + n - 1) / n;
+    per = (per + DN_SUB - 1) / DN_SUB * DN_SUB;
+    *span = (int)per;
+    *nspan = (int)((S + per - 1) / per);
+}
+
+size_t attn_dense_ws_layout(int64_t B, int64_t Hq, int64_t S, char *base, float **part, float2 **stat,
+                            uint32_t **cnt)
+{
+    int span, nspan;
+    dense_spans(S, &span, &nspan);
+    char *p = base + RMM_WS_HEADER_BYTES_INTERNAL;
+    if (cnt)
+        *cnt = (uint32_t *)base;
+    if (part)
+        *part = (float *)p;
+    p = align256(p + (size_t)(B * Hq * nspan * D) * 4);
+    if (stat)
+        *stat = (float2 *)p;
+    p = align256(p + (size_t)(B * Hq * nspan) * 8);
+    return (size_t)(p - base);
+}
+
+hipError_t launch_attn_dense(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v, float *out,
+                             float *lse, float *part, float2 *stat, uint32_t *cnt, hipStream_t st)
+{
+    int span, nspan;
+    dense_spans(s.S, &span, &nspan);
+    dim3 grid(nspan, (unsigned)(s.B * s.Hkv));
+    switch (s.G) {
+    case 1:
+        attn_dense_kernel<1><<<grid, 256, 0, st>>>(s, span, q, kt, v, part, stat, out, lse, cnt);
+        break;
+    case 2:
+        attn_dense_kernel<2><<<grid, 256, 0, st>>>(s, span, q, kt, v, part, stat, out, lse, cnt);
+        break;
+    case 4:
+        attn_dense_kernel<4><<<grid, 256, 0, st>>>(s, span, q, kt, v, part, stat, out, lse, cnt);
+        break;
+    case 8:
+        attn_dense_kernel<8><<<grid, 256, 0, st>>>(s, span, q, kt, v, part, stat, out, lse, cnt);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+void attn_init() {}
+
+} // namespace rmm

@@ -1,0 +1,76 @@
+// Device helpers for the RMM kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmm {
+
+constexpr int WAVE = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// element loads for the two storage types (bf16 bits in uint16_t, or float)
+__device__ __forceinline__ float ld_elem(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ float ld_elem(const float *p, int64_t i) { return p[i]; }
+
+// 16-byte vector of a row: 8 bf16 or 4 fp32 values, unpacked to float
+template <typename TE> struct Vec16;
+template <> struct Vec16<uint16_t> {
+    static constexpr int N = 8;
+    __device__ __forceinline__ static void load(const uint16_t *p, float (&v)[8]) {
+        uint4 u = *reinterpret_cast<const uint4 *>(p);
+        v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
+        v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+        v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
+        v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+    }
+    __device__ __forceinline__ static uint4 raw(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ static void unpack(uint4 u, float (&v)[8]) {
+        v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
+        v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+        v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
+        v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+    }
+};
+template <> struct Vec16<float> {
+    static constexpr int N = 4;
+    __device__ __forceinline__ static uint4 raw(const float *p) { return *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ static void unpack(uint4 u, float (&v)[4]) {
+        v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+        v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+    }
+};
+
+// Inclusive prefix sum over the whole block (blockDim.x threads, multiple of 64).
+// `tmp` holds at least blockDim.x/64 words of LDS.  Contains barriers: every
+// thread of the block must call it.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *tmp)
+{
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE, nw = blockDim.x / WAVE;
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+        uint32_t n = __shfl_up(v, off, WAVE);
+        if (lane >= off)
+            v += n;
+    }
+    if (lane == WAVE - 1)
+        tmp[w] = v;
+    __syncthreads();
+    uint32_t add = 0;
+    for (int i = 0; i < w && i < nw; ++i)
+        add += tmp[i];
+    __syncthreads();
+    return v + add;
+}
+
+// Non-negative float -> order-preserving uint32 key; -0 ranks as +0.
+__device__ __forceinline__ uint32_t nonneg_key(float s) { return __float_as_uint(s) & 0x7fffffffu; }
+
+} // namespace rmm

@@ -1,0 +1,91 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// ---- tuning constants (compile-time; override with -D for sweeps)
+#ifndef SELECT_DIRECT_ROWS
+#define SELECT_DIRECT_ROWS 16 // tiles with at most this many rows are scored inside the select kernel
+#endif
+#ifndef COLMAX_ROWS
+#define COLMAX_ROWS 64 // rows per column-max workgroup for larger tiles
+#endif
+#define SELECT_MAX_K 32768
+
+#ifndef GEMV_UNROLL
+#define GEMV_UNROLL 8
+#endif
+#ifndef GEMV_TARGET_WGS
+#define GEMV_TARGET_WGS 512
+#endif
+#ifndef GEMV_MIN_ROWS
+#define GEMV_MIN_ROWS 32
+#endif
+#ifndef GEMV_MAX_SPLIT
+#define GEMV_MAX_SPLIT 64
+#endif
+#define GEMV_ROWS_CAP 2048
+#define GEMV_MAX_COUNTERS 1024
+#define MFMA_MIN_TILE_ROWS 32 // bf16 tiles with at least this many tokens use the MFMA GEMM
+
+#define ATTN_D 128
+#define ATTN_QK_CHUNK 512   // positions per QK workgroup
+#define ATTN_KEY_CHUNK 2048 // positions per key/histogram workgroup
+#define ATTN_HIST_BINS 4096 // first radix level over the top 12 key bits
+#ifndef ATTN_PV_ROWS
+#define ATTN_PV_ROWS 128 // kept positions per PV workgroup (target)
+#endif
+#define ATTN_MAX_GROUPS 512 // B * Hsel limit (two counter banks in the workspace header)
+#define RMM_WS_HEADER_BYTES_INTERNAL 4096
+
+namespace rmm {
+
+// select.hip
+size_t select_ws_bytes(int64_t T, int64_t K, int64_t tile);
+size_t select_lds_bytes(int64_t K);
+hipError_t launch_select(const void *x, bool bf16, int64_t T, int64_t K, int64_t ldx, const float *c, int64_t tile,
+                         int64_t k, int32_t *idx, float *pmax_ws, hipStream_t st);
+void select_init();
+
+// linear.hip
+size_t gemv_ws_bytes(int64_t T, int64_t M, int64_t k, int64_t tile, bool bf16);
+hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const void *wt, int64_t ldw, int64_t M,
+                       const int32_t *idx, int64_t k, int64_t tile, bool dense, float *y, int64_t ldy, float *part,
+                       uint32_t *cnt, hipStream_t st);
+size_t gemm_ws_bytes(int64_t T, int64_t k);
+hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const void *wt, int64_t ldw, int64_t M,
+                       const int32_t *idx, int64_t k, int64_t tile, bool dense, float *y, int64_t ldy, void *xg,
+                       hipStream_t st);
+void linear_init();
+
+// attn.hip
+struct AttnShape {
+    int64_t B, Hq, Hkv, S, ldk, ldv;
+    int G;      // query heads per KV head
+    int GS;     // query heads per selection group (G or 1)
+    int Hsel;   // selection groups per batch element
+    int kd, ks; // kept head_dim slices, kept positions
+    float scale;
+};
+struct AttnWs {
+    float *logit;    // [B][Hq][S] unscaled q.k over kept dims
+    float2 *pstat;   // [B][Hq][nqk] (max, sum exp) per QK chunk
+    double *lse;     // [B][Hq]
+    uint32_t *keys;  // [B][Hsel][S]
+    uint32_t *hist;  // [B][Hsel][ATTN_HIST_BINS]
+    int32_t *pos;    // [B][Hsel][ks]
+    float *pvpart;   // [B][Hsel][npv][GS][D]
+    uint32_t *cnt;   // counter header
+};
+size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base);
+hipError_t launch_attn(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v, const float *kn,
+                       float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse, const AttnWs &ws, hipStream_t st);
+size_t attn_dense_ws_layout(int64_t B, int64_t Hq, int64_t S, char *base, float **part, float2 **stat,
+                            uint32_t **cnt);
+hipError_t launch_attn_dense(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v, float *out,
+                             float *lse, float *part, float2 *stat, uint32_t *cnt, hipStream_t st);
+void attn_init();
+
+} // namespace rmm

@@ -1,0 +1,466 @@
+// Reduced linear products.
+//
+// The blog on input-adaptive matrix-product reduction (section 2) reduces
+// Y = X @ W^T over the kept contraction slices J: Y ~= X[:,J] @ W^T[J,:];
+// section 5.3 gathers the kept slices so the product stays dense, and
+// section 8 warns that a gather copy costs bandwidth.  W^T is stored K-major,
+// so every kept slice is one contiguous row of W^T: the kernels read kept rows
+// in place and never copy W.
+//
+//  * gemv_kernel: few tokens per tile (decode).  HBM-streaming split-K over the
+//    kept rows; each wave streams 16-byte vectors of kept rows; partials are
+//    reduced in a fixed order by the last workgroup of each column slice, so
+//    results are deterministic.
+//  * gather_kernel + gemm_kernel: many tokens per tile (prefill).  The kept
+//    columns of the tile's activations are packed once (activations are the
+//    small operand), then a bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16, fp32
+//    accumulation) stages A tiles and the kept W^T rows through LDS.
+#include "device.h"
+#include "kernels.h"
+
+namespace rmm {
+
+// ============================================================================ GEMV
+constexpr int GEMV_THREADS = 256;
+constexpr int GEMV_WAVES = GEMV_THREADS / WAVE;
+
+template <typename TE, int NT, bool DENSE>
+__global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(
+    const TE *__restrict__ x, int64_t ldx, int T, int tile, const TE *__restrict__ wt, int64_t ldw, int M,
+    const int32_t *__restrict__ idx, int k, int groups_per_tile, int nslices, int nsplit, int rows_cap,
+    float *__restrict__ part, uint32_t *__restrict__ cnt, float *__restrict__ y, int64_t ldy)
+{
+    constexpr int VEC = Vec16<TE>::N;
+    constexpr int CW = WAVE * VEC;            // columns per slice
+    constexpr int U = GEMV_UNROLL;            // kept rows in flight per wave
+    extern __shared__ float gsm[];
+    __shared__ uint32_t last_flag;
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+
+    int bid = blockIdx.x;
+    const int slice = bid % nslices;
+    bid /= nslices;
+    const int split = bid % nsplit;
+    const int grp = bid / nsplit;
+    const int tau = grp / groups_per_tile, sub = grp % groups_per_tile;
+    const int t0 = tau * tile + sub * NT;
+    const int tend = min(T, tau * tile + tile);
+    const int nt = min(NT, tend - t0);
+    if (nt <= 0)
+        return; // the same for every split of this group: its counter is never touched
+
+    const int i0 = (int)((int64_t)k * split / nsplit), i1 = (int)((int64_t)k * (split + 1) / nsplit);
+    const int32_t *J = DENSE ? nullptr : idx + (int64_t)tau * k;
+    const int col = slice * CW + lane * VEC;
+    const bool active = col < M;
+    int *jrow = reinterpret_cast<int *>(gsm);
+    float *xs = gsm + rows_cap;
+
+    float acc[NT][VEC];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            acc[t][e] = 0.0f;
+
+    for (int b0 = i0; b0 < i1; b0 += rows_cap) {
+        const int nrows = min(rows_cap, i1 - b0);
+        for (int r = threadIdx.x; r < nrows; r += GEMV_THREADS) {
+            const int j = DENSE ? b0 + r : J[b0 + r];
+            jrow[r] = j;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                xs[t * rows_cap + r] = t < nt ? ld_elem(x, (int64_t)(t0 + t) * ldx + j) : 0.0f;
+        }
+        __syncthreads();
+        if (active) {
+            const TE *wcol = wt + col;
+            for (int base = w; base < nrows; base += GEMV_WAVES * U) {
+                uint4 u[U];
+#pragma unroll
+                for (int q = 0; q < U; ++q) {
+                    const int r = base + q * GEMV_WAVES;
+                    if (r < nrows)
+                        u[q] = Vec16<TE>::raw(wcol + (int64_t)jrow[r] * ldw);
+                }
+#pragma unroll
+                for (int q = 0; q < U; ++q) {
+                    const int r = base + q * GEMV_WAVES;
+                    if (r < nrows) {
+                        float v[VEC];
+                        Vec16<TE>::unpack(u[q], v);
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            const float xv = xs[t * rows_cap + r];
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e)
+                                acc[t][e] = fmaf(xv, v[e], acc[t][e]);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // cross-wave reduction in a fixed order
+    float *red = gsm;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            red[(w * NT + t) * CW + lane * VEC + e] = acc[t][e];
+    __syncthreads();
+
+    if (nsplit == 1) {
+        for (int i = threadIdx.x; i < NT * CW; i += GEMV_THREADS) {
+            const int t = i / CW, cc = i % CW;
+            float s = red[t * CW + cc];
+#pragma unroll
+            for (int ww = 1; ww < GEMV_WAVES; ++ww)
+                s += red[(ww * NT + t) * CW + cc];
+            if (t < nt && slice * CW + cc < M)
+                y[(int64_t)(t0 + t) * ldy + slice * CW + cc] = s;
+        }
+        return;
+    }
+
+    float *pbase = part + ((int64_t)grp * nslices + slice) * nsplit * (NT * CW);
+    float *mine = pbase + (int64_t)split * (NT * CW);
+    for (int i = threadIdx.x; i < NT * CW; i += GEMV_THREADS) {
+        const int t = i / CW, cc = i % CW;
+        float s = red[t * CW + cc];
+#pragma unroll
+        for (int ww = 1; ww < GEMV_WAVES; ++ww)
+            s += red[(ww * NT + t) * CW + cc];
+        mine[i] = s;
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last_flag = atomicInc(&cnt[grp * nslices + slice], (uint32_t)(nsplit - 1)) == (uint32_t)(nsplit - 1);
+    __syncthreads();
+    if (!last_flag)
+        return;
+    __threadfence();
+    // last workgroup of this slice: sum the split partials in split order
+    for (int i = threadIdx.x * 4; i < NT * CW; i += GEMV_THREADS * 4) {
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+        int sp = 0;
+        for (; sp + 8 <= nsplit; sp += 8) {
+            f32x4_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                v[q] = *reinterpret_cast<const f32x4_t *>(pbase + (int64_t)(sp + q) * (NT * CW) + i);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                s += v[q];
+        }
+        for (; sp < nsplit; ++sp)
+            s += *reinterpret_cast<const f32x4_t *>(pbase + (int64_t)sp * (NT * CW) + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = (i + e) / CW, cc = (i + e) % CW;
+            if (t < nt && slice * CW + cc < M)
+                y[(int64_t)(t0 + t) * ldy + slice * CW + cc] = s[e];
+        }
+    }
+}
+
+struct GemvPlan {
+    int nt, groups_per_tile, nslices, nsplit, rows_cap, ngroups;
+    size_t lds;
+};
+
+static int nt_for(int64_t rows)
+{
+    return rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : 8;
+}
+
+static GemvPlan gemv_plan(int64_t T, int64_t M, int64_t k, int64_t tile, bool bf16)
+{
+    GemvPlan p;
+    const int64_t rows = tile < T ? tile : T;
+    p.nt = nt_for(rows);
+    p.groups_per_tile = (int)((rows + p.nt - 1) / p.nt);
+    const int64_t ntiles = (T + tile - 1) / tile;
+    p.ngroups = (int)(ntiles * p.groups_per_tile);
+    const int cw = WAVE * (bf16 ? 8 : 4);
+    p.nslices = (int)((M + cw - 1) / cw);
+    const int64_t base = (int64_t)p.ngroups * p.nslices;
+    int64_t ns = 1;
+    if (base <= GEMV_MAX_COUNTERS) {
+        ns = (GEMV_TARGET_WGS + base - 1) / base;
+        int64_t by_rows = k / GEMV_MIN_ROWS;
+        if (ns > by_rows)
+            ns = by_rows;
+        if (ns > GEMV_MAX_SPLIT)
+            ns = GEMV_MAX_SPLIT;
+        if (ns < 1)
+            ns = 1;
+    }
+    p.nsplit = (int)ns;
+    const int64_t per = (k + ns - 1) / ns;
+    p.rows_cap = (int)(per < GEMV_ROWS_CAP ? per : GEMV_ROWS_CAP);
+    if (p.rows_cap < 1)
+        p.rows_cap = 1;
+    const size_t stage = (size_t)p.rows_cap * (1 + p.nt) * 4;
+    const size_t redb = (size_t)GEMV_WAVES * p.nt * cw * 4;
+    p.lds = stage > redb ? stage : redb;
+    return p;
+}
+
+size_t gemv_ws_bytes(int64_t T, int64_t M, int64_t k, int64_t tile, bool bf16)
+{
+    GemvPlan p = gemv_plan(T, M, k, tile, bf16);
+    if (p.nsplit == 1)
+        return 0;
+    const int cw = WAVE * (bf16 ? 8 : 4);
+    return (size_t)p.ngroups * p.nslices * p.nsplit * p.nt * cw * sizeof(float);
+}
+
+template <typename TE, bool DENSE>
+static hipError_t gemv_dispatch(const GemvPlan &p, const void *x, int64_t ldx, int64_t T, int64_t tile,
+                                const void *wt, int64_t ldw, int64_t M, const int32_t *idx, int64_t k, float *part,
+                                uint32_t *cnt, float *y, int64_t ldy, hipStream_t st)
+{
+    dim3 grid((unsigned)((int64_t)p.ngroups * p.nslices * p.nsplit));
+#define RMM_GEMV_CASE(NTV)                                                                                         \
+    case NTV:                                                                                                      \
+        gemv_kernel<TE, NTV, DENSE><<<grid, GEMV_THREADS, p.lds, st>>>(                                            \
+            (const TE *)x, ldx, (int)T, (int)tile, (const TE *)wt, ldw, (int)M, idx, (int)k, p.groups_per_tile,     \
+            p.nslices, p.nsplit, p.rows_cap, part, cnt, y, ldy);                                                   \
+        break;
+    switch (p.nt) {
+        RMM_GEMV_CASE(1)
+        RMM_GEMV_CASE(2)
+        RMM_GEMV_CASE(4)
+        RMM_GEMV_CASE(8)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef RMM_GEMV_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const void *wt, int64_t ldw, int64_t M,
+                       const int32_t *idx, int64_t k, int64_t tile, bool dense, float *y, int64_t ldy, float *part,
+                       uint32_t *cnt, hipStream_t st)
+{
+    GemvPlan p = gemv_plan(T, M, k, tile, bf16);
+    if (bf16)
+        return dense ? gemv_dispatch<uint16_t, true>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, cnt, y, ldy, st)
+                     : gemv_dispatch<uint16_t, false>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, cnt, y, ldy, st);
+    return dense ? gemv_dispatch<float, true>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, cnt, y, ldy, st)
+                 : gemv_dispatch<float, false>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, cnt, y, ldy, st);
+}
+
+// ============================================================================ gather
+// xg[t][i] = x[t][idx[t/tile][i]] for i < k, 0 for k <= i < kpad.
+__global__ __launch_bounds__(256) void gather_kernel(const uint16_t *__restrict__ x, int64_t ldx, int T, int tile,
+                                                     const int32_t *__restrict__ idx, int k, int kpad,
+                                                     uint16_t *__restrict__ xg)
+{
+    const int cpr = kpad / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)T * cpr)
+        return;
+    const int t = (int)(gid / cpr), ch = (int)(gid % cpr);
+    const int32_t *J = idx + (int64_t)(t / tile) * k;
+    const uint16_t *xr = x + (int64_t)t * ldx;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int i = ch * 8 + e;
+        h[e] = i < k ? xr[J[i]] : 0u;
+    }
+    uint4 o;
+    o.x = h[0] | (h[1] << 16);
+    o.y = h[2] | (h[3] << 16);
+    o.z = h[4] | (h[5] << 16);
+    o.w = h[6] | (h[7] << 16);
+    *reinterpret_cast<uint4 *>(xg + (int64_t)t * kpad + ch * 8) = o;
+}
+
+// ============================================================================ MFMA GEMM
+// C[t][n] = sum_i A[t][i] * W^T[row(i)][n], A = packed kept activations
+// (or x itself when dense), row(i) = idx[tile(t)][i] (or i when dense).
+// Workgroup tile 128 x 128, k step 64, 4 waves of 64 x 64 (2 x 2 MFMA 32x32x16).
+constexpr int GB_M = 128, GB_N = 128, GB_K = 64;
+constexpr int GEMM_THREADS = 256;
+constexpr int LPITCH = GB_K + 8; // bf16 per LDS row (pad against bank conflicts)
+
+template <bool DENSE>
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__restrict__ A, int64_t lda, int T,
+                                                            int tile, int mblocks, const uint16_t *__restrict__ wt,
+                                                            int64_t ldw, int M, const int32_t *__restrict__ idx,
+                                                            int k, int klim, float *__restrict__ y, int64_t ldy)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][GB_M * LPITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GB_N * LPITCH];
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    const int nb = blockIdx.x, mbk = blockIdx.y;
+    const int tau = mbk / mblocks, mm = mbk % mblocks;
+    const int row0 = tau * tile + mm * GB_M;
+    const int rowend = min(T, tau * tile + tile);
+    if (row0 >= rowend)
+        return;
+    const int n0 = nb * GB_N;
+    const int32_t *J = DENSE ? nullptr : idx + (int64_t)tau * k;
+    const int wm = w >> 1, wn = w & 1;
+
+    // A loader: 4 chunks of 8 bf16 per thread: row ar + 32p, k offset 8*ac
+    const int ar = tid >> 3, ac = tid & 7;
+    // B loader: lane = k row within the step, chunks w + 4p of 8 columns
+    uint4 ra[4], rb[4];
+
+    auto load_stage = [&](int kk) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = ar + 32 * p;
+            const int kc = kk + 8 * ac;
+            uint4 v = {0u, 0u, 0u, 0u};
+            if (row0 + r < rowend) {
+                const uint16_t *src = A + (int64_t)(row0 + r) * lda + kc;
+                if (!DENSE || kc + 8 <= klim) {
+                    v = *reinterpret_cast<const uint4 *>(src);
+                } else if (kc < klim) {
+                    uint32_t h[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        h[e] = kc + e < klim ? src[e] : 0u;
+                    v.x = h[0] | (h[1] << 16);
+                    v.y = h[2] | (h[3] << 16);
+                    v.z = h[4] | (h[5] << 16);
+                    v.w = h[6] | (h[7] << 16);
+                }
+            }
+            ra[p] = v;
+        }
+        int kr = kk + lane;
+        kr = kr < klim ? kr : klim - 1; // padded steps reuse a valid row (times zero A)
+        const int j = DENSE ? kr : J[kr];
+        const uint16_t *wrow = wt + (int64_t)j * ldw;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int nc = n0 + 8 * (w + 4 * p);
+            rb[p] = nc < M ? *reinterpret_cast<const uint4 *>(wrow + nc) : uint4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            *reinterpret_cast<uint4 *>(&As[buf][(ar + 32 * p) * LPITCH + 8 * ac]) = ra[p];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int nbase = 8 * (w + 4 * p);
+            const uint32_t q[4] = {rb[p].x, rb[p].y, rb[p].z, rb[p].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Bs[buf][(nbase + 2 * e) * LPITCH + lane] = (uint16_t)(q[e] & 0xffffu);
+                Bs[buf][(nbase + 2 * e + 1) * LPITCH + lane] = (uint16_t)(q[e] >> 16);
+            }
+        }
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][jn][r] = 0.0f;
+
+    const int ksteps = (klim + GB_K - 1) / GB_K;
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int s = 0; s < ksteps; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < ksteps)
+            load_stage((s + 1) * GB_K);
+#pragma unroll
+        for (int ks = 0; ks < GB_K / 16; ++ks) {
+            const int kofs = ks * 16 + 8 * (lane >> 5);
+            bf16x8_t a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = wm * 64 + i * 32 + (lane & 31);
+                a[i] = *reinterpret_cast<const bf16x8_t *>(&As[cur][row * LPITCH + kofs]);
+            }
+#pragma unroll
+            for (int jn = 0; jn < 2; ++jn) {
+                const int col = wn * 64 + jn * 32 + (lane & 31);
+                b[jn] = *reinterpret_cast<const bf16x8_t *>(&Bs[cur][col * LPITCH + kofs]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jn = 0; jn < 2; ++jn)
+                    acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[jn], acc[i][jn], 0, 0, 0);
+        }
+        if (s + 1 < ksteps)
+            store_stage(cur ^ 1);
+        __syncthreads();
+    }
+
+    // D layout of a 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn) {
+            const int col = n0 + wn * 64 + jn * 32 + (lane & 31);
+            if (col >= M)
+                continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (row < rowend)
+                    y[(int64_t)row * ldy + col] = acc[i][jn][r];
+            }
+        }
+}
+
+size_t gemm_ws_bytes(int64_t T, int64_t k)
+{
+    const int64_t kpad = (k + GB_K - 1) / GB_K * GB_K;
+    return (size_t)(T * kpad) * sizeof(uint16_t);
+}
+
+hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const void *wt, int64_t ldw, int64_t M,
+                       const int32_t *idx, int64_t k, int64_t tile, bool dense, float *y, int64_t ldy, void *xg,
+                       hipStream_t st)
+{
+    const int64_t rows = tile < T ? tile : T;
+    const int mblocks = (int)((rows + GB_M - 1) / GB_M);
+    const int64_t ntiles = (T + tile - 1) / tile;
+    dim3 grid((unsigned)((M + GB_N - 1) / GB_N), (unsigned)(ntiles * mblocks));
+    if (dense) {
+        gemm_kernel<true><<<grid, GEMM_THREADS, 0, st>>>((const uint16_t *)x, ldx, (int)T, (int)tile, mblocks,
+                                                         (const uint16_t *)wt, ldw, (int)M, nullptr, (int)K, (int)K,
+                                                         y, ldy);
+        return hipGetLastError();
+    }
+    const int64_t kpad = (k + GB_K - 1) / GB_K * GB_K;
+    const int64_t nthreads = T * (kpad / 8);
+    gather_kernel<<<(unsigned)((nthreads + 255) / 256), 256, 0, st>>>((const uint16_t *)x, ldx, (int)T, (int)tile,
+                                                                       idx, (int)k, (int)kpad, (uint16_t *)xg);
+    gemm_kernel<false><<<grid, GEMM_THREADS, 0, st>>>((const uint16_t *)xg, kpad, (int)T, (int)tile, mblocks,
+                                                      (const uint16_t *)wt, ldw, (int)M, idx, (int)k, (int)k, y, ldy);
+    return hipGetLastError();
+}
+
+void linear_init()
+{
+    (void)hipFuncSetAttribute((const void *)gemv_kernel<uint16_t, 8, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        160 * 1024);
+    (void)hipFuncSetAttribute((const void *)gemv_kernel<uint16_t, 8, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        160 * 1024);
+    (void)hipFuncSetAttribute((const void *)gemv_kernel<float, 8, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        160 * 1024);
+    (void)hipFuncSetAttribute((const void *)gemv_kernel<float, 8, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        160 * 1024);
+}
+
+} // namespace rmm

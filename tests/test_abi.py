@@ -1,0 +1,82 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/rmm.h declares, its host-only keep count agrees with the oracle's, and
+argument errors are reported before anything touches a device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import input_adaptive_reduced_score_amd as rmm
+import oracle
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "rmm.h")
+
+
+def declared():
+    txt = open(HDR).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(rmm_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    L = rmm.lib()
+    names = declared()
+    assert len(names) >= 13
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert sorted(rmm.EXPORTS) == names
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 12, 128, 4096, 14336, 131072])
+def test_keep_count_matches_oracle(n):
+    for r in (1e-6, 0.001, 0.07, 0.1, 1 / 3, 0.25, 0.3, 0.5, 0.75, 0.999, 1.0, 0.0, -1.0, 1.5, float("nan")):
+        assert rmm.keep_count(n, r) == oracle.keep_count(n, r), (n, r)
+
+
+def _call_select(**kw):
+    L = rmm.lib()
+    a = dict(x=C.c_void_p(16), xt=1, T=1, K=64, ldx=64, c=C.c_void_p(16), tile=1, r=0.5, idx=C.c_void_p(16),
+             ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.rmm_select(*a.values())
+
+
+def test_select_argument_errors_host_only():
+    L = rmm.lib()
+    assert _call_select(x=None) == 1
+    assert _call_select(r=0.0) == 1
+    assert _call_select(r=1.01) == 1
+    assert _call_select(T=0) == 1
+    assert _call_select(ldx=8) == 1
+    assert _call_select(xt=7) == 1
+    assert _call_select(K=40000, ldx=40000) == 2          # above the selector's K limit
+    assert _call_select(x=C.c_void_p(18)) == 2            # misaligned
+    assert _call_select() == 3                            # no workspace
+    assert b"workspace" in L.rmm_last_error()
+
+
+def test_linear_and_attn_argument_errors_host_only():
+    L = rmm.lib()
+    p = C.c_void_p(256)
+    # dtype mismatch
+    assert L.rmm_linear(p, 1, 1, 64, 64, p, 0, 64, 64, p, 8, 1, p, 64, None, 0, None) == 1
+    # k > K
+    assert L.rmm_linear(p, 1, 1, 64, 64, p, 1, 64, 64, p, 65, 1, p, 64, None, 0, None) == 1
+    # ldw not a multiple of 8 bf16 elements
+    assert L.rmm_linear(p, 1, 1, 64, 64, p, 1, 60, 60, p, 8, 1, p, 64, None, 0, None) == 2
+    # no workspace
+    assert L.rmm_linear(p, 1, 1, 64, 64, p, 1, 64, 64, p, 8, 1, p, 64, None, 0, None) == 3
+    args = [p, p, p, p, 1, 32, 8, 128, 1000, 1000, 1000, 0.088, 0.5, 0.5, 0, p, None, None, None, None, 0, None]
+    bad = list(args)
+    bad[5] = 30      # Hq not a multiple of Hkv
+    assert L.rmm_attn_decode(*bad) == 1
+    bad = list(args)
+    bad[7] = 64      # head_dim without a kernel
+    assert L.rmm_attn_decode(*bad) == 2
+    bad = list(args)
+    bad[12] = 0.0    # r_dim
+    assert L.rmm_attn_decode(*bad) == 1
+    assert L.rmm_attn_decode(*args) == 3  # no workspace
+    assert L.rmm_attn_decode_workspace_size(1, 32, 8, 128, 32768, 0.25, 0.25, 0) > 0
+    assert L.rmm_status_string(3).startswith(b"RMM_EWORKSPACE")

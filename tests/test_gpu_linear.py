@@ -1,0 +1,140 @@
+"""GPU parity of the linear path (rmm_select + rmm_linear + rmm_linear_dense)
+against the oracle, through the C ABI.
+
+Bar: kept index sets bit-exact (integer work); outputs within rel-L2 1e-5.
+Spec bars are 1e-5 (fp32 inputs) and 2e-2 (bf16 inputs); the tighter
+1e-5 is used for both because bf16 x bf16 products are exact in fp32, so the
+only error left is fp32 accumulation over <= 16K terms (~sqrt(n) * 2^-24 ~ 1e-5
+worst case), while a single dropped or duplicated slice moves the result by
+about 1/sqrt(k) (1e-2 at the decode shape) and would pass a 2e-2 bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import input_adaptive_reduced_score_amd as rmm
+import oracle
+import workloads as W
+from _util import dev, dev_padded, rel_l2
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def run_case(cs, r, rows=None):
+    x, wt, c = dev_padded(cs.x), dev_padded(cs.wt), dev(cs.c)
+    print(f"[case] {cs.name} r={r}", flush=True)
+    idx = rmm.select(x, c, cs.tile, r)
+    y = rmm.linear(x, wt, idx, cs.tile)
+    torch.cuda.synchronize()
+    idx_ref = oracle.select(cs.x, cs.c, cs.tile, r)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref), f"{cs.name} r={r}: kept slice sets differ"
+    yg = y.cpu().numpy()
+    if rows is None:
+        yr = oracle.linear(cs.x, cs.wt, idx_ref, cs.tile)
+        err = rel_l2(yg, yr)
+    else:
+        errs = []
+        for t in rows:
+            yr = oracle.linear(cs.x, cs.wt, idx_ref, cs.tile, rows=(t, t + 1))
+            errs.append(rel_l2(yg[t], yr[t]))
+        err = max(errs)
+    assert err <= TOL, f"{cs.name} r={r}: rel-L2 {err:.3e}"
+    return idx, y, err
+
+
+def test_tiny_linear_fp32():
+    cs = W.linear_tiny()
+    for r in (0.5, 0.25, 1.0, 1 / 3, 0.001):
+        run_case(cs, r)
+
+
+@pytest.mark.parametrize("r", [0.25, 0.5, 0.75, 1.0])
+def test_decode_down_proj_full_size(r):
+    cs = W.linear_decode()
+    run_case(cs, r)
+
+
+def test_prefill_full_size_sampled_rows():
+    cs = W.linear_prefill()
+    rows = [0, 1, 255, 256, 700, 1023, 1024, 1500, 1791, 1792, 2046, 2047]
+    for r in (0.5, 0.25):
+        run_case(cs, r, rows=rows)
+
+
+@pytest.mark.parametrize("T,K,M,tile,dtype", [
+    (37, 300, 200, 8, "bf16"),     # ragged K, M, tiles; streaming path
+    (37, 300, 200, 8, "f32"),
+    (5, 64, 520, 1, "bf16"),       # per-token tiles
+    (9, 1000, 130, 4, "f32"),
+    (1, 1, 8, 1, "bf16"),          # one slice
+    (100, 1000, 300, 64, "bf16"),  # MFMA path: tiles of 64 and 36 rows, ragged N
+    (300, 200, 136, 128, "bf16"),  # MFMA path, k not a multiple of 64
+    (64, 32768, 16, 64, "bf16"),   # maximum K of the selector
+])
+def test_ragged_and_edge_shapes(T, K, M, tile, dtype):
+    cs = W.linear_random(T, K, M, tile, dtype, seed=T + K)
+    for r in (0.3, 1.0, 1.0 / K):
+        run_case(cs, r)
+
+
+def test_strided_operands():
+    # leading dimensions larger than the logical sizes (views into bigger buffers)
+    cs = W.linear_random(40, 200, 72, 32, "bf16", seed=3)
+    xb = np.zeros((40, 264), np.uint16)
+    xb[:, :200] = cs.x
+    wb = np.zeros((200, 136), np.uint16)
+    wb[:, :72] = cs.wt
+    x = dev(xb)[:, :200]
+    wt = dev(wb)[:, :72]
+    c = dev(cs.c)
+    yb = torch.full((40, 100), float("nan"), device="cuda:0")
+    idx = rmm.select(x, c, 32, 0.5)
+    rmm.linear(x, wt, idx, 32, out=yb[:, :72])
+    torch.cuda.synchronize()
+    idx_ref = oracle.select(cs.x, cs.c, 32, 0.5)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    yr = oracle.linear(cs.x, cs.wt, idx_ref, 32)
+    yg = yb.cpu().numpy()
+    assert rel_l2(yg[:, :72], yr) <= TOL
+    assert np.isnan(yg[:, 72:]).all(), "wrote outside the output view"
+
+
+def test_ties_bit_exact():
+    # integer-valued activations and unit weights: many equal scores
+    rng = np.random.default_rng(0)
+    for T, K, tile in ((1, 5000, 1), (4, 777, 4), (64, 2048, 64)):
+        x = W.f32_to_bf16_bits(rng.integers(-3, 4, size=(T, K)).astype(np.float32))
+        c = np.ones(K, np.float32)
+        for r in (0.1, 0.5, 0.9):
+            idx = rmm.select(dev_padded(x), dev(c), tile, r)
+            torch.cuda.synchronize()
+            assert np.array_equal(idx.cpu().numpy(), oracle.select(x, c, tile, r)), (T, K, r)
+
+
+def test_all_equal_scores_keep_lowest_indices():
+    x = np.ones((1, 4096), np.float32)
+    c = np.ones(4096, np.float32)
+    idx = rmm.select(dev(x), dev(c), 1, 0.25)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy()[0], np.arange(1024))
+
+
+@pytest.mark.parametrize("T,K,M,dtype", [(1, 14336, 4096, "bf16"), (4, 512, 1024, "f32"), (256, 1024, 512, "bf16"),
+                                         (70, 300, 130, "bf16")])
+def test_dense_linear(T, K, M, dtype):
+    cs = W.linear_random(T, K, M, T, dtype, seed=5)
+    y = rmm.linear_dense(dev_padded(cs.x), dev_padded(cs.wt))
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), oracle.dense_linear(cs.x, cs.wt)) <= TOL
+
+
+def test_deterministic_repeat():
+    for cs in (W.linear_decode(), W.linear_random(512, 4096, 1024, 256, "bf16", seed=9)):
+        x, wt, c = dev(cs.x), dev(cs.wt), dev(cs.c)
+        a_idx = rmm.select(x, c, cs.tile, 0.5)
+        a = rmm.linear(x, wt, a_idx, cs.tile).clone()
+        b_idx = rmm.select(x, c, cs.tile, 0.5)
+        b = rmm.linear(x, wt, b_idx, cs.tile)
+        torch.cuda.synchronize()
+        assert torch.equal(a_idx, b_idx) and torch.equal(a, b)
