@@ -26,11 +26,10 @@
  *    results are valid once the stream reaches this point; inputs must stay
  *    unchanged until then.
  *  - Workspace: `ws` is caller-owned device memory of at least the size the
- *    matching *_workspace_size query returns.  Its first RMM_WS_HEADER_BYTES
- *    bytes hold completion counters: they must be zero before a workspace is
- *    used for the first time (e.g. allocate it zero-filled); every call leaves
- *    them zero again when it completes.  The same workspace may serve all entry
- *    points, but two calls must not use one workspace concurrently.
+ *    matching *_workspace_size query returns (its first RMM_WS_HEADER_BYTES
+ *    bytes are reserved).  Its contents on entry do not matter and need no
+ *    initialisation.  The same workspace may serve every entry point, but two
+ *    calls in flight at once must not share one workspace.
  *  - Errors: arguments are validated on the host before anything is enqueued;
  *    on any non-OK status nothing has been written.  RMM_EHIP reports a launch
  *    failure (text in rmm_last_error()).  No exception crosses the ABI, and the

@@ -78,13 +78,10 @@ template <int GS>
 __global__ __launch_bounds__(WAVE) void attn_qk_kernel(AttnShape s, int Sp, const uint16_t *__restrict__ q,
                                                        const uint16_t *__restrict__ kt, const float *__restrict__ kn,
                                                        float *__restrict__ logit, float2 *__restrict__ pstat,
-                                                       double *__restrict__ lse_ws, float *__restrict__ lse_out,
-                                                       int32_t *__restrict__ dim_idx_out, uint32_t *__restrict__ hist,
-                                                       uint32_t *__restrict__ cnt)
+                                                       int32_t *__restrict__ dim_idx_out, uint32_t *__restrict__ hist)
 {
     __shared__ int jd[D];
     __shared__ float qs[GS][D];
-    __shared__ uint32_t last;
     const int lane = threadIdx.x;
     const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel;
     const int h0 = sg * s.GS, g = h0 / s.G;
@@ -174,37 +171,10 @@ __global__ __launch_bounds__(WAVE) void attn_qk_kernel(AttnShape s, int Sp, cons
             pstat[((int64_t)b * s.Hq + h0 + hh) * nchunk + chunk] = make_float2(mx, z);
     }
 
-    // 4. the last workgroup of this group merges the statistics into lse
-    __threadfence();
-    __syncthreads();
-    if (lane == 0)
-        last = atomicInc(&cnt[grp], (uint32_t)(nchunk - 1)) == (uint32_t)(nchunk - 1);
-    __syncthreads();
-    if (!last)
-        return;
-    __threadfence();
-#pragma unroll 1
-    for (int hh = 0; hh < GS; ++hh) {
-        const float2 *ps = pstat + ((int64_t)b * s.Hq + h0 + hh) * nchunk;
-        float M = -INFINITY;
-        for (int i = lane; i < nchunk; i += WAVE)
-            M = fmaxf(M, ps[i].x);
-        M = wave_max(M);
-        double zs = 0.0;
-        for (int i = lane; i < nchunk; i += WAVE) {
-            const float2 st = ps[i];
-            zs += (double)st.y * exp((double)s.scale * ((double)st.x - (double)M));
-        }
-        zs = wave_sum(zs);
-        if (lane == 0) {
-            const double l = (double)s.scale * (double)M + log(zs);
-            lse_ws[(int64_t)b * s.Hq + h0 + hh] = l;
-            if (lse_out)
-                lse_out[(int64_t)b * s.Hq + h0 + hh] = (float)l;
-        }
-    }
-    for (int i = lane; i < ATTN_HIST_BINS; i += WAVE)
-        hist[(int64_t)grp * ATTN_HIST_BINS + i] = 0;
+    // 4. the first chunk's workgroup clears the group's key histogram for the key kernel
+    if (chunk == 0)
+        for (int i = lane; i < ATTN_HIST_BINS; i += WAVE)
+            hist[(int64_t)grp * ATTN_HIST_BINS + i] = 0;
 }
 
 // ------------------------------------------------------------------ keys
@@ -221,18 +191,61 @@ __device__ __forceinline__ uint32_t logprob_key(double L)
 }
 
 template <int GS>
-__global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, const float *__restrict__ logit,
-                                                       const double *__restrict__ lse_ws, uint32_t *__restrict__ keys,
+__global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, int nqk, const float *__restrict__ logit,
+                                                       const float2 *__restrict__ pstat, double *__restrict__ lse_ws,
+                                                       float *__restrict__ lse_out, uint32_t *__restrict__ keys,
                                                        uint32_t *__restrict__ hist)
 {
     __shared__ uint32_t lh[ATTN_HIST_BINS];
+    __shared__ float smax[GS][4];
+    __shared__ double ssum[GS][4];
+    __shared__ double lse_s[GS];
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS;
-    for (int i = threadIdx.x; i < ATTN_HIST_BINS; i += 256)
+    for (int i = tid; i < ATTN_HIST_BINS; i += 256)
         lh[i] = 0;
+    // merge the per-chunk softmax statistics of the group's heads into lse (double, fixed order)
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+        const float2 *ps = pstat + ((int64_t)b * s.Hq + h0 + hh) * nqk;
+        float m = -INFINITY;
+        for (int i = tid; i < nqk; i += 256)
+            m = fmaxf(m, ps[i].x);
+        m = wave_max(m);
+        if (lane == 0)
+            smax[hh][w] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+        const float M = fmaxf(fmaxf(smax[hh][0], smax[hh][1]), fmaxf(smax[hh][2], smax[hh][3]));
+        const float2 *ps = pstat + ((int64_t)b * s.Hq + h0 + hh) * nqk;
+        double z = 0.0;
+        for (int i = tid; i < nqk; i += 256) {
+            const float2 st = ps[i];
+            z += (double)st.y * exp((double)s.scale * ((double)st.x - (double)M));
+        }
+        z = wave_sum(z);
+        if (lane == 0)
+            ssum[hh][w] = z;
+    }
+    __syncthreads();
+    if (tid < GS) {
+        const float M = fmaxf(fmaxf(smax[tid][0], smax[tid][1]), fmaxf(smax[tid][2], smax[tid][3]));
+        const double z = ((ssum[tid][0] + ssum[tid][1]) + ssum[tid][2]) + ssum[tid][3];
+        const double l = (double)s.scale * (double)M + log(z);
+        lse_s[tid] = l;
+        if (blockIdx.x == 0) {
+            lse_ws[(int64_t)b * s.Hq + h0 + tid] = l;
+            if (lse_out)
+                lse_out[(int64_t)b * s.Hq + h0 + tid] = (float)l;
+        }
+    }
+    __syncthreads();
     double lse[GS];
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh)
-        lse[hh] = lse_ws[(int64_t)b * s.Hq + h0 + hh];
+        lse[hh] = lse_s[hh];
     __syncthreads();
     const int sp = blockIdx.x * ATTN_KEY_CHUNK + threadIdx.x * 8;
     if (sp < s.S) {
@@ -328,8 +341,10 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, 
                     ngt += __popcll(__ballot(ok && top > d));
                     if (ok && top == d) {
                         const uint32_t slot = atomicAdd(&ncand, 1u);
-                        ckey[slot] = kk[e];
-                        cpos[slot] = j;
+                        if (slot < (uint32_t)CAND_CAP) {
+                            ckey[slot] = kk[e];
+                            cpos[slot] = j;
+                        }
                     }
                 }
                 if (lane == 0 && ngt)
@@ -405,14 +420,12 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P
                                                       const float *__restrict__ logit, const double *__restrict__ lse_ws,
                                                       const uint32_t *__restrict__ keys, const SelInfo *__restrict__ sel,
                                                       const uint2 *__restrict__ info, int32_t *__restrict__ pos_out,
-                                                      float *__restrict__ part, float *__restrict__ out,
-                                                      uint32_t *__restrict__ cnt)
+                                                      float *__restrict__ part)
 {
     __shared__ int rows[PV_SUB];
     __shared__ float pr[GS][PV_SUB];
     __shared__ uint32_t wtot[2][4];
     __shared__ float red[4][GS][D];
-    __shared__ uint32_t last;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS, g = h0 / s.G;
     const int c = blockIdx.x, npv = gridDim.x;
@@ -471,9 +484,9 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P
             nkept += wtot[1][i];
         }
         const uint32_t oa = kept_w + kept_lane, ob = oa + (keepa ? 1u : 0u);
-        if (keepa)
+        if (keepa && oa < PV_SUB)
             rows[oa] = j0;
-        if (keepb)
+        if (keepb && ob < PV_SUB)
             rows[ob] = j0 + 1;
         __syncthreads();
         // probabilities of the kept rows, and the optional index output
@@ -482,7 +495,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P
 #pragma unroll
             for (int hh = 0; hh < GS; ++hh)
                 pr[hh][r] = expf(fmaf(s.scale, logit[((int64_t)b * s.Hq + h0 + hh) * Sp + sidx], -lsef[hh]));
-            if (pos_out)
+            if (pos_out && kept_before + r < (uint32_t)s.ks)
                 pos_out[(int64_t)grp * s.ks + kept_before + r] = sidx;
         }
         __syncthreads();
@@ -539,26 +552,25 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P
         const int hh = i / D, dd = i % D;
         mine[i] = ((red[0][hh][dd] + red[1][hh][dd]) + red[2][hh][dd]) + red[3][hh][dd];
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0)
-        last = atomicInc(&cnt[ATTN_MAX_GROUPS + grp], (uint32_t)(npv - 1)) == (uint32_t)(npv - 1);
-    __syncthreads();
-    if (!last)
-        return;
-    __threadfence();
+}
+
+// out[b, h0 + hh, :] = sum over PV chunks (in order) of the chunk partials.
+template <int GS>
+__global__ __launch_bounds__(256) void attn_pv_reduce_kernel(AttnShape s, int npv, const float *__restrict__ part,
+                                                             float *__restrict__ out)
+{
+    const int grp = blockIdx.x, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS;
     const float *pb = part + (int64_t)grp * npv * GS * D;
-    for (int i = tid; i < GS * D; i += 256) {
+    for (int i = threadIdx.x; i < GS * D; i += 256) {
         float vals[PV_MAX_CHUNKS];
 #pragma unroll
         for (int cc = 0; cc < PV_MAX_CHUNKS; ++cc)
             vals[cc] = cc < npv ? pb[(int64_t)cc * GS * D + i] : 0.0f;
-        float acc2 = 0.0f;
+        float a = 0.0f;
 #pragma unroll
         for (int cc = 0; cc < PV_MAX_CHUNKS; ++cc)
-            acc2 += vals[cc];
-        const int hh = i / D, dd = i % D;
-        out[((int64_t)b * s.Hq + h0 + hh) * D + dd] = acc2;
+            a += vals[cc];
+        out[((int64_t)b * s.Hq + h0 + i / D) * D + i % D] = a;
     }
 }
 
@@ -617,13 +629,13 @@ static hipError_t attn_run(const AttnShape &s, const uint16_t *q, const uint16_t
     pv_chunks(s.S, &P, &npv);
     SelInfo *sel = reinterpret_cast<SelInfo *>(ws.pos);
     uint2 *info = reinterpret_cast<uint2 *>(align256((char *)(sel + G)));
-    attn_qk_kernel<GS><<<dim3(nqk, G), WAVE, 0, st>>>(s, Sp, q, kt, kn, ws.logit, ws.pstat, ws.lse, lse, dim_idx,
-                                                      ws.hist, ws.cnt);
-    attn_key_kernel<GS><<<dim3((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK, G), 256, 0, st>>>(s, Sp, ws.logit, ws.lse,
-                                                                                              ws.keys, ws.hist);
+    attn_qk_kernel<GS><<<dim3(nqk, G), WAVE, 0, st>>>(s, Sp, q, kt, kn, ws.logit, ws.pstat, dim_idx, ws.hist);
+    attn_key_kernel<GS><<<dim3((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK, G), 256, 0, st>>>(
+        s, Sp, nqk, ws.logit, ws.pstat, ws.lse, lse, ws.keys, ws.hist);
     attn_select_kernel<<<G, 1024, 0, st>>>(s, Sp, P, npv, ws.keys, ws.hist, sel, info);
     attn_pv_kernel<GS><<<dim3(npv, G), 256, 0, st>>>(s, Sp, P, v, ws.logit, ws.lse, ws.keys, sel, info, pos_idx,
-                                                     ws.pvpart, out, ws.cnt);
+                                                     ws.pvpart);
+    attn_pv_reduce_kernel<GS><<<G, 256, 0, st>>>(s, npv, ws.pvpart, out);
     return hipGetLastError();
 }
 
@@ -654,15 +666,12 @@ constexpr int DN_MAX_SPANS = 64;
 template <int G>
 __global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, int span, const uint16_t *__restrict__ q,
                                                          const uint16_t *__restrict__ kt, const uint16_t *__restrict__ v,
-                                                         float *__restrict__ part, float2 *__restrict__ stat,
-                                                         float *__restrict__ out, float *__restrict__ lse_out,
-                                                         uint32_t *__restrict__ cnt)
+                                                         float *__restrict__ part, float2 *__restrict__ stat)
 {
     __shared__ float qs[G][D];
     __shared__ float lg[4][G][DN_SUB]; // per-wave partial dots, then wave 0's slot holds the sums
     __shared__ float red[4][G][D];
     __shared__ float mrun[G], zrun[G], fac[G];
-    __shared__ uint32_t last;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int grp = blockIdx.y, b = grp / s.Hkv, g = grp % s.Hkv, h0 = g * G;
     const int c = blockIdx.x, nspan = gridDim.x;
@@ -807,15 +816,16 @@ __global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, int span, 
     }
     if (tid < G)
         stat[((int64_t)grp * nspan + c) * G + tid] = make_float2(mrun[tid], zrun[tid]);
-    __threadfence();
-    __syncthreads();
-    if (tid == 0)
-        last = atomicInc(&cnt[grp], (uint32_t)(nspan - 1)) == (uint32_t)(nspan - 1);
-    __syncthreads();
-    if (!last)
-        return;
-    __threadfence();
-    for (int i = tid; i < G * D; i += 256) {
+}
+
+// Rescales every span's partial to the largest running max and sums them in span order.
+template <int G>
+__global__ __launch_bounds__(256) void attn_dense_reduce_kernel(AttnShape s, int nspan, const float *__restrict__ part,
+                                                                const float2 *__restrict__ stat,
+                                                                float *__restrict__ out, float *__restrict__ lse_out)
+{
+    const int grp = blockIdx.x, b = grp / s.Hkv, g = grp % s.Hkv, h0 = g * G;
+    for (int i = threadIdx.x; i < G * D; i += 256) {
         const int hh = i / D, dd = i % D;
         float M = -INFINITY;
         for (int cc = 0; cc < nspan; ++cc)
@@ -867,22 +877,22 @@ hipError_t launch_attn_dense(const AttnShape &s, const uint16_t *q, const uint16
     int span, nspan;
     dense_spans(s.S, &span, &nspan);
     dim3 grid(nspan, (unsigned)(s.B * s.Hkv));
+    const unsigned ng = (unsigned)(s.B * s.Hkv);
+    (void)cnt;
+#define RMM_DENSE_CASE(GV)                                                                                         \
+    case GV:                                                                                                       \
+        attn_dense_kernel<GV><<<grid, 256, 0, st>>>(s, span, q, kt, v, part, stat);                                \
+        attn_dense_reduce_kernel<GV><<<ng, 256, 0, st>>>(s, nspan, part, stat, out, lse);                          \
+        break;
     switch (s.G) {
-    case 1:
-        attn_dense_kernel<1><<<grid, 256, 0, st>>>(s, span, q, kt, v, part, stat, out, lse, cnt);
-        break;
-    case 2:
-        attn_dense_kernel<2><<<grid, 256, 0, st>>>(s, span, q, kt, v, part, stat, out, lse, cnt);
-        break;
-    case 4:
-        attn_dense_kernel<4><<<grid, 256, 0, st>>>(s, span, q, kt, v, part, stat, out, lse, cnt);
-        break;
-    case 8:
-        attn_dense_kernel<8><<<grid, 256, 0, st>>>(s, span, q, kt, v, part, stat, out, lse, cnt);
-        break;
+        RMM_DENSE_CASE(1)
+        RMM_DENSE_CASE(2)
+        RMM_DENSE_CASE(4)
+        RMM_DENSE_CASE(8)
     default:
         return hipErrorInvalidValue;
     }
+#undef RMM_DENSE_CASE
     return hipGetLastError();
 }
 

@@ -73,4 +73,41 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *tmp)
 // Non-negative float -> order-preserving uint32 key; -0 ranks as +0.
 __device__ __forceinline__ uint32_t nonneg_key(float s) { return __float_as_uint(s) & 0x7fffffffu; }
 
+// ---- wave64 DPP reductions and scans (GFX9 row_shr / row_bcast controls)
+// update_dpp(old, src, ctrl, row_mask, bank_mask, bound_ctrl): lanes without a
+// source (or outside row_mask) keep `old`, which is the operation's identity.
+#define RMM_DPP_ROW_SHR(n) (0x110 + (n))
+#define RMM_DPP_ROW_BCAST15 0x142
+#define RMM_DPP_ROW_BCAST31 0x143
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v, uint32_t ident, Op op)
+{
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, RMM_DPP_ROW_SHR(1), 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, RMM_DPP_ROW_SHR(2), 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, RMM_DPP_ROW_SHR(4), 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, RMM_DPP_ROW_SHR(8), 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, RMM_DPP_ROW_BCAST15, 0xa, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, RMM_DPP_ROW_BCAST31, 0xc, 0xf, false));
+    return v; // inclusive prefix over lanes 0..lane
+}
+struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) { return wave_scan_dpp(v, 0u, OpAdd()); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(v, 0u, OpMax()), WAVE - 1);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(v, 0xffffffffu, OpMin()), WAVE - 1);
+}
+__device__ __forceinline__ uint64_t lanemask_lt()
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+    return lane == 0 ? 0ull : (~0ull >> (WAVE - lane));
+}
+
 } // namespace rmm

@@ -18,16 +18,12 @@
 #define GEMV_UNROLL 8
 #endif
 #ifndef GEMV_TARGET_WGS
-#define GEMV_TARGET_WGS 512
+#define GEMV_TARGET_WGS 512 // workgroups (8 waves each) the split-K aims for
 #endif
 #ifndef GEMV_MIN_ROWS
-#define GEMV_MIN_ROWS 32
+#define GEMV_MIN_ROWS 8 // kept rows per wave below which splitting stops
 #endif
-#ifndef GEMV_MAX_SPLIT
 #define GEMV_MAX_SPLIT 64
-#endif
-#define GEMV_ROWS_CAP 2048
-#define GEMV_MAX_COUNTERS 1024
 #define MFMA_MIN_TILE_ROWS 32 // bf16 tiles with at least this many tokens use the MFMA GEMM
 
 #define ATTN_D 128

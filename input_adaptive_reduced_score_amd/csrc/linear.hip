@@ -7,10 +7,9 @@
 // so every kept slice is one contiguous row of W^T: the kernels read kept rows
 // in place and never copy W.
 //
-//  * gemv_kernel: few tokens per tile (decode).  HBM-streaming split-K over the
-//    kept rows; each wave streams 16-byte vectors of kept rows; partials are
-//    reduced in a fixed order by the last workgroup of each column slice, so
-//    results are deterministic.
+//  * gemv_kernel (+ gemv_reduce_kernel): few tokens per tile (decode).
+//    HBM-streaming split-K over the kept rows; partials are summed in a fixed
+//    order by a second small kernel, so results are deterministic.
 //  * gather_kernel + gemm_kernel: many tokens per tile (prefill).  The kept
 //    columns of the tile's activations are packed once (activations are the
 //    small operand), then a bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16, fp32
@@ -21,20 +20,27 @@
 namespace rmm {
 
 // ============================================================================ GEMV
-constexpr int GEMV_THREADS = 256;
-constexpr int GEMV_WAVES = GEMV_THREADS / WAVE;
+// Split-K over the kept list.  Workgroup (token group, column slice, split):
+// 8 waves; wave w streams a contiguous run of the split's kept rows over the
+// slice (64 lanes x 16 bytes).  The wave loads its run's indices and the
+// tokens' activations with one vector load per 64 rows and broadcasts them
+// with readlane, so each row load has a scalar base address and U rows are in
+// flight per wave.  Waves are summed through LDS in a fixed order; with more
+// than one split the partials go to the workspace and gemv_reduce_kernel sums
+// them in split order (a kernel boundary instead of per-workgroup fences).
+constexpr int GEMV_WAVES = 8;
+constexpr int GEMV_THREADS = GEMV_WAVES * WAVE;
 
 template <typename TE, int NT, bool DENSE>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(
     const TE *__restrict__ x, int64_t ldx, int T, int tile, const TE *__restrict__ wt, int64_t ldw, int M,
-    const int32_t *__restrict__ idx, int k, int groups_per_tile, int nslices, int nsplit, int rows_cap,
-    float *__restrict__ part, uint32_t *__restrict__ cnt, float *__restrict__ y, int64_t ldy)
+    const int32_t *__restrict__ idx, int k, int groups_per_tile, int nslices, int nsplit, float *__restrict__ part,
+    float *__restrict__ y, int64_t ldy)
 {
     constexpr int VEC = Vec16<TE>::N;
-    constexpr int CW = WAVE * VEC;            // columns per slice
-    constexpr int U = GEMV_UNROLL;            // kept rows in flight per wave
-    extern __shared__ float gsm[];
-    __shared__ uint32_t last_flag;
+    constexpr int CW = WAVE * VEC; // columns per slice
+    constexpr int U = GEMV_UNROLL; // kept rows in flight per wave
+    __shared__ float red[GEMV_WAVES][NT][CW];
     const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
 
     int bid = blockIdx.x;
@@ -47,14 +53,14 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(
     const int tend = min(T, tau * tile + tile);
     const int nt = min(NT, tend - t0);
     if (nt <= 0)
-        return; // the same for every split of this group: its counter is never touched
+        return;
 
     const int i0 = (int)((int64_t)k * split / nsplit), i1 = (int)((int64_t)k * (split + 1) / nsplit);
+    const int n = i1 - i0;
+    const int r0 = i0 + (int)((int64_t)n * w / GEMV_WAVES), r1 = i0 + (int)((int64_t)n * (w + 1) / GEMV_WAVES);
     const int32_t *J = DENSE ? nullptr : idx + (int64_t)tau * k;
     const int col = slice * CW + lane * VEC;
     const bool active = col < M;
-    int *jrow = reinterpret_cast<int *>(gsm);
-    float *xs = gsm + rows_cap;
 
     float acc[NT][VEC];
 #pragma unroll
@@ -63,113 +69,98 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(
         for (int e = 0; e < VEC; ++e)
             acc[t][e] = 0.0f;
 
-    for (int b0 = i0; b0 < i1; b0 += rows_cap) {
-        const int nrows = min(rows_cap, i1 - b0);
-        for (int r = threadIdx.x; r < nrows; r += GEMV_THREADS) {
-            const int j = DENSE ? b0 + r : J[b0 + r];
-            jrow[r] = j;
+    for (int b0 = r0; b0 < r1; b0 += WAVE) {
+        const int nb = min(WAVE, r1 - b0);
+        int jv = 0;
+        float xv[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            xv[t] = 0.0f;
+        if (lane < nb) {
+            jv = DENSE ? b0 + lane : J[b0 + lane];
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                xs[t * rows_cap + r] = t < nt ? ld_elem(x, (int64_t)(t0 + t) * ldx + j) : 0.0f;
+                if (t < nt)
+                    xv[t] = ld_elem(x, (int64_t)(t0 + t) * ldx + jv);
         }
-        __syncthreads();
-        if (active) {
-            const TE *wcol = wt + col;
-            for (int base = w; base < nrows; base += GEMV_WAVES * U) {
-                uint4 u[U];
+        for (int c0 = 0; c0 < nb; c0 += U) {
+            uint4 u[U];
 #pragma unroll
-                for (int q = 0; q < U; ++q) {
-                    const int r = base + q * GEMV_WAVES;
-                    if (r < nrows)
-                        u[q] = Vec16<TE>::raw(wcol + (int64_t)jrow[r] * ldw);
+            for (int q = 0; q < U; ++q) {
+                if (c0 + q < nb) {
+                    const int j = __builtin_amdgcn_readlane(jv, c0 + q); // wave-uniform row index
+                    if (active)
+                        u[q] = Vec16<TE>::raw(wt + (int64_t)j * ldw + col);
                 }
+            }
 #pragma unroll
-                for (int q = 0; q < U; ++q) {
-                    const int r = base + q * GEMV_WAVES;
-                    if (r < nrows) {
-                        float v[VEC];
-                        Vec16<TE>::unpack(u[q], v);
+            for (int q = 0; q < U; ++q) {
+                if (c0 + q < nb) {
+                    float v[VEC];
+                    Vec16<TE>::unpack(u[q], v);
 #pragma unroll
-                        for (int t = 0; t < NT; ++t) {
-                            const float xv = xs[t * rows_cap + r];
+                    for (int t = 0; t < NT; ++t) {
+                        const float xs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xv[t]), c0 + q));
 #pragma unroll
-                            for (int e = 0; e < VEC; ++e)
-                                acc[t][e] = fmaf(xv, v[e], acc[t][e]);
-                        }
+                        for (int e = 0; e < VEC; ++e)
+                            acc[t][e] = fmaf(xs, v[e], acc[t][e]);
                     }
                 }
             }
         }
-        __syncthreads();
     }
 
-    // cross-wave reduction in a fixed order
-    float *red = gsm;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
-            red[(w * NT + t) * CW + lane * VEC + e] = acc[t][e];
+            red[w][t][lane * VEC + e] = acc[t][e];
     __syncthreads();
-
-    if (nsplit == 1) {
-        for (int i = threadIdx.x; i < NT * CW; i += GEMV_THREADS) {
-            const int t = i / CW, cc = i % CW;
-            float s = red[t * CW + cc];
-#pragma unroll
-            for (int ww = 1; ww < GEMV_WAVES; ++ww)
-                s += red[(ww * NT + t) * CW + cc];
-            if (t < nt && slice * CW + cc < M)
-                y[(int64_t)(t0 + t) * ldy + slice * CW + cc] = s;
-        }
-        return;
-    }
-
-    float *pbase = part + ((int64_t)grp * nslices + slice) * nsplit * (NT * CW);
-    float *mine = pbase + (int64_t)split * (NT * CW);
     for (int i = threadIdx.x; i < NT * CW; i += GEMV_THREADS) {
         const int t = i / CW, cc = i % CW;
-        float s = red[t * CW + cc];
+        float s = red[0][t][cc];
 #pragma unroll
         for (int ww = 1; ww < GEMV_WAVES; ++ww)
-            s += red[(ww * NT + t) * CW + cc];
-        mine[i] = s;
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0)
-        last_flag = atomicInc(&cnt[grp * nslices + slice], (uint32_t)(nsplit - 1)) == (uint32_t)(nsplit - 1);
-    __syncthreads();
-    if (!last_flag)
-        return;
-    __threadfence();
-    // last workgroup of this slice: sum the split partials in split order
-    for (int i = threadIdx.x * 4; i < NT * CW; i += GEMV_THREADS * 4) {
-        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-        int sp = 0;
-        for (; sp + 8 <= nsplit; sp += 8) {
-            f32x4_t v[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                v[q] = *reinterpret_cast<const f32x4_t *>(pbase + (int64_t)(sp + q) * (NT * CW) + i);
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                s += v[q];
-        }
-        for (; sp < nsplit; ++sp)
-            s += *reinterpret_cast<const f32x4_t *>(pbase + (int64_t)sp * (NT * CW) + i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = (i + e) / CW, cc = (i + e) % CW;
+            s += red[ww][t][cc];
+        if (nsplit == 1) {
             if (t < nt && slice * CW + cc < M)
-                y[(int64_t)(t0 + t) * ldy + slice * CW + cc] = s[e];
+                y[(int64_t)(t0 + t) * ldy + slice * CW + cc] = s;
+        } else {
+            part[(((int64_t)grp * nslices + slice) * nsplit + split) * (NT * CW) + i] = s;
         }
     }
 }
 
+// y[t0+t][slice*CW + cc] = sum over splits (in order) of the partials.
+template <int NT, int CW>
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float *__restrict__ part, int T, int tile,
+                                                          int groups_per_tile, int nslices, int nsplit, int M,
+                                                          float *__restrict__ y, int64_t ldy)
+{
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; // over (grp, slice, NT*CW)
+    const int i = (int)(gid % (NT * CW));
+    const int64_t gs = gid / (NT * CW);
+    const int slice = (int)(gs % nslices), grp = (int)(gs / nslices);
+    const int tau = grp / groups_per_tile, sub = grp % groups_per_tile;
+    const int t0 = tau * tile + sub * NT;
+    const int t = i / CW, cc = i % CW;
+    const int tend = min(T, tau * tile + tile);
+    if (t0 + t >= tend || slice * CW + cc >= M)
+        return;
+    const float *p = part + ((int64_t)grp * nslices + slice) * nsplit * (NT * CW) + i;
+    float v[GEMV_MAX_SPLIT];
+#pragma unroll
+    for (int s = 0; s < GEMV_MAX_SPLIT; ++s)
+        v[s] = s < nsplit ? p[(int64_t)s * (NT * CW)] : 0.0f;
+    float a = 0.0f;
+#pragma unroll
+    for (int s = 0; s < GEMV_MAX_SPLIT; ++s)
+        a += v[s];
+    y[(int64_t)(t0 + t) * ldy + slice * CW + cc] = a;
+}
+
 struct GemvPlan {
-    int nt, groups_per_tile, nslices, nsplit, rows_cap, ngroups;
-    size_t lds;
+    int nt, groups_per_tile, nslices, nsplit, ngroups;
 };
 
 static int nt_for(int64_t rows)
@@ -188,25 +179,15 @@ static GemvPlan gemv_plan(int64_t T, int64_t M, int64_t k, int64_t tile, bool bf
     const int cw = WAVE * (bf16 ? 8 : 4);
     p.nslices = (int)((M + cw - 1) / cw);
     const int64_t base = (int64_t)p.ngroups * p.nslices;
-    int64_t ns = 1;
-    if (base <= GEMV_MAX_COUNTERS) {
-        ns = (GEMV_TARGET_WGS + base - 1) / base;
-        int64_t by_rows = k / GEMV_MIN_ROWS;
-        if (ns > by_rows)
-            ns = by_rows;
-        if (ns > GEMV_MAX_SPLIT)
-            ns = GEMV_MAX_SPLIT;
-        if (ns < 1)
-            ns = 1;
-    }
+    int64_t ns = (GEMV_TARGET_WGS + base - 1) / base;
+    const int64_t by_rows = (k + GEMV_WAVES * GEMV_MIN_ROWS - 1) / (GEMV_WAVES * GEMV_MIN_ROWS);
+    if (ns > by_rows)
+        ns = by_rows;
+    if (ns > GEMV_MAX_SPLIT)
+        ns = GEMV_MAX_SPLIT;
+    if (ns < 1)
+        ns = 1;
     p.nsplit = (int)ns;
-    const int64_t per = (k + ns - 1) / ns;
-    p.rows_cap = (int)(per < GEMV_ROWS_CAP ? per : GEMV_ROWS_CAP);
-    if (p.rows_cap < 1)
-        p.rows_cap = 1;
-    const size_t stage = (size_t)p.rows_cap * (1 + p.nt) * 4;
-    const size_t redb = (size_t)GEMV_WAVES * p.nt * cw * 4;
-    p.lds = stage > redb ? stage : redb;
     return p;
 }
 
@@ -222,14 +203,20 @@ size_t gemv_ws_bytes(int64_t T, int64_t M, int64_t k, int64_t tile, bool bf16)
 template <typename TE, bool DENSE>
 static hipError_t gemv_dispatch(const GemvPlan &p, const void *x, int64_t ldx, int64_t T, int64_t tile,
                                 const void *wt, int64_t ldw, int64_t M, const int32_t *idx, int64_t k, float *part,
-                                uint32_t *cnt, float *y, int64_t ldy, hipStream_t st)
+                                float *y, int64_t ldy, hipStream_t st)
 {
+    constexpr int CW = WAVE * Vec16<TE>::N;
     dim3 grid((unsigned)((int64_t)p.ngroups * p.nslices * p.nsplit));
+    const int64_t nred = (int64_t)p.ngroups * p.nslices * p.nt * CW;
+    dim3 rgrid((unsigned)((nred + 255) / 256));
 #define RMM_GEMV_CASE(NTV)                                                                                         \
     case NTV:                                                                                                      \
-        gemv_kernel<TE, NTV, DENSE><<<grid, GEMV_THREADS, p.lds, st>>>(                                            \
+        gemv_kernel<TE, NTV, DENSE><<<grid, GEMV_THREADS, 0, st>>>(                                                \
             (const TE *)x, ldx, (int)T, (int)tile, (const TE *)wt, ldw, (int)M, idx, (int)k, p.groups_per_tile,     \
-            p.nslices, p.nsplit, p.rows_cap, part, cnt, y, ldy);                                                   \
+            p.nslices, p.nsplit, part, y, ldy);                                                                    \
+        if (p.nsplit > 1)                                                                                          \
+            gemv_reduce_kernel<NTV, CW><<<rgrid, 256, 0, st>>>(part, (int)T, (int)tile, p.groups_per_tile,          \
+                                                                p.nslices, p.nsplit, (int)M, y, ldy);              \
         break;
     switch (p.nt) {
         RMM_GEMV_CASE(1)
@@ -247,12 +234,13 @@ hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const v
                        const int32_t *idx, int64_t k, int64_t tile, bool dense, float *y, int64_t ldy, float *part,
                        uint32_t *cnt, hipStream_t st)
 {
+    (void)cnt;
     GemvPlan p = gemv_plan(T, M, k, tile, bf16);
     if (bf16)
-        return dense ? gemv_dispatch<uint16_t, true>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, cnt, y, ldy, st)
-                     : gemv_dispatch<uint16_t, false>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, cnt, y, ldy, st);
-    return dense ? gemv_dispatch<float, true>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, cnt, y, ldy, st)
-                 : gemv_dispatch<float, false>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, cnt, y, ldy, st);
+        return dense ? gemv_dispatch<uint16_t, true>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, y, ldy, st)
+                     : gemv_dispatch<uint16_t, false>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, y, ldy, st);
+    return dense ? gemv_dispatch<float, true>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, y, ldy, st)
+                 : gemv_dispatch<float, false>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, y, ldy, st);
 }
 
 // ============================================================================ gather
@@ -451,16 +439,6 @@ hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const v
     return hipGetLastError();
 }
 
-void linear_init()
-{
-    (void)hipFuncSetAttribute((const void *)gemv_kernel<uint16_t, 8, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        160 * 1024);
-    (void)hipFuncSetAttribute((const void *)gemv_kernel<uint16_t, 8, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        160 * 1024);
-    (void)hipFuncSetAttribute((const void *)gemv_kernel<float, 8, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        160 * 1024);
-    (void)hipFuncSetAttribute((const void *)gemv_kernel<float, 8, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        160 * 1024);
-}
+void linear_init() {}
 
 } // namespace rmm
