@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--headline-only", action="store_true", help="only r = 0.5 of the decode shape (profiling)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run plain device-to-device copies of 256 MiB (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -145,8 +147,8 @@ def load_traffic(kernel: str, sha: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported (see DESIGN.md for how "
-              f"it would shard)", file=sys.stderr)
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported (multi-GPU sharding is "
+              f"a design, not a build)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -163,6 +165,16 @@ def main():
     torch.cuda.set_device(dev)
     rmm.lib()
     steps, warmup = args.steps, args.warmup
+    if args.calibrate_copy:
+        # a plain copy of known size: reads and writes exactly 256 MiB per launch
+        src = torch.empty(64 * 2**20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "launches": steps}))
+        return
 
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
