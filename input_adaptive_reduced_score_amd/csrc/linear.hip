@@ -244,30 +244,39 @@ hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const v
 }
 
 // ============================================================================ gather
-// xg[t][i] = x[t][idx[t/tile][i]] for i < k, 0 for k <= i < kpad.
-__global__ __launch_bounds__(256) void gather_kernel(const uint16_t *__restrict__ x, int64_t ldx, int T, int tile,
+// xg[t][i] = x[t][idx[t/tile][i]] for i < k, 0 for k <= i < kpad.  One workgroup
+// per token row: with STAGE the row is staged in LDS with 16-byte loads (rows up
+// to GATHER_LDS_MAX_K elements), then gathered; without, gathered from HBM.
+constexpr int GATHER_LDS_MAX_K = 32768;
+template <bool STAGE>
+__global__ __launch_bounds__(256) void gather_kernel(const uint16_t *__restrict__ x, int64_t ldx, int K, int tile,
                                                      const int32_t *__restrict__ idx, int k, int kpad,
                                                      uint16_t *__restrict__ xg)
 {
-    const int cpr = kpad / 8;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= (int64_t)T * cpr)
-        return;
-    const int t = (int)(gid / cpr), ch = (int)(gid % cpr);
-    const int32_t *J = idx + (int64_t)(t / tile) * k;
+    extern __shared__ uint16_t xrow[];
+    const int t = blockIdx.x;
     const uint16_t *xr = x + (int64_t)t * ldx;
-    uint32_t h[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int i = ch * 8 + e;
-        h[e] = i < k ? xr[J[i]] : 0u;
+    if (STAGE) {
+        // ldx is a multiple of 8, so the 16-byte run past K stays inside the row's pitch
+        for (int c = threadIdx.x * 8; c < K; c += 256 * 8)
+            *reinterpret_cast<uint4 *>(xrow + c) = *reinterpret_cast<const uint4 *>(xr + c);
+        __syncthreads();
     }
-    uint4 o;
-    o.x = h[0] | (h[1] << 16);
-    o.y = h[2] | (h[3] << 16);
-    o.z = h[4] | (h[5] << 16);
-    o.w = h[6] | (h[7] << 16);
-    *reinterpret_cast<uint4 *>(xg + (int64_t)t * kpad + ch * 8) = o;
+    const int32_t *J = idx + (int64_t)(t / tile) * k;
+    for (int ch = threadIdx.x; ch < kpad / 8; ch += 256) {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = ch * 8 + e;
+            h[e] = i < k ? (STAGE ? xrow[J[i]] : xr[J[i]]) : 0u;
+        }
+        uint4 o;
+        o.x = h[0] | (h[1] << 16);
+        o.y = h[2] | (h[3] << 16);
+        o.z = h[4] | (h[5] << 16);
+        o.w = h[6] | (h[7] << 16);
+        *reinterpret_cast<uint4 *>(xg + (int64_t)t * kpad + ch * 8) = o;
+    }
 }
 
 // ============================================================================ MFMA GEMM
@@ -301,8 +310,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__re
     const int ar = tid >> 3, ac = tid & 7;
     // B loader: lane = k row within the step, chunks w + 4p of 8 columns
     uint4 ra[4], rb[4];
-
-    auto load_stage = [&](int kk) {
+    // the W^T row index of this lane for a step, loaded one step before its rows are
+    auto jrow = [&](int kk) {
+        int kr = kk + lane;
+        kr = kr < klim ? kr : klim - 1; // padded steps reuse a valid row (times zero A)
+        return DENSE ? kr : J[kr];
+    };
+    auto load_stage = [&](int kk, int j) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int r = ar + 32 * p;
@@ -325,9 +339,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__re
             }
             ra[p] = v;
         }
-        int kr = kk + lane;
-        kr = kr < klim ? kr : klim - 1; // padded steps reuse a valid row (times zero A)
-        const int j = DENSE ? kr : J[kr];
         const uint16_t *wrow = wt + (int64_t)j * ldw;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -339,6 +350,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__re
 #pragma unroll
         for (int p = 0; p < 4; ++p)
             *reinterpret_cast<uint4 *>(&As[buf][(ar + 32 * p) * LPITCH + 8 * ac]) = ra[p];
+        // B^T: transposed on the way into LDS so both operands read as 16-byte k-runs
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int nbase = 8 * (w + 4 * p);
@@ -350,6 +362,15 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__re
             }
         }
     };
+    auto frags = [&](int cur, int ks, bf16x8_t(&a)[2], bf16x8_t(&b)[2]) {
+        const int kofs = ks * 16 + 8 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            a[i] = *reinterpret_cast<const bf16x8_t *>(&As[cur][(wm * 64 + i * 32 + (lane & 31)) * LPITCH + kofs]);
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn)
+            b[jn] = *reinterpret_cast<const bf16x8_t *>(&Bs[cur][(wn * 64 + jn * 32 + (lane & 31)) * LPITCH + kofs]);
+    };
 
     f32x16_t acc[2][2];
 #pragma unroll
@@ -359,36 +380,37 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__re
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 acc[i][jn][r] = 0.0f;
+    auto mma = [&](bf16x8_t(&a)[2], bf16x8_t(&b)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jn = 0; jn < 2; ++jn)
+                acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[jn], acc[i][jn], 0, 0, 0);
+    };
 
     const int ksteps = (klim + GB_K - 1) / GB_K;
-    load_stage(0);
+    load_stage(0, jrow(0));
+    int jnext = ksteps > 1 ? jrow(GB_K) : 0;
     store_stage(0);
     __syncthreads();
     for (int s = 0; s < ksteps; ++s) {
         const int cur = s & 1;
-        if (s + 1 < ksteps)
-            load_stage((s + 1) * GB_K);
-#pragma unroll
-        for (int ks = 0; ks < GB_K / 16; ++ks) {
-            const int kofs = ks * 16 + 8 * (lane >> 5);
-            bf16x8_t a[2], b[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = wm * 64 + i * 32 + (lane & 31);
-                a[i] = *reinterpret_cast<const bf16x8_t *>(&As[cur][row * LPITCH + kofs]);
-            }
-#pragma unroll
-            for (int jn = 0; jn < 2; ++jn) {
-                const int col = wn * 64 + jn * 32 + (lane & 31);
-                b[jn] = *reinterpret_cast<const bf16x8_t *>(&Bs[cur][col * LPITCH + kofs]);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int jn = 0; jn < 2; ++jn)
-                    acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[jn], acc[i][jn], 0, 0, 0);
-        }
-        if (s + 1 < ksteps)
+        const bool more = s + 1 < ksteps;
+        if (more)
+            load_stage((s + 1) * GB_K, jnext);
+        if (s + 2 < ksteps)
+            jnext = jrow((s + 2) * GB_K);
+        // fragments of sub-step ks+1 load while sub-step ks multiplies
+        bf16x8_t a0[2], b0[2], a1[2], b1[2];
+        frags(cur, 0, a0, b0);
+        frags(cur, 1, a1, b1);
+        mma(a0, b0);
+        frags(cur, 2, a0, b0);
+        mma(a1, b1);
+        frags(cur, 3, a1, b1);
+        mma(a0, b0);
+        mma(a1, b1);
+        if (more)
             store_stage(cur ^ 1);
         __syncthreads();
     }
@@ -431,14 +453,21 @@ hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const v
         return hipGetLastError();
     }
     const int64_t kpad = (k + GB_K - 1) / GB_K * GB_K;
-    const int64_t nthreads = T * (kpad / 8);
-    gather_kernel<<<(unsigned)((nthreads + 255) / 256), 256, 0, st>>>((const uint16_t *)x, ldx, (int)T, (int)tile,
-                                                                       idx, (int)k, (int)kpad, (uint16_t *)xg);
+    if (K <= GATHER_LDS_MAX_K)
+        gather_kernel<true><<<(unsigned)T, 256, (size_t)(K + 7) / 8 * 16, st>>>(
+            (const uint16_t *)x, ldx, (int)K, (int)tile, idx, (int)k, (int)kpad, (uint16_t *)xg);
+    else
+        gather_kernel<false><<<(unsigned)T, 256, 0, st>>>((const uint16_t *)x, ldx, (int)K, (int)tile, idx, (int)k,
+                                                          (int)kpad, (uint16_t *)xg);
     gemm_kernel<false><<<grid, GEMM_THREADS, 0, st>>>((const uint16_t *)xg, kpad, (int)T, (int)tile, mblocks,
                                                       (const uint16_t *)wt, ldw, (int)M, idx, (int)k, (int)k, y, ldy);
     return hipGetLastError();
 }
 
-void linear_init() {}
+void linear_init()
+{
+    (void)hipFuncSetAttribute((const void *)gather_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              GATHER_LDS_MAX_K * 2);
+}
 
 } // namespace rmm

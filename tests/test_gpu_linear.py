@@ -78,6 +78,24 @@ def test_ragged_and_edge_shapes(T, K, M, tile, dtype):
         run_case(cs, r)
 
 
+@pytest.mark.parametrize("K,dense", [(40000, False), (40000, True), (32776, False)])
+def test_linear_beyond_selector_k(K, dense):
+    # K above the selector's limit: the index list comes from the caller (here the
+    # oracle), the MFMA path gathers straight from HBM instead of staging the row
+    cs = W.linear_random(70, K, 136, 64, "bf16", seed=K)
+    print(f"[case] K={K} dense={dense}", flush=True)
+    x, wt = dev_padded(cs.x), dev_padded(cs.wt)
+    if dense:
+        y = rmm.linear_dense(x, wt)
+        yr = oracle.dense_linear(cs.x, cs.wt)
+    else:
+        idx_ref = oracle.select(cs.x, cs.c, 64, 0.05)
+        y = rmm.linear(x, wt, dev(idx_ref), 64)
+        yr = oracle.linear(cs.x, cs.wt, idx_ref, 64)
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), yr) <= TOL
+
+
 def test_strided_operands():
     # leading dimensions larger than the logical sizes (views into bigger buffers)
     cs = W.linear_random(40, 200, 72, 32, "bf16", seed=3)
