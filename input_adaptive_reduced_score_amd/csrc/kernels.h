@@ -40,7 +40,6 @@ namespace rmm {
 
 // select.hip
 size_t select_ws_bytes(int64_t T, int64_t K, int64_t tile);
-size_t select_lds_bytes(int64_t K);
 hipError_t launch_select(const void *x, bool bf16, int64_t T, int64_t K, int64_t ldx, const float *c, int64_t tile,
                          int64_t k, int32_t *idx, float *pmax_ws, hipStream_t st);
 void select_init();

@@ -131,32 +131,49 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(
     }
 }
 
-// y[t0+t][slice*CW + cc] = sum over splits (in order) of the partials.
+// y[t0+t][slice*CW + cc] = sum over splits of the partials, in a fixed order.
+// Workgroup = 64 consecutive partial elements of one (group, slice); wave w sums
+// the w-th eighth of the splits in split order, then wave 0 adds the eight
+// wave sums in wave order.
+constexpr int RED_WAVES = 8;
 template <int NT, int CW>
-__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float *__restrict__ part, int T, int tile,
-                                                          int groups_per_tile, int nslices, int nsplit, int M,
-                                                          float *__restrict__ y, int64_t ldy)
+__global__ __launch_bounds__(RED_WAVES * WAVE) void gemv_reduce_kernel(const float *__restrict__ part, int T,
+                                                                       int tile, int groups_per_tile, int nslices,
+                                                                       int nsplit, int M, float *__restrict__ y,
+                                                                       int64_t ldy)
 {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; // over (grp, slice, NT*CW)
-    const int i = (int)(gid % (NT * CW));
-    const int64_t gs = gid / (NT * CW);
-    const int slice = (int)(gs % nslices), grp = (int)(gs / nslices);
+    constexpr int CHUNKS = NT * CW / WAVE;
+    __shared__ float red[RED_WAVES][WAVE];
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+    const int chunk = blockIdx.x % CHUNKS;
+    const int gs = blockIdx.x / CHUNKS;
+    const int slice = gs % nslices, grp = gs / nslices;
+    const int i = chunk * WAVE + lane;
+    const float *p = part + (int64_t)gs * nsplit * (NT * CW) + i;
+    const int s0 = nsplit * w / RED_WAVES, s1 = nsplit * (w + 1) / RED_WAVES;
+    constexpr int MAXS = (GEMV_MAX_SPLIT + RED_WAVES - 1) / RED_WAVES;
+    float v[MAXS];
+#pragma unroll
+    for (int q = 0; q < MAXS; ++q)
+        v[q] = s0 + q < s1 ? p[(int64_t)(s0 + q) * (NT * CW)] : 0.0f;
+    float a = 0.0f;
+#pragma unroll
+    for (int q = 0; q < MAXS; ++q)
+        a += v[q];
+    red[w][lane] = a;
+    __syncthreads();
+    if (w != 0)
+        return;
+    float sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < RED_WAVES; ++q)
+        sum += red[q][lane];
     const int tau = grp / groups_per_tile, sub = grp % groups_per_tile;
     const int t0 = tau * tile + sub * NT;
     const int t = i / CW, cc = i % CW;
     const int tend = min(T, tau * tile + tile);
-    if (t0 + t >= tend || slice * CW + cc >= M)
-        return;
-    const float *p = part + ((int64_t)grp * nslices + slice) * nsplit * (NT * CW) + i;
-    float v[GEMV_MAX_SPLIT];
-#pragma unroll
-    for (int s = 0; s < GEMV_MAX_SPLIT; ++s)
-        v[s] = s < nsplit ? p[(int64_t)s * (NT * CW)] : 0.0f;
-    float a = 0.0f;
-#pragma unroll
-    for (int s = 0; s < GEMV_MAX_SPLIT; ++s)
-        a += v[s];
-    y[(int64_t)(t0 + t) * ldy + slice * CW + cc] = a;
+    if (t0 + t < tend && slice * CW + cc < M)
+        y[(int64_t)(t0 + t) * ldy + slice * CW + cc] = sum;
 }
 
 struct GemvPlan {
@@ -207,15 +224,14 @@ static hipError_t gemv_dispatch(const GemvPlan &p, const void *x, int64_t ldx, i
 {
     constexpr int CW = WAVE * Vec16<TE>::N;
     dim3 grid((unsigned)((int64_t)p.ngroups * p.nslices * p.nsplit));
-    const int64_t nred = (int64_t)p.ngroups * p.nslices * p.nt * CW;
-    dim3 rgrid((unsigned)((nred + 255) / 256));
+    dim3 rgrid((unsigned)((int64_t)p.ngroups * p.nslices * (p.nt * CW / WAVE)));
 #define RMM_GEMV_CASE(NTV)                                                                                         \
     case NTV:                                                                                                      \
         gemv_kernel<TE, NTV, DENSE><<<grid, GEMV_THREADS, 0, st>>>(                                                \
             (const TE *)x, ldx, (int)T, (int)tile, (const TE *)wt, ldw, (int)M, idx, (int)k, p.groups_per_tile,     \
             p.nslices, p.nsplit, part, y, ldy);                                                                    \
         if (p.nsplit > 1)                                                                                          \
-            gemv_reduce_kernel<NTV, CW><<<rgrid, 256, 0, st>>>(part, (int)T, (int)tile, p.groups_per_tile,          \
+            gemv_reduce_kernel<NTV, CW><<<rgrid, RED_WAVES * WAVE, 0, st>>>(part, (int)T, (int)tile, p.groups_per_tile,          \
                                                                 p.nslices, p.nsplit, (int)M, y, ldy);              \
         break;
     switch (p.nt) {

@@ -17,6 +17,8 @@
 namespace rmm {
 
 constexpr int SEL_THREADS = 1024;
+constexpr uint32_t SEL_CAND_CAP = 256; // crossing-digit keys ranked directly
+constexpr uint32_t SEL_RANK_SPLIT = SEL_THREADS / SEL_CAND_CAP; // threads per candidate in the ranking
 constexpr int COLMAX_THREADS = 256;
 
 // Partial column maxima of |x| over row chunks of a tile.
@@ -76,125 +78,156 @@ __global__ __launch_bounds__(COLMAX_THREADS) void colmax_kernel(const TE *__rest
     }
 }
 
-// Histogram bins are stored with one pad word per 32 bins so that wave 0,
-// whose lane l reads 32 consecutive bins, touches distinct LDS banks.
+// 8 consecutive elements from p as floats; `avail` of them are in range.  The
+// 16-byte vector holding the first element is always read (row pitches are
+// multiples of 16 bytes); for fp32 the second only if it holds one in range.
+__device__ __forceinline__ void load8(const uint16_t *p, int avail, float (&v)[8])
+{
+    (void)avail;
+    Vec16<uint16_t>::unpack(*reinterpret_cast<const uint4 *>(p), v);
+}
+__device__ __forceinline__ void load8(const float *p, int avail, float (&v)[8])
+{
+    const uint4 lo = *reinterpret_cast<const uint4 *>(p);
+    const uint4 hi = avail > 4 ? *reinterpret_cast<const uint4 *>(p + 4) : make_uint4(0u, 0u, 0u, 0u);
+    v[0] = __uint_as_float(lo.x); v[1] = __uint_as_float(lo.y); v[2] = __uint_as_float(lo.z); v[3] = __uint_as_float(lo.w);
+    v[4] = __uint_as_float(hi.x); v[5] = __uint_as_float(hi.y); v[6] = __uint_as_float(hi.z); v[7] = __uint_as_float(hi.w);
+}
+
+// Histogram bins are stored with one pad word per 32 bins: bin 32g+e sits at
+// word 33g+e, so the 32 bins of group g are contiguous and the 64 groups that
+// wave 0's lanes read start in distinct LDS banks.
 __device__ __forceinline__ int hpad(int b) { return b + (b >> 5); }
 constexpr int SEL_HIST_WORDS = SEL_BINS + SEL_BINS / 32;
 
-// Wave 0 finds the digit holding the krem-th largest key (lane l covers bins
-// 2047-32l down to 2016-32l), clears the histogram and publishes
-// (digit, rank inside the digit) in res[0..1].
-__device__ __forceinline__ void wave0_crossing(uint32_t *hist, uint32_t krem, uint32_t *res)
+// The whole block finds the digit holding the krem-th largest key, clears the
+// histogram and publishes (digit, rank inside the digit, keys in the digit) in
+// res[0..2].  Thread t owns bins 2047-2t and 2046-2t, so threads in ascending
+// order walk the bins from the top: a wave scan plus one exchange of wave
+// totals gives every thread the count above its bins.  Contains barriers.
+__device__ __forceinline__ void block_crossing(uint32_t *hist, uint32_t krem, uint32_t *wtot, uint32_t *res)
 {
-    const int lane = threadIdx.x & (WAVE - 1);
-    uint32_t h[32];
-    const int top = SEL_BINS - 1 - 32 * lane;
-    uint32_t tot = 0;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    const int b0 = SEL_BINS - 1 - 2 * tid; // the higher of the thread's two bins
+    const uint32_t h0 = hist[hpad(b0)], h1 = hist[hpad(b0 - 1)];
+    hist[hpad(b0)] = 0;
+    hist[hpad(b0 - 1)] = 0;
+    const uint32_t sum = h0 + h1;
+    const uint32_t incl = wave_incl_sum(sum);
+    if (lane == WAVE - 1)
+        wtot[w] = incl;
+    __syncthreads();
+    uint32_t above = incl - sum;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-        h[e] = hist[hpad(top - e)];
-        tot += h[e];
+    for (int v = 0; v < SEL_THREADS / WAVE; ++v)
+        above += v < w ? wtot[v] : 0u;
+    if (above < krem && krem <= above + sum) {
+        const bool hi = krem <= above + h0;
+        res[0] = (uint32_t)(hi ? b0 : b0 - 1);
+        res[1] = hi ? krem - above : krem - above - h0;
+        res[2] = hi ? h0 : h1;
     }
-#pragma unroll
-    for (int e = 0; e < 32; ++e)
-        hist[hpad(top - e)] = 0;
-    const uint32_t incl = wave_incl_sum(tot);
-    uint32_t run = incl - tot;
-    if (run < krem && krem <= incl) {
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            if (run < krem && krem <= run + h[e]) {
-                res[0] = (uint32_t)(top - e);
-                res[1] = krem - run;
-            }
-            run += h[e];
-        }
-    }
+    __syncthreads();
 }
 
 // Scorer + selector, one workgroup of 1024 threads (16 waves) per tile.
-// Wave w owns the contiguous block of slices [w*BW, (w+1)*BW); lane l handles
-// slices w*BW + 64*i + l (coalesced loads); keys live in LDS at their slice
-// index.  Keys are re-based as u = key - (smallest non-zero key) + 1 (0 stays
-// 0), an order-preserving map, so the first radix digit spans the keys' actual
-// range instead of the few float exponents they share.  The kept list is
-// written in ascending order by per-wave ballots after one exchange of wave
-// totals.  direct: score straight from x (few rows per tile); otherwise from
-// the column-max partials (row pitch Kp).
+// Thread t scores slices t*PER .. t*PER+PER-1 (16-byte loads) and keeps their
+// keys in registers for the whole kernel; threads in ascending order hold the
+// slices in ascending order, so every ordered count is a per-lane count plus a
+// wave scan plus one exchange of wave totals (vector ALU work, no per-element
+// ballots).  Slots past K hold key 0: they rank after every real key (value 0,
+// highest indices) and k <= K, so they are never kept.  Keys are re-based as
+// u = key - (smallest non-zero key) + 1 (0 stays 0), an order-preserving map,
+// so the first radix digit spans the keys' actual range instead of the few
+// float exponents they share.  direct: score straight from x (few rows per
+// tile); otherwise from the column-max partials (row pitch Kp).
 template <typename TE, int PER>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restrict__ x, int64_t ldx, int T, int K,
                                                              int tile, const float *__restrict__ c,
                                                              const float *__restrict__ pmax, int Kp, int nrsplit,
-                                                             int direct, int k, int32_t *__restrict__ idx)
+                                                             int direct, int cvec, int k, int32_t *__restrict__ idx)
 {
+    static_assert(PER % 8 == 0, "slices per thread come in 8-slice chunks");
     constexpr int NW = SEL_THREADS / WAVE;
-    constexpr int LB = PER < 16 ? PER : 16; // loads in flight per lane per batch
-    extern __shared__ uint32_t kl[];        // keys, then re-based keys, at slice index
+    constexpr int CH = PER / 8; // chunks per thread
     __shared__ uint32_t hist[SEL_HIST_WORDS];
-    __shared__ uint32_t wmin[NW], wmax[NW], wgt[NW], weq[NW];
-    __shared__ uint32_t res[2];
+    __shared__ uint32_t wmin[NW], wmax[NW], wgt[NW], weq[NW], wtot[NW];
+    __shared__ uint2 cand[SEL_CAND_CAP];
+    __shared__ uint32_t rk_above[SEL_RANK_SPLIT][SEL_CAND_CAP], rk_tie[SEL_RANK_SPLIT][SEL_CAND_CAP];
+    __shared__ uint32_t res[5], ncand;
+    extern __shared__ int32_t outl[]; // k entries: the kept list before it is written out
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, tau = blockIdx.x;
-    const int jb = w * (PER * WAVE) + lane; // slice of element i: jb + 64*i
+    const int j0 = tid * PER; // first slice of this thread
+    const int lim = K - j0;   // registers i < lim hold real slices
 
     for (int i = tid; i < SEL_HIST_WORDS; i += SEL_THREADS)
         hist[i] = 0;
     if (tid == 0) {
         res[0] = 0;
         res[1] = 1;
+        res[2] = 0;
+        res[3] = 0;
+        res[4] = 0;
+        ncand = 0;
     }
 
-    // 1. scores -> keys, in batches of LB loads per lane
+    // 1. scores -> keys
+    float a[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        a[i] = 0.0f;
+    if (direct) {
+        const int t0 = tau * tile, t1 = min(T, t0 + tile);
+        for (int t = t0; t < t1; ++t) {
+            const TE *xr = x + (int64_t)t * ldx;
+#pragma unroll
+            for (int m = 0; m < CH; ++m) {
+                const int jc = j0 + 8 * m;
+                if (jc < K) {
+                    float f[8];
+                    load8(xr + jc, K - jc, f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        a[8 * m + e] = fmaxf(a[8 * m + e], fabsf(f[e]));
+                }
+            }
+        }
+    } else {
+        const float *pm = pmax + (int64_t)tau * nrsplit * Kp;
+        for (int rs = 0; rs < nrsplit; ++rs) {
+#pragma unroll
+            for (int m = 0; m < CH; ++m) {
+                const int jc = j0 + 8 * m;
+                if (jc < K) {
+                    float f[8];
+                    load8(pm + (int64_t)rs * Kp + jc, K - jc, f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        a[8 * m + e] = fmaxf(a[8 * m + e], f[e]);
+                }
+            }
+        }
+    }
+    uint32_t uk[PER];
     uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-    for (int i0 = 0; i0 < PER; i0 += LB) {
-        float a[LB];
-#pragma unroll
-        for (int i = 0; i < LB; ++i)
-            a[i] = 0.0f;
-        if (direct) {
-            const int t0 = tau * tile, t1 = min(T, t0 + tile);
-            for (int t = t0; t < t1; ++t) {
-                const TE *xr = x + (int64_t)t * ldx;
-                float f[LB];
-#pragma unroll
-                for (int i = 0; i < LB; ++i) {
-                    const int j = jb + 64 * (i0 + i);
-                    f[i] = j < K ? ld_elem(xr, j) : 0.0f;
-                }
-#pragma unroll
-                for (int i = 0; i < LB; ++i)
-                    a[i] = fmaxf(a[i], fabsf(f[i]));
-            }
+    for (int m = 0; m < CH; ++m) {
+        const int jc = j0 + 8 * m;
+        const int avail = K - jc; // <= 0 past the end
+        float cw[8];
+        if (cvec && avail >= 8) {
+            load8(c + jc, 8, cw);
         } else {
-            const float *pm = pmax + (int64_t)tau * nrsplit * Kp;
-            for (int rs = 0; rs < nrsplit; ++rs) {
-                float f[LB];
 #pragma unroll
-                for (int i = 0; i < LB; ++i) {
-                    const int j = jb + 64 * (i0 + i);
-                    f[i] = j < K ? pm[(int64_t)rs * Kp + j] : 0.0f;
-                }
-#pragma unroll
-                for (int i = 0; i < LB; ++i)
-                    a[i] = fmaxf(a[i], f[i]);
-            }
-        }
-        float cw[LB];
-#pragma unroll
-        for (int i = 0; i < LB; ++i) {
-            const int j = jb + 64 * (i0 + i);
-            cw[i] = j < K ? c[j] : 0.0f;
+            for (int e = 0; e < 8; ++e)
+                cw[e] = e < avail ? c[jc + e] : 0.0f;
         }
 #pragma unroll
-        for (int i = 0; i < LB; ++i) {
-            const int j = jb + 64 * (i0 + i);
-            if (j < K) {
-                const uint32_t key = nonneg_key(__fmul_rn(a[i], cw[i]));
-                kl[j] = key;
-                if (key != 0u)
-                    mn = min(mn, key);
-                mx = max(mx, key);
-            }
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t key = e < avail ? nonneg_key(__fmul_rn(a[8 * m + e], cw[e])) : 0u;
+            uk[8 * m + e] = key;
+            mn = min(mn, key == 0u ? 0xffffffffu : key);
+            mx = max(mx, key);
         }
     }
     mn = wave_min_u32(mn);
@@ -209,83 +242,157 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
         mn = min(mn, wmin[i]);
         mx = max(mx, wmax[i]);
     }
-    // re-base in place: u = key - mn + 1 for key > 0, 0 stays 0 (mn = smallest non-zero key)
+    // re-base: u = key - mn + 1 for key > 0, 0 stays 0 (mn = smallest non-zero key)
     const uint32_t umax = mx == 0u ? 0u : mx - mn + 1u;
-    for (int i = 0; i < PER; ++i) {
-        const int j = jb + 64 * i;
-        if (j < K) {
-            const uint32_t key = kl[j];
-            kl[j] = key == 0u ? 0u : key - mn + 1u;
-        }
-    }
     const int L = umax == 0u ? 0 : 32 - __clz(umax);
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        uk[i] = uk[i] == 0u ? 0u : uk[i] - mn + 1u;
 
-    // 2. radix passes from the top bit of umax, up to 11 bits each
+    // 2. radix passes from the top bit of umax, up to 11 bits each.  After a
+    // pass, if few keys share the crossing digit they are gathered and ranked
+    // exactly (key descending, then slice ascending), which settles the rest.
     uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k;
     int top = L;
     while (top > 0) {
         const int nb = top < 11 ? top : 11;
         const int sh = top - nb;
         const uint32_t dm = (1u << nb) - 1u;
-#pragma unroll 4
+        // zero keys (all in bin 0) are counted per lane and added once per
+        // wave: same-address LDS atomics serialise
+        uint32_t zc = 0;
+#pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int j = jb + 64 * i;
-            if (j < K) {
-                const uint32_t uu = kl[j];
-                if ((uu & pmask) == prefix)
-                    atomicAdd(&hist[hpad((int)((uu >> sh) & dm))], 1u);
+            if (i < lim && (uk[i] & pmask) == prefix) {
+                if (uk[i] == 0u)
+                    ++zc;
+                else
+                    atomicAdd(&hist[hpad((int)((uk[i] >> sh) & dm))], 1u);
             }
         }
+        if (prefix == 0u) {
+            const uint32_t zw = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(zc), WAVE - 1);
+            if (lane == 0 && zw != 0u)
+                atomicAdd(&hist[hpad(0)], zw);
+        }
         __syncthreads();
-        if (w == 0)
-            wave0_crossing(hist, krem, res);
-        __syncthreads();
+        block_crossing(hist, krem, wtot, res);
         prefix |= res[0] << sh;
         pmask |= dm << sh;
         krem = res[1];
+        const uint32_t nc = res[2];
         top = sh;
+        if (top > 0 && nc <= SEL_CAND_CAP) {
+            // gather the crossing digit's keys (any order): per-lane count, wave
+            // scan, one slot reservation per wave
+            uint32_t cl = 0;
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                cl += i < lim && (uk[i] & pmask) == prefix;
+            const uint32_t cincl = wave_incl_sum(cl);
+            const uint32_t wcount = (uint32_t)__builtin_amdgcn_readlane((int)cincl, WAVE - 1);
+            uint32_t base = 0;
+            if (lane == 0 && wcount != 0u)
+                base = atomicAdd(&ncand, wcount);
+            base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+            uint32_t slot = base + cincl - cl;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                if (i < lim && (uk[i] & pmask) == prefix) {
+                    if (slot < SEL_CAND_CAP)
+                        cand[slot] = make_uint2(uk[i], (uint32_t)(j0 + i));
+                    ++slot;
+                }
+            }
+            __syncthreads();
+            // the candidate ranked krem-th fixes the threshold key and how many
+            // keys equal to it (lowest slices first) are kept.  Thread t compares
+            // candidate t % CAP with every SEL_RANK_SPLIT-th other candidate.
+            {
+                const uint32_t me_i = (uint32_t)tid % SEL_CAND_CAP, part = (uint32_t)tid / SEL_CAND_CAP;
+                if (me_i < nc) {
+                    const uint2 me = cand[me_i];
+                    uint32_t ab0 = 0, ab1 = 0, ti0 = 0, ti1 = 0;
+                    uint32_t i = part;
+                    for (; i + SEL_RANK_SPLIT < nc; i += 2 * SEL_RANK_SPLIT) {
+                        const uint2 o0 = cand[i], o1 = cand[i + SEL_RANK_SPLIT];
+                        ab0 += (o0.x > me.x) || (o0.x == me.x && o0.y < me.y);
+                        ti0 += o0.x == me.x && o0.y <= me.y;
+                        ab1 += (o1.x > me.x) || (o1.x == me.x && o1.y < me.y);
+                        ti1 += o1.x == me.x && o1.y <= me.y;
+                    }
+                    if (i < nc) {
+                        const uint2 o0 = cand[i];
+                        ab0 += (o0.x > me.x) || (o0.x == me.x && o0.y < me.y);
+                        ti0 += o0.x == me.x && o0.y <= me.y;
+                    }
+                    rk_above[part][me_i] = ab0 + ab1;
+                    rk_tie[part][me_i] = ti0 + ti1;
+                }
+            }
+            __syncthreads();
+            if (tid < (int)nc) {
+                uint32_t above = 0, tie_upto = 0;
+#pragma unroll
+                for (int q = 0; q < SEL_RANK_SPLIT; ++q) {
+                    above += rk_above[q][tid];
+                    tie_upto += rk_tie[q][tid];
+                }
+                if (above + 1u == krem) {
+                    res[3] = cand[tid].x;
+                    res[4] = tie_upto;
+                }
+            }
+            __syncthreads();
+            prefix = res[3];
+            krem = res[4];
+            break;
+        }
     }
     // (L == 0: every key is zero; prefix 0 and krem = k ties)
 
-    // 3. order-preserving compaction: per-wave counts, one exchange, ballot-ranked stores
-    uint32_t gt = 0, eq = 0;
-#pragma unroll 4
+    // 3. order-preserving compaction.  Kept: u > prefix, or u == prefix among
+    // the first krem such slices.  Output position of a slice = slices kept
+    // before it = (greater before) + min(equal before, krem).
+    uint32_t gl = 0, el = 0;
+#pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int j = jb + 64 * i;
-        const uint32_t uu = j < K ? kl[j] : 0u;
-        gt += __popcll(__ballot(j < K && uu > prefix));
-        eq += __popcll(__ballot(j < K && uu == prefix));
+        gl += uk[i] > prefix;
+        el += uk[i] == prefix;
     }
-    if (lane == 0) {
-        wgt[w] = gt;
-        weq[w] = eq;
+    const uint32_t gincl = wave_incl_sum(gl), eincl = wave_incl_sum(el);
+    if (lane == WAVE - 1) {
+        wgt[w] = gincl;
+        weq[w] = eincl;
     }
     __syncthreads();
-    uint32_t gtb = 0, eqb = 0;
-    for (int i = 0; i < w; ++i) {
-        gtb += wgt[i];
-        eqb += weq[i];
+    uint32_t gb = gincl - gl, eb = eincl - el;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        gb += v < w ? wgt[v] : 0u;
+        eb += v < w ? weq[v] : 0u;
     }
-    const uint64_t lt = lanemask_lt();
-    int32_t *dst = idx + (int64_t)tau * k;
-#pragma unroll 2
+#pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int j = jb + 64 * i;
-        const uint32_t uu = j < K ? kl[j] : 0u;
-        const bool g = j < K && uu > prefix, e = j < K && uu == prefix;
-        const uint64_t mg = __ballot(g), me = __ballot(e);
-        const uint32_t tie_rank = eqb + __popcll(me & lt);
-        const bool keep = g || (e && tie_rank < krem);
-        const uint64_t mk = __ballot(keep);
-        const uint32_t pos = gtb + min(eqb, krem) + __popcll(mk & lt);
+        const bool g = uk[i] > prefix, e = uk[i] == prefix;
+        const bool keep = g || (e && eb < krem);
+        const uint32_t pos = gb + min(eb, krem);
         if (keep && pos < (uint32_t)k)
-            dst[pos] = j;
-        gtb += __popcll(mg);
-        eqb += __popcll(me);
+            outl[pos] = j0 + i;
+        gb += g;
+        eb += e;
     }
+    // the list is staged in LDS, then written with coalesced stores
+    __syncthreads();
+    int32_t *dst = idx + (int64_t)tau * k;
+    for (int p = tid; p < k; p += SEL_THREADS)
+        dst[p] = outl[p];
 }
 
-size_t select_lds_bytes(int64_t K) { return (size_t)K * 4; }
+static int per_for(int64_t K)
+{
+    return K <= 8 * SEL_THREADS ? 8 : K <= 16 * SEL_THREADS ? 16 : 32;
+}
 
 static int64_t pad8(int64_t n) { return (n + 7) / 8 * 8; }
 
@@ -295,6 +402,7 @@ hipError_t launch_select(const void *x, bool bf16, int64_t T, int64_t K, int64_t
     const int ntiles = (int)((T + tile - 1) / tile);
     const int rows = (int)(tile < T ? tile : T);
     const bool direct = rows <= SELECT_DIRECT_ROWS;
+    const int cvec = ((uintptr_t)c & 15u) == 0u;
     const int Kp = (int)pad8(K);
     int nrsplit = 1;
     if (!direct) {
@@ -308,24 +416,28 @@ hipError_t launch_select(const void *x, bool bf16, int64_t T, int64_t K, int64_t
             colmax_kernel<float><<<grid, COLMAX_THREADS, 0, st>>>((const float *)x, ldx, (int)T, (int)K, (int)tile,
                                                                    COLMAX_ROWS, nrsplit, Kp, pmax_ws);
     }
-#define RMM_SEL_LAUNCH(TE, PER)                                                                                    \
-    select_kernel<TE, PER><<<ntiles, SEL_THREADS, select_lds_bytes(K), st>>>(                                      \
-        (const TE *)x, ldx, (int)T, (int)K, (int)tile, c, pmax_ws, Kp, nrsplit, direct, (int)k, idx)
-    if (K <= 4 * SEL_THREADS) {
-        if (bf16)
-            RMM_SEL_LAUNCH(uint16_t, 4);
-        else
-            RMM_SEL_LAUNCH(float, 4);
-    } else if (K <= 16 * SEL_THREADS) {
-        if (bf16)
-            RMM_SEL_LAUNCH(uint16_t, 16);
-        else
-            RMM_SEL_LAUNCH(float, 16);
-    } else {
-        if (bf16)
-            RMM_SEL_LAUNCH(uint16_t, 32);
-        else
-            RMM_SEL_LAUNCH(float, 32);
+    const size_t lds = (size_t)(k + 3) / 4 * 16;
+#define RMM_SEL_LAUNCH(PER)                                                                                        \
+    do {                                                                                                           \
+        if (bf16)                                                                                                  \
+            select_kernel<uint16_t, PER><<<ntiles, SEL_THREADS, lds, st>>>(                                         \
+                (const uint16_t *)x, ldx, (int)T, (int)K, (int)tile, c, pmax_ws, Kp, nrsplit, direct, cvec, (int)k, \
+                idx);                                                                                              \
+        else                                                                                                       \
+            select_kernel<float, PER><<<ntiles, SEL_THREADS, lds, st>>>(                                            \
+                (const float *)x, ldx, (int)T, (int)K, (int)tile, c, pmax_ws, Kp, nrsplit, direct, cvec, (int)k,   \
+                idx);                                                                                              \
+    } while (0)
+    switch (per_for(K)) {
+    case 8:
+        RMM_SEL_LAUNCH(8);
+        break;
+    case 16:
+        RMM_SEL_LAUNCH(16);
+        break;
+    default:
+        RMM_SEL_LAUNCH(32);
+        break;
     }
 #undef RMM_SEL_LAUNCH
     return hipGetLastError();
@@ -343,11 +455,13 @@ size_t select_ws_bytes(int64_t T, int64_t K, int64_t tile)
 
 void select_init()
 {
-    const int lds = (int)select_lds_bytes(SELECT_MAX_K);
-    (void)hipFuncSetAttribute((const void *)select_kernel<uint16_t, 32>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    (void)hipFuncSetAttribute((const void *)select_kernel<float, 32>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    const int lds = SELECT_MAX_K * 4;
+    (void)hipFuncSetAttribute((const void *)select_kernel<uint16_t, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipFuncSetAttribute((const void *)select_kernel<float, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     (void)hipFuncSetAttribute((const void *)select_kernel<uint16_t, 16>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     (void)hipFuncSetAttribute((const void *)select_kernel<float, 16>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipFuncSetAttribute((const void *)select_kernel<uint16_t, 32>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipFuncSetAttribute((const void *)select_kernel<float, 32>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }
 
 } // namespace rmm

@@ -118,6 +118,18 @@ def test_strided_operands():
     assert np.isnan(yg[:, 72:]).all(), "wrote outside the output view"
 
 
+@pytest.mark.parametrize("K", [4096, 1003])
+def test_select_unaligned_weights(K):
+    # c starting 4 bytes past a 16-byte boundary takes the per-element load path
+    cs = W.linear_random(3, K, 8, 3, "bf16", seed=K)
+    cbuf = torch.zeros(K + 1, dtype=torch.float32, device="cuda:0")
+    cbuf[1:] = dev(cs.c)
+    for r in (0.3, 0.5):
+        idx = rmm.select(dev_padded(cs.x), cbuf[1:], 3, r)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), oracle.select(cs.x, cs.c, 3, r)), (K, r)
+
+
 def test_ties_bit_exact():
     # integer-valued activations and unit weights: many equal scores
     rng = np.random.default_rng(0)
