@@ -94,11 +94,34 @@ __device__ __forceinline__ void load8(const float *p, int avail, float (&v)[8])
     v[4] = __uint_as_float(hi.x); v[5] = __uint_as_float(hi.y); v[6] = __uint_as_float(hi.z); v[7] = __uint_as_float(hi.w);
 }
 
+// 0/1 predicates computed with integer arithmetic on values below 2^31 (keys,
+// slice indices, counts): they stay in vector registers, whereas comparisons
+// combined with && / || become lane-mask logic on the one scalar unit the
+// workgroup's 16 waves share.
+__device__ __forceinline__ uint32_t lt31(uint32_t a, uint32_t b) { return (a - b) >> 31; }        // a < b
+__device__ __forceinline__ uint32_t eq31(uint32_t a, uint32_t b) { return ((a ^ b) - 1u) >> 31; } // a == b
+__device__ __forceinline__ uint32_t ilt(int a, int b) { return ((uint32_t)a - (uint32_t)b) >> 31; } // a < b, |a-b| < 2^31
+// A copy of v the compiler cannot see through: predicates built from it stay in
+// the phase that uses them instead of being hoisted (and held in registers)
+// across the whole kernel.
+__device__ __forceinline__ int opaque(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+template <int N> __device__ __forceinline__ void opaque_all(uint32_t (&v)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        asm volatile("" : "+v"(v[i]));
+}
+
 // Histogram bins are stored with one pad word per 32 bins: bin 32g+e sits at
 // word 33g+e, so the 32 bins of group g are contiguous and the 64 groups that
 // wave 0's lanes read start in distinct LDS banks.
 __device__ __forceinline__ int hpad(int b) { return b + (b >> 5); }
 constexpr int SEL_HIST_WORDS = SEL_BINS + SEL_BINS / 32;
+constexpr int SEL_DUMMY = SEL_HIST_WORDS; // + lane: per-lane sink for masked-off histogram atomics
 
 // The whole block finds the digit holding the krem-th largest key, clears the
 // histogram and publishes (digit, rank inside the digit, keys in the digit) in
@@ -150,7 +173,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
     static_assert(PER % 8 == 0, "slices per thread come in 8-slice chunks");
     constexpr int NW = SEL_THREADS / WAVE;
     constexpr int CH = PER / 8; // chunks per thread
-    __shared__ uint32_t hist[SEL_HIST_WORDS];
+    __shared__ uint32_t hist[SEL_HIST_WORDS + WAVE];
     __shared__ uint32_t wmin[NW], wmax[NW], wgt[NW], weq[NW], wtot[NW];
     __shared__ uint2 cand[SEL_CAND_CAP];
     __shared__ uint32_t rk_above[SEL_RANK_SPLIT][SEL_CAND_CAP], rk_tie[SEL_RANK_SPLIT][SEL_CAND_CAP];
@@ -255,19 +278,34 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
     uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k;
     int top = L;
     while (top > 0) {
+        opaque_all(uk);
         const int nb = top < 11 ? top : 11;
         const int sh = top - nb;
         const uint32_t dm = (1u << nb) - 1u;
         // zero keys (all in bin 0) are counted per lane and added once per
-        // wave: same-address LDS atomics serialise
+        // wave: same-address LDS atomics serialise.  The first pass (every key
+        // eligible) adds unconditionally, masked-off lanes into their own sink.
         uint32_t zc = 0;
+        if (pmask == 0u) {
+            const int lim1 = opaque(lim);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (i < lim && (uk[i] & pmask) == prefix) {
-                if (uk[i] == 0u)
-                    ++zc;
-                else
-                    atomicAdd(&hist[hpad((int)((uk[i] >> sh) & dm))], 1u);
+            for (int i = 0; i < PER; ++i) {
+                const uint32_t real = ilt(i, lim1), nz = lt31(0u, uk[i]);
+                const uint32_t in = real & nz;
+                zc += real - in;
+                const uint32_t word = in * (uint32_t)hpad((int)((uk[i] >> sh) & dm)) + (1u - in) * (SEL_DUMMY + lane);
+                atomicAdd(&hist[word], 1u);
+            }
+        } else {
+            const int lim2 = opaque(lim);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                if (i < lim2 && (uk[i] & pmask) == prefix) {
+                    if (uk[i] == 0u)
+                        ++zc;
+                    else
+                        atomicAdd(&hist[hpad((int)((uk[i] >> sh) & dm))], 1u);
+                }
             }
         }
         if (prefix == 0u) {
@@ -314,17 +352,21 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
                     const uint2 me = cand[me_i];
                     uint32_t ab0 = 0, ab1 = 0, ti0 = 0, ti1 = 0;
                     uint32_t i = part;
+                    // o ranks above me: larger key, or equal key at a lower slice;
+                    // tie_upto counts equal keys at slices <= me's
                     for (; i + SEL_RANK_SPLIT < nc; i += 2 * SEL_RANK_SPLIT) {
                         const uint2 o0 = cand[i], o1 = cand[i + SEL_RANK_SPLIT];
-                        ab0 += (o0.x > me.x) || (o0.x == me.x && o0.y < me.y);
-                        ti0 += o0.x == me.x && o0.y <= me.y;
-                        ab1 += (o1.x > me.x) || (o1.x == me.x && o1.y < me.y);
-                        ti1 += o1.x == me.x && o1.y <= me.y;
+                        const uint32_t e0 = eq31(o0.x, me.x), e1 = eq31(o1.x, me.x);
+                        ab0 += lt31(me.x, o0.x) | (e0 & lt31(o0.y, me.y));
+                        ti0 += e0 & (1u - lt31(me.y, o0.y));
+                        ab1 += lt31(me.x, o1.x) | (e1 & lt31(o1.y, me.y));
+                        ti1 += e1 & (1u - lt31(me.y, o1.y));
                     }
                     if (i < nc) {
                         const uint2 o0 = cand[i];
-                        ab0 += (o0.x > me.x) || (o0.x == me.x && o0.y < me.y);
-                        ti0 += o0.x == me.x && o0.y <= me.y;
+                        const uint32_t e0 = eq31(o0.x, me.x);
+                        ab0 += lt31(me.x, o0.x) | (e0 & lt31(o0.y, me.y));
+                        ti0 += e0 & (1u - lt31(me.y, o0.y));
                     }
                     rk_above[part][me_i] = ab0 + ab1;
                     rk_tie[part][me_i] = ti0 + ti1;
@@ -354,11 +396,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
     // 3. order-preserving compaction.  Kept: u > prefix, or u == prefix among
     // the first krem such slices.  Output position of a slice = slices kept
     // before it = (greater before) + min(equal before, krem).
+    opaque_all(uk);
     uint32_t gl = 0, el = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        gl += uk[i] > prefix;
-        el += uk[i] == prefix;
+        gl += lt31(prefix, uk[i]);
+        el += eq31(uk[i], prefix);
     }
     const uint32_t gincl = wave_incl_sum(gl), eincl = wave_incl_sum(el);
     if (lane == WAVE - 1) {
@@ -374,10 +417,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const bool g = uk[i] > prefix, e = uk[i] == prefix;
-        const bool keep = g || (e && eb < krem);
+        const uint32_t g = lt31(prefix, uk[i]), e = eq31(uk[i], prefix);
         const uint32_t pos = gb + min(eb, krem);
-        if (keep && pos < (uint32_t)k)
+        if ((g | (e & lt31(eb, krem))) & lt31(pos, (uint32_t)k))
             outl[pos] = j0 + i;
         gb += g;
         eb += e;
