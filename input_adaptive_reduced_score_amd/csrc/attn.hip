@@ -28,8 +28,10 @@ namespace rmm {
 
 constexpr int D = ATTN_D;
 constexpr int QK_U = 16;      // kept key rows in flight per lane
-constexpr int PV_SUB = 512;   // positions examined per PV sub-chunk
-constexpr int PV_MAX_CHUNKS = 32;
+constexpr int QK_THREADS = 256; // 4 waves split the kept dims of one chunk
+constexpr int PV_SUB = 512;   // positions examined per PV pass (2 per thread)
+constexpr int PV_MAX_CHUNKS = 64;
+constexpr int PV_U = 16;      // kept V rows in flight per lane
 
 __device__ __forceinline__ float wave_max(float v)
 {
@@ -75,21 +77,29 @@ __device__ __forceinline__ void wave_select128(uint32_t key0, uint32_t key1, int
 
 // ------------------------------------------------------------------ qk
 template <int GS>
-__global__ __launch_bounds__(WAVE) void attn_qk_kernel(AttnShape s, int Sp, const uint16_t *__restrict__ q,
-                                                       const uint16_t *__restrict__ kt, const float *__restrict__ kn,
-                                                       float *__restrict__ logit, float2 *__restrict__ pstat,
-                                                       int32_t *__restrict__ dim_idx_out, uint32_t *__restrict__ hist)
+__global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, int Sp, const uint16_t *__restrict__ q,
+                                                             const uint16_t *__restrict__ kt,
+                                                             const float *__restrict__ kn, float *__restrict__ logit,
+                                                             float2 *__restrict__ pstat,
+                                                             int32_t *__restrict__ dim_idx_out,
+                                                             uint32_t *__restrict__ hist)
 {
+    constexpr int NWQ = QK_THREADS / WAVE;
     __shared__ int jd[D];
     __shared__ float qs[GS][D];
-    const int lane = threadIdx.x;
+    __shared__ float part[NWQ][GS][ATTN_QK_CHUNK];
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel;
     const int h0 = sg * s.GS, g = h0 / s.G;
     const int chunk = blockIdx.x, nchunk = gridDim.x;
     const uint16_t *qb = q + ((int64_t)b * s.Hq + h0) * D;
 
-    // 1. head_dim selection: sigma_j = fl32(max_h |q_h[j]| * kn[j])
-    {
+    // q of the group's heads, staged once (all threads) while wave 0 selects
+    __shared__ float qall[GS][D];
+    for (int i = tid; i < GS * D; i += QK_THREADS)
+        qall[i / D][i % D] = bf16_to_f32(qb[i]);
+    // 1. head_dim selection (wave 0): sigma_j = fl32(max_h |q_h[j]| * kn[j])
+    if (w == 0) {
         uint32_t key[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -103,19 +113,20 @@ __global__ __launch_bounds__(WAVE) void attn_qk_kernel(AttnShape s, int Sp, cons
         wave_select128(key[0], key[1], s.kd, jd);
     }
     __syncthreads();
-    for (int i = lane; i < s.kd; i += WAVE) {
+    for (int i = tid; i < s.kd; i += QK_THREADS) {
         const int j = jd[i];
 #pragma unroll
         for (int hh = 0; hh < GS; ++hh)
-            qs[hh][i] = bf16_to_f32(qb[hh * D + j]);
+            qs[hh][i] = qall[hh][j];
         if (chunk == 0 && dim_idx_out)
             dim_idx_out[(int64_t)grp * s.kd + i] = j;
     }
     __syncthreads();
 
-    // 2. unscaled dot products over the kept dims (ascending), 8 positions per lane
+    // 2. partial dot products: wave w takes kept dims [i0, i1) (ascending), 8 positions per lane
     const int sp = chunk * ATTN_QK_CHUNK + lane * 8;
     const bool act = sp < s.S;
+    const int i0 = s.kd * w / NWQ, i1 = s.kd * (w + 1) / NWQ;
     float acc[GS][8];
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh)
@@ -124,20 +135,20 @@ __global__ __launch_bounds__(WAVE) void attn_qk_kernel(AttnShape s, int Sp, cons
             acc[hh][e] = 0.0f;
     if (act) {
         const uint16_t *kbase = kt + ((int64_t)b * s.Hkv + g) * D * s.ldk + sp;
-        for (int i0 = 0; i0 < s.kd; i0 += QK_U) {
+        for (int ib = i0; ib < i1; ib += QK_U) {
             uint4 u[QK_U];
 #pragma unroll
             for (int qq = 0; qq < QK_U; ++qq)
-                if (i0 + qq < s.kd)
-                    u[qq] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)jd[i0 + qq] * s.ldk);
+                if (ib + qq < i1)
+                    u[qq] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)jd[ib + qq] * s.ldk);
 #pragma unroll
             for (int qq = 0; qq < QK_U; ++qq) {
-                if (i0 + qq < s.kd) {
+                if (ib + qq < i1) {
                     float v[8];
                     Vec16<uint16_t>::unpack(u[qq], v);
 #pragma unroll
                     for (int hh = 0; hh < GS; ++hh) {
-                        const float qv = qs[hh][i0 + qq];
+                        const float qv = qs[hh][ib + qq];
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
                             acc[hh][e] = fmaf(qv, v[e], acc[hh][e]);
@@ -146,26 +157,41 @@ __global__ __launch_bounds__(WAVE) void attn_qk_kernel(AttnShape s, int Sp, cons
             }
         }
     }
-
-    // 3. logits and per-chunk softmax statistics (max, sum exp) per head
 #pragma unroll
-    for (int hh = 0; hh < GS; ++hh) {
+    for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            part[w][hh][lane * 8 + e] = acc[hh][e];
+    __syncthreads();
+
+    // 3. logits (the waves' partials added in wave order) and per-chunk softmax
+    // statistics (max, sum exp) per head; wave w handles heads w, w + NWQ, ...
+    for (int hh = w; hh < GS; hh += NWQ) {
+        float a8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = part[0][hh][lane * 8 + e];
+#pragma unroll
+            for (int ww = 1; ww < NWQ; ++ww)
+                x += part[ww][hh][lane * 8 + e];
+            a8[e] = x;
+        }
         if (act) {
             float *dst = logit + ((int64_t)b * s.Hq + h0 + hh) * Sp + sp;
-            reinterpret_cast<f32x4_t *>(dst)[0] = f32x4_t{acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]};
-            reinterpret_cast<f32x4_t *>(dst)[1] = f32x4_t{acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]};
+            reinterpret_cast<f32x4_t *>(dst)[0] = f32x4_t{a8[0], a8[1], a8[2], a8[3]};
+            reinterpret_cast<f32x4_t *>(dst)[1] = f32x4_t{a8[4], a8[5], a8[6], a8[7]};
         }
         float mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             if (sp + e < s.S)
-                mx = fmaxf(mx, acc[hh][e]);
+                mx = fmaxf(mx, a8[e]);
         mx = wave_max(mx);
         float z = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             if (sp + e < s.S)
-                z += expf(s.scale * (acc[hh][e] - mx));
+                z += expf(s.scale * (a8[e] - mx));
         z = wave_sum(z);
         if (lane == 0)
             pstat[((int64_t)b * s.Hq + h0 + hh) * nchunk + chunk] = make_float2(mx, z);
@@ -173,7 +199,7 @@ __global__ __launch_bounds__(WAVE) void attn_qk_kernel(AttnShape s, int Sp, cons
 
     // 4. the first chunk's workgroup clears the group's key histogram for the key kernel
     if (chunk == 0)
-        for (int i = lane; i < ATTN_HIST_BINS; i += WAVE)
+        for (int i = tid; i < ATTN_HIST_BINS; i += QK_THREADS)
             hist[(int64_t)grp * ATTN_HIST_BINS + i] = 0;
 }
 
@@ -204,6 +230,17 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, int 
     const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS;
     for (int i = tid; i < ATTN_HIST_BINS; i += 256)
         lh[i] = 0;
+    // this thread's logits are loaded first so their latency overlaps the statistics merge
+    const int sp = blockIdx.x * ATTN_KEY_CHUNK + threadIdx.x * 8;
+    f32x4_t a[GS][2];
+    if (sp < s.S) {
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh) {
+            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(logit + ((int64_t)b * s.Hq + h0 + hh) * Sp + sp);
+            a[hh][0] = src[0];
+            a[hh][1] = src[1];
+        }
+    }
     // merge the per-chunk softmax statistics of the group's heads into lse (double, fixed order)
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh) {
@@ -247,15 +284,7 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, int 
     for (int hh = 0; hh < GS; ++hh)
         lse[hh] = lse_s[hh];
     __syncthreads();
-    const int sp = blockIdx.x * ATTN_KEY_CHUNK + threadIdx.x * 8;
     if (sp < s.S) {
-        f32x4_t a[GS][2];
-#pragma unroll
-        for (int hh = 0; hh < GS; ++hh) {
-            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(logit + ((int64_t)b * s.Hq + h0 + hh) * Sp + sp);
-            a[hh][0] = src[0];
-            a[hh][1] = src[1];
-        }
         uint32_t kk[8];
         const double sc = (double)s.scale;
 #pragma unroll
@@ -281,15 +310,19 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, int 
 // ------------------------------------------------------------------ select
 // Threshold key thr and tie quota of the group, then per PV chunk c (P
 // positions): info[c] = (kept before the chunk, ties at thr before the chunk).
-// Fast path: the 4096-bin histogram names the bin holding the k-th key; one
-// pass over the keys counts, per chunk, the keys in higher bins and collects
-// the bin's keys (candidates) into LDS, where the last 20 bits are resolved.
-// If the bin holds more than CAND_CAP keys, two radix passes over all keys and
-// a counting pass run instead.
+// Fast path: the 4096-bin histogram names the bin d holding the k-th key; one
+// pass over the keys counts, per chunk, the keys in higher bins and gathers the
+// bin's keys (candidates) into LDS.  Up to SEL_RANK_MAX candidates are ranked
+// exactly (key descending, position ascending); up to CAND_CAP the last 20 key
+// bits are resolved by two radix passes over the candidates (ranking costs
+// O(n^2) LDS reads); beyond that two
+// radix passes and a counting pass run over all keys.
 struct SelInfo {
     uint32_t thr, quota;
 };
 constexpr int CAND_CAP = 8192;
+constexpr int SEL_RANK_MAX = 256;
+constexpr int SEL_KB = 4; // 16-byte key loads in flight per thread
 
 __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, int P, int npv,
                                                            const uint32_t *__restrict__ keys,
@@ -301,63 +334,128 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, 
     __shared__ uint32_t cgt[PV_MAX_CHUNKS], ceq[PV_MAX_CHUNKS];
     __shared__ uint32_t ckey[CAND_CAP];
     __shared__ int cpos[CAND_CAP];
-    __shared__ uint32_t ncand;
+    __shared__ uint32_t rk_above[1024], rk_tie[1024]; // one slot per thread: (part, candidate)
+    __shared__ uint32_t ncand, res[2];
     const int grp = blockIdx.x;
-    const int lane = threadIdx.x & (WAVE - 1);
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const uint32_t *K = keys + (int64_t)grp * Sp;
     const uint32_t *H = hist + (int64_t)grp * ATTN_HIST_BINS;
     uint32_t krem = (uint32_t)s.ks;
     const uint32_t d = hist_crossing(H, ATTN_HIST_BINS, krem, tmp);
     const uint32_t nbin = H[d];
-    if (threadIdx.x < PV_MAX_CHUNKS) {
-        cgt[threadIdx.x] = 0;
-        ceq[threadIdx.x] = 0;
+    if (tid < PV_MAX_CHUNKS) {
+        cgt[tid] = 0;
+        ceq[tid] = 0;
     }
-    if (threadIdx.x == 0)
+    if (tid == 0) {
         ncand = 0;
+        res[0] = 0;
+        res[1] = 0;
+    }
     __syncthreads();
     const uint4 *k4 = reinterpret_cast<const uint4 *>(K);
     const int n4 = (int)((s.S + 3) / 4), step = 1024;
     uint32_t thr, quota;
     if (nbin <= (uint32_t)CAND_CAP) {
-        for (int i0 = threadIdx.x; i0 < n4; i0 += 8 * step) {
-            uint4 u[8];
+        for (int i0 = tid; i0 - lane < n4; i0 += SEL_KB * step) {
+            uint4 u[SEL_KB];
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                if (i0 + q * step < n4)
-                    u[q] = k4[i0 + q * step];
+            for (int q = 0; q < SEL_KB; ++q)
+                u[q] = i0 + q * step < n4 ? k4[i0 + q * step] : make_uint4(0u, 0u, 0u, 0u);
+            // candidates of the batch: per-lane count, wave scan, one slot reservation per wave
+            uint32_t cl = 0;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int i = i0 + q * step; // a wave covers 256 consecutive positions: one chunk
-                if (i0 + q * step - lane >= n4)
-                    break;
+            for (int q = 0; q < SEL_KB; ++q) {
+                const int i = i0 + q * step;
                 const uint32_t kk[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
-                int ngt = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    cl += (4 * i + e < s.S) & ((kk[e] >> 20) == d);
+            }
+            const uint32_t cincl = wave_incl_sum(cl);
+            const uint32_t wcount = (uint32_t)__builtin_amdgcn_readlane((int)cincl, WAVE - 1);
+            uint32_t base = 0;
+            if (lane == 0 && wcount != 0u)
+                base = atomicAdd(&ncand, wcount);
+            base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+            uint32_t slot = base + cincl - cl;
+#pragma unroll
+            for (int q = 0; q < SEL_KB; ++q) {
+                const int i = i0 + q * step; // one wave load covers 256 consecutive positions: one chunk
+                const uint32_t kk[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+                uint32_t ngt = 0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 4 * i + e;
-                    const bool ok = i < n4 && j < s.S;
+                    const bool ok = j < s.S;
                     const uint32_t top = kk[e] >> 20;
-                    ngt += __popcll(__ballot(ok && top > d));
+                    ngt += ok & (top > d);
                     if (ok && top == d) {
-                        const uint32_t slot = atomicAdd(&ncand, 1u);
                         if (slot < (uint32_t)CAND_CAP) {
                             ckey[slot] = kk[e];
                             cpos[slot] = j;
                         }
+                        ++slot;
                     }
                 }
-                if (lane == 0 && ngt)
-                    atomicAdd(&cgt[(4 * (i - lane)) / P], (uint32_t)ngt);
+                const uint32_t wgt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(ngt), WAVE - 1);
+                if (lane == 0 && wgt != 0u)
+                    atomicAdd(&cgt[(4 * (i - lane)) / P], wgt);
             }
         }
         __syncthreads();
-        uint32_t prefix = d << 20, pmask = 0xfff00000u;
-        radix_pass(ckey, (int)nbin, prefix, pmask, 10, 10, krem, h2, tmp);
-        radix_pass(ckey, (int)nbin, prefix, pmask, 0, 10, krem, h2, tmp);
-        thr = prefix;
-        quota = krem;
-        for (int i = threadIdx.x; i < (int)nbin; i += 1024) {
+        const uint32_t nc = min(nbin, (uint32_t)CAND_CAP);
+        if (nc <= (uint32_t)SEL_RANK_MAX) {
+            // rank: thread t compares candidate t % RS with every (1024 / RS)-th other
+            const uint32_t RS = nc <= 256u ? 256u : nc <= 512u ? 512u : 1024u;
+            const uint32_t split = 1024u / RS, me_i = (uint32_t)tid % RS, part = (uint32_t)tid / RS;
+            if (me_i < nc) {
+                const uint32_t mk = ckey[me_i];
+                const int mp = cpos[me_i];
+                // 8 independent comparisons per step keep the LDS reads pipelined
+                uint32_t ab[8] = {0, 0, 0, 0, 0, 0, 0, 0}, ti[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                uint32_t i = part;
+                for (; i + 7 * split < nc; i += 8 * split) {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const uint32_t ok = ckey[i + u * split];
+                        const int op = cpos[i + u * split];
+                        ab[u] += (ok > mk) || (ok == mk && op < mp);
+                        ti[u] += ok == mk && op <= mp;
+                    }
+                }
+                for (; i < nc; i += split) {
+                    const uint32_t ok = ckey[i];
+                    const int op = cpos[i];
+                    ab[0] += (ok > mk) || (ok == mk && op < mp);
+                    ti[0] += ok == mk && op <= mp;
+                }
+                rk_above[tid] = ((ab[0] + ab[1]) + (ab[2] + ab[3])) + ((ab[4] + ab[5]) + (ab[6] + ab[7]));
+                rk_tie[tid] = ((ti[0] + ti[1]) + (ti[2] + ti[3])) + ((ti[4] + ti[5]) + (ti[6] + ti[7]));
+            }
+            __syncthreads();
+            if ((uint32_t)tid < nc) {
+                uint32_t above = 0, tie_upto = 0;
+                for (uint32_t q = 0; q < split; ++q) {
+                    above += rk_above[q * RS + tid];
+                    tie_upto += rk_tie[q * RS + tid];
+                }
+                if (above + 1u == krem) {
+                    res[0] = ckey[tid];
+                    res[1] = tie_upto;
+                }
+            }
+            __syncthreads();
+            thr = res[0];
+            quota = res[1];
+        } else {
+            uint32_t prefix = d << 20, pmask = 0xfff00000u;
+            radix_pass(ckey, (int)nc, prefix, pmask, 10, 10, krem, h2, tmp);
+            radix_pass(ckey, (int)nc, prefix, pmask, 0, 10, krem, h2, tmp);
+            thr = prefix;
+            quota = krem;
+        }
+        for (int i = tid; i < (int)nc; i += 1024) {
             if (ckey[i] > thr)
                 atomicAdd(&cgt[cpos[i] / P], 1u);
             else if (ckey[i] == thr)
@@ -369,37 +467,35 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, 
         radix_pass_v4(K, (int)s.S, prefix, pmask, 0, 10, krem, h2, tmp);
         thr = prefix;
         quota = krem;
-        for (int i0 = threadIdx.x; i0 < n4; i0 += 8 * step) {
-            uint4 u[8];
+        for (int i0 = tid; i0 - lane < n4; i0 += SEL_KB * step) {
+            uint4 u[SEL_KB];
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                if (i0 + q * step < n4)
-                    u[q] = k4[i0 + q * step];
+            for (int q = 0; q < SEL_KB; ++q)
+                u[q] = i0 + q * step < n4 ? k4[i0 + q * step] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            for (int q = 0; q < SEL_KB; ++q) {
                 const int i = i0 + q * step;
-                if (i0 + q * step - lane >= n4)
-                    break;
                 const uint32_t kk[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
-                int ngt = 0, neq = 0;
+                uint32_t ngt = 0, neq = 0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int j = 4 * i + e;
-                    const bool ok = i < n4 && j < s.S;
-                    ngt += __popcll(__ballot(ok && kk[e] > thr));
-                    neq += __popcll(__ballot(ok && kk[e] == thr));
+                    const bool ok = 4 * i + e < s.S;
+                    ngt += ok & (kk[e] > thr);
+                    neq += ok & (kk[e] == thr);
                 }
+                const uint32_t wgt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(ngt), WAVE - 1);
+                const uint32_t weq = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(neq), WAVE - 1);
                 if (lane == 0) {
-                    if (ngt)
-                        atomicAdd(&cgt[(4 * (i - lane)) / P], (uint32_t)ngt);
-                    if (neq)
-                        atomicAdd(&ceq[(4 * (i - lane)) / P], (uint32_t)neq);
+                    if (wgt)
+                        atomicAdd(&cgt[(4 * (i - lane)) / P], wgt);
+                    if (weq)
+                        atomicAdd(&ceq[(4 * (i - lane)) / P], weq);
                 }
             }
         }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         uint32_t gacc = 0, eacc = 0;
         uint2 *o = info + (int64_t)grp * npv;
         for (int c = 0; c < npv; ++c) {
@@ -424,7 +520,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P
 {
     __shared__ int rows[PV_SUB];
     __shared__ float pr[GS][PV_SUB];
-    __shared__ uint32_t wtot[2][4];
+    __shared__ uint32_t wgt[4], weq[4];
     __shared__ float red[4][GS][D];
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS, g = h0 / s.G;
@@ -437,8 +533,9 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P
     for (int hh = 0; hh < GS; ++hh)
         lsef[hh] = (float)lse_ws[(int64_t)b * s.Hq + h0 + hh];
     const uint32_t *K = keys + (int64_t)grp * Sp;
+    const float *L = logit + ((int64_t)b * s.Hq + h0) * Sp;
     const uint16_t *vb = v + ((int64_t)b * s.Hkv + g) * s.ldv * D;
-    const int quarter = lane >> 4, dl = lane & 15;
+    const int quarter = lane >> 4, dl = lane & 15, slot = w * 4 + quarter;
 
     float acc[GS][8];
 #pragma unroll
@@ -449,83 +546,88 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P
 
     const int p0 = c * P, p1 = min((int)s.S, p0 + P);
     for (int sb = p0; sb < p1; sb += PV_SUB) {
-        // order-preserving selection of this sub-chunk: thread tid covers positions sb + 2*tid, +1
+        // thread tid holds positions j0, j0+1 (j0 even and Sp a multiple of 8: j0 < S keeps both in the row)
         const int j0 = sb + 2 * tid;
-        uint32_t ka = j0 < p1 ? K[j0] : 0u, kb = j0 + 1 < p1 ? K[j0 + 1] : 0u;
-        const bool va = j0 < p1, vbb = j0 + 1 < p1;
-        const bool ea = va && ka == thr, eb = vbb && kb == thr;
-        // tie ranks (index order) across the block
-        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        const uint64_t ma = __ballot(ea), mb = __ballot(eb);
-        // positions are interleaved a,b per thread: ties before (tid, a) = ties of lower lanes (both) + none
-        uint32_t tie_lane = __popcll(ma & lt) + __popcll(mb & lt);
-        if (lane == 0)
-            wtot[0][w] = __popcll(ma) + __popcll(mb);
-        __syncthreads();
-        uint32_t tie_w = 0;
-        for (int i = 0; i < w; ++i)
-            tie_w += wtot[0][i];
-        const uint32_t ra = ties_before + tie_w + tie_lane;
-        const uint32_t rb = ra + (ea ? 1u : 0u);
-        const bool keepa = va && (ka > thr || (ea && ra < quota));
-        const bool keepb = vbb && (kb > thr || (eb && rb < quota));
-        uint32_t sub_ties = 0;
-        for (int i = 0; i < 4; ++i)
-            sub_ties += wtot[0][i];
-        const uint64_t qa = __ballot(keepa), qb = __ballot(keepb);
-        const uint32_t kept_lane = __popcll(qa & lt) + __popcll(qb & lt);
-        if (lane == 0)
-            wtot[1][w] = __popcll(qa) + __popcll(qb);
-        __syncthreads();
-        uint32_t kept_w = 0, nkept = 0;
-        for (int i = 0; i < 4; ++i) {
-            if (i < w)
-                kept_w += wtot[1][i];
-            nkept += wtot[1][i];
-        }
-        const uint32_t oa = kept_w + kept_lane, ob = oa + (keepa ? 1u : 0u);
-        if (keepa && oa < PV_SUB)
-            rows[oa] = j0;
-        if (keepb && ob < PV_SUB)
-            rows[ob] = j0 + 1;
-        __syncthreads();
-        // probabilities of the kept rows, and the optional index output
-        for (int r = tid; r < (int)nkept; r += 256) {
-            const int sidx = rows[r];
+        uint2 kk = make_uint2(0u, 0u);
+        float2 lg[GS];
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh)
+            lg[hh] = make_float2(0.0f, 0.0f);
+        if (j0 < p1) {
+            kk = *reinterpret_cast<const uint2 *>(K + j0);
 #pragma unroll
             for (int hh = 0; hh < GS; ++hh)
-                pr[hh][r] = expf(fmaf(s.scale, logit[((int64_t)b * s.Hq + h0 + hh) * Sp + sidx], -lsef[hh]));
-            if (pos_out && kept_before + r < (uint32_t)s.ks)
-                pos_out[(int64_t)grp * s.ks + kept_before + r] = sidx;
+                lg[hh] = *reinterpret_cast<const float2 *>(L + (int64_t)hh * Sp + j0);
+        }
+        const uint32_t va = j0 < p1, vb1 = j0 + 1 < p1;
+        const uint32_t ga = va & (kk.x > thr), gb = vb1 & (kk.y > thr);
+        const uint32_t ea = va & (kk.x == thr), eb = vb1 & (kk.y == thr);
+        // kept before a position = greater before + min(equal before, quota): one scan of each
+        const uint32_t gi = wave_incl_sum(ga + gb), ei = wave_incl_sum(ea + eb);
+        if (lane == WAVE - 1) {
+            wgt[w] = gi;
+            weq[w] = ei;
         }
         __syncthreads();
-        // stream kept V rows: wave w, quarter q handles rows w*4 + q, +16, ...
-        for (int r0 = w * 4 + quarter; r0 < (int)nkept; r0 += 16 * 4) {
-            uint4 u[4];
+        uint32_t gbw = 0, ebw = 0, gtot = 0, etot = 0;
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
+        for (int i = 0; i < 4; ++i) {
+            gbw += i < w ? wgt[i] : 0u;
+            ebw += i < w ? weq[i] : 0u;
+            gtot += wgt[i];
+            etot += weq[i];
+        }
+        const uint32_t gpa = gbw + gi - (ga + gb), epa = ties_before + ebw + ei - (ea + eb); // before position a
+        const uint32_t gpb = gpa + ga, epb = epa + ea;
+        const uint32_t base0 = min(ties_before, quota); // kept ties before this pass
+        const uint32_t keepa = ga | (ea & (epa < quota)), keepb = gb | (eb & (epb < quota));
+        const uint32_t la = gpa + min(epa, quota) - base0, lb = gpb + min(epb, quota) - base0; // pass-local slots
+        const uint32_t nkept = gtot + min(ties_before + etot, quota) - base0;
+        if (keepa && la < PV_SUB) {
+            rows[la] = j0;
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+                pr[hh][la] = expf(fmaf(s.scale, lg[hh].x, -lsef[hh]));
+            if (pos_out && kept_before + la < (uint32_t)s.ks)
+                pos_out[(int64_t)grp * s.ks + kept_before + la] = j0;
+        }
+        if (keepb && lb < PV_SUB) {
+            rows[lb] = j0 + 1;
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+                pr[hh][lb] = expf(fmaf(s.scale, lg[hh].y, -lsef[hh]));
+            if (pos_out && kept_before + lb < (uint32_t)s.ks)
+                pos_out[(int64_t)grp * s.ks + kept_before + lb] = j0 + 1;
+        }
+        __syncthreads();
+        // stream kept V rows: slot (wave, quarter) takes rows slot + 16 m, PV_U rows in flight per lane
+        const int nk = (int)min(nkept, (uint32_t)PV_SUB);
+        for (int r0 = slot; r0 < nk; r0 += 16 * PV_U) {
+            uint4 u[PV_U];
+#pragma unroll
+            for (int qq = 0; qq < PV_U; ++qq) {
                 const int r = r0 + 16 * qq;
-                if (r < (int)nkept)
+                if (r < nk)
                     u[qq] = *reinterpret_cast<const uint4 *>(vb + (int64_t)rows[r] * D + dl * 8);
             }
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
+            for (int qq = 0; qq < PV_U; ++qq) {
                 const int r = r0 + 16 * qq;
-                if (r < (int)nkept) {
+                if (r < nk) {
                     float vv[8];
                     Vec16<uint16_t>::unpack(u[qq], vv);
 #pragma unroll
                     for (int hh = 0; hh < GS; ++hh) {
-                        const float p = pr[hh][r];
+                        const float pv = pr[hh][r];
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
-                            acc[hh][e] = fmaf(p, vv[e], acc[hh][e]);
+                            acc[hh][e] = fmaf(pv, vv[e], acc[hh][e]);
                     }
                 }
             }
         }
         kept_before += nkept;
-        ties_before += sub_ties;
+        ties_before += etot;
         __syncthreads();
     }
 
@@ -629,7 +731,7 @@ static hipError_t attn_run(const AttnShape &s, const uint16_t *q, const uint16_t
     pv_chunks(s.S, &P, &npv);
     SelInfo *sel = reinterpret_cast<SelInfo *>(ws.pos);
     uint2 *info = reinterpret_cast<uint2 *>(align256((char *)(sel + G)));
-    attn_qk_kernel<GS><<<dim3(nqk, G), WAVE, 0, st>>>(s, Sp, q, kt, kn, ws.logit, ws.pstat, dim_idx, ws.hist);
+    attn_qk_kernel<GS><<<dim3(nqk, G), QK_THREADS, 0, st>>>(s, Sp, q, kt, kn, ws.logit, ws.pstat, dim_idx, ws.hist);
     attn_key_kernel<GS><<<dim3((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK, G), 256, 0, st>>>(
         s, Sp, nqk, ws.logit, ws.pstat, ws.lse, lse, ws.keys, ws.hist);
     attn_select_kernel<<<G, 1024, 0, st>>>(s, Sp, P, npv, ws.keys, ws.hist, sel, info);
@@ -766,16 +868,17 @@ __global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, int span, 
                 o[hh][e] *= fac[hh];
         // P V over this sub-chunk's rows
         const int nr = min(DN_SUB, p1 - sb);
-        for (int r0 = w * 4 + quarter; r0 < nr; r0 += 64) {
-            uint4 u[4];
+        // 8 rows in flight per lane: rows r0 + 16 qq
+        for (int r0 = w * 4 + quarter; r0 < nr; r0 += 128) {
+            uint4 u[8];
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
+            for (int qq = 0; qq < 8; ++qq) {
                 const int r = r0 + 16 * qq;
                 if (r < nr)
                     u[qq] = *reinterpret_cast<const uint4 *>(vb + (int64_t)(sb + r) * D + dl * 8);
             }
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
+            for (int qq = 0; qq < 8; ++qq) {
                 const int r = r0 + 16 * qq;
                 if (r < nr) {
                     float vv[8];
@@ -818,29 +921,48 @@ __global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, int span, 
         stat[((int64_t)grp * nspan + c) * G + tid] = make_float2(mrun[tid], zrun[tid]);
 }
 
-// Rescales every span's partial to the largest running max and sums them in span order.
+// Rescales every span's partial to the largest running max and sums them in
+// span order.  One workgroup per (group, head), one thread per dim; the span
+// statistics are staged in LDS and the partials are loaded DN_MAX_SPANS deep.
 template <int G>
-__global__ __launch_bounds__(256) void attn_dense_reduce_kernel(AttnShape s, int nspan, const float *__restrict__ part,
-                                                                const float2 *__restrict__ stat,
-                                                                float *__restrict__ out, float *__restrict__ lse_out)
+__global__ __launch_bounds__(D) void attn_dense_reduce_kernel(AttnShape s, int nspan, const float *__restrict__ part,
+                                                              const float2 *__restrict__ stat,
+                                                              float *__restrict__ out, float *__restrict__ lse_out)
 {
-    const int grp = blockIdx.x, b = grp / s.Hkv, g = grp % s.Hkv, h0 = g * G;
-    for (int i = threadIdx.x; i < G * D; i += 256) {
-        const int hh = i / D, dd = i % D;
-        float M = -INFINITY;
-        for (int cc = 0; cc < nspan; ++cc)
-            M = fmaxf(M, stat[((int64_t)grp * nspan + cc) * G + hh].x);
-        float num = 0.0f, den = 0.0f;
-        for (int cc = 0; cc < nspan; ++cc) {
-            const float2 st2 = stat[((int64_t)grp * nspan + cc) * G + hh];
-            const float f = expf(st2.x - M);
-            num += f * part[((int64_t)grp * nspan + cc) * G * D + i];
-            den += f * st2.y;
-        }
-        out[((int64_t)b * s.Hq + h0 + hh) * D + dd] = num / den;
-        if (lse_out && dd == 0)
-            lse_out[(int64_t)b * s.Hq + h0 + hh] = M + logf(den);
+    __shared__ float fs[DN_MAX_SPANS];
+    __shared__ float Ms, dens;
+    const int grp = blockIdx.x, hh = blockIdx.y, b = grp / s.Hkv, g = grp % s.Hkv, h0 = g * G;
+    const int dd = threadIdx.x;
+    const float2 *st = stat + (int64_t)grp * nspan * G + hh;
+    const float2 mine = dd < nspan ? st[(int64_t)dd * G] : make_float2(-INFINITY, 0.0f);
+    if (dd < WAVE) {
+        // nspan <= DN_MAX_SPANS = 64: wave 0 holds one span per lane
+        const float M = wave_max(mine.x);
+        const float f = dd < nspan ? expf(mine.x - M) : 0.0f;
+        fs[dd] = f;
+        if (dd == 0)
+            Ms = M;
     }
+    __syncthreads();
+    if (dd == 0) {
+        float den = 0.0f;
+        for (int cc = 0; cc < nspan; ++cc)
+            den += fs[cc] * st[(int64_t)cc * G].y;
+        dens = den;
+    }
+    const float *pp = part + (int64_t)grp * nspan * G * D + hh * D + dd;
+    float v[DN_MAX_SPANS];
+#pragma unroll
+    for (int cc = 0; cc < DN_MAX_SPANS; ++cc)
+        v[cc] = cc < nspan ? pp[(int64_t)cc * G * D] : 0.0f;
+    float num = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < DN_MAX_SPANS; ++cc)
+        num += fs[cc] * v[cc];
+    __syncthreads();
+    out[((int64_t)b * s.Hq + h0 + hh) * D + dd] = num / dens;
+    if (lse_out && dd == 0)
+        lse_out[(int64_t)b * s.Hq + h0 + hh] = Ms + logf(dens);
 }
 
 static void dense_spans(int64_t S, int *span, int *nspan)
@@ -882,7 +1004,7 @@ hipError_t launch_attn_dense(const AttnShape &s, const uint16_t *q, const uint16
 #define RMM_DENSE_CASE(GV)                                                                                         \
     case GV:                                                                                                       \
         attn_dense_kernel<GV><<<grid, 256, 0, st>>>(s, span, q, kt, v, part, stat);                                \
-        attn_dense_reduce_kernel<GV><<<ng, 256, 0, st>>>(s, nspan, part, stat, out, lse);                          \
+        attn_dense_reduce_kernel<GV><<<dim3(ng, GV), D, 0, st>>>(s, nspan, part, stat, out, lse);                   \
         break;
     switch (s.G) {
         RMM_DENSE_CASE(1)
