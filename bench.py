@@ -330,7 +330,8 @@ def main():
     k_head = head["k"]
     sha = src_hash(["input_adaptive_reduced_score_amd/csrc/linear.hip", "input_adaptive_reduced_score_amd/csrc/device.h",
                     "input_adaptive_reduced_score_amd/csrc/kernels.h"])
-    roofline = {"kernel": "gemv_kernel<bf16,NT=1> (reduced streaming GEMV)", "bound": "hbm",
+    roofline = {"kernel": "reduced decode product launch: gemv_kernel<bf16,NT=1> + split-K gemv_reduce_kernel",
+                "bound": "hbm",
                 "achieved": head["gemv_GBps"], "peak": A.HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": head["gemv_GBps"] / A.HBM_PEAK_GBS,
                 "algorithmic_bytes_per_launch": A.gemv_launch_bytes(k_head, M),

@@ -15,7 +15,7 @@
 #define SELECT_MAX_K 32768
 
 #ifndef GEMV_UNROLL
-#define GEMV_UNROLL 8
+#define GEMV_UNROLL 16     // kept rows in flight per wave
 #endif
 #ifndef GEMV_TARGET_WGS
 #define GEMV_TARGET_WGS 512 // workgroups (8 waves each) the split-K aims for
