@@ -51,6 +51,10 @@ def lib():
         L.ora_scores.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp]
         L.ora_select.restype = i32
         L.ora_select.argtypes = [vp, i32, i64, i64, i64, vp, i64, dbl, vp]
+        L.ora_block_keep_count.restype = i64
+        L.ora_block_keep_count.argtypes = [i64, dbl]
+        L.ora_select_blocks.restype = i32
+        L.ora_select_blocks.argtypes = [vp, i32, i64, i64, i64, i64, i64, dbl, vp]
         L.ora_linear.restype = i32
         L.ora_linear.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, i64, i64, i64, i64,
                                  vp, i64, vp]
@@ -107,6 +111,25 @@ def select(x, c, tile, r):
     nt = -(-T // tile)
     idx = np.empty((nt, k), dtype=np.int32)
     _check(lib().ora_select(_p(x), _dt(x), T, K, K, _p(c), tile, float(r), _p(idx)), "select")
+    return idx
+
+
+def block_keep_count(nb, keep):
+    return int(lib().ora_block_keep_count(int(nb), float(keep)))
+
+
+def select_blocks(x, tile, block, keep):
+    """Block-granular selection: idx [n_tiles, nk*block] int32 (kept blocks ascending, expanded)."""
+    x = np.ascontiguousarray(x)
+    T, K = x.shape
+    if block < 1 or K % block:
+        raise ValueError("K must be a multiple of block")
+    nk = block_keep_count(K // block, keep)
+    if nk < 0:
+        raise ValueError("keep must be in (0, 1]")
+    nt = -(-T // tile)
+    idx = np.empty((nt, nk * block), dtype=np.int32)
+    _check(lib().ora_select_blocks(_p(x), _dt(x), T, K, K, tile, block, float(keep), _p(idx)), "select_blocks")
     return idx
 
 

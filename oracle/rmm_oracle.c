@@ -146,6 +146,68 @@ int ora_select(const void *x, int xt, int64_t T, int64_t K, int64_t ldx,
 /* ---------------------------------------------------------------- products
  * Blog section 2: Y = X @ W^T; RMM keeps W^T rows (contraction slices) j in J
  * and computes Y ~= X[:,J] @ W^T[J,:].  Output shape is the dense one. */
+/* ---------------------------------------------------------------- block variant
+ * Blog section 6.1 demo code (ffn_block_reduce): keep_num = max(1,
+ * int(num_blocks * keep_ratio)), i.e. the double product truncated, at least 1. */
+int64_t ora_block_keep_count(int64_t nb, double keep)
+{
+    if (nb < 1 || !(keep > 0.0) || !(keep <= 1.0))
+        return -1;
+    double p = floor((double)nb * keep);
+    int64_t k = (int64_t)p;
+    if (k < 1)
+        k = 1;
+    if (k > nb)
+        k = nb;
+    return k;
+}
+
+/* Blog sections 5.1 (block-mean |h| as the block's importance), 5.2 (top-k over
+ * blocks, bool mask expanded to neuron indices) and 6.1 (the demo code). */
+int ora_select_blocks(const void *x, int xt, int64_t T, int64_t K, int64_t ldx, int64_t tile,
+                      int64_t block, double keep, int32_t *idx)
+{
+    if (T < 1 || K < 1 || tile < 1 || ldx < K || block < 1 || K % block != 0)
+        return 1;
+    int64_t nb = K / block;
+    int64_t nk = ora_block_keep_count(nb, keep);
+    if (nk < 0)
+        return 1;
+    int64_t ntiles = (T + tile - 1) / tile;
+    double *score = (double *)malloc((size_t)nb * sizeof *score);
+    int32_t *kept = (int32_t *)malloc((size_t)nk * sizeof *kept);
+    if (!score || !kept) {
+        free(score);
+        free(kept);
+        return 2;
+    }
+    int rc = 0;
+    for (int64_t tau = 0; rc == 0 && tau < ntiles; ++tau) {
+        int64_t t0 = tau * tile, t1 = t0 + tile < T ? t0 + tile : T;
+        for (int64_t b = 0; b < nb; ++b) {
+            double sum = 0.0;
+            for (int64_t e = 0; e < block; ++e) {
+                int64_t j = b * block + e;
+                float a = 0.0f;
+                for (int64_t t = t0; t < t1; ++t) {
+                    float v = fabsf(elem(x, xt, t * ldx + j));
+                    if (v > a)
+                        a = v;
+                }
+                sum += (double)a;
+            }
+            score[b] = sum / (double)block;
+        }
+        rc = topk_ascending(score, nb, nk, kept);
+        for (int64_t i = 0; rc == 0 && i < nk; ++i)
+            for (int64_t e = 0; e < block; ++e)
+                idx[tau * nk * block + i * block + e] = (int32_t)(kept[i] * block + e);
+    }
+    free(score);
+    free(kept);
+    return rc;
+}
+
 int ora_linear(const void *x, int xt, int64_t T, int64_t K, int64_t ldx,
                const void *wt, int wtt, int64_t M, int64_t ldw,
                const int32_t *idx, int64_t k, int64_t tile, int64_t t0, int64_t t1,

@@ -47,6 +47,19 @@ int ora_scores(const void *x, int xt, int64_t T, int64_t K, int64_t ldx,
 int ora_select(const void *x, int xt, int64_t T, int64_t K, int64_t ldx,
                const float *c, int64_t tile, double r, int32_t *idx);
 
+/* block-granular variant (blog section 6.1 demo code, ffn_block_reduce): the
+ * contraction dimension in blocks of `block` consecutive slices (K % block == 0);
+ * block score = mean over the block's slices, in ascending order and double
+ * precision, of max_{t in tile} |x[t,j]|; the nk = ora_block_keep_count(K/block,
+ * keep) blocks of largest score are kept (ties to the lower block), in ascending
+ * block order, and expanded to their slice indices:
+ * idx[tau*nk*block + i*block + e] = b_i*block + e.
+ * Pinned: hand example; block=1 equals ora_select with c=1 when the counts agree;
+ * brute force over block subsets. */
+int64_t ora_block_keep_count(int64_t nb, double keep);
+int ora_select_blocks(const void *x, int xt, int64_t T, int64_t K, int64_t ldx, int64_t tile,
+                      int64_t block, double keep, int32_t *idx);
+
 /* reduced product over kept slices, rows t in [t0,t1):
  * y[t*ldy+m] = (float) sum_{j in J_tau(t), ascending} (double)x[t,j]*(double)wt[j,m].
  * yd (optional, may be NULL) receives the unrounded double sums.

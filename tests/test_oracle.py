@@ -311,3 +311,72 @@ def test_attn_strided_cache_equals_packed():
     b = oracle.attn_decode(cs.q, ktp, vp, cs.kn, cs.scale, 0.5, 0.25, 0, S=40)
     for key in ("out", "dim_idx", "pos_idx", "lse"):
         assert np.array_equal(a[key], b[key])
+
+
+# ---------------------------------------------------------------- block-granular variant
+# Blog section 6.1 demo (ffn_block_reduce): block-mean |h| scores, keep_num =
+# max(1, int(num_blocks * keep_ratio)), top blocks re-sorted ascending, expanded.
+
+def test_block_select_hand_example():
+    # block means (1+3)/2 = 2, 0, 2, (5+0)/2 = 2.5; keep 2 of 4: block 3, then the
+    # lower of the tied blocks 0 and 2
+    x = np.array([[1, -3, 0, 0, 2, 2, -5, 0]], np.float32)
+    assert list(oracle.select_blocks(x, 1, 2, 0.5)[0]) == [0, 1, 6, 7]
+
+
+@pytest.mark.parametrize("nb,keep,want", [(64, 0.5, 32), (10, 0.01, 1), (100, 0.29, 28), (7, 1.0, 7),
+                                          (3, 0.5, 1), (4, 0.75, 3)])
+def test_block_keep_count_truncates(nb, keep, want):
+    # int() of the double product, as the demo code writes it (100 * 0.29 = 28.999999999999996)
+    assert oracle.block_keep_count(nb, keep) == want
+
+
+def test_block_keep_count_rejects_bad_ratio():
+    assert oracle.block_keep_count(8, 0.0) == -1
+    assert oracle.block_keep_count(8, 1.5) == -1
+
+
+def _brute_blocks(m, block, nk):
+    """Exact rational block means; the lexicographically first maximising set."""
+    nb = len(m) // block
+    fr = [Fraction(float(v)) for v in m]
+    means = [sum(fr[b * block:(b + 1) * block]) / block for b in range(nb)]
+    best, best_set = None, None
+    for comb in itertools.combinations(range(nb), nk):
+        tot = sum(means[b] for b in comb)
+        if best is None or tot > best:
+            best, best_set = tot, comb
+    return [b * block + e for b in best_set for e in range(block)]
+
+
+@pytest.mark.parametrize("block", [1, 2, 3, 4, 6])
+def test_block_select_brute_force(block):
+    K = 12
+    nb = K // block
+    for seed in range(25):
+        rng = np.random.default_rng(seed)
+        T, tile = (3, 3) if seed % 2 else (4, 2)
+        if seed % 3 == 0:
+            x = rng.integers(-2, 3, size=(T, K)).astype(np.float32)  # many tied block means
+        else:
+            x = rng.standard_normal((T, K)).astype(np.float32)
+        colmax = [np.abs(x[t0:t0 + tile]).max(axis=0) for t0 in range(0, T, tile)]
+        for nk in range(1, nb + 1):
+            keep = nk / nb
+            assert oracle.block_keep_count(nb, keep) == nk
+            idx = oracle.select_blocks(x, tile, block, keep)
+            for tau, m in enumerate(colmax):
+                assert list(idx[tau]) == _brute_blocks(m, block, nk), (block, seed, nk, tau)
+
+
+def test_block1_equals_slice_selector_with_unit_weights():
+    # block = 1 scores |x| exactly as the slice scorer with c = 1; with r*K an exact
+    # integer both counts agree, so the index sets must be identical
+    K = 64
+    for seed in range(10):
+        rng = np.random.default_rng(100 + seed)
+        x = rng.standard_normal((2, K)).astype(np.float32)
+        for k in (1, 16, 32, 63, 64):
+            a = oracle.select_blocks(x, 2, 1, k / K)
+            b = oracle.select(x, np.ones(K, np.float32), 2, k / K)
+            assert np.array_equal(a, b), (seed, k)

@@ -54,6 +54,13 @@ MUTATIONS = {
         "                    if (pg[hh * S + s] > a)\n                        a = pg[hh * S + s];\n",
         "                    a += pg[hh * S + s];\n",
         [lambda: P.test_attn_selections_brute_force(0)]),
+    "block keep count rounds up": (
+        "    double p = floor((double)nb * keep);", "    double p = ceil((double)nb * keep);",
+        [lambda: P.test_block_keep_count_truncates(100, 0.29, 28)]),
+    "blocks interleaved instead of contiguous": (
+        "                int64_t j = b * block + e;\n                float a = 0.0f;",
+        "                int64_t j = e * nb + b;\n                float a = 0.0f;",
+        [lambda: P.test_block_select_brute_force(3)]),
     "head_dim score reads one head only": (
         "for (int64_t h = h0; h < h0 + gsize; ++h) {\n                    float qa",
         "for (int64_t h = h0; h < h0 + 1; ++h) {\n                    float qa",
