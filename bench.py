@@ -230,6 +230,45 @@ def main():
         log(f"[bench] decode dense GEMV {t_dense * 1e6:.2f} us, torch.matmul (hipBLASLt) {t_blas * 1e6:.2f} us")
     del xs, ws_, cs_
 
+    # ------------------------------------------------------------------ block-granular variant (blog demo shape)
+    if not args.no_sweep and not args.headline_only:
+        log("[bench] ffn block demo: generating inputs")
+        bd = W.ffn_block_demo()
+        Kb, Mb = bd.K, bd.M
+        xb0, wb0, cb0 = bf(bd.x), bf(bd.wt), torch.from_numpy(bd.c).to(dev)
+        nbc = n_copies(wb0.numel() * 2, wb0.numel())
+        xbs = [xb0.clone() for _ in range(nbc)]
+        wbs = [wb0 if i == 0 else wb0.clone() for i in range(nbc)]
+        cbs = [cb0.clone() for _ in range(nbc)]
+        ybb = torch.empty((1, Mb), dtype=torch.float32, device=dev)
+        nk = rmm.block_keep_count(Kb // 64, 0.5)
+        kb = nk * 64
+        ibs = [rmm.select_blocks(xbs[i], 1, 64, 0.5) for i in range(nbc)]
+        isl = [rmm.select(xbs[i], cbs[i], 1, 0.5) for i in range(nbc)]
+
+        def bstep(i):
+            j = i % nbc
+            rmm.select_blocks(xbs[j], 1, 64, 0.5, idx=ibs[j])
+            rmm.linear(xbs[j], wbs[j], ibs[j], 1, out=ybb)
+
+        def sstep(i):
+            j = i % nbc
+            rmm.select(xbs[j], cbs[j], 1, 0.5, idx=isl[j])
+            rmm.linear(xbs[j], wbs[j], isl[j], 1, out=ybb)
+
+        t_b = time_loop(bstep, steps, warmup, torch)
+        t_s = time_loop(sstep, steps, warmup, torch)
+        t_bsel = event_avg(lambda i: rmm.select_blocks(xbs[i % nbc], 1, 64, 0.5, idx=ibs[i % nbc]), steps, torch)
+        t_d = event_avg(lambda i: rmm.linear_dense(xbs[i % nbc], wbs[i % nbc], out=ybb), steps, torch)
+        rec = {"workload": "ffn_block_demo", "block": 64, "keep": 0.5, "k": kb,
+               "block_step_us": t_b * 1e6, "block_select_us": t_bsel * 1e6, "slice_step_us": t_s * 1e6,
+               "dense_us": t_d * 1e6, "retained_bytes": A.decode_step_bytes(Kb, Mb, kb),
+               "block_step_GBps": A.decode_step_bytes(Kb, Mb, kb) / t_b / 1e9}
+        sweep.append(rec)
+        log(f"[bench] ffn block demo (K={Kb}, N={Mb}, 64-slice blocks, keep 0.5): block step {t_b * 1e6:.2f} us "
+            f"(select_blocks {t_bsel * 1e6:.2f} us), slice step {t_s * 1e6:.2f} us, dense GEMV {t_d * 1e6:.2f} us")
+        del xbs, wbs, cbs
+
     # ------------------------------------------------------------------ prefill (MFMA)
     if not args.no_sweep and not args.headline_only:
         log("[bench] prefill: generating inputs")

@@ -89,6 +89,26 @@ rmm_status_t rmm_select(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int
                         const float *c, int64_t tile, double r,
                         int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ block-granular selection
+ * The blog's block variant (section 5.1: a block's importance is the mean
+ * absolute activation over its neurons; 5.2: top-k over blocks, the block mask
+ * expanded to neuron indices; 6.1: the demo's ffn_block_reduce).  The
+ * contraction dimension is cut into nb = K / block blocks of `block`
+ * consecutive slices.  Per tile (as in rmm_select) and block b:
+ *     score[b] = ( sum_{j in b, ascending} (double) max_{t in tile} |x[t,j]| ) / block
+ * (the sum and the division in IEEE double).  The nk = rmm_block_keep_count(nb,
+ * keep) blocks of largest score are kept (equal scores: the lower block wins),
+ * in ASCENDING block order, each expanded to its `block` slice indices:
+ *   idx  out, int32 [ceil(T/tile)][nk*block]: idx[tau][i*block + e] = b_i*block + e
+ * The list feeds rmm_linear unchanged (k = nk*block).
+ * Limits: K % block == 0 (else RMM_EINVAL), K <= 32768, nb <= 1024.
+ * Deterministic. */
+int64_t rmm_block_keep_count(int64_t nb, double keep); /* max(1, floor(nb*keep)) clamped to nb; -1 if keep not in (0,1] */
+size_t rmm_select_blocks_workspace_size(int64_t T, int64_t K, int64_t tile, int64_t block, rmm_dtype_t xt);
+rmm_status_t rmm_select_blocks(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int64_t ldx,
+                               int64_t tile, int64_t block, double keep,
+                               int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ linear
  * Reduced product (blog sections 2 and 5.3; paper abstract):
  *     y[t,m] = sum_{j in idx[t/tile]} x[t,j] * wt[j,m]      (fp32 accumulation)

@@ -87,6 +87,9 @@ def lib():
                 "rmm_keep_count": (i64, [i64, dbl]),
                 "rmm_select_workspace_size": (sz, [i64, i64, i64, i32]),
                 "rmm_select": (i32, [vp, i32, i64, i64, i64, vp, i64, dbl, vp, vp, sz, vp]),
+                "rmm_block_keep_count": (i64, [i64, dbl]),
+                "rmm_select_blocks_workspace_size": (sz, [i64, i64, i64, i64, i32]),
+                "rmm_select_blocks": (i32, [vp, i32, i64, i64, i64, i64, i64, dbl, vp, vp, sz, vp]),
                 "rmm_linear_workspace_size": (sz, [i64, i64, i64, i64, i64, i32]),
                 "rmm_linear": (i32, [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, i64, i64, vp, i64, vp, sz, vp]),
                 "rmm_linear_dense_workspace_size": (sz, [i64, i64, i64, i32]),
@@ -108,7 +111,8 @@ def lib():
     return _lib
 
 
-EXPORTS = ("rmm_keep_count", "rmm_select_workspace_size", "rmm_select", "rmm_linear_workspace_size", "rmm_linear",
+EXPORTS = ("rmm_keep_count", "rmm_select_workspace_size", "rmm_select", "rmm_block_keep_count",
+           "rmm_select_blocks_workspace_size", "rmm_select_blocks", "rmm_linear_workspace_size", "rmm_linear",
            "rmm_linear_dense_workspace_size", "rmm_linear_dense", "rmm_attn_decode_workspace_size",
            "rmm_attn_decode", "rmm_attn_decode_dense_workspace_size", "rmm_attn_decode_dense", "rmm_status_string",
            "rmm_last_error")
@@ -183,6 +187,31 @@ def select(x: torch.Tensor, c: torch.Tensor, tile: int, r: float, idx: torch.Ten
     w = ws if ws is not None else _WS.get(need, x.device)
     _check(L.rmm_select(_ptr(x), _dtype(x), T, K, _ld(x), _ptr(c), tile, float(r), _ptr(idx), _ptr(w),
                         w.numel() * w.element_size(), _stream()))
+    return idx
+
+
+def block_keep_count(nb: int, keep: float) -> int:
+    """max(1, floor(nb * keep)) clamped to nb; -1 if keep is not in (0, 1]."""
+    return int(lib().rmm_block_keep_count(int(nb), float(keep)))
+
+
+def select_blocks(x: torch.Tensor, tile: int, block: int, keep: float, idx: torch.Tensor | None = None, ws=None):
+    """Block-granular selection: idx int32 [ceil(T/tile), nk*block], kept blocks ascending, expanded to slices."""
+    L = lib()
+    _dev(x, "x")
+    T, K = x.shape
+    if block < 1 or K % block:
+        raise RmmError(1, f"K = {K} is not a multiple of the block size {block}")
+    nk = block_keep_count(K // block, keep)
+    if nk < 0:
+        raise RmmError(1, f"keep ratio {keep} not in (0, 1]")
+    nt = -(-T // tile)
+    if idx is None:
+        idx = torch.empty((nt, nk * block), dtype=torch.int32, device=x.device)
+    need = L.rmm_select_blocks_workspace_size(T, K, tile, block, _dtype(x))
+    w = ws if ws is not None else _WS.get(need, x.device)
+    _check(L.rmm_select_blocks(_ptr(x), _dtype(x), T, K, _ld(x), tile, block, float(keep), _ptr(idx), _ptr(w),
+                               w.numel() * w.element_size(), _stream()))
     return idx
 
 

@@ -176,6 +176,63 @@ rmm_status_t rmm_select(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int
     return launch_status(rmm::launch_select(x, xt == RMM_BF16, T, K, ldx, c, tile, k, idx, pmax, stream), "select");
 }
 
+// ------------------------------------------------------------------ block-granular selection
+int64_t rmm_block_keep_count(int64_t nb, double keep)
+{
+    if (nb < 1 || !(keep > 0.0) || !(keep <= 1.0))
+        return -1;
+    int64_t kk = (int64_t)floor((double)nb * keep); // truncation of the double product
+    if (kk < 1)
+        kk = 1;
+    if (kk > nb)
+        kk = nb;
+    return kk;
+}
+
+size_t rmm_select_blocks_workspace_size(int64_t T, int64_t K, int64_t tile, int64_t block, rmm_dtype_t xt)
+{
+    (void)xt;
+    if (T < 1 || K < 1 || tile < 1 || block < 1)
+        return 0;
+    return RMM_WS_HEADER_BYTES + round256(rmm::select_ws_bytes(T, K, tile));
+}
+
+rmm_status_t rmm_select_blocks(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int64_t ldx, int64_t tile,
+                               int64_t block, double keep, int32_t *idx, void *ws, size_t ws_bytes,
+                               hipStream_t stream)
+{
+    if (!x || !idx)
+        return fail(RMM_EINVAL, "null pointer (x=%p idx=%p)", x, (void *)idx);
+    if (T < 1 || K < 1 || tile < 1 || block < 1)
+        return fail(RMM_EINVAL, "sizes must be positive (T=%lld K=%lld tile=%lld block=%lld)", (long long)T,
+                    (long long)K, (long long)tile, (long long)block);
+    if (xt != RMM_F32 && xt != RMM_BF16)
+        return fail(RMM_EINVAL, "unknown dtype %d", (int)xt);
+    if (ldx < K)
+        return fail(RMM_EINVAL, "ldx (%lld) < K (%lld)", (long long)ldx, (long long)K);
+    if (K % block)
+        return fail(RMM_EINVAL, "K = %lld is not a multiple of the block size %lld", (long long)K, (long long)block);
+    const int64_t nb = K / block;
+    const int64_t nk = rmm_block_keep_count(nb, keep);
+    if (nk < 0)
+        return fail(RMM_EINVAL, "keep ratio %g not in (0, 1]", keep);
+    if (K > SELECT_MAX_K || nb > SELECT_BLOCKS_MAX_NB)
+        return fail(RMM_EUNSUPPORTED, "K = %lld or %lld blocks above the limits %d / %d", (long long)K,
+                    (long long)nb, SELECT_MAX_K, SELECT_BLOCKS_MAX_NB);
+    if (T > INT32_MAX)
+        return fail(RMM_EUNSUPPORTED, "T beyond 2^31");
+    const int ve = vec_elems(xt);
+    if (!aligned16(x) || ldx % ve)
+        return fail(RMM_EUNSUPPORTED, "x must be 16-byte aligned with ldx a multiple of %d elements", ve);
+    const size_t need = rmm_select_blocks_workspace_size(T, K, tile, block, xt);
+    if (!ws || ws_bytes < need)
+        return fail(RMM_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    init_once();
+    float *pmax = (float *)((char *)ws + RMM_WS_HEADER_BYTES);
+    return launch_status(
+        rmm::launch_select_blocks(x, xt == RMM_BF16, T, K, ldx, tile, block, nk, idx, pmax, stream), "select_blocks");
+}
+
 // ------------------------------------------------------------------ linear
 size_t rmm_linear_workspace_size(int64_t T, int64_t K, int64_t M, int64_t k, int64_t tile, rmm_dtype_t xt)
 {

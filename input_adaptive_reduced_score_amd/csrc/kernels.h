@@ -42,6 +42,9 @@ namespace rmm {
 size_t select_ws_bytes(int64_t T, int64_t K, int64_t tile);
 hipError_t launch_select(const void *x, bool bf16, int64_t T, int64_t K, int64_t ldx, const float *c, int64_t tile,
                          int64_t k, int32_t *idx, float *pmax_ws, hipStream_t st);
+hipError_t launch_select_blocks(const void *x, bool bf16, int64_t T, int64_t K, int64_t ldx, int64_t tile,
+                                int64_t block, int64_t nk, int32_t *idx, float *pmax_ws, hipStream_t st);
+#define SELECT_BLOCKS_MAX_NB 1024
 void select_init();
 
 // linear.hip

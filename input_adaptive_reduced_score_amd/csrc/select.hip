@@ -431,6 +431,116 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
         dst[p] = outl[p];
 }
 
+// Block-granular variant (blog section 5.1 block-mean |h| importance, 5.2
+// block top-k with the mask expanded to slice indices, 6.1 demo code): block b
+// of `block` consecutive slices scores mean_{j in b} max_{t in tile} |x[t,j]|,
+// summed in ascending slice order in double and divided once; the nk best
+// blocks (ties to the lower block) are listed in ascending order, expanded to
+// their slices.  One workgroup of 1024 threads per tile, one thread per block.
+template <typename TE>
+__global__ __launch_bounds__(SEL_THREADS) void select_blocks_kernel(const TE *__restrict__ x, int64_t ldx, int T,
+                                                                    int K, int tile, const float *__restrict__ pmax,
+                                                                    int Kp, int nrsplit, int direct, int block,
+                                                                    int nb, int nk, int32_t *__restrict__ idx)
+{
+    constexpr int NW = SEL_THREADS / WAVE;
+    extern __shared__ float mj[]; // K column maxima of the tile
+    __shared__ double bs[SEL_THREADS];
+    __shared__ uint32_t wk[NW];
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, tau = blockIdx.x;
+    // 1. column maxima (coalesced over j)
+    if (direct) {
+        const int t0 = tau * tile, t1 = min(T, t0 + tile);
+        for (int j = tid; j < K; j += SEL_THREADS) {
+            float a = 0.0f;
+            for (int t = t0; t < t1; ++t)
+                a = fmaxf(a, fabsf(ld_elem(x, (int64_t)t * ldx + j)));
+            mj[j] = a;
+        }
+    } else {
+        const float *pm = pmax + (int64_t)tau * nrsplit * Kp;
+        for (int j = tid; j < K; j += SEL_THREADS) {
+            float a = 0.0f;
+            for (int rs = 0; rs < nrsplit; ++rs)
+                a = fmaxf(a, pm[(int64_t)rs * Kp + j]);
+            mj[j] = a;
+        }
+    }
+    __syncthreads();
+    // 2. block means
+    if (tid < nb) {
+        double sum = 0.0;
+        for (int e = 0; e < block; ++e)
+            sum += (double)mj[tid * block + e];
+        bs[tid] = sum / (double)block;
+    }
+    __syncthreads();
+    // 3. rank by counting: blocks with a larger mean, or an equal mean at a lower index
+    uint32_t keep = 0;
+    if (tid < nb) {
+        const double me = bs[tid];
+        uint32_t a0 = 0, a1 = 0;
+        int o = 0;
+        for (; o + 1 < nb; o += 2) {
+            const double v0 = bs[o], v1 = bs[o + 1];
+            a0 += (v0 > me) || (v0 == me && o < tid);
+            a1 += (v1 > me) || (v1 == me && o + 1 < tid);
+        }
+        if (o < nb) {
+            const double v0 = bs[o];
+            a0 += (v0 > me) || (v0 == me && o < tid);
+        }
+        keep = a0 + a1 < (uint32_t)nk;
+    }
+    // 4. position among the kept blocks (ascending block order)
+    const uint32_t incl = wave_incl_sum(keep);
+    if (lane == WAVE - 1)
+        wk[w] = incl;
+    __syncthreads();
+    uint32_t pos = incl - keep;
+#pragma unroll
+    for (int v = 0; v < NW; ++v)
+        pos += v < w ? wk[v] : 0u;
+    // 5. expanded slice indices
+    if (keep && pos < (uint32_t)nk) {
+        int32_t *dst = idx + ((int64_t)tau * nk + pos) * block;
+        for (int e = 0; e < block; ++e)
+            dst[e] = tid * block + e;
+    }
+}
+
+hipError_t launch_select_blocks(const void *x, bool bf16, int64_t T, int64_t K, int64_t ldx, int64_t tile,
+                                int64_t block, int64_t nk, int32_t *idx, float *pmax_ws, hipStream_t st)
+{
+    const int ntiles = (int)((T + tile - 1) / tile);
+    const int rows = (int)(tile < T ? tile : T);
+    const bool direct = rows <= SELECT_DIRECT_ROWS;
+    const int Kp = (int)((K + 7) / 8 * 8);
+    int nrsplit = 1;
+    if (!direct) {
+        const int vec = bf16 ? 8 : 4;
+        nrsplit = (rows + COLMAX_ROWS - 1) / COLMAX_ROWS;
+        dim3 grid(ntiles * nrsplit, (unsigned)((K + WAVE * vec - 1) / (WAVE * vec)));
+        if (bf16)
+            colmax_kernel<uint16_t><<<grid, COLMAX_THREADS, 0, st>>>((const uint16_t *)x, ldx, (int)T, (int)K,
+                                                                      (int)tile, COLMAX_ROWS, nrsplit, Kp, pmax_ws);
+        else
+            colmax_kernel<float><<<grid, COLMAX_THREADS, 0, st>>>((const float *)x, ldx, (int)T, (int)K, (int)tile,
+                                                                   COLMAX_ROWS, nrsplit, Kp, pmax_ws);
+    }
+    const size_t lds = (size_t)K * sizeof(float);
+    const int nb = (int)(K / block);
+    if (bf16)
+        select_blocks_kernel<uint16_t><<<ntiles, SEL_THREADS, lds, st>>>(
+            (const uint16_t *)x, ldx, (int)T, (int)K, (int)tile, pmax_ws, Kp, nrsplit, direct, (int)block, nb,
+            (int)nk, idx);
+    else
+        select_blocks_kernel<float><<<ntiles, SEL_THREADS, lds, st>>>((const float *)x, ldx, (int)T, (int)K,
+                                                                       (int)tile, pmax_ws, Kp, nrsplit, direct,
+                                                                       (int)block, nb, (int)nk, idx);
+    return hipGetLastError();
+}
+
 static int per_for(int64_t K)
 {
     return K <= 8 * SEL_THREADS ? 8 : K <= 16 * SEL_THREADS ? 16 : 32;
@@ -504,6 +614,10 @@ void select_init()
     (void)hipFuncSetAttribute((const void *)select_kernel<float, 16>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     (void)hipFuncSetAttribute((const void *)select_kernel<uint16_t, 32>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     (void)hipFuncSetAttribute((const void *)select_kernel<float, 32>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipFuncSetAttribute((const void *)select_blocks_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              SELECT_MAX_K * (int)sizeof(float));
+    (void)hipFuncSetAttribute((const void *)select_blocks_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              SELECT_MAX_K * (int)sizeof(float));
 }
 
 } // namespace rmm

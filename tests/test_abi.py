@@ -80,3 +80,31 @@ def test_linear_and_attn_argument_errors_host_only():
     assert L.rmm_attn_decode(*args) == 3  # no workspace
     assert L.rmm_attn_decode_workspace_size(1, 32, 8, 128, 32768, 0.25, 0.25, 0) > 0
     assert L.rmm_status_string(3).startswith(b"RMM_EWORKSPACE")
+
+
+@pytest.mark.parametrize("nb", [1, 3, 7, 64, 100, 1024])
+def test_block_keep_count_matches_oracle(nb):
+    for keep in (1e-6, 0.01, 0.29, 1 / 3, 0.5, 0.75, 0.999, 1.0, 0.0, -0.5, 1.5, float("nan")):
+        assert rmm.block_keep_count(nb, keep) == oracle.block_keep_count(nb, keep), (nb, keep)
+
+
+def _call_select_blocks(**kw):
+    L = rmm.lib()
+    a = dict(x=C.c_void_p(16), xt=1, T=1, K=4096, ldx=4096, tile=1, block=64, keep=0.5, idx=C.c_void_p(16),
+             ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.rmm_select_blocks(*a.values())
+
+
+def test_select_blocks_argument_errors_host_only():
+    L = rmm.lib()
+    assert _call_select_blocks(x=None) == 1
+    assert _call_select_blocks(block=0) == 1
+    assert _call_select_blocks(block=100) == 1               # K not a multiple of the block size
+    assert b"multiple" in L.rmm_last_error()
+    assert _call_select_blocks(keep=0.0) == 1
+    assert _call_select_blocks(keep=2.0) == 1
+    assert _call_select_blocks(block=2) == 2                 # 2048 blocks: above the block-count limit
+    assert _call_select_blocks(K=40960, ldx=40960) == 2      # above the selector's K limit
+    assert _call_select_blocks(x=C.c_void_p(18)) == 2        # misaligned
+    assert _call_select_blocks() == 3                        # no workspace

@@ -29,6 +29,7 @@ import numpy as np
 
 # tensor stream ids: one independent random stream per role
 S_X, S_W, S_A, S_B, S_OUTLIER, S_Q, S_K, S_V, S_HOT = 1, 2, 3, 4, 5, 6, 7, 8, 9
+S_WG, S_WU = 10, 11
 
 SLAB = 1 << 24  # elements per independently seeded slab
 
@@ -194,6 +195,22 @@ def linear_prefill(seed: int = 0, T: int = 2048, K: int = 4096, M: int = 4096,
     c = row_l2_f32(wt, True)
     return LinearCase(f"prefill_bf16_T{T}_K{K}_M{M}_tile{tile}", xb, wt, c, tile, "bf16",
                       (0.25, 0.5, 0.75, 1.0))
+
+
+def ffn_block_demo(seed: int = 42, H: int = 1024, Mi: int = 4096) -> LinearCase:
+    """The blog's block demo shape (section 6.1 run_demo): one token x[1,H] ~N(0,1),
+    W_gate, W_up [Mi,H] ~N(0,0.02); the down projection's input h = silu(W_gate x) *
+    (W_up x) [1,Mi] (float64 products, rounded to bf16) is the activation; W^T =
+    W_down^T [Mi,H] bf16 ~N(0,0.02).  Synthetic stand-in for the demo's torch draws."""
+    x_in = normal_f32(seed, S_X, H).astype(np.float64)
+    wg = normal_f32(seed, S_WG, Mi * H, 0.02).reshape(Mi, H).astype(np.float64)
+    wu = normal_f32(seed, S_WU, Mi * H, 0.02).reshape(Mi, H).astype(np.float64)
+    g, u = wg @ x_in, wu @ x_in
+    h = (g / (1.0 + np.exp(-g))) * u
+    xb = f32_to_bf16_bits(h.astype(np.float32)).reshape(1, Mi)
+    wt = normal_bf16(seed, S_W, Mi * H, 0.02).reshape(Mi, H)
+    c = row_l2_f32(wt, True)
+    return LinearCase(f"ffn_block_demo_bf16_Mi{Mi}_H{H}", xb, wt, c, 1, "bf16", (0.5,))
 
 
 # ----------------------------------------------------------------------------
