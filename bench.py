@@ -230,6 +230,48 @@ def main():
         log(f"[bench] decode dense GEMV {t_dense * 1e6:.2f} us, torch.matmul (hipBLASLt) {t_blas * 1e6:.2f} us")
     del xs, ws_, cs_
 
+    # ------------------------------------------------------------------ batched decode (per-token vs shared selection)
+    if not args.no_sweep and not args.headline_only:
+        log("[bench] batched decode: generating inputs")
+        bB = 16
+        bc = W.linear_random(bB, K, M, 1, "bf16", seed=3, xsigma=1.0, wsigma=0.02)
+        xq = bf(W.silu_times_b_bf16(3, bB * K).reshape(bB, K))
+        wq0, cq0 = bf(bc.wt), torch.from_numpy(bc.c).to(dev)
+        nq = n_copies(wq0.numel() * 2, 2 * rmm.keep_count(K, 0.5) * M)
+        wqs = [wq0 if i == 0 else wq0.clone() for i in range(nq)]
+        del wq0
+        for B in (4, 16):
+            xB = xq[:B].contiguous()
+            yq = torch.empty((B, M), dtype=torch.float32, device=dev)
+            r = 0.5
+            k = rmm.keep_count(K, r)
+            ipt = rmm.select(xB, cq0, 1, r)          # one kept set per token
+            ish = rmm.select(xB, cq0, B, r)          # one kept set for the batch (max over its tokens)
+            torch.cuda.synchronize()
+            per_tok = ipt.cpu().numpy()
+            union = len(np.unique(per_tok))
+            shared_cover = np.mean([len(np.intersect1d(per_tok[t], ish.cpu().numpy()[0])) / k for t in range(B)])
+
+            def ptok(i):
+                rmm.select(xB, cq0, 1, r, idx=ipt)
+                rmm.linear(xB, wqs[i % nq], ipt, 1, out=yq)
+
+            def shr(i):
+                rmm.select(xB, cq0, B, r, idx=ish)
+                rmm.linear(xB, wqs[i % nq], ish, B, out=yq)
+
+            t_pt = time_loop(ptok, steps, warmup, torch)
+            t_sh = time_loop(shr, steps, warmup, torch)
+            t_dn = event_avg(lambda i: rmm.linear_dense(xB, wqs[i % nq], out=yq), steps, torch)
+            rec = {"workload": "decode_batch", "B": B, "r": r, "k": k, "per_token_step_us": t_pt * 1e6,
+                   "shared_step_us": t_sh * 1e6, "dense_us": t_dn * 1e6, "union_rows": int(union),
+                   "union_frac_of_K": union / K, "shared_covers_own_top_k": float(shared_cover)}
+            sweep.append(rec)
+            log(f"[bench] batched decode B={B}, r={r}: per-token selection {t_pt * 1e6:.1f} us, shared selection "
+                f"{t_sh * 1e6:.1f} us, dense {t_dn * 1e6:.1f} us; union of per-token sets = {union / K:.1%} of K, "
+                f"shared set holds {shared_cover:.1%} of each token's own top-k")
+        del wqs
+
     # ------------------------------------------------------------------ block-granular variant (blog demo shape)
     if not args.no_sweep and not args.headline_only:
         log("[bench] ffn block demo: generating inputs")

@@ -96,6 +96,15 @@ def test_linear_beyond_selector_k(K, dense):
     assert rel_l2(y.cpu().numpy(), yr) <= TOL
 
 
+@pytest.mark.parametrize("tile", [1, 4, 16])
+def test_batched_decode_shape(tile):
+    # 16 tokens at the decode shape: per-token selection (tile 1), groups of 4, one shared set
+    x = W.silu_times_b_bf16(3, 16 * 14336).reshape(16, 14336)
+    wt = W.normal_bf16(3, W.S_W, 14336 * 4096, 0.02).reshape(14336, 4096)
+    cs = W.LinearCase("decode_batch16", x, wt, W.row_l2_f32(wt, True), tile, "bf16")
+    run_case(cs, 0.5, rows=[0, 5, 15])
+
+
 def test_strided_operands():
     # leading dimensions larger than the logical sizes (views into bigger buffers)
     cs = W.linear_random(40, 200, 72, 32, "bf16", seed=3)
