@@ -62,7 +62,7 @@ def lib():
         L.ora_dense_linear.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, i64, i64, i64, vp, i64, vp]
         L.ora_attn_decode.restype = i32
         L.ora_attn_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, C.c_float,
-                                      dbl, dbl, i32, vp, vp, vp, vp, vp, vp, vp]
+                                      dbl, dbl, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.ora_dense_attn.restype = i32
         L.ora_dense_attn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, C.c_float, vp]
         _lib = L
@@ -162,17 +162,21 @@ def dense_linear(x, wt, rows=None, want_double=False):
     return (y, yd) if want_double else y
 
 
-def attn_decode(q, kt, v, kn, scale, r_dim, r_pos, mode=0, S=None, want=("out",)):
+def attn_decode(q, kt, v, kn, scale, r_dim, r_pos, mode=0, S=None, want=("out",), vn=None):
     """Reduced GQA decode attention. q [B,Hq,D], kt [B,Hkv,D,ldk], v [B,Hkv,ldv,D] uint16 (bf16),
-    kn [B,Hkv,D] float32.  Returns a dict with the requested entries among
+    kn [B,Hkv,D] float32; vn [B,Hkv,ldv] float32 (optional: weights the position score by the
+    value-row norm).  Returns a dict with the requested entries among
     out, dim_idx, pos_idx, lse, pi, p, out_d."""
     q = np.ascontiguousarray(q, dtype=np.uint16)
     kt = np.ascontiguousarray(kt, dtype=np.uint16)
     v = np.ascontiguousarray(v, dtype=np.uint16)
     kn = np.ascontiguousarray(kn, dtype=np.float32)
+    vn = None if vn is None else np.ascontiguousarray(vn, dtype=np.float32)
     B, Hq, D = q.shape
     Hkv, ldk = kt.shape[1], kt.shape[3]
     ldv = v.shape[2]
+    if vn is not None and vn.shape != (B, Hkv, ldv):
+        raise ValueError("vn must be [B, Hkv, ldv]")
     S = ldk if S is None else S
     Hsel = Hkv if mode == 0 else Hq
     kd, ks = keep_count(D, r_dim), keep_count(S, r_pos)
@@ -189,7 +193,7 @@ def attn_decode(q, kt, v, kn, scale, r_dim, r_pos, mode=0, S=None, want=("out",)
     _check(lib().ora_attn_decode(_p(q), _p(kt), _p(v), _p(kn), B, Hq, Hkv, D, S, ldk, ldv, float(scale),
                                  float(r_dim), float(r_pos), int(mode), _p(res["out"]), _p(res["dim_idx"]),
                                  _p(res["pos_idx"]), _p(res["lse"]), _p(res["pi"]), _p(res["p"]),
-                                 _p(res["out_d"])), "attn_decode")
+                                 _p(res["out_d"]), _p(vn)), "attn_decode")
     return res
 
 

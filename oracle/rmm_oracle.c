@@ -275,7 +275,7 @@ int ora_attn_decode(const uint16_t *q, const uint16_t *kt, const uint16_t *v, co
                     int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,
                     int64_t ldk, int64_t ldv, float scale, double r_dim, double r_pos, int mode,
                     float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
-                    double *pi, double *p, double *out_d)
+                    double *pi, double *p, double *out_d, const float *vn)
 {
     if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || S < 1 || Hq % Hkv != 0 || ldk < S || ldv < S)
         return 1;
@@ -351,13 +351,14 @@ int ora_attn_decode(const uint16_t *q, const uint16_t *kt, const uint16_t *v, co
                     memcpy(p + (b * Hq + h) * S, ph, (size_t)S * sizeof *ph);
             }
 
-            /* 4. position scores and selection */
+            /* 4. position scores and selection; with vn the score is weighted by the
+             * norm of the value row, p * ||V_s|| (the analogue of the linear scorer) */
             for (int64_t s = 0; s < S; ++s) {
                 double a = pg[s];
                 for (int64_t hh = 1; hh < gsize; ++hh)
                     if (pg[hh * S + s] > a)
                         a = pg[hh * S + s];
-                pis[s] = a;
+                pis[s] = vn ? a * (double)vn[(b * Hkv + g) * ldv + s] : a;
             }
             if (pi)
                 memcpy(pi + (b * Hsel + sg) * S, pis, (size_t)S * sizeof *pis);

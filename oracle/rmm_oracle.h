@@ -83,13 +83,16 @@ int ora_dense_linear(const void *x, int xt, int64_t T, int64_t K, int64_t ldx,
  * pos_idx [B][Hsel][k_s], lse [B][Hq] float, pi [B][Hsel][S] double (the
  * position scores), p [B][Hq][S] double (softmax probabilities),
  * out_d [B][Hq][D] double.
- * Pinned: brute force (D=S=12), softmax sums to 1, r=1 equals textbook
- * attention (float64 library), dropped-position identity. */
+ * vn (may be NULL): [B][Hkv][ldv] fp32 norms of the value rows; when given the
+ * position score is max_h p_h[s] * vn[s] instead of max_h p_h[s].
+ * Pinned: brute force (D=S=12, with and without vn), softmax sums to 1, r=1
+ * equals textbook attention (float64 library), dropped-position identity,
+ * vn = 1 equals the probability score. */
 int ora_attn_decode(const uint16_t *q, const uint16_t *kt, const uint16_t *v, const float *kn,
                     int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,
                     int64_t ldk, int64_t ldv, float scale, double r_dim, double r_pos, int mode,
                     float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
-                    double *pi, double *p, double *out_d);
+                    double *pi, double *p, double *out_d, const float *vn);
 
 /* textbook dense attention in double (no reduction): out_d [B][Hq][D]. */
 int ora_dense_attn(const uint16_t *q, const uint16_t *kt, const uint16_t *v,

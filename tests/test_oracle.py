@@ -380,3 +380,55 @@ def test_block1_equals_slice_selector_with_unit_weights():
             a = oracle.select_blocks(x, 2, 1, k / K)
             b = oracle.select(x, np.ones(K, np.float32), 2, k / K)
             assert np.array_equal(a, b), (seed, k)
+
+
+# ---------------------------------------------------------------- value-norm-weighted position score
+# The analogue of the linear scorer for positions: p_h[s] * ||V[s,:]|| (max over the group's heads).
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_attn_vn_ones_equals_probability_score(mode):
+    cs = W.attn_case(1, 50, Hq=4, Hkv=2, D=16, seed=8, n_hot=3)
+    ones = np.ones((1, 2, 50), np.float32)
+    a = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.5, 0.3, mode)
+    b = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.5, 0.3, mode, vn=ones)
+    for key in ("out", "dim_idx", "pos_idx", "lse"):
+        assert np.array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_attn_vn_brute_force(mode):
+    for seed in range(10):
+        cs = W.attn_case(1, 12, Hq=4, Hkv=1, D=12, seed=seed, n_hot=2)
+        vn = W.value_row_norms(cs.v)
+        for ks in range(1, 13):
+            res = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.5, ks / 12, mode, want=("pi", "p"),
+                                     vn=vn)
+            groups = [[0, 1, 2, 3]] if mode == 0 else [[h] for h in range(4)]
+            for sg, heads in enumerate(groups):
+                want = res["p"][0, heads].max(axis=0) * vn[0, 0].astype(np.float64)
+                assert np.array_equal(res["pi"][0, sg], want)
+                assert list(res["pos_idx"][0, sg]) == _brute_topk(want, ks)
+
+
+def test_attn_vn_scale_invariant():
+    cs = W.attn_case(1, 64, Hq=4, Hkv=2, D=16, seed=9, n_hot=4)
+    vn = W.value_row_norms(cs.v)
+    a = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.5, 0.25, 0, vn=vn)
+    b = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.5, 0.25, 0, vn=vn * np.float32(8.0))
+    assert np.array_equal(a["pos_idx"], b["pos_idx"]) and np.array_equal(a["out"], b["out"])
+
+
+def test_attn_vn_strided_equals_packed():
+    cs = W.attn_case(1, 40, Hq=4, Hkv=2, D=16, seed=6, n_hot=3)
+    rng = np.random.default_rng(1)
+    vn = rng.uniform(0.5, 2.0, size=(1, 2, 40)).astype(np.float32)
+    ktp = np.zeros((1, 2, 16, 64), np.uint16)
+    ktp[..., :40] = cs.kt
+    vp = np.zeros((1, 2, 56, 16), np.uint16)
+    vp[:, :, :40] = cs.v
+    vnp = np.full((1, 2, 56), 100.0, np.float32)  # spare capacity: must never be read
+    vnp[:, :, :40] = vn
+    a = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, 0.5, 0.25, 0, vn=vn)
+    b = oracle.attn_decode(cs.q, ktp, vp, cs.kn, cs.scale, 0.5, 0.25, 0, S=40, vn=vnp)
+    for key in ("out", "dim_idx", "pos_idx", "lse"):
+        assert np.array_equal(a[key], b[key])

@@ -61,6 +61,13 @@ MUTATIONS = {
         "                int64_t j = b * block + e;\n                float a = 0.0f;",
         "                int64_t j = e * nb + b;\n                float a = 0.0f;",
         [lambda: P.test_block_select_brute_force(3)]),
+    "value norms ignored": (
+        "pis[s] = vn ? a * (double)vn[(b * Hkv + g) * ldv + s] : a;", "pis[s] = a;",
+        [lambda: P.test_attn_vn_brute_force(0)]),
+    "value norms read with the wrong pitch": (
+        "pis[s] = vn ? a * (double)vn[(b * Hkv + g) * ldv + s] : a;",
+        "pis[s] = vn ? a * (double)vn[(b * Hkv + g) * S + s] : a;",
+        [P.test_attn_vn_strided_equals_packed]),
     "head_dim score reads one head only": (
         "for (int64_t h = h0; h < h0 + gsize; ++h) {\n                    float qa",
         "for (int64_t h = h0; h < h0 + 1; ++h) {\n                    float qa",

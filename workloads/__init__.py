@@ -281,6 +281,13 @@ def attn_case(B: int, S: int, Hq: int = 32, Hkv: int = 8, D: int = 128, seed: in
     return AttnCase(nm, q, kt, v, kn, float(np.float32(1.0 / math.sqrt(D))), hot)
 
 
+def value_row_norms(v: np.ndarray) -> np.ndarray:
+    """vn [B,Hkv,ldv] float32: L2 norm of every stored bf16 value row (float64 sum, rounded once),
+    the per-position side input a cache owner keeps next to V."""
+    vf = bf16_bits_to_f32(v).astype(np.float64)
+    return np.sqrt((vf * vf).sum(axis=-1)).astype(np.float32)
+
+
 def attn_32k(seed: int = 0) -> AttnCase:
     cs = attn_case(1, 32768, seed=seed)
     cs.r_pairs = ((0.25, 0.25), (0.5, 0.5))
