@@ -381,6 +381,19 @@ def main():
                        "retained_bytes": by, "GBps": by / t / 1e9, "frac_hbm": by / t / 1e9 / A.HBM_PEAK_GBS}
                 sweep.append(rec)
                 log(f"[bench] {name} r=({rd},{rp}): {rec['call_us']:.1f} us, {rec['GBps']:.0f} GB/s retained")
+            if S <= 32768:
+                # position score weighted by the value-row norm: one more fp32 read per position
+                vns = [torch.from_numpy(W.value_row_norms(ac.v)).to(dev) for _ in range(nac)]
+                rd, rp = 0.25, 0.25
+                kd, kss = rmm.keep_count(D, rd), rmm.keep_count(S, rp)
+                t = time_loop(lambda i: rmm.attn_decode(qs[i % nac], ks_[i % nac], vs_[i % nac], kns[i % nac], rd, rp,
+                                                        scale=ac.scale, out=out, want_idx=False, vn=vns[i % nac]),
+                              asteps, 3, torch)
+                by = A.attn_step_bytes(B, Hq, Hkv, D, S, kd, kss) + 4 * B * Hkv * S
+                sweep.append({"workload": name + "_vnorm", "r_dim": rd, "r_pos": rp, "kd": kd, "ks": kss,
+                              "call_us": t * 1e6, "retained_bytes": by, "GBps": by / t / 1e9})
+                log(f"[bench] {name} value-norm score r=({rd},{rp}): {t * 1e6:.1f} us")
+                del vns
             t = time_loop(lambda i: rmm.attn_decode_dense(qs[i % nac], ks_[i % nac], vs_[i % nac], scale=ac.scale,
                                                           out=out), asteps, 3, torch)
             by = A.attn_dense_bytes(B, Hq, Hkv, D, S)

@@ -170,6 +170,26 @@ rmm_status_t rmm_attn_decode(const void *q, const void *kt, const void *v, const
                              float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
                              void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Same as rmm_attn_decode, with the position score optionally weighted by the
+ * norm of the value row: step 4 ranks pi_s = max_{h in group} p_h[s] * vn[b,g,s]
+ * instead of max_h p_h[s] -- the counterpart, for the PV product, of the linear
+ * scorer's |x| * ||W^T row|| (blog section 5.1: a slice's weight is its input
+ * magnitude times its weight norm).  Step 5 is unchanged (no renormalisation,
+ * p_h[s] unweighted).
+ *   vn  NULL, or fp32 [B][Hkv][ldv], 16-byte aligned, vn[b,g,s] >= 0 for s < S
+ *       (vn[b,g,s] = L2 norm of V[b,g,s,:], kept by the cache owner; entries
+ *       s >= S are read but ignored)
+ * The fixed-point key holds log(pi_s) with 2^-25 resolution over [-120, 8):
+ * norms above e^8 (about 2981) saturate.  vn = NULL gives exactly
+ * rmm_attn_decode's results; the workspace size is rmm_attn_decode's. */
+rmm_status_t rmm_attn_decode_ex(const void *q, const void *kt, const void *v, const float *kn,
+                                const float *vn,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,
+                                int64_t ldk, int64_t ldv, float scale,
+                                double r_dim, double r_pos, rmm_sel_mode_t mode,
+                                float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Dense decode attention (all D dims, all S positions, online softmax) -- the
  * r = 1 baseline.  Same layouts; lse optional. */
 size_t rmm_attn_decode_dense_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S);

@@ -97,6 +97,8 @@ def lib():
                 "rmm_attn_decode_workspace_size": (sz, [i64, i64, i64, i64, i64, dbl, dbl, i32]),
                 "rmm_attn_decode": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, flt, dbl, dbl, i32,
                                           vp, vp, vp, vp, vp, sz, vp]),
+                "rmm_attn_decode_ex": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, flt, dbl, dbl,
+                                             i32, vp, vp, vp, vp, vp, sz, vp]),
                 "rmm_attn_decode_dense_workspace_size": (sz, [i64, i64, i64, i64, i64]),
                 "rmm_attn_decode_dense": (i32, [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, flt, vp, vp, vp, sz,
                                                 vp]),
@@ -114,7 +116,7 @@ def lib():
 EXPORTS = ("rmm_keep_count", "rmm_select_workspace_size", "rmm_select", "rmm_block_keep_count",
            "rmm_select_blocks_workspace_size", "rmm_select_blocks", "rmm_linear_workspace_size", "rmm_linear",
            "rmm_linear_dense_workspace_size", "rmm_linear_dense", "rmm_attn_decode_workspace_size",
-           "rmm_attn_decode", "rmm_attn_decode_dense_workspace_size", "rmm_attn_decode_dense", "rmm_status_string",
+           "rmm_attn_decode", "rmm_attn_decode_ex", "rmm_attn_decode_dense_workspace_size", "rmm_attn_decode_dense", "rmm_status_string",
            "rmm_last_error")
 
 
@@ -249,9 +251,10 @@ def linear_dense(x: torch.Tensor, wt: torch.Tensor, out: torch.Tensor | None = N
 
 def attn_decode(q, kt, v, kn, r_dim: float, r_pos: float, scale: float | None = None, mode: int = PER_KV_GROUP,
                 S: int | None = None, out=None, dim_idx=None, pos_idx=None, lse=None, want_idx: bool = True,
-                ws=None):
+                ws=None, vn=None):
     """Reduced GQA decode attention.  q [B,Hq,D] bf16; kt [B,Hkv,D,ldk] bf16 (dim-major keys);
-    v [B,Hkv,ldv,D] bf16; kn [B,Hkv,D] fp32.  Returns (out, dim_idx, pos_idx, lse)."""
+    v [B,Hkv,ldv,D] bf16; kn [B,Hkv,D] fp32; vn None or [B,Hkv,ldv] fp32 value-row norms, which
+    weight the position score (p * ||V_s||).  Returns (out, dim_idx, pos_idx, lse)."""
     L = lib()
     _dev(q, "q")
     B, Hq, D = q.shape
@@ -261,6 +264,10 @@ def attn_decode(q, kt, v, kn, r_dim: float, r_pos: float, scale: float | None = 
     for t, n in ((q, "q"), (kt, "kt"), (v, "v"), (kn, "kn")):
         if not t.is_contiguous():
             raise ValueError(f"{n} must be contiguous")
+    if vn is not None:
+        _dev(vn, "vn")
+        if vn.dtype != torch.float32 or tuple(vn.shape) != (B, Hkv, ldv) or not vn.is_contiguous():
+            raise ValueError(f"vn must be a contiguous float32 tensor of shape {(B, Hkv, ldv)}")
     scale = float(D) ** -0.5 if scale is None else float(scale)
     Hsel = Hkv if mode == PER_KV_GROUP else Hq
     kd, ks = keep_count(D, r_dim), keep_count(S, r_pos)
@@ -278,9 +285,14 @@ def attn_decode(q, kt, v, kn, r_dim: float, r_pos: float, scale: float | None = 
             lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     need = L.rmm_attn_decode_workspace_size(B, Hq, Hkv, D, S, float(r_dim), float(r_pos), mode)
     w = ws if ws is not None else _WS.get(need, dev)
-    _check(L.rmm_attn_decode(_ptr(q), _ptr(kt), _ptr(v), _ptr(kn), B, Hq, Hkv, D, S, ldk, ldv, scale, float(r_dim),
-                             float(r_pos), mode, _ptr(out), _ptr(dim_idx), _ptr(pos_idx), _ptr(lse), _ptr(w),
-                             w.numel() * w.element_size(), _stream()))
+    if vn is None:
+        _check(L.rmm_attn_decode(_ptr(q), _ptr(kt), _ptr(v), _ptr(kn), B, Hq, Hkv, D, S, ldk, ldv, scale,
+                                 float(r_dim), float(r_pos), mode, _ptr(out), _ptr(dim_idx), _ptr(pos_idx),
+                                 _ptr(lse), _ptr(w), w.numel() * w.element_size(), _stream()))
+    else:
+        _check(L.rmm_attn_decode_ex(_ptr(q), _ptr(kt), _ptr(v), _ptr(kn), _ptr(vn), B, Hq, Hkv, D, S, ldk, ldv,
+                                    scale, float(r_dim), float(r_pos), mode, _ptr(out), _ptr(dim_idx),
+                                    _ptr(pos_idx), _ptr(lse), _ptr(w), w.numel() * w.element_size(), _stream()))
     return out, dim_idx, pos_idx, lse
 
 

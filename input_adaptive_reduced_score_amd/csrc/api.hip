@@ -348,10 +348,11 @@ size_t rmm_attn_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_
     return rmm::attn_ws_layout(s, nullptr, nullptr);
 }
 
-rmm_status_t rmm_attn_decode(const void *q, const void *kt, const void *v, const float *kn, int64_t B, int64_t Hq,
-                             int64_t Hkv, int64_t D, int64_t S, int64_t ldk, int64_t ldv, float scale, double r_dim,
-                             double r_pos, rmm_sel_mode_t mode, float *out, int32_t *dim_idx, int32_t *pos_idx,
-                             float *lse, void *ws, size_t ws_bytes, hipStream_t stream)
+rmm_status_t rmm_attn_decode_ex(const void *q, const void *kt, const void *v, const float *kn, const float *vn,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S, int64_t ldk, int64_t ldv,
+                                float scale, double r_dim, double r_pos, rmm_sel_mode_t mode, float *out,
+                                int32_t *dim_idx, int32_t *pos_idx, float *lse, void *ws, size_t ws_bytes,
+                                hipStream_t stream)
 {
     if (!q || !kt || !v || !kn || !out)
         return fail(RMM_EINVAL, "null required pointer");
@@ -361,15 +362,26 @@ rmm_status_t rmm_attn_decode(const void *q, const void *kt, const void *v, const
         return st;
     if (!aligned16(q) || !aligned16(kt) || !aligned16(v) || ((uintptr_t)out & 3u))
         return fail(RMM_EUNSUPPORTED, "q, kt and v must be 16-byte aligned, out 4-byte aligned");
+    if (vn && !aligned16(vn))
+        return fail(RMM_EUNSUPPORTED, "vn must be 16-byte aligned");
     const size_t need = rmm::attn_ws_layout(s, nullptr, nullptr);
     if (!ws || ws_bytes < need)
         return fail(RMM_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     init_once();
     rmm::AttnWs w;
     rmm::attn_ws_layout(s, &w, (char *)ws);
-    return launch_status(rmm::launch_attn(s, (const uint16_t *)q, (const uint16_t *)kt, (const uint16_t *)v, kn, out,
-                                          dim_idx, pos_idx, lse, w, stream),
+    return launch_status(rmm::launch_attn(s, (const uint16_t *)q, (const uint16_t *)kt, (const uint16_t *)v, kn, vn,
+                                          out, dim_idx, pos_idx, lse, w, stream),
                          "attn_decode");
+}
+
+rmm_status_t rmm_attn_decode(const void *q, const void *kt, const void *v, const float *kn, int64_t B, int64_t Hq,
+                             int64_t Hkv, int64_t D, int64_t S, int64_t ldk, int64_t ldv, float scale, double r_dim,
+                             double r_pos, rmm_sel_mode_t mode, float *out, int32_t *dim_idx, int32_t *pos_idx,
+                             float *lse, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return rmm_attn_decode_ex(q, kt, v, kn, nullptr, B, Hq, Hkv, D, S, ldk, ldv, scale, r_dim, r_pos, mode, out,
+                              dim_idx, pos_idx, lse, ws, ws_bytes, stream);
 }
 
 size_t rmm_attn_decode_dense_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S)

@@ -205,10 +205,13 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, int Sp
 
 // ------------------------------------------------------------------ keys
 // Position key: max over the group's heads of the log-probability
-// scale*a_h[s] - lse_h (double), as fixed point floor((L + 128) * 2^25), clamped.
-__device__ __forceinline__ uint32_t logprob_key(double L)
+// scale*a_h[s] - lse_h (double), plus log ||V_s|| when the score is weighted by
+// the value-row norm, as fixed point floor((L + off) * 2^25), clamped to 32 bits.
+// off = 128 covers L in [-128, 0) (plain probabilities); off = 120 covers
+// [-120, 8) (probability times a norm below e^8).
+__device__ __forceinline__ uint32_t logprob_key(double L, double off)
 {
-    const double t = (L + 128.0) * 33554432.0;
+    const double t = (L + off) * 33554432.0;
     if (!(t > 0.0))
         return 0u;
     if (t >= 4294967295.0)
@@ -219,8 +222,8 @@ __device__ __forceinline__ uint32_t logprob_key(double L)
 template <int GS>
 __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, int nqk, const float *__restrict__ logit,
                                                        const float2 *__restrict__ pstat, double *__restrict__ lse_ws,
-                                                       float *__restrict__ lse_out, uint32_t *__restrict__ keys,
-                                                       uint32_t *__restrict__ hist)
+                                                       float *__restrict__ lse_out, const float *__restrict__ vn,
+                                                       uint32_t *__restrict__ keys, uint32_t *__restrict__ hist)
 {
     __shared__ uint32_t lh[ATTN_HIST_BINS];
     __shared__ float smax[GS][4];
@@ -287,13 +290,23 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, int 
     if (sp < s.S) {
         uint32_t kk[8];
         const double sc = (double)s.scale;
+        // value-row norms of the 8 positions (sp + 8 <= ldv: ldv is a multiple of 8)
+        f32x4_t nv[2] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};
+        const double off = vn ? 120.0 : 128.0;
+        if (vn) {
+            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(vn + ((int64_t)b * s.Hkv + h0 / s.G) * s.ldv + sp);
+            nv[0] = src[0];
+            nv[1] = src[1];
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             double m = sc * (double)a[0][e >> 2][e & 3] - lse[0];
 #pragma unroll
             for (int hh = 1; hh < GS; ++hh)
                 m = fmax(m, sc * (double)a[hh][e >> 2][e & 3] - lse[hh]);
-            kk[e] = logprob_key(m);
+            if (vn)
+                m += log((double)nv[e >> 2][e & 3]);
+            kk[e] = logprob_key(m, off);
             if (sp + e < s.S)
                 atomicAdd(&lh[kk[e] >> 20], 1u);
         }
@@ -721,7 +734,7 @@ size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base)
 
 template <int GS>
 static hipError_t attn_run(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v,
-                           const float *kn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
+                           const float *kn, const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
                            const AttnWs &ws, hipStream_t st)
 {
     const int Sp = (int)((s.S + 7) / 8 * 8);
@@ -733,7 +746,7 @@ static hipError_t attn_run(const AttnShape &s, const uint16_t *q, const uint16_t
     uint2 *info = reinterpret_cast<uint2 *>(align256((char *)(sel + G)));
     attn_qk_kernel<GS><<<dim3(nqk, G), QK_THREADS, 0, st>>>(s, Sp, q, kt, kn, ws.logit, ws.pstat, dim_idx, ws.hist);
     attn_key_kernel<GS><<<dim3((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK, G), 256, 0, st>>>(
-        s, Sp, nqk, ws.logit, ws.pstat, ws.lse, lse, ws.keys, ws.hist);
+        s, Sp, nqk, ws.logit, ws.pstat, ws.lse, lse, vn, ws.keys, ws.hist);
     attn_select_kernel<<<G, 1024, 0, st>>>(s, Sp, P, npv, ws.keys, ws.hist, sel, info);
     attn_pv_kernel<GS><<<dim3(npv, G), 256, 0, st>>>(s, Sp, P, v, ws.logit, ws.lse, ws.keys, sel, info, pos_idx,
                                                      ws.pvpart);
@@ -742,17 +755,17 @@ static hipError_t attn_run(const AttnShape &s, const uint16_t *q, const uint16_t
 }
 
 hipError_t launch_attn(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v, const float *kn,
-                       float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse, const AttnWs &ws, hipStream_t st)
+                       const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse, const AttnWs &ws, hipStream_t st)
 {
     switch (s.GS) {
     case 1:
-        return attn_run<1>(s, q, kt, v, kn, out, dim_idx, pos_idx, lse, ws, st);
+        return attn_run<1>(s, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
     case 2:
-        return attn_run<2>(s, q, kt, v, kn, out, dim_idx, pos_idx, lse, ws, st);
+        return attn_run<2>(s, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
     case 4:
-        return attn_run<4>(s, q, kt, v, kn, out, dim_idx, pos_idx, lse, ws, st);
+        return attn_run<4>(s, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
     case 8:
-        return attn_run<8>(s, q, kt, v, kn, out, dim_idx, pos_idx, lse, ws, st);
+        return attn_run<8>(s, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
     default:
         return hipErrorInvalidValue;
     }

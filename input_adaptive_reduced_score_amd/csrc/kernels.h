@@ -79,7 +79,7 @@ struct AttnWs {
 };
 size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base);
 hipError_t launch_attn(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v, const float *kn,
-                       float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse, const AttnWs &ws, hipStream_t st);
+                       const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse, const AttnWs &ws, hipStream_t st);
 size_t attn_dense_ws_layout(int64_t B, int64_t Hq, int64_t S, char *base, float **part, float2 **stat,
                             uint32_t **cnt);
 hipError_t launch_attn_dense(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v, float *out,

@@ -78,6 +78,15 @@ def test_linear_and_attn_argument_errors_host_only():
     bad[12] = 0.0    # r_dim
     assert L.rmm_attn_decode(*bad) == 1
     assert L.rmm_attn_decode(*args) == 3  # no workspace
+    # the value-norm variant: vn inserted after kn, NULL allowed, 16-byte alignment checked
+    ex = args[:4] + [None] + args[4:]
+    assert L.rmm_attn_decode_ex(*ex) == 3
+    ex[4] = p
+    assert L.rmm_attn_decode_ex(*ex) == 3
+    ex[4] = C.c_void_p(260)
+    assert L.rmm_attn_decode_ex(*ex) == 2
+    ex[4], ex[0] = p, None
+    assert L.rmm_attn_decode_ex(*ex) == 1
     assert L.rmm_attn_decode_workspace_size(1, 32, 8, 128, 32768, 0.25, 0.25, 0) > 0
     assert L.rmm_status_string(3).startswith(b"RMM_EWORKSPACE")
 

@@ -31,17 +31,18 @@ def padded_keys(kt):
     return out
 
 
-def run_attn(cs, r_dim, r_pos, mode=0, kt=None, v=None, S=None):
+def run_attn(cs, r_dim, r_pos, mode=0, kt=None, v=None, S=None, vn=None):
     kt = cs.kt if kt is None else kt
     v = cs.v if v is None else v
     if S is None:
         S = cs.S
     kt = padded_keys(kt)
-    print(f"[case] {cs.name} r_dim={r_dim} r_pos={r_pos} mode={mode}", flush=True)
+    print(f"[case] {cs.name} r_dim={r_dim} r_pos={r_pos} mode={mode} vn={vn is not None}", flush=True)
     out, dim_idx, pos_idx, lse = rmm.attn_decode(dev(cs.q), dev(kt), dev(v), dev(cs.kn), r_dim, r_pos,
-                                                 scale=cs.scale, mode=mode, S=S)
+                                                 scale=cs.scale, mode=mode, S=S,
+                                                 vn=None if vn is None else dev(vn))
     torch.cuda.synchronize()
-    ref = oracle.attn_decode(cs.q, kt, v, cs.kn, cs.scale, r_dim, r_pos, mode, S=S, want=("pi",))
+    ref = oracle.attn_decode(cs.q, kt, v, cs.kn, cs.scale, r_dim, r_pos, mode, S=S, want=("pi",), vn=vn)
     assert np.array_equal(dim_idx.cpu().numpy(), ref["dim_idx"]), "head_dim selections differ"
     B, Hsel = ref["pos_idx"].shape[:2]
     gi = pos_idx.cpu().numpy().reshape(B * Hsel, -1)
@@ -125,3 +126,49 @@ def test_deterministic_repeat():
     torch.cuda.synchronize()
     for u, w in zip(a, b):
         assert torch.equal(u, w)
+
+
+# ---- position score weighted by the value-row norm (p * ||V_s||)
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("r_dim,r_pos", [(0.5, 0.5), (0.25, 0.1), (1.0, 1.0), (1 / 128, 1e-3)])
+def test_value_norm_small_gqa(mode, r_dim, r_pos):
+    cs = W.attn_case(2, 1000, Hq=8, Hkv=2, seed=11, n_hot=8)
+    run_attn(cs, r_dim, r_pos, mode, vn=W.value_row_norms(cs.v))
+
+
+def test_value_norm_changes_the_selection():
+    # norms spread over four decades: the weighted set must follow the oracle's
+    # weighted scores, and differ from the probability-only set
+    cs = W.attn_case(1, 4000, Hq=8, Hkv=2, seed=12, n_hot=4)
+    rng = np.random.default_rng(12)
+    vn = (W.value_row_norms(cs.v) * 10.0 ** rng.uniform(-2, 2, size=(1, 2, 4000))).astype(np.float32)
+    run_attn(cs, 0.5, 0.25, 0, vn=vn)
+    _, _, plain, _ = rmm.attn_decode(dev(cs.q), dev(cs.kt), dev(cs.v), dev(cs.kn), 0.5, 0.25, scale=cs.scale)
+    _, _, weighted, _ = rmm.attn_decode(dev(cs.q), dev(cs.kt), dev(cs.v), dev(cs.kn), 0.5, 0.25, scale=cs.scale,
+                                        vn=dev(vn))
+    torch.cuda.synchronize()
+    assert not torch.equal(plain, weighted)
+
+
+def test_value_norm_ones_is_probability_score():
+    cs = W.attn_case(1, 3000, Hq=8, Hkv=2, seed=13, n_hot=4)
+    ndiff, _ = run_attn(cs, 0.5, 0.3, 1, vn=np.ones((1, 2, 3000), np.float32))
+    assert ndiff == 0
+
+
+@pytest.mark.parametrize("S", [7, 513, 9999])
+def test_value_norm_ragged_spare_capacity(S):
+    # ldv > S; the norms beyond S hold NaN and must not influence anything
+    cs = W.attn_case(1, S, Hq=4, Hkv=1, seed=S + 1, n_hot=min(4, S))
+    ldv = -(-S // 8) * 8 + 8
+    v = np.zeros((1, 1, ldv, 128), np.uint16)
+    v[:, :, :S] = cs.v
+    vn = np.full((1, 1, ldv), np.nan, np.float32)
+    vn[..., :S] = W.value_row_norms(cs.v)
+    run_attn(cs, 0.5, 0.3, 0, v=v, S=S, vn=vn)
+
+
+def test_value_norm_32k_full_size():
+    cs = W.attn_32k()
+    run_attn(cs, 0.25, 0.25, 0, vn=W.value_row_norms(cs.v))
