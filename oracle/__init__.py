@@ -63,6 +63,8 @@ def lib():
         L.ora_attn_decode.restype = i32
         L.ora_attn_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, C.c_float,
                                       dbl, dbl, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.ora_gate_up.restype = i32
+        L.ora_gate_up.argtypes = [vp, i64, i64, i64, vp, vp, i64, i64, i64, vp, i64, vp, vp]
         L.ora_dense_attn.restype = i32
         L.ora_dense_attn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, C.c_float, vp]
         _lib = L
@@ -160,6 +162,26 @@ def dense_linear(x, wt, rows=None, want_double=False):
     _check(lib().ora_dense_linear(_p(x), _dt(x), T, K, K, _p(wt), _dt(wt), M, M, t0, t1, _p(y), M, _p(yd)),
            "dense_linear")
     return (y, yd) if want_double else y
+
+
+def gate_up(x, wg, wu, tile=1):
+    """Gated FFN producer (blog section 6.1 demo code, ffn_full; sections 5.1, 6.2).
+    x [T,H] uint16 (bf16); wg, wu [H,Mi] uint16 (W_gate^T, W_up^T, K-major).
+    Returns (h [T,Mi] uint16 bf16, pmax [ceil(T/tile),Mi] float32, hd [T,Mi] float64):
+    h = bf16(silu(g)*u) with g, u summed in double, pmax = tile maxima of |h|,
+    hd = silu(g)*u before the rounding."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    wg = np.ascontiguousarray(wg, dtype=np.uint16)
+    wu = np.ascontiguousarray(wu, dtype=np.uint16)
+    T, H = x.shape
+    if wg.shape != wu.shape or wg.shape[0] != H:
+        raise ValueError("wg and wu must both be [H, Mi]")
+    Mi = wg.shape[1]
+    h = np.zeros((T, Mi), dtype=np.uint16)
+    pmax = np.zeros((-(-T // tile), Mi), dtype=np.float32)
+    hd = np.zeros((T, Mi), dtype=np.float64)
+    _check(lib().ora_gate_up(_p(x), T, H, H, _p(wg), _p(wu), Mi, Mi, tile, _p(h), Mi, _p(pmax), _p(hd)), "gate_up")
+    return h, pmax, hd
 
 
 def attn_decode(q, kt, v, kn, scale, r_dim, r_pos, mode=0, S=None, want=("out",), vn=None):

@@ -261,6 +261,78 @@ int ora_dense_linear(const void *x, int xt, int64_t T, int64_t K, int64_t ldx,
     return 0;
 }
 
+/* ---------------------------------------------------------------- FFN producer
+ * The gated FFN of the blog's section 6.1 demo code (ffn_full): gate = x W_gate^T,
+ * up = x W_up^T, h = silu(gate) * up, which is the down projection's input; the
+ * blog's section 5.1 scores the down projection's slices from this activation,
+ * and section 6.2 notes that gate and up are computed in full.
+ * Double rounded once to bfloat16, to nearest with ties to even, without an
+ * intermediate float: the quantum of the result is 2^(e-7) for |d| in
+ * [2^e, 2^(e+1)), e >= -126, and 2^-133 below (bfloat16 subnormals). */
+static uint16_t bf16_from_double(double d)
+{
+    if (d != d)
+        return 0x7fc0;
+    double a = fabs(d);
+    double q = a >= ldexp(1.0, -126) ? ldexp(1.0, ilogb(a) - 7) : ldexp(1.0, -133);
+    double r = a == 0.0 ? 0.0 : nearbyint(a / q) * q; /* default rounding mode: ties to even */
+    uint32_t u;
+    if (r >= ldexp(1.0, 128)) {
+        u = 0x7f800000u;
+    } else {
+        float f = (float)r; /* exact: at most 8 significant bits */
+        memcpy(&u, &f, sizeof u);
+    }
+    return (uint16_t)((u >> 16) | (signbit(d) ? 0x8000u : 0u));
+}
+
+int ora_gate_up(const uint16_t *x, int64_t T, int64_t H, int64_t ldx,
+                const uint16_t *wg, const uint16_t *wu, int64_t ldw, int64_t Mi, int64_t tile,
+                uint16_t *h, int64_t ldh, float *pmax, double *hd)
+{
+    if (T < 1 || H < 1 || Mi < 1 || tile < 1 || ldx < H || ldw < Mi || ldh < Mi)
+        return 1;
+    const int64_t ntiles = (T + tile - 1) / tile;
+    double *g = (double *)malloc((size_t)Mi * sizeof *g), *u = (double *)malloc((size_t)Mi * sizeof *u);
+    if (!g || !u) {
+        free(g);
+        free(u);
+        return 2;
+    }
+    if (pmax)
+        for (int64_t i = 0; i < ntiles * Mi; ++i)
+            pmax[i] = 0.0f;
+    for (int64_t t = 0; t < T; ++t) {
+        /* every g[m], u[m] is summed in ascending j */
+        for (int64_t m = 0; m < Mi; ++m)
+            g[m] = u[m] = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            double xv = (double)bf16_value(x[t * ldx + j]);
+            for (int64_t m = 0; m < Mi; ++m) {
+                g[m] += xv * (double)bf16_value(wg[j * ldw + m]);
+                u[m] += xv * (double)bf16_value(wu[j * ldw + m]);
+            }
+        }
+        for (int64_t m = 0; m < Mi; ++m) {
+            double v = g[m] / (1.0 + exp(-g[m])) * u[m];
+            uint16_t b = bf16_from_double(v);
+            if (h)
+                h[t * ldh + m] = b;
+            if (hd)
+                hd[t * ldh + m] = v;
+            if (pmax) {
+                float mag = fabsf(bf16_value(b));
+                float *pm = pmax + (t / tile) * Mi + m;
+                if (mag > *pm)
+                    *pm = mag;
+            }
+        }
+    }
+    free(g);
+    free(u);
+    return 0;
+}
+
 /* ---------------------------------------------------------------- attention
  * Reduced decode attention for one batch element and one selection group:
  *  1. head_dim slices (the contraction of Q K^T) scored by

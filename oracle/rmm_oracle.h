@@ -75,6 +75,21 @@ int ora_dense_linear(const void *x, int xt, int64_t T, int64_t K, int64_t ldx,
                      const void *wt, int wtt, int64_t M, int64_t ldw, int64_t t0, int64_t t1,
                      float *y, int64_t ldy, double *yd);
 
+/* gated FFN producer (blog section 6.1 demo code; 5.1; 6.2): for every token t
+ * and intermediate column m < Mi
+ *   g = sum_j x[t,j] * wg[j,m],  u = sum_j x[t,j] * wu[j,m]   (double, ascending j)
+ *   h[t,m] = bf16( silu(g) * u ),  silu(g) = g / (1 + e^-g)    (double, one rounding)
+ *   pmax[tau][m] = max_{t in tile tau} |h[t,m]|               (the scorer's column max)
+ * x [T][ldx] bf16; wg, wu [H][ldw] bf16 (W_gate^T and W_up^T, row j = what x_j
+ * multiplies); h [T][ldh] bf16; pmax [ceil(T/tile)][Mi] float; hd [T][ldh]
+ * double (h before rounding).  Any output may be NULL.
+ * Pinned: float64 library products and the logistic function of scipy with the
+ * nearest-bfloat16 check, a hand example with silu(+-64), rounding ties and
+ * subnormals, tile maxima. */
+int ora_gate_up(const uint16_t *x, int64_t T, int64_t H, int64_t ldx,
+                const uint16_t *wg, const uint16_t *wu, int64_t ldw, int64_t Mi, int64_t tile,
+                uint16_t *h, int64_t ldh, float *pmax, double *hd);
+
 /* reduced GQA attention decode (all bf16 inputs, fp32 kn).
  *  q  [B][Hq][D], kt [B][Hkv][D][ldk] (dim-major keys), v [B][Hkv][ldv][D], kn [B][Hkv][D].
  *  mode 0: one selection per KV head (its G = Hq/Hkv query heads share it);

@@ -432,3 +432,70 @@ def test_attn_vn_strided_equals_packed():
     b = oracle.attn_decode(cs.q, ktp, vp, cs.kn, cs.scale, 0.5, 0.25, 0, S=40, vn=vnp)
     for key in ("out", "dim_idx", "pos_idx", "lse"):
         assert np.array_equal(a[key], b[key])
+
+
+# --------------------------------------------------------------------------- gated FFN producer
+# Blog section 6.1 demo code (ffn_full): gate = x W_gate^T, up = x W_up^T,
+# h = silu(gate) * up; section 5.1 scores the down projection from h.
+
+def _bf16_bits(vals):
+    """float values that are exactly bfloat16 -> uint16 bit patterns."""
+    u = np.asarray(vals, dtype=np.float32).view(np.uint32)
+    assert np.all(u & 0xFFFF == 0), "value not representable in bfloat16"
+    return (u >> 16).astype(np.uint16)
+
+
+def test_gate_up_hand_example():
+    # g = 64 x_t, u = x_t * wu: silu(64) is 64 in double (1 + e^-64 rounds to 1) and
+    # silu(128) is 128, so tokens with x > 0 give h = g*u exactly; x = -1 gives the
+    # negative branch, -64 / (1 + e^64) = -1.03e-26, times u
+    x = _bf16_bits([[1.0], [-1.0], [1.0], [2.0]])
+    wg = _bf16_bits([[64.0, 64.0, 64.0]])
+    wu = _bf16_bits([[0.5, -2.0, 3.0]])
+    h, pmax, hd = oracle.gate_up(x, wg, wu, tile=2)
+    hv = W.bf16_bits_to_f32(h)
+    assert np.array_equal(hv[0], [32.0, -128.0, 192.0])
+    assert np.array_equal(hv[2], [32.0, -128.0, 192.0])
+    assert np.array_equal(hv[3], [128.0, -512.0, 768.0])
+    neg = 64.0 * math.exp(-64.0) * np.array([0.5, -2.0, 3.0])  # -silu(-64) ~ 64 e^-64 to 1e-27 relative
+    assert np.all(np.sign(hv[1]) == np.sign(neg))
+    assert np.allclose(hv[1], neg, rtol=2 ** -8, atol=0)
+    assert np.allclose(hd[1], neg, rtol=1e-12, atol=0)
+    assert np.array_equal(pmax, [[32.0, 128.0, 192.0], [128.0, 512.0, 768.0]])
+
+
+def test_gate_up_rounding_ties_and_subnormals():
+    # g = 64 for both tokens, so h = 64 u exactly in double.  Token 0 lands on the
+    # bfloat16 ties 1 + 2^-8 (-> 1, even) and 1 + 3*2^-8 (-> 1 + 2^-6, even); token 1
+    # lands on 8.5 and 9.5 subnormal quanta 2^-133 (-> 8 and 10 quanta).
+    e = math.ldexp
+    x = _bf16_bits([[1.0, 1.0, 0.0, 0.0], [0.0, 0.0, e(1, -8), e(1, -8)]])
+    wg = _bf16_bits([[64.0, 64.0], [0.0, 0.0], [e(1, 14), e(1, 14)], [0.0, 0.0]])
+    wu = _bf16_bits([[e(1, -6), e(1, -6)], [e(1, -14), 3 * e(1, -14)], [e(1, -128), e(1, -128)],
+                     [e(1, -132), 3 * e(1, -132)]])
+    h, _, hd = oracle.gate_up(x, wg, wu)
+    assert hd[0, 0] == 1 + e(1, -8) and hd[0, 1] == 1 + 3 * e(1, -8)
+    assert hd[1, 0] == 8.5 * e(1, -133) and hd[1, 1] == 9.5 * e(1, -133)
+    assert [int(v) for v in h[0]] == [0x3F80, 0x3F82]
+    assert [int(v) for v in h[1]] == [0x0008, 0x000A]
+
+
+def test_gate_up_equals_library_products():
+    # float64 library matmul of the exact bf16 values and scipy's logistic function;
+    # the oracle's h must be the bfloat16 nearest to silu(g) * u
+    from scipy.special import expit
+    T, H, Mi = 3, 64, 40
+    x = W.normal_bf16(5, W.S_X, T * H).reshape(T, H)
+    wg = W.normal_bf16(5, W.S_WG, H * Mi, 0.2).reshape(H, Mi)
+    wu = W.normal_bf16(5, W.S_WU, H * Mi, 0.2).reshape(H, Mi)
+    h, pmax, hd = oracle.gate_up(x, wg, wu, tile=2)
+    f = lambda a: W.bf16_bits_to_f32(a).astype(np.float64)
+    g, u = f(x) @ f(wg), f(x) @ f(wu)
+    want = g * expit(g) * u
+    assert np.allclose(hd, want, rtol=1e-12, atol=1e-300)
+    hv = f(h)
+    # nearest: no other bfloat16 is closer than the chosen one (one ulp above and below)
+    mag = np.abs(want)  # the spacing at the exact value: below a power of two it is the finer one
+    ulp = np.ldexp(1.0, np.maximum(np.floor(np.log2(np.where(mag > 0, mag, 1.0))).astype(int) - 7, -133))
+    assert np.all(np.abs(hv - want) <= 0.5 * ulp * (1 + 1e-9))
+    assert np.array_equal(pmax[0], np.abs(hv[:2]).max(axis=0)) and np.array_equal(pmax[1], np.abs(hv[2]))

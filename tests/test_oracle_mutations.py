@@ -14,6 +14,18 @@ import test_oracle as P
 SRC = open(oracle.SRC).read()
 
 MUTATIONS = {
+    "silu replaced by the logistic function": (
+        "double v = g[m] / (1.0 + exp(-g[m])) * u[m];", "double v = 1.0 / (1.0 + exp(-g[m])) * u[m];",
+        [P.test_gate_up_hand_example]),
+    "gate and up swapped in the producer": (
+        "double v = g[m] / (1.0 + exp(-g[m])) * u[m];", "double v = u[m] / (1.0 + exp(-u[m])) * g[m];",
+        [P.test_gate_up_equals_library_products]),
+    "bfloat16 rounding truncates": (
+        "nearbyint(a / q) * q;", "floor(a / q) * q;",
+        [P.test_gate_up_rounding_ties_and_subnormals]),
+    "producer tile maxima over the whole batch": (
+        "float *pm = pmax + (t / tile) * Mi + m;", "float *pm = pmax + 0 * (t / tile) * Mi + m;",
+        [P.test_gate_up_hand_example]),
     "scorer sums instead of max": (
         "                if (v > a)\n                    a = v;\n",
         "                a += v;\n",
