@@ -311,6 +311,80 @@ def main():
             f"(select_blocks {t_bsel * 1e6:.2f} us), slice step {t_s * 1e6:.2f} us, dense GEMV {t_d * 1e6:.2f} us")
         del xbs, wbs, cbs
 
+    # ------------------------------------------------------------------ decode layer: QKV, o_proj, gated FFN
+    if not args.no_sweep and not args.headline_only:
+        log("[bench] decode layer: generating inputs")
+        Hh, Mi, Dq = 4096, 14336, 6144   # hidden, FFN intermediate, q+k+v outputs (32 q heads, 8 kv heads, D 128)
+        fc = W.ffn_case(1, Hh, Mi, 1, seed=5)
+        qc = W.linear_random(1, Hh, Dq, 1, "bf16", seed=6, xsigma=1.0, wsigma=0.02)
+        oc = W.linear_random(1, Hh, Hh, 1, "bf16", seed=7, xsigma=1.0, wsigma=0.02)
+        layer_bytes = 2 * (Hh * Dq + Hh * Hh + 3 * Hh * Mi)
+        nl = n_copies(layer_bytes, layer_bytes // 2)
+        L = []
+        for i in range(nl):
+            L.append({"xq": bf(qc.x), "wq": bf(qc.wt), "cq": torch.from_numpy(qc.c).to(dev),
+                      "xo": bf(oc.x), "wo": bf(oc.wt), "co": torch.from_numpy(oc.c).to(dev),
+                      "xf": bf(fc.x), "wg": bf(fc.wg), "wu": bf(fc.wu), "wd": bf(fc.wd),
+                      "cd": torch.from_numpy(fc.c).to(dev)})
+        yq = torch.empty((1, Dq), dtype=torch.float32, device=dev)
+        yo = torch.empty((1, Hh), dtype=torch.float32, device=dev)
+        yd = torch.empty((1, Hh), dtype=torch.float32, device=dev)
+        hb = [torch.empty((1, Mi), dtype=torch.bfloat16, device=dev) for _ in range(nl)]
+        pm = [torch.empty((1, Mi), dtype=torch.float32, device=dev) for _ in range(nl)]
+        r = 0.5
+        iq = [rmm.select(l["xq"], l["cq"], 1, r) for l in L]
+        io = [rmm.select(l["xo"], l["co"], 1, r) for l in L]
+        idd = [torch.empty((1, rmm.keep_count(Mi, r)), dtype=torch.int32, device=dev) for _ in range(nl)]
+
+        def gu(i):
+            j = i % nl
+            rmm.gate_up(L[j]["xf"], L[j]["wg"], L[j]["wu"], 1, h=hb[j], pmax=pm[j])
+
+        def ffn_red(i):
+            j = i % nl
+            gu(i)
+            rmm.select(pm[j], L[j]["cd"], 1, r, idx=idd[j])
+            rmm.linear(hb[j], L[j]["wd"], idd[j], 1, out=yd)
+
+        def ffn_dense(i):
+            j = i % nl
+            gu(i)
+            rmm.linear_dense(hb[j], L[j]["wd"], out=yd)
+
+        def attn_proj_red(i):
+            j = i % nl
+            rmm.select(L[j]["xq"], L[j]["cq"], 1, r, idx=iq[j])      # one selection shared by Wq, Wk, Wv
+            rmm.linear(L[j]["xq"], L[j]["wq"], iq[j], 1, out=yq)
+            rmm.select(L[j]["xo"], L[j]["co"], 1, r, idx=io[j])
+            rmm.linear(L[j]["xo"], L[j]["wo"], io[j], 1, out=yo)
+
+        def attn_proj_dense(i):
+            j = i % nl
+            rmm.linear_dense(L[j]["xq"], L[j]["wq"], out=yq)
+            rmm.linear_dense(L[j]["xo"], L[j]["wo"], out=yo)
+
+        t_gu = event_avg(gu, steps, torch)
+        t_fr = time_loop(ffn_red, steps, warmup, torch)
+        t_fd = time_loop(ffn_dense, steps, warmup, torch)
+        t_ar = time_loop(attn_proj_red, steps, warmup, torch)
+        t_ad = time_loop(attn_proj_dense, steps, warmup, torch)
+        t_lr = time_loop(lambda i: (attn_proj_red(i), ffn_red(i)), steps, warmup, torch)
+        t_ld = time_loop(lambda i: (attn_proj_dense(i), ffn_dense(i)), steps, warmup, torch)
+        gbytes = A.gateup_bytes(1, Hh, Mi)
+        rec = {"workload": "decode_layer_linears", "r": r, "H": Hh, "Mi": Mi, "qkv_out": Dq,
+               "gate_up_us": t_gu * 1e6, "gate_up_GBps": gbytes / t_gu / 1e9,
+               "ffn_reduced_us": t_fr * 1e6, "ffn_dense_us": t_fd * 1e6,
+               "qkv_o_reduced_us": t_ar * 1e6, "qkv_o_dense_us": t_ad * 1e6,
+               "layer_reduced_us": t_lr * 1e6, "layer_dense_us": t_ld * 1e6,
+               "layer_weight_bytes_dense": layer_bytes,
+               "layer_weight_bytes_reduced": 2 * (rmm.keep_count(Hh, r) * (Dq + Hh) + 2 * Hh * Mi
+                                                  + rmm.keep_count(Mi, r) * Hh)}
+        sweep.append(rec)
+        log(f"[bench] decode layer r={r}: gate/up producer {t_gu * 1e6:.1f} us ({gbytes / t_gu / 1e9:.0f} GB/s); "
+            f"FFN reduced {t_fr * 1e6:.1f} vs dense {t_fd * 1e6:.1f} us; QKV+o reduced {t_ar * 1e6:.1f} vs dense "
+            f"{t_ad * 1e6:.1f} us; layer linears reduced {t_lr * 1e6:.1f} vs dense {t_ld * 1e6:.1f} us")
+        del L, hb, pm
+
     # ------------------------------------------------------------------ prefill (MFMA)
     if not args.no_sweep and not args.headline_only:
         log("[bench] prefill: generating inputs")

@@ -136,6 +136,29 @@ rmm_status_t rmm_linear_dense(const void *x, rmm_dtype_t xt, int64_t T, int64_t 
                               const void *wt, rmm_dtype_t wt_t, int64_t M, int64_t ldw,
                               float *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ gated FFN producer
+ * The FFN's intermediate activation, the down projection's input (blog section
+ * 6.1, the demo's ffn_full: gate = x W_gate^T, up = x W_up^T, h = silu(gate) *
+ * up; section 5.1 scores the down projection from h; section 6.2: gate and up
+ * stay full).  For every token t and column m < Mi:
+ *     g = sum_j x[t,j] * wg[j,m],  u = sum_j x[t,j] * wu[j,m]     (fp32 accumulation)
+ *     h[t,m] = bf16( silu(g) * u ),  silu(g) = g / (1 + e^-g)     (fp32, nearest-even)
+ *     pmax[tau][m] = max_{t in tile tau} |h[t,m]|                 (optional)
+ * pmax is exactly what rmm_select would take as the tile's column maxima, so
+ * rmm_select(pmax, RMM_F32, ceil(T/tile), Mi, Mi, c, 1, r, ...) keeps the same
+ * slices as rmm_select(h, RMM_BF16, T, Mi, ldh, c, tile, r, ...).
+ *   x    bf16 [T][ldx], ldx >= H
+ *   wg   bf16 [H][ldw]  W_gate^T, K-major (row j = the weights x[t,j] multiplies)
+ *   wu   bf16 [H][ldw]  W_up^T, same layout and pitch
+ *   h    out, bf16 [T][ldh], ldh >= Mi, 2-byte aligned
+ *   pmax optional out (NULL ok), fp32 [ceil(T/tile)][Mi]
+ * Deterministic (fixed-order split reduction). */
+size_t rmm_gate_up_workspace_size(int64_t T, int64_t H, int64_t Mi, int64_t tile);
+rmm_status_t rmm_gate_up(const void *x, int64_t T, int64_t H, int64_t ldx,
+                         const void *wg, const void *wu, int64_t ldw, int64_t Mi, int64_t tile,
+                         void *h, int64_t ldh, float *pmax, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 /* ------------------------------------------------------------------ attention decode
  * Reduced grouped-query attention for one decode step (blog sections 3.1 and
  * 3.3; GEMM notes section 1: scores = Q K^T, out = softmax(scores) V).

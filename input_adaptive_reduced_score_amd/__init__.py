@@ -21,7 +21,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "librmm.so")
-SOURCES = ["select.hip", "linear.hip", "attn.hip", "api.hip"]
+SOURCES = ["select.hip", "linear.hip", "ffn.hip", "attn.hip", "api.hip"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
@@ -99,6 +99,8 @@ def lib():
                                           vp, vp, vp, vp, vp, sz, vp]),
                 "rmm_attn_decode_ex": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, flt, dbl, dbl,
                                              i32, vp, vp, vp, vp, vp, sz, vp]),
+                "rmm_gate_up_workspace_size": (sz, [i64, i64, i64, i64]),
+                "rmm_gate_up": (i32, [vp, i64, i64, i64, vp, vp, i64, i64, i64, vp, i64, vp, vp, sz, vp]),
                 "rmm_attn_decode_dense_workspace_size": (sz, [i64, i64, i64, i64, i64]),
                 "rmm_attn_decode_dense": (i32, [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, flt, vp, vp, vp, sz,
                                                 vp]),
@@ -116,6 +118,7 @@ def lib():
 EXPORTS = ("rmm_keep_count", "rmm_select_workspace_size", "rmm_select", "rmm_block_keep_count",
            "rmm_select_blocks_workspace_size", "rmm_select_blocks", "rmm_linear_workspace_size", "rmm_linear",
            "rmm_linear_dense_workspace_size", "rmm_linear_dense", "rmm_attn_decode_workspace_size",
+           "rmm_gate_up_workspace_size", "rmm_gate_up",
            "rmm_attn_decode", "rmm_attn_decode_ex", "rmm_attn_decode_dense_workspace_size", "rmm_attn_decode_dense", "rmm_status_string",
            "rmm_last_error")
 
@@ -247,6 +250,30 @@ def linear_dense(x: torch.Tensor, wt: torch.Tensor, out: torch.Tensor | None = N
     _check(L.rmm_linear_dense(_ptr(x), _dtype(x), T, K, _ld(x), _ptr(wt), _dtype(wt), M, _ld(wt), _ptr(out),
                               _ld(out), _ptr(w), w.numel() * w.element_size(), _stream()))
     return out
+
+
+def gate_up(x, wg, wu, tile: int = 1, h=None, pmax=None, want_pmax: bool = True, ws=None):
+    """Gated FFN producer: h = bf16(silu(x W_gate^T) * (x W_up^T)) and the tile maxima of |h|.
+    x [T,H] bf16; wg, wu [H,Mi] bf16 (W_gate^T, W_up^T, K-major, same pitch).
+    Returns (h [T,Mi] bf16, pmax [ceil(T/tile),Mi] fp32 or None)."""
+    L = lib()
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16 or wg.dtype != torch.bfloat16 or wu.dtype != torch.bfloat16:
+        raise ValueError("x, wg and wu must be bfloat16")
+    T, H = x.shape
+    Mi = wg.shape[1]
+    if wg.shape[0] != H or tuple(wu.shape) != tuple(wg.shape) or _ld(wg) != _ld(wu):
+        raise ValueError("wg and wu must both be [H, Mi] with the same row pitch")
+    dev = x.device
+    if h is None:
+        h = torch.empty((T, Mi), dtype=torch.bfloat16, device=dev)
+    if pmax is None and want_pmax:
+        pmax = torch.empty((-(-T // tile), Mi), dtype=torch.float32, device=dev)
+    need = L.rmm_gate_up_workspace_size(T, H, Mi, tile)
+    w = ws if ws is not None else _WS.get(need, dev)
+    _check(L.rmm_gate_up(_ptr(x), T, H, _ld(x), _ptr(wg), _ptr(wu), _ld(wg), Mi, tile, _ptr(h), _ld(h), _ptr(pmax),
+                         _ptr(w), w.numel() * w.element_size(), _stream()))
+    return h, pmax
 
 
 def attn_decode(q, kt, v, kn, r_dim: float, r_pos: float, scale: float | None = None, mode: int = PER_KV_GROUP,

@@ -46,3 +46,10 @@ def attn_step_bytes(B: int, Hq: int, Hkv: int, D: int, S: int, kd: int, ks: int,
 
 def attn_dense_bytes(B: int, Hq: int, Hkv: int, D: int, S: int) -> int:
     return B * Hkv * S * D * 2 * 2 + B * Hq * D * (2 + 4)
+
+
+def gateup_bytes(T: int, H: int, Mi: int, tile: int = 1) -> int:
+    """Gated FFN producer: W_gate^T and W_up^T read once (bf16), x read, h written
+    (bf16) and the tile maxima written (fp32)."""
+    ntiles = -(-T // tile)
+    return 2 * 2 * H * Mi + 2 * T * H + 2 * T * Mi + 4 * ntiles * Mi

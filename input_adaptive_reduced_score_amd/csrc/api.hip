@@ -294,6 +294,45 @@ rmm_status_t rmm_linear_dense(const void *x, rmm_dtype_t xt, int64_t T, int64_t 
     return linear_common(x, xt, T, K, ldx, wt, M, ldw, nullptr, K, T, true, y, ldy, ws, ws_bytes, stream);
 }
 
+// ------------------------------------------------------------------ gated FFN producer
+size_t rmm_gate_up_workspace_size(int64_t T, int64_t H, int64_t Mi, int64_t tile)
+{
+    if (T < 1 || H < 1 || Mi < 1 || tile < 1 || T > INT32_MAX || H > INT32_MAX || Mi > INT32_MAX)
+        return 0;
+    return RMM_WS_HEADER_BYTES + round256(rmm::gateup_ws_bytes(T, H, Mi, tile < T ? tile : T));
+}
+
+rmm_status_t rmm_gate_up(const void *x, int64_t T, int64_t H, int64_t ldx, const void *wg, const void *wu,
+                         int64_t ldw, int64_t Mi, int64_t tile, void *h, int64_t ldh, float *pmax, void *ws,
+                         size_t ws_bytes, hipStream_t stream)
+{
+    if (!x || !wg || !wu || !h)
+        return fail(RMM_EINVAL, "null pointer (x=%p wg=%p wu=%p h=%p)", x, wg, wu, h);
+    if (T < 1 || H < 1 || Mi < 1 || tile < 1)
+        return fail(RMM_EINVAL, "sizes must be positive (T=%lld H=%lld Mi=%lld tile=%lld)", (long long)T,
+                    (long long)H, (long long)Mi, (long long)tile);
+    if (ldx < H || ldw < Mi || ldh < Mi)
+        return fail(RMM_EINVAL, "leading dimension too small (ldx=%lld H=%lld, ldw=%lld ldh=%lld Mi=%lld)",
+                    (long long)ldx, (long long)H, (long long)ldw, (long long)ldh, (long long)Mi);
+    if (T > INT32_MAX || H > INT32_MAX || Mi > INT32_MAX)
+        return fail(RMM_EUNSUPPORTED, "sizes beyond 2^31");
+    if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || ldx % 8 || ldw % 8 || ((uintptr_t)h & 1u) ||
+        ((uintptr_t)pmax & 3u))
+        return fail(RMM_EUNSUPPORTED, "x, wg and wu must be 16-byte aligned with ldx/ldw multiples of 8 elements, "
+                                      "h 2-byte and pmax 4-byte aligned");
+    const int64_t tl = tile < T ? tile : T;
+    const size_t need = rmm_gate_up_workspace_size(T, H, Mi, tile);
+    if (!ws || ws_bytes < need)
+        return fail(RMM_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    if (rmm::gateup_grid(T, H, Mi, tl) > (int64_t)INT32_MAX)
+        return fail(RMM_EUNSUPPORTED, "too many workgroups");
+    init_once();
+    float *part = (float *)((char *)ws + RMM_WS_HEADER_BYTES);
+    return launch_status(rmm::launch_gateup((const uint16_t *)x, T, H, ldx, (const uint16_t *)wg,
+                                            (const uint16_t *)wu, ldw, Mi, tl, (uint16_t *)h, ldh, pmax, part, stream),
+                         "gate_up");
+}
+
 // ------------------------------------------------------------------ attention
 static rmm_status_t attn_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S, int64_t ldk, int64_t ldv,
                                float scale, double r_dim, double r_pos, int mode, rmm::AttnShape *s)

@@ -25,6 +25,16 @@
 #endif
 #define GEMV_MAX_SPLIT 64
 #define MFMA_MIN_TILE_ROWS 32 // bf16 tiles with at least this many tokens use the MFMA GEMM
+#ifndef GATEUP_UNROLL
+#define GATEUP_UNROLL 8 // rows of each of W_gate^T and W_up^T in flight per wave
+#endif
+#ifndef GATEUP_TARGET_WGS
+#define GATEUP_TARGET_WGS 512
+#endif
+#ifndef GATEUP_MIN_ROWS
+#define GATEUP_MIN_ROWS 8
+#endif
+#define GATEUP_MAX_SPLIT 64
 
 #define ATTN_D 128
 #define ATTN_QK_CHUNK 512   // positions per QK workgroup
@@ -57,6 +67,13 @@ hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const v
                        const int32_t *idx, int64_t k, int64_t tile, bool dense, float *y, int64_t ldy, void *xg,
                        hipStream_t st);
 void linear_init();
+
+// ffn.hip
+size_t gateup_ws_bytes(int64_t T, int64_t H, int64_t Mi, int64_t tile);
+int64_t gateup_grid(int64_t T, int64_t H, int64_t Mi, int64_t tile);
+hipError_t launch_gateup(const uint16_t *x, int64_t T, int64_t H, int64_t ldx, const uint16_t *wg,
+                         const uint16_t *wu, int64_t ldw, int64_t Mi, int64_t tile, uint16_t *h, int64_t ldh,
+                         float *pmax, float *part, hipStream_t st);
 
 // attn.hip
 struct AttnShape {

@@ -196,7 +196,9 @@ static GemvPlan gemv_plan(int64_t T, int64_t M, int64_t k, int64_t tile, bool bf
     const int cw = WAVE * (bf16 ? 8 : 4);
     p.nslices = (int)((M + cw - 1) / cw);
     const int64_t base = (int64_t)p.ngroups * p.nslices;
-    int64_t ns = (GEMV_TARGET_WGS + base - 1) / base;
+    // as many splits as keep the grid within one round of resident workgroups:
+    // a partial second round runs at the latency of a whole workgroup
+    int64_t ns = GEMV_TARGET_WGS / base;
     const int64_t by_rows = (k + GEMV_WAVES * GEMV_MIN_ROWS - 1) / (GEMV_WAVES * GEMV_MIN_ROWS);
     if (ns > by_rows)
         ns = by_rows;

@@ -213,6 +213,42 @@ def ffn_block_demo(seed: int = 42, H: int = 1024, Mi: int = 4096) -> LinearCase:
     return LinearCase(f"ffn_block_demo_bf16_Mi{Mi}_H{H}", xb, wt, c, 1, "bf16", (0.5,))
 
 
+@dataclass
+class FfnCase:
+    """Gated FFN of one decoder layer: x [T,H] -> h = silu(x Wg^T)*(x Wu^T) [T,Mi] -> h W_down^T."""
+    name: str
+    x: np.ndarray        # [T, H] uint16 (bf16): the FFN input
+    wg: np.ndarray       # [H, Mi] uint16: W_gate^T, K-major
+    wu: np.ndarray       # [H, Mi] uint16: W_up^T, K-major
+    wd: np.ndarray       # [Mi, H] uint16: W_down^T, K-major (row j = slice j of the down projection)
+    c: np.ndarray        # [Mi] float32 row norms of wd (the down projection's scorer weights)
+    tile: int
+
+    @property
+    def T(self):
+        return self.x.shape[0]
+
+    @property
+    def H(self):
+        return self.x.shape[1]
+
+    @property
+    def Mi(self):
+        return self.wg.shape[1]
+
+
+def ffn_case(T: int = 1, H: int = 4096, Mi: int = 14336, tile: int = 1, seed: int = 0,
+             xsigma: float = 1.0, wsigma: float = 0.02, name: str | None = None) -> FfnCase:
+    """x ~N(0, xsigma) (a normalised hidden state), all three weight matrices ~N(0, wsigma), bf16.
+    The default is the decode FFN of the down-projection shape (H 4096, Mi 14336, one token)."""
+    x = normal_bf16(seed, S_X, T * H, xsigma).reshape(T, H)
+    wg = normal_bf16(seed, S_WG, H * Mi, wsigma).reshape(H, Mi)
+    wu = normal_bf16(seed, S_WU, H * Mi, wsigma).reshape(H, Mi)
+    wd = normal_bf16(seed, S_W, Mi * H, wsigma).reshape(Mi, H)
+    c = row_l2_f32(wd, True)
+    return FfnCase(name or f"ffn_decode_bf16_T{T}_H{H}_Mi{Mi}", x, wg, wu, wd, c, tile)
+
+
 # ----------------------------------------------------------------------------
 # attention decode workloads
 # ----------------------------------------------------------------------------
