@@ -316,8 +316,8 @@ def main():
         log("[bench] decode layer: generating inputs")
         Hh, Mi, Dq = 4096, 14336, 6144   # hidden, FFN intermediate, q+k+v outputs (32 q heads, 8 kv heads, D 128)
         fc = W.ffn_case(1, Hh, Mi, 1, seed=5)
-        qc = W.linear_random(1, Hh, Dq, 1, "bf16", seed=6, xsigma=1.0, wsigma=0.02)
-        oc = W.linear_random(1, Hh, Hh, 1, "bf16", seed=7, xsigma=1.0, wsigma=0.02)
+        qc = W.linear_qkv_decode()
+        oc = W.linear_o_decode()
         layer_bytes = 2 * (Hh * Dq + Hh * Hh + 3 * Hh * Mi)
         nl = n_copies(layer_bytes, layer_bytes // 2)
         L = []

@@ -55,6 +55,17 @@ def test_decode_down_proj_full_size(r):
     run_case(cs, r)
 
 
+@pytest.mark.parametrize("r", [0.25, 0.5])
+def test_qkv_shared_selection_full_size(r):
+    # one kept set over the hidden dimension serves the Q, K and V products at once
+    run_case(W.linear_qkv_decode(), r)
+
+
+@pytest.mark.parametrize("r", [0.25, 0.5])
+def test_o_proj_full_size(r):
+    run_case(W.linear_o_decode(), r)
+
+
 def test_prefill_full_size_sampled_rows():
     cs = W.linear_prefill()
     rows = [0, 1, 255, 256, 700, 1023, 1024, 1500, 1791, 1792, 2046, 2047]

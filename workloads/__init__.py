@@ -183,6 +183,23 @@ def linear_decode(seed: int = 0, K: int = 14336, M: int = 4096) -> LinearCase:
                       (0.25, 0.5, 0.75, 1.0))
 
 
+def linear_qkv_decode(seed: int = 6, H: int = 4096, Hq: int = 32, Hkv: int = 8, D: int = 128) -> LinearCase:
+    """One decode token into the fused Q, K, V projections of a GQA layer: x[1,H] ~N(0,1) bf16,
+    W_qkv^T [H, (Hq+2*Hkv)*D] bf16 ~N(0,0.02) (the three K-major matrices side by side).  A single
+    selection over H is shared by the three products: c_j is the norm of the whole row j."""
+    cs = linear_random(1, H, (Hq + 2 * Hkv) * D, 1, "bf16", seed, 1.0, 0.02,
+                       f"decode_qkv_proj_bf16_K{H}_M{(Hq + 2 * Hkv) * D}")
+    cs.rs = (0.25, 0.5)
+    return cs
+
+
+def linear_o_decode(seed: int = 7, H: int = 4096) -> LinearCase:
+    """One decode token into the attention output projection: x[1,H] ~N(0,1), W_o^T [H,H] ~N(0,0.02)."""
+    cs = linear_random(1, H, H, 1, "bf16", seed, 1.0, 0.02, f"decode_o_proj_bf16_K{H}_M{H}")
+    cs.rs = (0.25, 0.5)
+    return cs
+
+
 def linear_prefill(seed: int = 0, T: int = 2048, K: int = 4096, M: int = 4096,
                    tile: int = 256, outlier_frac: float = 0.01, outlier_scale: float = 20.0) -> LinearCase:
     """Prefill: X[2048,4096] bf16 ~N(0,1) with ceil(1%) outlier columns x20; W^T[4096,4096] bf16 ~N(0,0.02)."""
