@@ -182,7 +182,7 @@ rmm_status_t rmm_gate_up(const void *x, int64_t T, int64_t H, int64_t ldx,
  *   pos_idx optional out (NULL ok), int32 [B][Hsel][k_s] ascending
  *   lse     optional out (NULL ok), fp32 [B][Hq] = log sum_s exp(l_h[s])
  *   Hsel = Hkv (PER_KV_GROUP) or Hq (PER_Q_HEAD).
- * Limits: D == 128, Hq/Hkv in {1,2,4,8}, S <= 2^24, ldk/ldv multiples of 8.
+ * Limits: D == 128, Hq/Hkv in {1,2,4,8}, S <= 2^24, ldk a multiple of 8.
  * Deterministic. */
 size_t rmm_attn_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,
                                       double r_dim, double r_pos, rmm_sel_mode_t mode);
@@ -199,7 +199,8 @@ rmm_status_t rmm_attn_decode(const void *q, const void *kt, const void *v, const
  * scorer's |x| * ||W^T row|| (blog section 5.1: a slice's weight is its input
  * magnitude times its weight norm).  Step 5 is unchanged (no renormalisation,
  * p_h[s] unweighted).
- *   vn  NULL, or fp32 [B][Hkv][ldv], 16-byte aligned, vn[b,g,s] >= 0 for s < S
+ *   vn  NULL, or fp32 [B][Hkv][ldv], 16-byte aligned (ldv then a multiple of 8),
+ *       vn[b,g,s] >= 0 for s < S
  *       (vn[b,g,s] = L2 norm of V[b,g,s,:], kept by the cache owner; entries
  *       s >= S are read but ignored)
  * The fixed-point key holds log(pi_s) with 2^-25 resolution over [-120, 8):
@@ -212,6 +213,45 @@ rmm_status_t rmm_attn_decode_ex(const void *q, const void *kt, const void *v, co
                                 double r_dim, double r_pos, rmm_sel_mode_t mode,
                                 float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
                                 void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Paged caches and ragged batches.  Decode servers keep each sequence's KV
+ * cache in fixed-size pages and batch sequences of different lengths (GEMM
+ * notes section 7: continuous batching and paged attention in decode; blog
+ * section 8: batching is the main practical conflict of input-adaptive
+ * reduction).  The computation is rmm_attn_decode_ex's, per sequence b over its
+ * own S_b = seqlens[b] positions (values outside [1, S] are clamped), with its
+ * own kept count k_b = rmm_keep_count(S_b, r_pos).
+ *   k_pages  bf16 [num_pages][Hkv][D][page]  dim-major keys: row j of a page holds dim j
+ *   v_pages  bf16 [num_pages][Hkv][page][D]
+ *   vn_pages NULL, or fp32 [num_pages][Hkv][page] value-row norms (16-byte aligned)
+ *   block_table int32 [B][max_pages]: entry i of row b names the page holding
+ *            positions [i*page, (i+1)*page) of sequence b; only the first
+ *            ceil(S_b/page) entries are read, and their contents are trusted
+ *   seqlens  int32 [B] (device memory)
+ *   kn       fp32 [B][Hkv][D] key-column norms over each sequence's own positions
+ *   S        a bound on every S_b (at most max_pages*page): it sizes the
+ *            workspace (rmm_attn_decode_workspace_size with this S) and pos_idx
+ *   pos_idx  optional out, int32 [B][Hsel][rmm_keep_count(S, r_pos)]: row (b, .)
+ *            holds its k_b kept positions ascending, then -1
+ * Limits: page a multiple of 8 in [8, 2^24]; otherwise as rmm_attn_decode. */
+rmm_status_t rmm_attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                                   const float *kn, const float *vn_pages,
+                                   const int32_t *block_table, int64_t max_pages, int64_t page,
+                                   const int32_t *seqlens,
+                                   int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,
+                                   float scale, double r_dim, double r_pos, rmm_sel_mode_t mode,
+                                   float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
+                                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dense decode attention over paged, ragged caches (the r = 1 baseline of
+ * rmm_attn_decode_paged): same layouts; workspace from
+ * rmm_attn_decode_dense_workspace_size with the same S. */
+rmm_status_t rmm_attn_decode_dense_paged(const void *q, const void *k_pages, const void *v_pages,
+                                         const int32_t *block_table, int64_t max_pages, int64_t page,
+                                         const int32_t *seqlens,
+                                         int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,
+                                         float scale, float *out, float *lse,
+                                         void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Dense decode attention (all D dims, all S positions, online softmax) -- the
  * r = 1 baseline.  Same layouts; lse optional. */

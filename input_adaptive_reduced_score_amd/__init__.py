@@ -101,6 +101,10 @@ def lib():
                                              i32, vp, vp, vp, vp, vp, sz, vp]),
                 "rmm_gate_up_workspace_size": (sz, [i64, i64, i64, i64]),
                 "rmm_gate_up": (i32, [vp, i64, i64, i64, vp, vp, i64, i64, i64, vp, i64, vp, vp, sz, vp]),
+                "rmm_attn_decode_paged": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, vp, i64, i64, i64, i64, i64, flt,
+                                                dbl, dbl, i32, vp, vp, vp, vp, vp, sz, vp]),
+                "rmm_attn_decode_dense_paged": (i32, [vp, vp, vp, vp, i64, i64, vp, i64, i64, i64, i64, i64, flt,
+                                                      vp, vp, vp, sz, vp]),
                 "rmm_attn_decode_dense_workspace_size": (sz, [i64, i64, i64, i64, i64]),
                 "rmm_attn_decode_dense": (i32, [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, flt, vp, vp, vp, sz,
                                                 vp]),
@@ -119,7 +123,7 @@ EXPORTS = ("rmm_keep_count", "rmm_select_workspace_size", "rmm_select", "rmm_blo
            "rmm_select_blocks_workspace_size", "rmm_select_blocks", "rmm_linear_workspace_size", "rmm_linear",
            "rmm_linear_dense_workspace_size", "rmm_linear_dense", "rmm_attn_decode_workspace_size",
            "rmm_gate_up_workspace_size", "rmm_gate_up",
-           "rmm_attn_decode", "rmm_attn_decode_ex", "rmm_attn_decode_dense_workspace_size", "rmm_attn_decode_dense", "rmm_status_string",
+           "rmm_attn_decode", "rmm_attn_decode_ex", "rmm_attn_decode_paged", "rmm_attn_decode_dense_paged", "rmm_attn_decode_dense_workspace_size", "rmm_attn_decode_dense", "rmm_status_string",
            "rmm_last_error")
 
 
@@ -162,6 +166,9 @@ class Workspace:
         self._bufs = {}
 
     def get(self, nbytes: int, device) -> torch.Tensor:
+        if nbytes <= 0:
+            raise RmmError(1, "workspace size query rejected the arguments: " +
+                           lib().rmm_last_error().decode(errors="replace"))
         key = torch.device(device).index
         buf = self._bufs.get(key)
         if buf is None or buf.numel() < nbytes:
@@ -321,6 +328,76 @@ def attn_decode(q, kt, v, kn, r_dim: float, r_pos: float, scale: float | None = 
                                     scale, float(r_dim), float(r_pos), mode, _ptr(out), _ptr(dim_idx),
                                     _ptr(pos_idx), _ptr(lse), _ptr(w), w.numel() * w.element_size(), _stream()))
     return out, dim_idx, pos_idx, lse
+
+
+def _paged_args(q, k_pages, v_pages, block_table, seqlens, S):
+    _dev(q, "q")
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
+                 (seqlens, "seqlens")):
+        _dev(t, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if block_table.dtype != torch.int32 or seqlens.dtype != torch.int32:
+        raise ValueError("block_table and seqlens must be int32")
+    B, Hq, D = q.shape
+    npages, Hkv, Dk, page = k_pages.shape
+    if Dk != D or tuple(v_pages.shape) != (npages, Hkv, page, D):
+        raise ValueError("k_pages must be [num_pages, Hkv, D, page] and v_pages [num_pages, Hkv, page, D]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seqlens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seqlens [B]")
+    maxp = block_table.shape[1]
+    S = maxp * page if S is None else int(S)
+    return B, Hq, Hkv, D, page, maxp, S
+
+
+def attn_decode_paged(q, k_pages, v_pages, kn, block_table, seqlens, r_dim: float, r_pos: float,
+                      scale: float | None = None, mode: int = PER_KV_GROUP, S: int | None = None, vn_pages=None,
+                      out=None, want_idx: bool = True, ws=None):
+    """Reduced GQA decode over paged, ragged caches.  k_pages [P,Hkv,D,page], v_pages [P,Hkv,page,D] bf16;
+    block_table [B,max_pages], seqlens [B] int32 (device); kn [B,Hkv,D] fp32; vn_pages None or
+    [P,Hkv,page] fp32; S bounds every sequence length (default max_pages*page).
+    Returns (out, dim_idx, pos_idx, lse); pos_idx rows end in -1 past each sequence's kept count."""
+    L = lib()
+    B, Hq, Hkv, D, page, maxp, S = _paged_args(q, k_pages, v_pages, block_table, seqlens, S)
+    if vn_pages is not None:
+        _dev(vn_pages, "vn_pages")
+        if vn_pages.dtype != torch.float32 or tuple(vn_pages.shape) != tuple(k_pages.shape[:2]) + (page,):
+            raise ValueError("vn_pages must be float32 [num_pages, Hkv, page]")
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    Hsel = Hkv if mode == PER_KV_GROUP else Hq
+    kd, ks = keep_count(D, r_dim), keep_count(S, r_pos)
+    if kd < 0 or ks < 0:
+        raise RmmError(1, "ratios must be in (0, 1]")
+    dev = q.device
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev) if out is None else out
+    dim_idx = pos_idx = lse = None
+    if want_idx:
+        dim_idx = torch.empty((B, Hsel, kd), dtype=torch.int32, device=dev)
+        pos_idx = torch.empty((B, Hsel, ks), dtype=torch.int32, device=dev)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = L.rmm_attn_decode_workspace_size(B, Hq, Hkv, D, S, float(r_dim), float(r_pos), mode)
+    w = ws if ws is not None else _WS.get(need, dev)
+    _check(L.rmm_attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(kn), _ptr(vn_pages),
+                                   _ptr(block_table), maxp, page, _ptr(seqlens), B, Hq, Hkv, D, S, scale,
+                                   float(r_dim), float(r_pos), mode, _ptr(out), _ptr(dim_idx), _ptr(pos_idx),
+                                   _ptr(lse), _ptr(w), w.numel() * w.element_size(), _stream()))
+    return out, dim_idx, pos_idx, lse
+
+
+def attn_decode_dense_paged(q, k_pages, v_pages, block_table, seqlens, scale: float | None = None,
+                            S: int | None = None, out=None, lse=None, ws=None):
+    """Dense decode attention over paged, ragged caches (r = 1 baseline).  Returns (out, lse)."""
+    L = lib()
+    B, Hq, Hkv, D, page, maxp, S = _paged_args(q, k_pages, v_pages, block_table, seqlens, S)
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    dev = q.device
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev) if out is None else out
+    need = L.rmm_attn_decode_dense_workspace_size(B, Hq, Hkv, D, S)
+    w = ws if ws is not None else _WS.get(need, dev)
+    _check(L.rmm_attn_decode_dense_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), maxp, page,
+                                         _ptr(seqlens), B, Hq, Hkv, D, S, scale, _ptr(out), _ptr(lse), _ptr(w),
+                                         w.numel() * w.element_size(), _stream()))
+    return out, lse
 
 
 def attn_decode_dense(q, kt, v, scale: float | None = None, S: int | None = None, out=None, lse=None, ws=None):

@@ -382,7 +382,8 @@ size_t rmm_attn_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_
                                       double r_pos, rmm_sel_mode_t mode)
 {
     rmm::AttnShape s;
-    if (attn_shape(B, Hq, Hkv, D, S, S, S, 1.0f, r_dim, r_pos, (int)mode, &s) != RMM_OK)
+    const int64_t S8 = (S + 7) / 8 * 8; // the size does not depend on the pitches
+    if (attn_shape(B, Hq, Hkv, D, S, S8, S8, 1.0f, r_dim, r_pos, (int)mode, &s) != RMM_OK)
         return 0;
     return rmm::attn_ws_layout(s, nullptr, nullptr);
 }
@@ -401,17 +402,66 @@ rmm_status_t rmm_attn_decode_ex(const void *q, const void *kt, const void *v, co
         return st;
     if (!aligned16(q) || !aligned16(kt) || !aligned16(v) || ((uintptr_t)out & 3u))
         return fail(RMM_EUNSUPPORTED, "q, kt and v must be 16-byte aligned, out 4-byte aligned");
-    if (vn && !aligned16(vn))
-        return fail(RMM_EUNSUPPORTED, "vn must be 16-byte aligned");
+    if (vn && (!aligned16(vn) || ldv % 8))
+        return fail(RMM_EUNSUPPORTED, "vn must be 16-byte aligned and ldv a multiple of 8");
     const size_t need = rmm::attn_ws_layout(s, nullptr, nullptr);
     if (!ws || ws_bytes < need)
         return fail(RMM_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     init_once();
     rmm::AttnWs w;
     rmm::attn_ws_layout(s, &w, (char *)ws);
-    return launch_status(rmm::launch_attn(s, (const uint16_t *)q, (const uint16_t *)kt, (const uint16_t *)v, kn, vn,
-                                          out, dim_idx, pos_idx, lse, w, stream),
+    const rmm::KvMap m{nullptr, nullptr, 0, 0, r_pos};
+    return launch_status(rmm::launch_attn(s, m, (const uint16_t *)q, (const uint16_t *)kt, (const uint16_t *)v, kn,
+                                          vn, out, dim_idx, pos_idx, lse, w, stream),
                          "attn_decode");
+}
+
+// paged caches: shape checks shared by the reduced and the dense entry points
+static rmm_status_t paged_map(const void *kp, const void *vp, const int32_t *block_table, int64_t max_pages,
+                              int64_t page, const int32_t *seqlens, int64_t S, double r_pos, rmm::KvMap *m)
+{
+    if (!kp || !vp || !block_table || !seqlens)
+        return fail(RMM_EINVAL, "null page pool, block table or sequence lengths");
+    if (page < 8 || page % 8 || page > (1 << 24))
+        return fail(RMM_EUNSUPPORTED, "page size %lld must be a multiple of 8 in [8, 2^24]", (long long)page);
+    if (max_pages < 1 || S > max_pages * page)
+        return fail(RMM_EINVAL, "S = %lld exceeds max_pages * page = %lld", (long long)S,
+                    (long long)(max_pages * page));
+    if (!aligned16(kp) || !aligned16(vp))
+        return fail(RMM_EUNSUPPORTED, "page pools must be 16-byte aligned");
+    *m = rmm::KvMap{block_table, seqlens, max_pages, (int)page, r_pos};
+    return RMM_OK;
+}
+
+rmm_status_t rmm_attn_decode_paged(const void *q, const void *k_pages, const void *v_pages, const float *kn,
+                                   const float *vn_pages, const int32_t *block_table, int64_t max_pages, int64_t page,
+                                   const int32_t *seqlens, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,
+                                   float scale, double r_dim, double r_pos, rmm_sel_mode_t mode, float *out,
+                                   int32_t *dim_idx, int32_t *pos_idx, float *lse, void *ws, size_t ws_bytes,
+                                   hipStream_t stream)
+{
+    if (!q || !kn || !out)
+        return fail(RMM_EINVAL, "null required pointer");
+    rmm::AttnShape s;
+    const int64_t S8 = (S + 7) / 8 * 8;
+    rmm_status_t st = attn_shape(B, Hq, Hkv, D, S, S8, S8, scale, r_dim, r_pos, (int)mode, &s);
+    if (st != RMM_OK)
+        return st;
+    rmm::KvMap m;
+    if ((st = paged_map(k_pages, v_pages, block_table, max_pages, page, seqlens, S, r_pos, &m)) != RMM_OK)
+        return st;
+    if (!aligned16(q) || ((uintptr_t)out & 3u) || (vn_pages && !aligned16(vn_pages)))
+        return fail(RMM_EUNSUPPORTED, "q and vn must be 16-byte aligned, out 4-byte aligned");
+    const size_t need = rmm::attn_ws_layout(s, nullptr, nullptr);
+    if (!ws || ws_bytes < need)
+        return fail(RMM_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    init_once();
+    rmm::AttnWs w;
+    rmm::attn_ws_layout(s, &w, (char *)ws);
+    return launch_status(rmm::launch_attn(s, m, (const uint16_t *)q, (const uint16_t *)k_pages,
+                                          (const uint16_t *)v_pages, kn, vn_pages, out, dim_idx, pos_idx, lse, w,
+                                          stream),
+                         "attn_decode_paged");
 }
 
 rmm_status_t rmm_attn_decode(const void *q, const void *kt, const void *v, const float *kn, int64_t B, int64_t Hq,
@@ -426,7 +476,8 @@ rmm_status_t rmm_attn_decode(const void *q, const void *kt, const void *v, const
 size_t rmm_attn_decode_dense_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S)
 {
     rmm::AttnShape s;
-    if (attn_shape(B, Hq, Hkv, D, S, S, S, 1.0f, 1.0, 1.0, 0, &s) != RMM_OK)
+    const int64_t S8 = (S + 7) / 8 * 8;
+    if (attn_shape(B, Hq, Hkv, D, S, S8, S8, 1.0f, 1.0, 1.0, 0, &s) != RMM_OK)
         return 0;
     return rmm::attn_dense_ws_layout(B, Hq, S, nullptr, nullptr, nullptr, nullptr);
 }
@@ -451,9 +502,41 @@ rmm_status_t rmm_attn_decode_dense(const void *q, const void *kt, const void *v,
     float2 *stat;
     uint32_t *cnt;
     rmm::attn_dense_ws_layout(B, Hq, S, (char *)ws, &part, &stat, &cnt);
-    return launch_status(rmm::launch_attn_dense(s, (const uint16_t *)q, (const uint16_t *)kt, (const uint16_t *)v,
+    const rmm::KvMap m{nullptr, nullptr, 0, 0, 1.0};
+    return launch_status(rmm::launch_attn_dense(s, m, (const uint16_t *)q, (const uint16_t *)kt, (const uint16_t *)v,
                                                 out, lse, part, stat, cnt, stream),
                          "attn_decode_dense");
+}
+
+rmm_status_t rmm_attn_decode_dense_paged(const void *q, const void *k_pages, const void *v_pages,
+                                         const int32_t *block_table, int64_t max_pages, int64_t page,
+                                         const int32_t *seqlens, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                         int64_t S, float scale, float *out, float *lse, void *ws, size_t ws_bytes,
+                                         hipStream_t stream)
+{
+    if (!q || !out)
+        return fail(RMM_EINVAL, "null required pointer");
+    rmm::AttnShape s;
+    const int64_t S8 = (S + 7) / 8 * 8;
+    rmm_status_t st = attn_shape(B, Hq, Hkv, D, S, S8, S8, scale, 1.0, 1.0, 0, &s);
+    if (st != RMM_OK)
+        return st;
+    rmm::KvMap m;
+    if ((st = paged_map(k_pages, v_pages, block_table, max_pages, page, seqlens, S, 1.0, &m)) != RMM_OK)
+        return st;
+    if (!aligned16(q) || ((uintptr_t)out & 3u))
+        return fail(RMM_EUNSUPPORTED, "q must be 16-byte aligned, out 4-byte aligned");
+    const size_t need = rmm::attn_dense_ws_layout(B, Hq, S, nullptr, nullptr, nullptr, nullptr);
+    if (!ws || ws_bytes < need)
+        return fail(RMM_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    init_once();
+    float *part;
+    float2 *stat;
+    uint32_t *cnt;
+    rmm::attn_dense_ws_layout(B, Hq, S, (char *)ws, &part, &stat, &cnt);
+    return launch_status(rmm::launch_attn_dense(s, m, (const uint16_t *)q, (const uint16_t *)k_pages,
+                                                (const uint16_t *)v_pages, out, lse, part, stat, cnt, stream),
+                         "attn_decode_dense_paged");
 }
 
 } // extern "C"

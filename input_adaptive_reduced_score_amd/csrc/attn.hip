@@ -48,6 +48,59 @@ template <typename F> __device__ __forceinline__ F wave_sum(F v)
     return v;
 }
 
+// ---- cache addressing (contiguous or paged) and per-sequence lengths
+__device__ __forceinline__ int seq_len(const AttnShape &s, const KvMap &m, int b)
+{
+    if (!m.seqlens)
+        return (int)s.S;
+    const int v = m.seqlens[b];
+    return v < 1 ? 1 : (v > (int)s.S ? (int)s.S : v);
+}
+
+// The keep count of the C ABI (paper abstract, retention-ratio control) for a
+// sequence length known only on the device: ceil(r*n), r*n snapped to the
+// nearest integer within 1e-9 relative, clamped to [1, n]; the same IEEE
+// double operations as on the host.
+__device__ __forceinline__ int keep_count_dev(int n, double r)
+{
+    const double prod = r * (double)n;
+    const double near = rint(prod);
+    const double tol = 1e-9 * (prod > 1.0 ? prod : 1.0);
+    double kk = fabs(prod - near) <= tol ? near : ceil(prod);
+    kk = kk < 1.0 ? 1.0 : kk;
+    kk = kk > (double)n ? (double)n : kk;
+    return (int)kk;
+}
+
+__device__ __forceinline__ int seq_keep(const AttnShape &s, const KvMap &m, int Sb)
+{
+    return m.seqlens ? keep_count_dev(Sb, m.r_pos) : s.ks;
+}
+
+// Row of position p of KV head g of sequence b: the V row (times D elements)
+// and the value-norm entry share this index.  Needs p < the sequence's length
+// (block-table entries beyond it are never read).
+__device__ __forceinline__ int64_t kv_row(const AttnShape &s, const KvMap &m, int b, int g, int p)
+{
+    if (!m.pages)
+        return ((int64_t)b * s.Hkv + g) * s.ldv + p;
+    const int64_t pg = m.pages[(int64_t)b * m.maxp + p / m.page];
+    return (pg * s.Hkv + g) * m.page + p % m.page;
+}
+
+// Element offset of dim 0 at position p in the dim-major keys of (b, g), and
+// the pitch between dims.  p is a multiple of 8, so p .. p + 7 share a page.
+__device__ __forceinline__ int64_t kt_off(const AttnShape &s, const KvMap &m, int b, int g, int p, int64_t &pitch)
+{
+    if (!m.pages) {
+        pitch = s.ldk;
+        return ((int64_t)b * s.Hkv + g) * D * s.ldk + p;
+    }
+    const int64_t pg = m.pages[(int64_t)b * m.maxp + p / m.page];
+    pitch = m.page;
+    return (pg * s.Hkv + g) * D * m.page + p % m.page;
+}
+
 // Keeps the kd largest of 128 keys held two per lane (j = lane, lane + 64),
 // ties to the lower index, and writes the kept indices in ascending order.
 __device__ __forceinline__ void wave_select128(uint32_t key0, uint32_t key1, int kd, int *jd)
@@ -77,7 +130,7 @@ __device__ __forceinline__ void wave_select128(uint32_t key0, uint32_t key1, int
 
 // ------------------------------------------------------------------ qk
 template <int GS>
-__global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, int Sp, const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, KvMap m, int Sp, const uint16_t *__restrict__ q,
                                                              const uint16_t *__restrict__ kt,
                                                              const float *__restrict__ kn, float *__restrict__ logit,
                                                              float2 *__restrict__ pstat,
@@ -92,7 +145,15 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, int Sp
     const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel;
     const int h0 = sg * s.GS, g = h0 / s.G;
     const int chunk = blockIdx.x, nchunk = gridDim.x;
+    const int Sb = seq_len(s, m, b);
+    if (chunk * ATTN_QK_CHUNK >= Sb)
+        return; // past this sequence's end: its statistics are never read
     const uint16_t *qb = q + ((int64_t)b * s.Hq + h0) * D;
+    // this lane's key columns (the page lookup overlaps the staging and selection below)
+    const int sp = chunk * ATTN_QK_CHUNK + lane * 8;
+    const bool act = sp < Sb;
+    int64_t kpitch = 0;
+    const int64_t koff = act ? kt_off(s, m, b, g, sp, kpitch) : 0;
 
     // q of the group's heads, staged once (all threads) while wave 0 selects
     __shared__ float qall[GS][D];
@@ -124,8 +185,6 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, int Sp
     __syncthreads();
 
     // 2. partial dot products: wave w takes kept dims [i0, i1) (ascending), 8 positions per lane
-    const int sp = chunk * ATTN_QK_CHUNK + lane * 8;
-    const bool act = sp < s.S;
     const int i0 = s.kd * w / NWQ, i1 = s.kd * (w + 1) / NWQ;
     float acc[GS][8];
 #pragma unroll
@@ -134,13 +193,13 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, int Sp
         for (int e = 0; e < 8; ++e)
             acc[hh][e] = 0.0f;
     if (act) {
-        const uint16_t *kbase = kt + ((int64_t)b * s.Hkv + g) * D * s.ldk + sp;
+        const uint16_t *kbase = kt + koff;
         for (int ib = i0; ib < i1; ib += QK_U) {
             uint4 u[QK_U];
 #pragma unroll
             for (int qq = 0; qq < QK_U; ++qq)
                 if (ib + qq < i1)
-                    u[qq] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)jd[ib + qq] * s.ldk);
+                    u[qq] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)jd[ib + qq] * kpitch);
 #pragma unroll
             for (int qq = 0; qq < QK_U; ++qq) {
                 if (ib + qq < i1) {
@@ -184,13 +243,13 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, int Sp
         float mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            if (sp + e < s.S)
+            if (sp + e < Sb)
                 mx = fmaxf(mx, a8[e]);
         mx = wave_max(mx);
         float z = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            if (sp + e < s.S)
+            if (sp + e < Sb)
                 z += expf(s.scale * (a8[e] - mx));
         z = wave_sum(z);
         if (lane == 0)
@@ -220,7 +279,8 @@ __device__ __forceinline__ uint32_t logprob_key(double L, double off)
 }
 
 template <int GS>
-__global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, int nqk, const float *__restrict__ logit,
+__global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int Sp, int nqk_all,
+                                                       const float *__restrict__ logit,
                                                        const float2 *__restrict__ pstat, double *__restrict__ lse_ws,
                                                        float *__restrict__ lse_out, const float *__restrict__ vn,
                                                        uint32_t *__restrict__ keys, uint32_t *__restrict__ hist)
@@ -231,12 +291,16 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, int 
     __shared__ double lse_s[GS];
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS;
+    const int Sb = seq_len(s, m, b);
+    if (blockIdx.x * ATTN_KEY_CHUNK >= Sb)
+        return;
+    const int nqk = (Sb + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK; // this sequence's QK chunks
     for (int i = tid; i < ATTN_HIST_BINS; i += 256)
         lh[i] = 0;
     // this thread's logits are loaded first so their latency overlaps the statistics merge
     const int sp = blockIdx.x * ATTN_KEY_CHUNK + threadIdx.x * 8;
     f32x4_t a[GS][2];
-    if (sp < s.S) {
+    if (sp < Sb) {
 #pragma unroll
         for (int hh = 0; hh < GS; ++hh) {
             const f32x4_t *src = reinterpret_cast<const f32x4_t *>(logit + ((int64_t)b * s.Hq + h0 + hh) * Sp + sp);
@@ -247,19 +311,19 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, int 
     // merge the per-chunk softmax statistics of the group's heads into lse (double, fixed order)
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh) {
-        const float2 *ps = pstat + ((int64_t)b * s.Hq + h0 + hh) * nqk;
-        float m = -INFINITY;
+        const float2 *ps = pstat + ((int64_t)b * s.Hq + h0 + hh) * nqk_all;
+        float mx = -INFINITY;
         for (int i = tid; i < nqk; i += 256)
-            m = fmaxf(m, ps[i].x);
-        m = wave_max(m);
+            mx = fmaxf(mx, ps[i].x);
+        mx = wave_max(mx);
         if (lane == 0)
-            smax[hh][w] = m;
+            smax[hh][w] = mx;
     }
     __syncthreads();
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh) {
         const float M = fmaxf(fmaxf(smax[hh][0], smax[hh][1]), fmaxf(smax[hh][2], smax[hh][3]));
-        const float2 *ps = pstat + ((int64_t)b * s.Hq + h0 + hh) * nqk;
+        const float2 *ps = pstat + ((int64_t)b * s.Hq + h0 + hh) * nqk_all;
         double z = 0.0;
         for (int i = tid; i < nqk; i += 256) {
             const float2 st = ps[i];
@@ -287,27 +351,27 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, int Sp, int 
     for (int hh = 0; hh < GS; ++hh)
         lse[hh] = lse_s[hh];
     __syncthreads();
-    if (sp < s.S) {
+    if (sp < Sb) {
         uint32_t kk[8];
         const double sc = (double)s.scale;
-        // value-row norms of the 8 positions (sp + 8 <= ldv: ldv is a multiple of 8)
+        // value-row norms of the 8 positions (one page or row: pitches and pages are multiples of 8)
         f32x4_t nv[2] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};
         const double off = vn ? 120.0 : 128.0;
         if (vn) {
-            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(vn + ((int64_t)b * s.Hkv + h0 / s.G) * s.ldv + sp);
+            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(vn + kv_row(s, m, b, h0 / s.G, sp));
             nv[0] = src[0];
             nv[1] = src[1];
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            double m = sc * (double)a[0][e >> 2][e & 3] - lse[0];
+            double lp = sc * (double)a[0][e >> 2][e & 3] - lse[0];
 #pragma unroll
             for (int hh = 1; hh < GS; ++hh)
-                m = fmax(m, sc * (double)a[hh][e >> 2][e & 3] - lse[hh]);
+                lp = fmax(lp, sc * (double)a[hh][e >> 2][e & 3] - lse[hh]);
             if (vn)
-                m += log((double)nv[e >> 2][e & 3]);
-            kk[e] = logprob_key(m, off);
-            if (sp + e < s.S)
+                lp += log((double)nv[e >> 2][e & 3]);
+            kk[e] = logprob_key(lp, off);
+            if (sp + e < Sb)
                 atomicAdd(&lh[kk[e] >> 20], 1u);
         }
         uint4 *dst = reinterpret_cast<uint4 *>(keys + (int64_t)grp * Sp + sp);
@@ -337,10 +401,10 @@ constexpr int CAND_CAP = 8192;
 constexpr int SEL_RANK_MAX = 256;
 constexpr int SEL_KB = 4; // 16-byte key loads in flight per thread
 
-__global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, int P, int npv,
+__global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, KvMap m, int Sp, int P, int npv,
                                                            const uint32_t *__restrict__ keys,
                                                            const uint32_t *__restrict__ hist, SelInfo *__restrict__ sel,
-                                                           uint2 *__restrict__ info)
+                                                           uint2 *__restrict__ info, int32_t *__restrict__ pos_out)
 {
     __shared__ uint32_t h2[SEL_BINS];
     __shared__ uint32_t tmp[64];
@@ -353,7 +417,13 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, 
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const uint32_t *K = keys + (int64_t)grp * Sp;
     const uint32_t *H = hist + (int64_t)grp * ATTN_HIST_BINS;
-    uint32_t krem = (uint32_t)s.ks;
+    const int Sb = seq_len(s, m, grp / (int)s.Hsel);
+    const int ksb = seq_keep(s, m, Sb);
+    // a shorter sequence keeps fewer positions: the rest of its index row is -1
+    if (pos_out)
+        for (int i = ksb + tid; i < s.ks; i += 1024)
+            pos_out[(int64_t)grp * s.ks + i] = -1;
+    uint32_t krem = (uint32_t)ksb;
     const uint32_t d = hist_crossing(H, ATTN_HIST_BINS, krem, tmp);
     const uint32_t nbin = H[d];
     if (tid < PV_MAX_CHUNKS) {
@@ -367,7 +437,7 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, 
     }
     __syncthreads();
     const uint4 *k4 = reinterpret_cast<const uint4 *>(K);
-    const int n4 = (int)((s.S + 3) / 4), step = 1024;
+    const int n4 = (int)((Sb + 3) / 4), step = 1024;
     uint32_t thr, quota;
     if (nbin <= (uint32_t)CAND_CAP) {
         for (int i0 = tid; i0 - lane < n4; i0 += SEL_KB * step) {
@@ -383,7 +453,7 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, 
                 const uint32_t kk[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    cl += (4 * i + e < s.S) & ((kk[e] >> 20) == d);
+                    cl += (4 * i + e < Sb) & ((kk[e] >> 20) == d);
             }
             const uint32_t cincl = wave_incl_sum(cl);
             const uint32_t wcount = (uint32_t)__builtin_amdgcn_readlane((int)cincl, WAVE - 1);
@@ -400,7 +470,7 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 4 * i + e;
-                    const bool ok = j < s.S;
+                    const bool ok = j < Sb;
                     const uint32_t top = kk[e] >> 20;
                     ngt += ok & (top > d);
                     if (ok && top == d) {
@@ -476,8 +546,8 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, 
         }
     } else {
         uint32_t prefix = d << 20, pmask = 0xfff00000u;
-        radix_pass_v4(K, (int)s.S, prefix, pmask, 10, 10, krem, h2, tmp);
-        radix_pass_v4(K, (int)s.S, prefix, pmask, 0, 10, krem, h2, tmp);
+        radix_pass_v4(K, Sb, prefix, pmask, 10, 10, krem, h2, tmp);
+        radix_pass_v4(K, Sb, prefix, pmask, 0, 10, krem, h2, tmp);
         thr = prefix;
         quota = krem;
         for (int i0 = tid; i0 - lane < n4; i0 += SEL_KB * step) {
@@ -492,7 +562,7 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, 
                 uint32_t ngt = 0, neq = 0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const bool ok = 4 * i + e < s.S;
+                    const bool ok = 4 * i + e < Sb;
                     ngt += ok & (kk[e] > thr);
                     neq += ok & (kk[e] == thr);
                 }
@@ -525,13 +595,13 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, int Sp, 
 // One workgroup per (chunk of P positions, group).  4 waves; each wave
 // quarter (16 lanes) holds one 256-byte V row, 8 dims per lane.
 template <int GS>
-__global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P, const uint16_t *__restrict__ v,
+__global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, KvMap m, int Sp, int P, const uint16_t *__restrict__ v,
                                                       const float *__restrict__ logit, const double *__restrict__ lse_ws,
                                                       const uint32_t *__restrict__ keys, const SelInfo *__restrict__ sel,
                                                       const uint2 *__restrict__ info, int32_t *__restrict__ pos_out,
                                                       float *__restrict__ part)
 {
-    __shared__ int rows[PV_SUB];
+    __shared__ int64_t rows[PV_SUB]; // V row index of each kept position of the pass
     __shared__ float pr[GS][PV_SUB];
     __shared__ uint32_t wgt[4], weq[4];
     __shared__ float red[4][GS][D];
@@ -547,7 +617,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P
         lsef[hh] = (float)lse_ws[(int64_t)b * s.Hq + h0 + hh];
     const uint32_t *K = keys + (int64_t)grp * Sp;
     const float *L = logit + ((int64_t)b * s.Hq + h0) * Sp;
-    const uint16_t *vb = v + ((int64_t)b * s.Hkv + g) * s.ldv * D;
+    const int Sb = seq_len(s, m, b), ksb = seq_keep(s, m, Sb);
     const int quarter = lane >> 4, dl = lane & 15, slot = w * 4 + quarter;
 
     float acc[GS][8];
@@ -557,16 +627,19 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P
         for (int e = 0; e < 8; ++e)
             acc[hh][e] = 0.0f;
 
-    const int p0 = c * P, p1 = min((int)s.S, p0 + P);
+    const int p0 = c * P, p1 = min(Sb, p0 + P);
     for (int sb = p0; sb < p1; sb += PV_SUB) {
-        // thread tid holds positions j0, j0+1 (j0 even and Sp a multiple of 8: j0 < S keeps both in the row)
+        // thread tid holds positions j0, j0+1 (j0 even and Sp a multiple of 8: j0 < S keeps both in the row;
+        // pages hold a multiple of 8 positions, so both share j0's page)
         const int j0 = sb + 2 * tid;
         uint2 kk = make_uint2(0u, 0u);
         float2 lg[GS];
+        int64_t vrow = 0;
 #pragma unroll
         for (int hh = 0; hh < GS; ++hh)
             lg[hh] = make_float2(0.0f, 0.0f);
         if (j0 < p1) {
+            vrow = kv_row(s, m, b, g, j0);
             kk = *reinterpret_cast<const uint2 *>(K + j0);
 #pragma unroll
             for (int hh = 0; hh < GS; ++hh)
@@ -597,19 +670,19 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P
         const uint32_t la = gpa + min(epa, quota) - base0, lb = gpb + min(epb, quota) - base0; // pass-local slots
         const uint32_t nkept = gtot + min(ties_before + etot, quota) - base0;
         if (keepa && la < PV_SUB) {
-            rows[la] = j0;
+            rows[la] = vrow;
 #pragma unroll
             for (int hh = 0; hh < GS; ++hh)
                 pr[hh][la] = expf(fmaf(s.scale, lg[hh].x, -lsef[hh]));
-            if (pos_out && kept_before + la < (uint32_t)s.ks)
+            if (pos_out && kept_before + la < (uint32_t)ksb)
                 pos_out[(int64_t)grp * s.ks + kept_before + la] = j0;
         }
         if (keepb && lb < PV_SUB) {
-            rows[lb] = j0 + 1;
+            rows[lb] = vrow + 1;
 #pragma unroll
             for (int hh = 0; hh < GS; ++hh)
                 pr[hh][lb] = expf(fmaf(s.scale, lg[hh].y, -lsef[hh]));
-            if (pos_out && kept_before + lb < (uint32_t)s.ks)
+            if (pos_out && kept_before + lb < (uint32_t)ksb)
                 pos_out[(int64_t)grp * s.ks + kept_before + lb] = j0 + 1;
         }
         __syncthreads();
@@ -621,7 +694,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, int Sp, int P
             for (int qq = 0; qq < PV_U; ++qq) {
                 const int r = r0 + 16 * qq;
                 if (r < nk)
-                    u[qq] = *reinterpret_cast<const uint4 *>(vb + (int64_t)rows[r] * D + dl * 8);
+                    u[qq] = *reinterpret_cast<const uint4 *>(v + rows[r] * D + dl * 8);
             }
 #pragma unroll
             for (int qq = 0; qq < PV_U; ++qq) {
@@ -733,8 +806,8 @@ size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base)
 }
 
 template <int GS>
-static hipError_t attn_run(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v,
-                           const float *kn, const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
+static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt,
+                           const uint16_t *v, const float *kn, const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
                            const AttnWs &ws, hipStream_t st)
 {
     const int Sp = (int)((s.S + 7) / 8 * 8);
@@ -744,28 +817,30 @@ static hipError_t attn_run(const AttnShape &s, const uint16_t *q, const uint16_t
     pv_chunks(s.S, &P, &npv);
     SelInfo *sel = reinterpret_cast<SelInfo *>(ws.pos);
     uint2 *info = reinterpret_cast<uint2 *>(align256((char *)(sel + G)));
-    attn_qk_kernel<GS><<<dim3(nqk, G), QK_THREADS, 0, st>>>(s, Sp, q, kt, kn, ws.logit, ws.pstat, dim_idx, ws.hist);
+    attn_qk_kernel<GS><<<dim3(nqk, G), QK_THREADS, 0, st>>>(s, m, Sp, q, kt, kn, ws.logit, ws.pstat, dim_idx,
+                                                             ws.hist);
     attn_key_kernel<GS><<<dim3((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK, G), 256, 0, st>>>(
-        s, Sp, nqk, ws.logit, ws.pstat, ws.lse, lse, vn, ws.keys, ws.hist);
-    attn_select_kernel<<<G, 1024, 0, st>>>(s, Sp, P, npv, ws.keys, ws.hist, sel, info);
-    attn_pv_kernel<GS><<<dim3(npv, G), 256, 0, st>>>(s, Sp, P, v, ws.logit, ws.lse, ws.keys, sel, info, pos_idx,
+        s, m, Sp, nqk, ws.logit, ws.pstat, ws.lse, lse, vn, ws.keys, ws.hist);
+    attn_select_kernel<<<G, 1024, 0, st>>>(s, m, Sp, P, npv, ws.keys, ws.hist, sel, info, pos_idx);
+    attn_pv_kernel<GS><<<dim3(npv, G), 256, 0, st>>>(s, m, Sp, P, v, ws.logit, ws.lse, ws.keys, sel, info, pos_idx,
                                                      ws.pvpart);
     attn_pv_reduce_kernel<GS><<<G, 256, 0, st>>>(s, npv, ws.pvpart, out);
     return hipGetLastError();
 }
 
-hipError_t launch_attn(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v, const float *kn,
-                       const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse, const AttnWs &ws, hipStream_t st)
+hipError_t launch_attn(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt, const uint16_t *v,
+                       const float *kn, const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
+                       const AttnWs &ws, hipStream_t st)
 {
     switch (s.GS) {
     case 1:
-        return attn_run<1>(s, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
+        return attn_run<1>(s, m, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
     case 2:
-        return attn_run<2>(s, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
+        return attn_run<2>(s, m, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
     case 4:
-        return attn_run<4>(s, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
+        return attn_run<4>(s, m, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
     case 8:
-        return attn_run<8>(s, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
+        return attn_run<8>(s, m, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
     default:
         return hipErrorInvalidValue;
     }
@@ -779,7 +854,7 @@ constexpr int DN_SUB = 512;
 constexpr int DN_MAX_SPANS = 64;
 
 template <int G>
-__global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, int span, const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, KvMap m, int span, const uint16_t *__restrict__ q,
                                                          const uint16_t *__restrict__ kt, const uint16_t *__restrict__ v,
                                                          float *__restrict__ part, float2 *__restrict__ stat)
 {
@@ -787,6 +862,7 @@ __global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, int span, 
     __shared__ float lg[4][G][DN_SUB]; // per-wave partial dots, then wave 0's slot holds the sums
     __shared__ float red[4][G][D];
     __shared__ float mrun[G], zrun[G], fac[G];
+    __shared__ int64_t vrow[DN_SUB]; // V row index of each position of the sub-chunk
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int grp = blockIdx.y, b = grp / s.Hkv, g = grp % s.Hkv, h0 = g * G;
     const int c = blockIdx.x, nspan = gridDim.x;
@@ -796,8 +872,7 @@ __global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, int span, 
         mrun[tid] = -INFINITY;
         zrun[tid] = 0.0f;
     }
-    const uint16_t *kb = kt + ((int64_t)b * s.Hkv + g) * D * s.ldk;
-    const uint16_t *vb = v + ((int64_t)b * s.Hkv + g) * s.ldv * D;
+    const int Sb = seq_len(s, m, b);
     const int quarter = lane >> 4, dl = lane & 15;
     float o[G][8];
 #pragma unroll
@@ -806,7 +881,7 @@ __global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, int span, 
         for (int e = 0; e < 8; ++e)
             o[hh][e] = 0.0f;
     __syncthreads();
-    const int p0 = c * span, p1 = min((int)s.S, p0 + span);
+    const int p0 = c * span, p1 = min(Sb, p0 + span);
     for (int sb = p0; sb < p1; sb += DN_SUB) {
         // QK: wave w takes dims [32w, 32w+32) for 8 positions per lane
         const int sp = sb + lane * 8;
@@ -816,12 +891,16 @@ __global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, int span, 
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 a[hh][e] = 0.0f;
+        for (int i = tid; i < min(DN_SUB, p1 - sb); i += 256)
+            vrow[i] = kv_row(s, m, b, g, sb + i);
         if (sp < p1) {
+            int64_t kpitch;
+            const uint16_t *kb = kt + kt_off(s, m, b, g, sp, kpitch);
             for (int j0 = 32 * w; j0 < 32 * w + 32; j0 += 16) {
                 uint4 u[16];
 #pragma unroll
                 for (int qq = 0; qq < 16; ++qq)
-                    u[qq] = *reinterpret_cast<const uint4 *>(kb + (int64_t)(j0 + qq) * s.ldk + sp);
+                    u[qq] = *reinterpret_cast<const uint4 *>(kb + (int64_t)(j0 + qq) * kpitch);
 #pragma unroll
                 for (int qq = 0; qq < 16; ++qq) {
                     float kv[8];
@@ -888,7 +967,7 @@ __global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, int span, 
             for (int qq = 0; qq < 8; ++qq) {
                 const int r = r0 + 16 * qq;
                 if (r < nr)
-                    u[qq] = *reinterpret_cast<const uint4 *>(vb + (int64_t)(sb + r) * D + dl * 8);
+                    u[qq] = *reinterpret_cast<const uint4 *>(v + vrow[r] * D + dl * 8);
             }
 #pragma unroll
             for (int qq = 0; qq < 8; ++qq) {
@@ -1006,8 +1085,9 @@ size_t attn_dense_ws_layout(int64_t B, int64_t Hq, int64_t S, char *base, float 
     return (size_t)(p - base);
 }
 
-hipError_t launch_attn_dense(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v, float *out,
-                             float *lse, float *part, float2 *stat, uint32_t *cnt, hipStream_t st)
+hipError_t launch_attn_dense(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt,
+                             const uint16_t *v, float *out, float *lse, float *part, float2 *stat, uint32_t *cnt,
+                             hipStream_t st)
 {
     int span, nspan;
     dense_spans(s.S, &span, &nspan);
@@ -1016,7 +1096,7 @@ hipError_t launch_attn_dense(const AttnShape &s, const uint16_t *q, const uint16
     (void)cnt;
 #define RMM_DENSE_CASE(GV)                                                                                         \
     case GV:                                                                                                       \
-        attn_dense_kernel<GV><<<grid, 256, 0, st>>>(s, span, q, kt, v, part, stat);                                \
+        attn_dense_kernel<GV><<<grid, 256, 0, st>>>(s, m, span, q, kt, v, part, stat);                             \
         attn_dense_reduce_kernel<GV><<<dim3(ng, GV), D, 0, st>>>(s, nspan, part, stat, out, lse);                   \
         break;
     switch (s.G) {

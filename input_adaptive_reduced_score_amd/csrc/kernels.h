@@ -94,13 +94,24 @@ struct AttnWs {
     float *pvpart;   // [B][Hsel][npv][GS][D]
     uint32_t *cnt;   // counter header
 };
+// Where the cache of sequence b keeps position p (contiguous caches, or pages
+// named by a block table) and how long each sequence is.
+struct KvMap {
+    const int32_t *pages;   // block table [B][maxp], or null: contiguous caches with pitches ldk / ldv
+    const int32_t *seqlens; // [B] positions per sequence (clamped to [1, S]), or null: every sequence has S
+    int64_t maxp;           // block-table row length
+    int page;               // positions per page (a multiple of 8)
+    double r_pos;           // position keep ratio (per-sequence keep counts)
+};
 size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base);
-hipError_t launch_attn(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v, const float *kn,
-                       const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse, const AttnWs &ws, hipStream_t st);
+hipError_t launch_attn(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt, const uint16_t *v,
+                       const float *kn, const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
+                       const AttnWs &ws, hipStream_t st);
 size_t attn_dense_ws_layout(int64_t B, int64_t Hq, int64_t S, char *base, float **part, float2 **stat,
                             uint32_t **cnt);
-hipError_t launch_attn_dense(const AttnShape &s, const uint16_t *q, const uint16_t *kt, const uint16_t *v, float *out,
-                             float *lse, float *part, float2 *stat, uint32_t *cnt, hipStream_t st);
+hipError_t launch_attn_dense(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt,
+                             const uint16_t *v, float *out, float *lse, float *part, float2 *stat, uint32_t *cnt,
+                             hipStream_t st);
 void attn_init();
 
 } // namespace rmm

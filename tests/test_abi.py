@@ -88,6 +88,10 @@ def test_linear_and_attn_argument_errors_host_only():
     ex[4], ex[0] = p, None
     assert L.rmm_attn_decode_ex(*ex) == 1
     assert L.rmm_attn_decode_workspace_size(1, 32, 8, 128, 32768, 0.25, 0.25, 0) > 0
+    # lengths that are not a multiple of 8 still get a size (it grows with S)
+    a = L.rmm_attn_decode_workspace_size(2, 8, 2, 128, 2500, 0.5, 0.25, 1)
+    assert a >= L.rmm_attn_decode_workspace_size(2, 8, 2, 128, 2496, 0.5, 0.25, 1) > 0
+    assert L.rmm_attn_decode_dense_workspace_size(1, 8, 2, 128, 9999) > 0
     assert L.rmm_status_string(3).startswith(b"RMM_EWORKSPACE")
 
 

@@ -356,3 +356,73 @@ def attn_128k(seed: int = 0) -> AttnCase:
 def attn_small(B: int = 1, S: int = 1000, Hq: int = 8, Hkv: int = 2, D: int = 128, seed: int = 0,
                n_hot: int = 8) -> AttnCase:
     return attn_case(B, S, Hq, Hkv, D, seed, n_hot)
+
+
+# ----------------------------------------------------------------------------
+# paged, ragged decode batches
+# ----------------------------------------------------------------------------
+
+BF16_INF = 0x7F80
+
+
+@dataclass
+class PagedAttnCase:
+    """A decode batch of sequences of different lengths whose caches live in a shared page pool.
+    seqs[b] holds sequence b as a contiguous one-sequence AttnCase (its own q, keys, values, kn);
+    the pool holds the same keys and values scattered over pages in a shuffled order."""
+    name: str
+    seqs: list               # AttnCase per sequence (B = 1, S = its length)
+    q: np.ndarray            # [B, Hq, D] uint16
+    kn: np.ndarray           # [B, Hkv, D] float32
+    k_pages: np.ndarray      # [P, Hkv, D, page] uint16 (dim-major keys per page)
+    v_pages: np.ndarray      # [P, Hkv, page, D] uint16
+    vn_pages: np.ndarray     # [P, Hkv, page] float32 value-row norms
+    block_table: np.ndarray  # [B, max_pages] int32
+    seqlens: np.ndarray      # [B] int32
+    page: int
+    scale: float
+
+    @property
+    def B(self):
+        return len(self.seqs)
+
+    @property
+    def S(self):
+        return int(self.seqlens.max())
+
+
+def attn_paged(lengths, page: int = 256, Hq: int = 32, Hkv: int = 8, D: int = 128, seed: int = 0,
+               n_hot: int = 8, spare_pages: int = 3, name: str | None = None) -> PagedAttnCase:
+    """Sequence b is attn_case(1, lengths[b], seed = seed*1000 + b) (so q and kn are per sequence).
+    Pages are assigned to sequences in a seeded random order from a pool with `spare_pages` extra
+    pages; positions past a sequence's end inside its last page, the spare pages and the
+    block-table entries past a sequence's pages (which name a spare page) hold +inf keys and
+    values and huge norms, so any read of them would show in the results."""
+    lengths = [int(n) for n in lengths]
+    seqs = [attn_case(1, n, Hq, Hkv, D, seed * 1000 + b, min(n_hot, n)) for b, n in enumerate(lengths)]
+    npg = [-(-n // page) for n in lengths]
+    P = sum(npg) + spare_pages
+    perm = _gen(seed, S_HOT, 7).permutation(P).astype(np.int32)
+    k_pages = np.full((P, Hkv, D, page), BF16_INF, np.uint16)
+    v_pages = np.full((P, Hkv, page, D), BF16_INF, np.uint16)
+    vn_pages = np.full((P, Hkv, page), 1e30, np.float32)
+    maxp = max(npg)
+    poison = perm[-1]  # a spare page
+    bt = np.full((len(lengths), maxp), poison, np.int32)
+    nxt = 0
+    for b, cs in enumerate(seqs):
+        n = lengths[b]
+        vn = value_row_norms(cs.v)[0]                      # [Hkv, n]
+        for i in range(npg[b]):
+            pg = perm[nxt]
+            nxt += 1
+            bt[b, i] = pg
+            lo, hi = i * page, min(n, (i + 1) * page)
+            k_pages[pg, :, :, :hi - lo] = cs.kt[0, :, :, lo:hi]
+            v_pages[pg, :, :hi - lo, :] = cs.v[0, :, lo:hi, :]
+            vn_pages[pg, :, :hi - lo] = vn[:, lo:hi]
+    q = np.concatenate([cs.q for cs in seqs], axis=0)
+    kn = np.concatenate([cs.kn for cs in seqs], axis=0)
+    nm = name or f"attn_paged_B{len(lengths)}_Hq{Hq}_Hkv{Hkv}_page{page}_S{max(lengths)}"
+    return PagedAttnCase(nm, seqs, q, kn, k_pages, v_pages, vn_pages, bt, np.array(lengths, np.int32), page,
+                         seqs[0].scale)
