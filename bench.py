@@ -475,6 +475,37 @@ def main():
             log(f"[bench] {name} dense flash-decode: {t * 1e6:.1f} us ({by / t / 1e9:.0f} GB/s)")
             del qs, ks_, vs_, kns, q0, k0, v0
 
+    # ------------------------------------------------------------------ paged, ragged decode batch
+    if not args.no_sweep and not args.headline_only:
+        lengths = [65536, 40000, 32768, 16384, 8192, 4096, 2048, 1000]
+        log(f"[bench] paged ragged batch: generating inputs ({len(lengths)} sequences, {sum(lengths)} positions)")
+        pc = W.attn_paged(lengths, page=256, Hq=32, Hkv=8, seed=11, n_hot=64, spare_pages=1)
+        B, Hq, Hkv, D, S = pc.B, 32, 8, 128, pc.S
+        pool = (pc.k_pages.size + pc.v_pages.size) * 2
+        npc = n_copies(pool, pool // 3)
+        q0, kn0 = bf(pc.q), torch.from_numpy(pc.kn).to(dev)
+        bt0, sl0 = torch.from_numpy(pc.block_table).to(dev), torch.from_numpy(pc.seqlens).to(dev)
+        kps = [bf(pc.k_pages) for _ in range(npc)]
+        vps = [bf(pc.v_pages) for _ in range(npc)]
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        psteps = max(5, steps // 20)
+        for rd, rp in ((0.25, 0.25), (0.5, 0.5)):
+            t = time_loop(lambda i: rmm.attn_decode_paged(q0, kps[i % npc], vps[i % npc], kn0, bt0, sl0, rd, rp,
+                                                          scale=pc.scale, S=S, out=out, want_idx=False),
+                          psteps, 2, torch)
+            by = sum(A.attn_step_bytes(1, Hq, Hkv, D, n, rmm.keep_count(D, rd), rmm.keep_count(n, rp))
+                     for n in lengths)
+            sweep.append({"workload": "attn_paged_ragged_b8", "lengths": lengths, "page": 256, "r_dim": rd,
+                          "r_pos": rp, "call_us": t * 1e6, "retained_bytes": by, "GBps": by / t / 1e9})
+            log(f"[bench] paged ragged batch r=({rd},{rp}): {t * 1e6:.1f} us, {by / t / 1e9:.0f} GB/s retained")
+        t = time_loop(lambda i: rmm.attn_decode_dense_paged(q0, kps[i % npc], vps[i % npc], bt0, sl0, scale=pc.scale,
+                                                            S=S, out=out), psteps, 2, torch)
+        by = sum(A.attn_dense_bytes(1, Hq, Hkv, D, n) for n in lengths)
+        sweep.append({"workload": "attn_paged_ragged_b8_dense", "call_us": t * 1e6, "bytes": by,
+                      "GBps": by / t / 1e9})
+        log(f"[bench] paged ragged batch dense: {t * 1e6:.1f} us ({by / t / 1e9:.0f} GB/s)")
+        del kps, vps, pc
+
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
