@@ -278,6 +278,17 @@ __device__ __forceinline__ uint32_t logprob_key(double L, double off)
     return (uint32_t)t;
 }
 
+// Histogram bin of a position key: 4096 bins of 1/128 nat over (L + off) in
+// [96, 128), i.e. log-probabilities in [-32, 0) (or [-24, 8) with value norms);
+// every key below that window falls into bin 0.  Bin d >= 1 holds exactly the
+// keys with kk >> 18 == d + KEY_BIN_BASE.
+constexpr uint32_t KEY_BIN_BASE = 96u << 7; // (96 * 2^25) >> 18
+__device__ __forceinline__ uint32_t key_bin(uint32_t kk)
+{
+    const uint32_t t = kk >> 18;
+    return t > KEY_BIN_BASE ? t - KEY_BIN_BASE : 0u;
+}
+
 template <int GS>
 __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int Sp, int nqk_all,
                                                        const float *__restrict__ logit,
@@ -372,7 +383,9 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int
                 lp += log((double)nv[e >> 2][e & 3]);
             kk[e] = logprob_key(lp, off);
             if (sp + e < Sb)
-                atomicAdd(&lh[kk[e] >> 20], 1u);
+                atomicAdd(&lh[key_bin(kk[e])], 1u);
+            else
+                kk[e] = 0u; // past the sequence's end: the lowest key, in no bin above 0
         }
         uint4 *dst = reinterpret_cast<uint4 *>(keys + (int64_t)grp * Sp + sp);
         dst[0] = uint4{kk[0], kk[1], kk[2], kk[3]};
@@ -387,19 +400,20 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int
 // ------------------------------------------------------------------ select
 // Threshold key thr and tie quota of the group, then per PV chunk c (P
 // positions): info[c] = (kept before the chunk, ties at thr before the chunk).
-// Fast path: the 4096-bin histogram names the bin d holding the k-th key; one
-// pass over the keys counts, per chunk, the keys in higher bins and gathers the
-// bin's keys (candidates) into LDS.  Up to SEL_RANK_MAX candidates are ranked
-// exactly (key descending, position ascending); up to CAND_CAP the last 20 key
-// bits are resolved by two radix passes over the candidates (ranking costs
-// O(n^2) LDS reads); beyond that two
-// radix passes and a counting pass run over all keys.
+// Fast path: the 4096-bin histogram (1/128 nat per bin, key_bin) names the bin
+// d holding the k-th key; one pass over the keys counts, per chunk, the keys in
+// higher bins and gathers the bin's keys (candidates) into LDS.  Up to
+// SEL_RANK_MAX candidates are ranked exactly (key descending, position
+// ascending); up to CAND_CAP the last 18 key bits are resolved by two radix
+// passes over the candidates (ranking costs O(n^2) LDS reads); beyond that the
+// radix passes and a counting pass run over all keys, over all 32 bits when the
+// k-th key lies below the histogram's window (bin 0).
 struct SelInfo {
     uint32_t thr, quota;
 };
 constexpr int CAND_CAP = 8192;
 constexpr int SEL_RANK_MAX = 256;
-constexpr int SEL_KB = 4; // 16-byte key loads in flight per thread
+constexpr int SEL_KB = 8; // 16-byte key loads in flight per thread
 
 __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, KvMap m, int Sp, int P, int npv,
                                                            const uint32_t *__restrict__ keys,
@@ -411,8 +425,9 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, KvMap m,
     __shared__ uint32_t cgt[PV_MAX_CHUNKS], ceq[PV_MAX_CHUNKS];
     __shared__ uint32_t ckey[CAND_CAP];
     __shared__ int cpos[CAND_CAP];
-    __shared__ uint32_t rk_above[1024], rk_tie[1024]; // one slot per thread: (part, candidate)
-    __shared__ uint32_t ncand, res[2];
+    __shared__ uint32_t rk_above[1024]; // one slot per thread: (part, candidate)
+    __shared__ uint64_t ck64[SEL_RANK_MAX];
+    __shared__ uint32_t ncand, nquota, res[2];
     const int grp = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const uint32_t *K = keys + (int64_t)grp * Sp;
@@ -424,37 +439,63 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, KvMap m,
         for (int i = ksb + tid; i < s.ks; i += 1024)
             pos_out[(int64_t)grp * s.ks + i] = -1;
     uint32_t krem = (uint32_t)ksb;
-    const uint32_t d = hist_crossing(H, ATTN_HIST_BINS, krem, tmp);
-    const uint32_t nbin = H[d];
+    // the histogram's loads first, then the first batch of keys (it does not depend on
+    // the threshold bin), so the key loads stay in flight through the histogram phase
+    static_assert(ATTN_HIST_BINS == 4 * 1024, "four histogram bins per thread");
+    uint32_t hc[4];
+    hist_counts<4>(H, hc);
+    const uint4 *k4 = reinterpret_cast<const uint4 *>(K);
+    const int n4 = (int)((Sb + 3) / 4), step = 1024;
+    uint4 u[SEL_KB];
+#pragma unroll
+    for (int q = 0; q < SEL_KB; ++q) { // unconditional loads (an in-range address), zeroed past n4
+        const int ii = tid + q * step;
+        const uint4 t = k4[min(ii, n4 - 1)];
+        const uint32_t keep = 0u - ilt(ii, n4);
+        u[q] = make_uint4(t.x & keep, t.y & keep, t.z & keep, t.w & keep);
+    }
+    uint32_t nbin;
+    const uint32_t d = crossing_from_counts<4>(hc, krem, tmp, &nbin);
     if (tid < PV_MAX_CHUNKS) {
         cgt[tid] = 0;
         ceq[tid] = 0;
     }
     if (tid == 0) {
         ncand = 0;
+        nquota = 0;
         res[0] = 0;
         res[1] = 0;
     }
     __syncthreads();
-    const uint4 *k4 = reinterpret_cast<const uint4 *>(K);
-    const int n4 = (int)((Sb + 3) / 4), step = 1024;
+    const uint32_t tD = d + KEY_BIN_BASE; // kk >> 18 of the crossing bin's keys (d >= 1)
     uint32_t thr, quota;
-    if (nbin <= (uint32_t)CAND_CAP) {
+    if (d > 0 && nbin <= (uint32_t)CAND_CAP) {
         for (int i0 = tid; i0 - lane < n4; i0 += SEL_KB * step) {
-            uint4 u[SEL_KB];
+            if (i0 != tid) {
 #pragma unroll
-            for (int q = 0; q < SEL_KB; ++q)
-                u[q] = i0 + q * step < n4 ? k4[i0 + q * step] : make_uint4(0u, 0u, 0u, 0u);
-            // candidates of the batch: per-lane count, wave scan, one slot reservation per wave
-            uint32_t cl = 0;
+                for (int q = 0; q < SEL_KB; ++q)
+                    u[q] = i0 + q * step < n4 ? k4[i0 + q * step] : make_uint4(0u, 0u, 0u, 0u);
+            }
+            // predicates as integer arithmetic (bins are 14-bit): per element, in bin tD
+            // (a candidate) or above it; candidates also as a bit mask.  Keys past the
+            // sequence's end (up to the 8-position boundary the loads reach) are 0, in
+            // neither; loads past n4 give 0 as well.
+            uint32_t cl = 0, cmask = 0, ngt[SEL_KB];
 #pragma unroll
             for (int q = 0; q < SEL_KB; ++q) {
-                const int i = i0 + q * step;
                 const uint32_t kk[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+                ngt[q] = 0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    cl += (4 * i + e < Sb) & ((kk[e] >> 20) == d);
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t top = kk[e] >> 18;
+                    const uint32_t g = (tD - top) >> 31, ge = (tD - 1u - top) >> 31; // top > tD, top >= tD
+                    const uint32_t c = ge - g;
+                    cl += c;
+                    cmask |= c << (4 * q + e);
+                    ngt[q] += g;
+                }
             }
+            // candidates: per-lane count, wave scan, one slot reservation per wave
             const uint32_t cincl = wave_incl_sum(cl);
             const uint32_t wcount = (uint32_t)__builtin_amdgcn_readlane((int)cincl, WAVE - 1);
             uint32_t base = 0;
@@ -462,26 +503,26 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, KvMap m,
                 base = atomicAdd(&ncand, wcount);
             base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
             uint32_t slot = base + cincl - cl;
+            while (cmask) { // rare: the bin holds ~1/100 of the keys
+                const int b = __builtin_ctz(cmask);
+                cmask &= cmask - 1u;
+                const int q = b >> 2, e = b & 3;
+                uint32_t kv = 0; // u[q] selected with compile-time indices (no private-memory copy of u)
+#pragma unroll
+                for (int qq = 0; qq < SEL_KB; ++qq)
+                    if (qq == q)
+                        kv = e == 0 ? u[qq].x : e == 1 ? u[qq].y : e == 2 ? u[qq].z : u[qq].w;
+                if (slot < (uint32_t)CAND_CAP) {
+                    ckey[slot] = kv;
+                    cpos[slot] = 4 * (i0 + q * step) + e;
+                }
+                ++slot;
+            }
+            // keys above the bin, per PV chunk (one wave load covers 256 consecutive positions: one chunk)
 #pragma unroll
             for (int q = 0; q < SEL_KB; ++q) {
-                const int i = i0 + q * step; // one wave load covers 256 consecutive positions: one chunk
-                const uint32_t kk[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
-                uint32_t ngt = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 4 * i + e;
-                    const bool ok = j < Sb;
-                    const uint32_t top = kk[e] >> 20;
-                    ngt += ok & (top > d);
-                    if (ok && top == d) {
-                        if (slot < (uint32_t)CAND_CAP) {
-                            ckey[slot] = kk[e];
-                            cpos[slot] = j;
-                        }
-                        ++slot;
-                    }
-                }
-                const uint32_t wgt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(ngt), WAVE - 1);
+                const int i = i0 + q * step;
+                const uint32_t wgt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(ngt[q]), WAVE - 1);
                 if (lane == 0 && wgt != 0u)
                     atomicAdd(&cgt[(4 * (i - lane)) / P], wgt);
             }
@@ -489,52 +530,56 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, KvMap m,
         __syncthreads();
         const uint32_t nc = min(nbin, (uint32_t)CAND_CAP);
         if (nc <= (uint32_t)SEL_RANK_MAX) {
-            // rank: thread t compares candidate t % RS with every (1024 / RS)-th other
-            const uint32_t RS = nc <= 256u ? 256u : nc <= 512u ? 512u : 1024u;
-            const uint32_t split = 1024u / RS, me_i = (uint32_t)tid % RS, part = (uint32_t)tid / RS;
+            // Rank by one 64-bit order key per candidate: the 18 key bits under the bin
+            // (candidates share its top 14), then the complemented position (< 2^24), so
+            // larger means earlier in the total order and no two are equal.  Thread t
+            // counts the candidates above candidate t % 256 among every fourth one.
+            const uint32_t kb = tD << 18;
+            for (int i = tid; i < (int)nc; i += 1024)
+                ck64[i] = ((uint64_t)(ckey[i] - kb) << 24) | (uint64_t)(0xffffffu - (uint32_t)cpos[i]);
+            __syncthreads();
+            constexpr uint32_t RS = SEL_RANK_MAX, split = 1024u / RS;
+            const uint32_t me_i = (uint32_t)tid % RS, part = (uint32_t)tid / RS;
             if (me_i < nc) {
-                const uint32_t mk = ckey[me_i];
-                const int mp = cpos[me_i];
-                // 8 independent comparisons per step keep the LDS reads pipelined
-                uint32_t ab[8] = {0, 0, 0, 0, 0, 0, 0, 0}, ti[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                const uint64_t mk = ck64[me_i];
+                // 8 independent comparisons per step keep the LDS reads pipelined; a
+                // difference of two keys below 2^42 has its top bit set iff the other is larger
+                uint32_t ab[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                 uint32_t i = part;
                 for (; i + 7 * split < nc; i += 8 * split) {
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const uint32_t ok = ckey[i + u * split];
-                        const int op = cpos[i + u * split];
-                        ab[u] += (ok > mk) || (ok == mk && op < mp);
-                        ti[u] += ok == mk && op <= mp;
-                    }
+                    for (int u = 0; u < 8; ++u)
+                        ab[u] += (uint32_t)((mk - ck64[i + u * split]) >> 63);
                 }
-                for (; i < nc; i += split) {
-                    const uint32_t ok = ckey[i];
-                    const int op = cpos[i];
-                    ab[0] += (ok > mk) || (ok == mk && op < mp);
-                    ti[0] += ok == mk && op <= mp;
-                }
+                for (; i < nc; i += split)
+                    ab[0] += (uint32_t)((mk - ck64[i]) >> 63);
                 rk_above[tid] = ((ab[0] + ab[1]) + (ab[2] + ab[3])) + ((ab[4] + ab[5]) + (ab[6] + ab[7]));
-                rk_tie[tid] = ((ti[0] + ti[1]) + (ti[2] + ti[3])) + ((ti[4] + ti[5]) + (ti[6] + ti[7]));
             }
             __syncthreads();
             if ((uint32_t)tid < nc) {
-                uint32_t above = 0, tie_upto = 0;
-                for (uint32_t q = 0; q < split; ++q) {
+                uint32_t above = 0;
+#pragma unroll
+                for (uint32_t q = 0; q < split; ++q)
                     above += rk_above[q * RS + tid];
-                    tie_upto += rk_tie[q * RS + tid];
-                }
-                if (above + 1u == krem) {
+                if (above + 1u == krem) { // the krem-th candidate: the threshold key and its position
                     res[0] = ckey[tid];
-                    res[1] = tie_upto;
+                    res[1] = (uint32_t)cpos[tid];
                 }
             }
             __syncthreads();
             thr = res[0];
-            quota = res[1];
+            // quota: the threshold's rank among its ties, i.e. equal keys at positions <= its own
+            const uint32_t pk = res[1];
+            for (int i = tid; i < (int)nc; i += 1024)
+                if (ckey[i] == thr && (uint32_t)cpos[i] <= pk)
+                    atomicAdd(&nquota, 1u);
+            __syncthreads();
+            quota = nquota;
         } else {
-            uint32_t prefix = d << 20, pmask = 0xfff00000u;
-            radix_pass(ckey, (int)nc, prefix, pmask, 10, 10, krem, h2, tmp);
-            radix_pass(ckey, (int)nc, prefix, pmask, 0, 10, krem, h2, tmp);
+            uint32_t prefix = tD << 18, pmask = 0xfffc0000u;
+#pragma clang loop unroll(disable)
+            for (int ps = 0; ps < 2; ++ps) // bits 9..17, then 0..8 (one copy of the pass: smaller code)
+                radix_pass(ckey, (int)nc, prefix, pmask, 9 - 9 * ps, 9, krem, h2, tmp);
             thr = prefix;
             quota = krem;
         }
@@ -545,9 +590,19 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, KvMap m,
                 atomicAdd(&ceq[cpos[i] / P], 1u);
         }
     } else {
-        uint32_t prefix = d << 20, pmask = 0xfff00000u;
-        radix_pass_v4(K, Sb, prefix, pmask, 10, 10, krem, h2, tmp);
-        radix_pass_v4(K, Sb, prefix, pmask, 0, 10, krem, h2, tmp);
+        // a crowded bin: the 18 bits under it (9 + 9); a threshold below the histogram's
+        // window (bin 0): all 32 bits (11 + 11 + 10)
+        const bool full = d == 0;
+        uint32_t prefix = full ? 0u : tD << 18, pmask = full ? 0u : 0xfffc0000u;
+        if (full)
+            krem = (uint32_t)ksb;
+        const int npass = full ? 3 : 2;
+#pragma clang loop unroll(disable)
+        for (int ps = 0; ps < npass; ++ps) {
+            const int shift = full ? (ps == 0 ? 21 : ps == 1 ? 10 : 0) : (ps == 0 ? 9 : 0);
+            const int nbits = full ? (ps == 2 ? 10 : 11) : 9;
+            radix_pass_v4(K, Sb, prefix, pmask, shift, nbits, krem, h2, tmp);
+        }
         thr = prefix;
         quota = krem;
         for (int i0 = tid; i0 - lane < n4; i0 += SEL_KB * step) {
@@ -578,16 +633,16 @@ __global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, KvMap m,
         }
     }
     __syncthreads();
-    if (tid == 0) {
-        uint32_t gacc = 0, eacc = 0;
-        uint2 *o = info + (int64_t)grp * npv;
-        for (int c = 0; c < npv; ++c) {
-            o[c] = make_uint2(gacc + min(eacc, quota), eacc);
-            gacc += cgt[c];
-            eacc += ceq[c];
+    if (w == 0) {
+        // per chunk: kept and tied positions before it (npv <= 64 chunks: one lane each, DPP scans)
+        const uint32_t cg = lane < npv ? cgt[lane] : 0u, ce = lane < npv ? ceq[lane] : 0u;
+        const uint32_t gex = wave_incl_sum(cg) - cg, eex = wave_incl_sum(ce) - ce;
+        if (lane < npv)
+            info[(int64_t)grp * npv + lane] = make_uint2(gex + min(eex, quota), eex);
+        if (lane == 0) {
+            sel[grp].thr = thr;
+            sel[grp].quota = quota;
         }
-        sel[grp].thr = thr;
-        sel[grp].quota = quota;
     }
 }
 

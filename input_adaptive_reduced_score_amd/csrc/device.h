@@ -48,6 +48,28 @@ template <> struct Vec16<float> {
     }
 };
 
+// Predicates as integer arithmetic (0 or 1) on the vector ALU: a compare would
+// produce a lane mask in scalar registers, and combining masks runs on the
+// scalar ALU, which the 16 waves of a 1024-thread workgroup share.
+// lt31 and eq31 need a, b < 2^31; ilt needs |a - b| < 2^31.
+__device__ __forceinline__ uint32_t lt31(uint32_t a, uint32_t b) { return (a - b) >> 31; }        // a < b
+__device__ __forceinline__ uint32_t eq31(uint32_t a, uint32_t b) { return ((a ^ b) - 1u) >> 31; } // a == b
+__device__ __forceinline__ uint32_t ilt(int a, int b) { return ((uint32_t)a - (uint32_t)b) >> 31; } // a < b
+// A copy of v the compiler cannot see through: predicates built from it stay in
+// the phase that uses them instead of being hoisted (and held in registers)
+// across the whole kernel.
+__device__ __forceinline__ int opaque(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+template <int N> __device__ __forceinline__ void opaque_all(uint32_t (&v)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        asm volatile("" : "+v"(v[i]));
+}
+
 // Inclusive prefix sum over the whole block (blockDim.x threads, multiple of 64).
 // `tmp` holds at least blockDim.x/64 words of LDS.  Contains barriers: every
 // thread of the block must call it.

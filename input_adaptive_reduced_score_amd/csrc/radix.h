@@ -86,28 +86,77 @@ __device__ __forceinline__ void compact_ascending(const uint32_t *keys, int n, u
 
 
 // Finds, in a histogram of `nbins` digit counts (nbins a multiple of
-// blockDim.x; LDS or global), the digit holding the krem-th largest key; returns
-// it and updates krem to the rank inside that digit.  Every thread calls it.
-__device__ __forceinline__ uint32_t hist_crossing(const uint32_t *hist, int nbins, uint32_t &krem, uint32_t *tmp)
+// blockDim.x, at most 8 per thread; LDS or global), the digit holding the
+// krem-th largest key; returns it, updates krem to the rank inside that digit
+// and, if `count` is given, sets it to that digit's count.  Each count is read
+// once (a global histogram costs one round trip).  Every thread calls it.
+__device__ __forceinline__ uint32_t hist_crossing(const uint32_t *hist, int nbins, uint32_t &krem, uint32_t *tmp,
+                                                  uint32_t *count = nullptr)
 {
+    constexpr int MAXPER = 8;
     const int per = nbins / (int)blockDim.x;
     const int top = nbins - 1 - (int)threadIdx.x * per; // this thread covers bins top, top-1, ..., top-per+1
+    uint32_t c[MAXPER];
     uint32_t tot = 0;
-    for (int q = 0; q < per; ++q)
-        tot += hist[top - q];
+#pragma unroll
+    for (int q = 0; q < MAXPER; ++q) {
+        c[q] = q < per ? hist[top - q] : 0u;
+        tot += c[q];
+    }
     const uint32_t incl = block_incl_scan(tot, tmp);
     uint32_t run = incl - tot;
-    for (int q = 0; q < per; ++q) {
-        const uint32_t c = hist[top - q];
-        if (run < krem && krem <= run + c) {
+#pragma unroll
+    for (int q = 0; q < MAXPER; ++q) {
+        if (q < per && run < krem && krem <= run + c[q]) {
             tmp[32] = (uint32_t)(top - q);
             tmp[33] = krem - run;
+            tmp[34] = c[q];
         }
-        run += c;
+        run += c[q];
     }
     __syncthreads();
     const uint32_t d = tmp[32];
     krem = tmp[33];
+    if (count)
+        *count = tmp[34];
+    __syncthreads();
+    return d;
+}
+
+// hist_crossing in two steps, so that other loads can be issued between the
+// histogram's loads and their use: hist_counts loads this thread's PER bins
+// (nbins == PER * blockDim.x), crossing_from_counts finishes as hist_crossing.
+template <int PER> __device__ __forceinline__ void hist_counts(const uint32_t *hist, uint32_t (&c)[PER])
+{
+    const int top = PER * (int)blockDim.x - 1 - (int)threadIdx.x * PER;
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+        c[q] = hist[top - q];
+}
+template <int PER>
+__device__ __forceinline__ uint32_t crossing_from_counts(const uint32_t (&c)[PER], uint32_t &krem, uint32_t *tmp,
+                                                         uint32_t *count)
+{
+    const int top = PER * (int)blockDim.x - 1 - (int)threadIdx.x * PER;
+    uint32_t tot = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+        tot += c[q];
+    const uint32_t incl = block_incl_scan(tot, tmp);
+    uint32_t run = incl - tot;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        if (run < krem && krem <= run + c[q]) {
+            tmp[32] = (uint32_t)(top - q);
+            tmp[33] = krem - run;
+            tmp[34] = c[q];
+        }
+        run += c[q];
+    }
+    __syncthreads();
+    const uint32_t d = tmp[32];
+    krem = tmp[33];
+    *count = tmp[34];
     __syncthreads();
     return d;
 }

@@ -98,24 +98,6 @@ __device__ __forceinline__ void load8(const float *p, int avail, float (&v)[8])
 // slice indices, counts): they stay in vector registers, whereas comparisons
 // combined with && / || become lane-mask logic on the one scalar unit the
 // workgroup's 16 waves share.
-__device__ __forceinline__ uint32_t lt31(uint32_t a, uint32_t b) { return (a - b) >> 31; }        // a < b
-__device__ __forceinline__ uint32_t eq31(uint32_t a, uint32_t b) { return ((a ^ b) - 1u) >> 31; } // a == b
-__device__ __forceinline__ uint32_t ilt(int a, int b) { return ((uint32_t)a - (uint32_t)b) >> 31; } // a < b, |a-b| < 2^31
-// A copy of v the compiler cannot see through: predicates built from it stay in
-// the phase that uses them instead of being hoisted (and held in registers)
-// across the whole kernel.
-__device__ __forceinline__ int opaque(int v)
-{
-    asm volatile("" : "+v"(v));
-    return v;
-}
-template <int N> __device__ __forceinline__ void opaque_all(uint32_t (&v)[N])
-{
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        asm volatile("" : "+v"(v[i]));
-}
-
 // Histogram bins are stored with one pad word per 32 bins: bin 32g+e sits at
 // word 33g+e, so the 32 bins of group g are contiguous and the 64 groups that
 // wave 0's lanes read start in distinct LDS banks.

@@ -172,3 +172,13 @@ def test_value_norm_ragged_spare_capacity(S):
 def test_value_norm_32k_full_size():
     cs = W.attn_32k()
     run_attn(cs, 0.25, 0.25, 0, vn=W.value_row_norms(cs.v))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_threshold_below_histogram_window(mode):
+    # a sharp softmax (scale 2): the k-th log-probability lies near -80, below the key
+    # histogram's [-32, 0) window, so the selector resolves all 32 key bits by radix passes
+    cs = W.attn_case(1, 4000, Hq=4, Hkv=1, seed=21, n_hot=4)
+    cs.scale = 2.0
+    run_attn(cs, 0.5, 0.5, mode)
+    run_attn(cs, 0.25, 0.9, mode)
