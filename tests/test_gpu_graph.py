@@ -96,3 +96,54 @@ def test_attention_graph_replays_match_eager():
         rmm.attn_decode_dense(q, kt, v, scale=cs.scale)
         torch.cuda.synchronize()
     assert np.isfinite(out.cpu().numpy()).all()
+
+
+def test_decode_ffn_chain_graph_replays_match_eager():
+    # gated producer -> selection on its tile maxima -> reduced down projection
+    cs = W.ffn_case(1, 4096, 14336, 1, seed=4)
+    x, wg, wu, wd, c = dev(cs.x), dev(cs.wg), dev(cs.wu), dev(cs.wd), dev(cs.c)
+    h = torch.empty((1, 14336), dtype=torch.bfloat16, device="cuda:0")
+    pm = torch.empty((1, 14336), dtype=torch.float32, device="cuda:0")
+    idx = torch.empty((1, rmm.keep_count(14336, 0.5)), dtype=torch.int32, device="cuda:0")
+    y = torch.empty((1, 4096), dtype=torch.float32, device="cuda:0")
+
+    def step():
+        rmm.gate_up(x, wg, wu, 1, h=h, pmax=pm)
+        rmm.select(pm, c, 1, 0.5, idx=idx)
+        rmm.linear(h, wd, idx, 1, out=y)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (h, pm, idx, y)]
+    g = _capture(step)
+    for rep in range(3):
+        for t in (pm, y):
+            t.fill_(float("nan"))
+        idx.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((h, pm, idx, y), ref):
+            assert torch.equal(a, b), f"replay {rep}"
+        rmm.gate_up(x[:, :1024], wg[:1024], wu[:1024], 1)  # eager work on the same workspace
+        torch.cuda.synchronize()
+
+
+def test_paged_attention_graph_replays_match_eager():
+    pc = W.attn_paged([3000, 17, 9000], page=128, Hq=8, Hkv=2, seed=5, n_hot=4)
+    args = (dev(pc.q), dev(pc.k_pages), dev(pc.v_pages), dev(pc.kn), dev(pc.block_table), dev(pc.seqlens))
+    out = torch.empty((3, 8, 128), dtype=torch.float32, device="cuda:0")
+
+    def step():
+        rmm.attn_decode_paged(*args, 0.5, 0.25, scale=pc.scale, S=pc.S, out=out, want_idx=False)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = _capture(step)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep}"
+        rmm.attn_decode_dense_paged(*args[:3], *args[4:], scale=pc.scale, S=pc.S)
+        torch.cuda.synchronize()
