@@ -2,8 +2,8 @@
 against the oracle, through the C ABI.
 
 Bar: kept index sets bit-exact (integer work); outputs within rel-L2 1e-5.
-Spec bars are 1e-5 (fp32 inputs) and 2e-2 (bf16 inputs); the tighter
-1e-5 is used for both because bf16 x bf16 products are exact in fp32, so the
+A looser 2e-2 bar for bf16 inputs is not used: 1e-5 holds for both dtypes
+because bf16 x bf16 products are exact in fp32, so the
 only error left is fp32 accumulation over <= 16K terms (~sqrt(n) * 2^-24 ~ 1e-5
 worst case), while a single dropped or duplicated slice moves the result by
 about 1/sqrt(k) (1e-2 at the decode shape) and would pass a 2e-2 bar.
