@@ -121,3 +121,57 @@ def test_select_blocks_argument_errors_host_only():
     assert _call_select_blocks(K=40960, ldx=40960) == 2      # above the selector's K limit
     assert _call_select_blocks(x=C.c_void_p(18)) == 2        # misaligned
     assert _call_select_blocks() == 3                        # no workspace
+
+
+def test_gate_up_argument_errors_host_only():
+    L = rmm.lib()
+    p = C.c_void_p(256)
+    ok = dict(x=p, T=1, H=64, ldx=64, wg=p, wu=p, ldw=128, Mi=128, tile=1, h=p, ldh=128, pmax=None, ws=None,
+              ws_bytes=0, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.rmm_gate_up(*a.values())
+
+    assert call(x=None) == 1
+    assert call(h=None) == 1
+    assert call(T=0) == 1
+    assert call(tile=0) == 1
+    assert call(ldx=32) == 1               # ldx < H
+    assert call(ldw=120) == 1              # ldw < Mi
+    assert call(ldh=100) == 1              # ldh < Mi
+    assert call(ldw=132) == 2              # pitch not a multiple of 8
+    assert call(wu=C.c_void_p(264)) == 2   # misaligned
+    assert call(h=C.c_void_p(257)) == 2    # h not 2-byte aligned
+    assert call() == 3                     # no workspace
+    assert L.rmm_gate_up_workspace_size(1, 4096, 14336, 1) > 0
+    assert L.rmm_gate_up_workspace_size(0, 4096, 14336, 1) == 0
+
+
+def test_paged_attention_argument_errors_host_only():
+    L = rmm.lib()
+    p = C.c_void_p(256)
+    ok = dict(q=p, kp=p, vp=p, kn=p, vn=None, bt=p, maxp=4, page=256, sl=p, B=2, Hq=32, Hkv=8, D=128, S=1000,
+              scale=0.088, r_dim=0.5, r_pos=0.5, mode=0, out=p, dim_idx=None, pos_idx=None, lse=None, ws=None,
+              ws_bytes=0, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.rmm_attn_decode_paged(*a.values())
+
+    assert call(bt=None) == 1              # no block table
+    assert call(sl=None) == 1              # no lengths
+    assert call(S=1025) == 1               # S above max_pages * page
+    assert call(page=12) == 2              # page not a multiple of 8
+    assert call(page=4) == 2
+    assert call(kp=C.c_void_p(264)) == 2   # misaligned pool
+    assert call(vn=C.c_void_p(260)) == 2   # misaligned value norms
+    assert call(D=64) == 2                 # head_dim without a kernel
+    assert call(r_pos=0.0) == 1
+    assert call() == 3                     # no workspace
+    d = [p, p, p, p, 4, 256, p, 2, 32, 8, 128, 1000, 0.088, p, None, None, 0, None]
+    assert L.rmm_attn_decode_dense_paged(*d) == 3
+    d[4] = 3                               # 3 pages of 256 < S
+    assert L.rmm_attn_decode_dense_paged(*d) == 1
