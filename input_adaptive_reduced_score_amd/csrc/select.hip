@@ -305,10 +305,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
         if (top > 0 && nc <= SEL_CAND_CAP) {
             // gather the crossing digit's keys (any order): per-lane count, wave
             // scan, one slot reservation per wave
-            uint32_t cl = 0;
+            // (the lane's candidates as a bit mask; only set bits are visited below)
+            opaque_all(uk);
+            const int limc = opaque(lim);
+            uint32_t cmask = 0;
 #pragma unroll
             for (int i = 0; i < PER; ++i)
-                cl += i < lim && (uk[i] & pmask) == prefix;
+                cmask |= (ilt(i, limc) & eq31(uk[i] & pmask, prefix)) << i;
+            const uint32_t cl = (uint32_t)__popc(cmask);
             const uint32_t cincl = wave_incl_sum(cl);
             const uint32_t wcount = (uint32_t)__builtin_amdgcn_readlane((int)cincl, WAVE - 1);
             uint32_t base = 0;
@@ -316,13 +320,16 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
                 base = atomicAdd(&ncand, wcount);
             base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
             uint32_t slot = base + cincl - cl;
+            while (cmask) {
+                const int b = __builtin_ctz(cmask);
+                cmask &= cmask - 1u;
+                uint32_t kv = 0; // uk[b] through compile-time indices (no private-memory copy of uk)
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                if (i < lim && (uk[i] & pmask) == prefix) {
-                    if (slot < SEL_CAND_CAP)
-                        cand[slot] = make_uint2(uk[i], (uint32_t)(j0 + i));
-                    ++slot;
-                }
+                for (int q = 0; q < PER; ++q)
+                    kv = q == b ? uk[q] : kv;
+                if (slot < SEL_CAND_CAP)
+                    cand[slot] = make_uint2(kv, (uint32_t)(j0 + b));
+                ++slot;
             }
             __syncthreads();
             // the candidate ranked krem-th fixes the threshold key and how many
@@ -378,13 +385,19 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
     // 3. order-preserving compaction.  Kept: u > prefix, or u == prefix among
     // the first krem such slices.  Output position of a slice = slices kept
     // before it = (greater before) + min(equal before, krem).
+    // The lane's greater and equal slices as bit masks (masked-off registers hold 0,
+    // which is never above the threshold; a zero threshold is matched only by real
+    // slices); only kept bits are visited when writing.
     opaque_all(uk);
-    uint32_t gl = 0, el = 0;
+    const int limk = opaque(lim);
+    uint32_t gmask = 0, emask = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        gl += lt31(prefix, uk[i]);
-        el += eq31(uk[i], prefix);
+        const uint32_t real = ilt(i, limk);
+        gmask |= (real & lt31(prefix, uk[i])) << i;
+        emask |= (real & eq31(uk[i], prefix)) << i;
     }
+    const uint32_t gl = (uint32_t)__popc(gmask), el = (uint32_t)__popc(emask);
     const uint32_t gincl = wave_incl_sum(gl), eincl = wave_incl_sum(el);
     if (lane == WAVE - 1) {
         wgt[w] = gincl;
@@ -397,14 +410,25 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
         gb += v < w ? wgt[v] : 0u;
         eb += v < w ? weq[v] : 0u;
     }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const uint32_t g = lt31(prefix, uk[i]), e = eq31(uk[i], prefix);
-        const uint32_t pos = gb + min(eb, krem);
-        if ((g | (e & lt31(eb, krem))) & lt31(pos, (uint32_t)k))
-            outl[pos] = j0 + i;
-        gb += g;
-        eb += e;
+    // kept: every greater slice, and equal slices while fewer than krem equal ones precede them
+    uint32_t kmask = gmask;
+    {
+        uint32_t em = emask, ebr = eb;
+        while (em) { // rare: usually only the threshold's own slice
+            const int b = __builtin_ctz(em);
+            em &= em - 1u;
+            kmask |= lt31(ebr, krem) << b;
+            ++ebr;
+        }
+    }
+    // in ascending slice order from the count of slices kept before this thread
+    uint32_t pos = gb + min(eb, krem);
+    while (kmask) {
+        const int b = __builtin_ctz(kmask);
+        kmask &= kmask - 1u;
+        if (pos < (uint32_t)k)
+            outl[pos] = j0 + b;
+        ++pos;
     }
     // the list is staged in LDS, then written with coalesced stores
     __syncthreads();
