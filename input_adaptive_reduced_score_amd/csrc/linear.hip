@@ -14,6 +14,8 @@
 //    columns of the tile's activations are packed once (activations are the
 //    small operand), then a bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16, fp32
 //    accumulation) stages A tiles and the kept W^T rows through LDS.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -262,39 +264,97 @@ hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const v
 }
 
 // ============================================================================ gather
-// xg[t][i] = x[t][idx[t/tile][i]] for i < k, 0 for k <= i < kpad.  One workgroup
-// per token row: with STAGE the row is staged in LDS with 16-byte loads (rows up
-// to GATHER_LDS_MAX_K elements), then gathered; without, gathered from HBM.
+// xg[t][i] = x[t][idx[t/tile][i]] for i < k, 0 for k <= i < kpad.
+// A workgroup takes up to `rows` consecutive token rows of one tile (they share
+// the kept list).  Thread t owns 8-column chunks t, t + 256, ... of the packed
+// rows; it loads the indices of its chunks once, with clamped addresses so that
+// every load is issued before the first wait, and reuses them for each row.
+// With STAGE the rows are first staged in LDS with 16-byte loads, all rows in
+// flight together (rows x K elements, K up to GATHER_LDS_MAX_K); without, each
+// element is read from global memory.
 constexpr int GATHER_LDS_MAX_K = 32768;
+constexpr int GATHER_LDS_BUDGET = 32768;  // bytes of staged rows per workgroup (one row may exceed it)
+constexpr int GATHER_MAX_ROWS = 8;
+constexpr int GATHER_CH = 4;              // chunks per thread held in registers per pass
 template <bool STAGE>
-__global__ __launch_bounds__(256) void gather_kernel(const uint16_t *__restrict__ x, int64_t ldx, int K, int tile,
-                                                     const int32_t *__restrict__ idx, int k, int kpad,
-                                                     uint16_t *__restrict__ xg)
+__global__ __launch_bounds__(256) void gather_kernel(const uint16_t *__restrict__ x, int64_t ldx, int T, int K, int tile,
+                                                     const int32_t *__restrict__ idx, int k, int kpad, int rows,
+                                                     int groups_per_tile, uint16_t *__restrict__ xg)
 {
     extern __shared__ uint16_t xrow[];
-    const int t = blockIdx.x;
-    const uint16_t *xr = x + (int64_t)t * ldx;
+    const int tau = blockIdx.x / groups_per_tile, grp = blockIdx.x % groups_per_tile;
+    const int t0 = tau * tile + grp * rows;
+    const int nr = min(rows, min(T, tau * tile + tile) - t0);
+    if (nr <= 0)
+        return;
+    const int32_t *J = idx + (int64_t)tau * k;
+    const int K8 = (K + 7) / 8;
     if (STAGE) {
         // ldx is a multiple of 8, so the 16-byte run past K stays inside the row's pitch
-        for (int c = threadIdx.x * 8; c < K; c += 256 * 8)
-            *reinterpret_cast<uint4 *>(xrow + c) = *reinterpret_cast<const uint4 *>(xr + c);
+        const int per = (K8 + 255) / 256;
+        for (int r = 0; r < nr; ++r) {
+            const uint16_t *xr = x + (int64_t)(t0 + r) * ldx;
+            for (int q = 0; q < per; ++q) {
+                const int c = min((int)threadIdx.x + 256 * q, K8 - 1);
+                *reinterpret_cast<uint4 *>(xrow + (int64_t)r * K8 * 8 + c * 8) =
+                    *reinterpret_cast<const uint4 *>(xr + c * 8);
+            }
+        }
         __syncthreads();
     }
-    const int32_t *J = idx + (int64_t)(t / tile) * k;
-    for (int ch = threadIdx.x; ch < kpad / 8; ch += 256) {
-        uint32_t h[8];
+    const int nch = kpad / 8;
+    for (int c0 = 0; c0 < nch; c0 += 256 * GATHER_CH) {
+        int jv[GATHER_CH][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int i = ch * 8 + e;
-            h[e] = i < k ? (STAGE ? xrow[J[i]] : xr[J[i]]) : 0u;
+        for (int c = 0; c < GATHER_CH; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                jv[c][e] = J[min((c0 + (int)threadIdx.x + 256 * c) * 8 + e, k - 1)];
+        for (int r = 0; r < nr; ++r) {
+            const uint16_t *src = STAGE ? xrow + (int64_t)r * K8 * 8 : x + (int64_t)(t0 + r) * ldx;
+#pragma unroll
+            for (int c = 0; c < GATHER_CH; ++c) {
+                const int ch = c0 + (int)threadIdx.x + 256 * c;
+                if (ch >= nch)
+                    break;
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t v = src[jv[c][e]]; // clamped index: always in bounds
+                    h[e] = ch * 8 + e < k ? v : 0u;
+                }
+                uint4 o;
+                o.x = h[0] | (h[1] << 16);
+                o.y = h[2] | (h[3] << 16);
+                o.z = h[4] | (h[5] << 16);
+                o.w = h[6] | (h[7] << 16);
+                *reinterpret_cast<uint4 *>(xg + (int64_t)(t0 + r) * kpad + ch * 8) = o;
+            }
         }
-        uint4 o;
-        o.x = h[0] | (h[1] << 16);
-        o.y = h[2] | (h[3] << 16);
-        o.z = h[4] | (h[5] << 16);
-        o.w = h[6] | (h[7] << 16);
-        *reinterpret_cast<uint4 *>(xg + (int64_t)t * kpad + ch * 8) = o;
     }
+}
+
+struct GatherPlan {
+    int rows, groups_per_tile, ntiles;
+    size_t lds;
+    bool stage;
+};
+
+static GatherPlan gather_plan(int64_t T, int64_t K, int64_t tile)
+{
+    GatherPlan g;
+    const int64_t rowbytes = (K + 7) / 8 * 16;
+    g.stage = K <= GATHER_LDS_MAX_K;
+    int64_t r = g.stage ? GATHER_LDS_BUDGET / rowbytes : GATHER_MAX_ROWS;
+    r = r < 1 ? 1 : r > GATHER_MAX_ROWS ? GATHER_MAX_ROWS : r;
+    const int64_t trows = tile < T ? tile : T;
+    if (r > trows)
+        r = trows;
+    g.rows = (int)r;
+    g.groups_per_tile = (int)((trows + r - 1) / r);
+    g.ntiles = (int)((T + tile - 1) / tile);
+    g.lds = g.stage ? (size_t)(r * rowbytes) : 0;
+    return g;
 }
 
 // ============================================================================ MFMA GEMM
@@ -450,6 +510,387 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__re
         }
 }
 
+// ============================================================================ MFMA GEMM, LDS DMA
+// The same product for k steps that are whole (packed activations, or a dense
+// K that is a multiple of 64).  Workgroup tile 128 x 256, k step 64, 4 waves of
+// 64 x 128 (2 x 4 v_mfma_f32_32x32x16_bf16 per 16-deep slice), one workgroup
+// per CU (144 KiB of LDS).
+//
+// Both operands go from global memory straight into LDS (global_load_lds_dwordx4:
+// lane l's 16 bytes land at the wave's LDS base + 16 l), three k steps ahead,
+// so no registers hold tiles in flight.  The compiler drains every outstanding
+// LDS DMA before an LDS read it schedules itself, which would leave one stage
+// in flight; the fragment reads are therefore inline asm, each block of 10
+// reads interleaved with the 8 MFMAs of the previous slice and closed by its
+// own lgkmcnt(0), and the DMA waits (vmcnt) are explicit.
+//
+// LDS per stage.  A: 128 rows x 128 bytes; the 16-byte chunk c of row r sits
+// at chunk c ^ (r & 7).  B (kept W^T rows): 64 rows x 512 bytes; chunk c of
+// row q sits at chunk c ^ 2(q & 3).  Each spreads a fragment read over all
+// banks; the DMA stores a chunk anywhere in its 1 KiB by the choice of the
+// lane's source address.
+constexpr int GD_M = 128, GD_N = 256, GD_K = 64;
+constexpr int GD_A_STAGE = GD_M * GD_K * 2;            // 16 KiB
+constexpr int GD_B_STAGE = GD_K * GD_N * 2;            // 32 KiB
+constexpr int GD_B_BASE = 3 * GD_A_STAGE;              // A stages first, then B stages
+constexpr int GD_J_BASE = 3 * (GD_A_STAGE + GD_B_STAGE); // then the kept-row indices: [stage][wave][64 words]
+constexpr int GD_LDS = GD_J_BASE + 3 * 4 * 256;           // 147 KiB
+
+typedef int gd_v2i __attribute__((ext_vector_type(2)));
+typedef int gd_v4i __attribute__((ext_vector_type(4)));
+
+// One 16-deep slice: the 8 MFMAs on fragments a, b, with the next slice's
+// fragments read from LDS in between (A rows at pa + OA and + OA + 4096, B
+// halves at pb[jn] + OB and + OB + 2048).  The block waits for its own reads.
+template <int OA, int OB>
+__device__ __forceinline__ void gd_slice(f32x16_t (&c)[2][4], const bf16x8_t (&a)[2], const bf16x8_t (&b)[4],
+                                         bf16x8_t (&an)[2], gd_v2i (&bl)[4], gd_v2i (&bh)[4], uint32_t pa,
+                                         const uint32_t (&pb)[4])
+{
+    asm volatile("s_nop 1\n\t"
+                 "ds_read_b128 %[an0], %[pa] offset:%[oa0]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"
+                 "ds_read_b128 %[an1], %[pa] offset:%[oa1]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"
+                 "ds_read_b64_tr_b16 %[bl0], %[pb0] offset:%[ob0]\n\t"
+                 "ds_read_b64_tr_b16 %[bh0], %[pb0] offset:%[ob1]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c02], %[a0], %[b2], %[c02]\n\t"
+                 "ds_read_b64_tr_b16 %[bl1], %[pb1] offset:%[ob0]\n\t"
+                 "ds_read_b64_tr_b16 %[bh1], %[pb1] offset:%[ob1]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c03], %[a0], %[b3], %[c03]\n\t"
+                 "ds_read_b64_tr_b16 %[bl2], %[pb2] offset:%[ob0]\n\t"
+                 "ds_read_b64_tr_b16 %[bh2], %[pb2] offset:%[ob1]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"
+                 "ds_read_b64_tr_b16 %[bl3], %[pb3] offset:%[ob0]\n\t"
+                 "ds_read_b64_tr_b16 %[bh3], %[pb3] offset:%[ob1]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c12], %[a1], %[b2], %[c12]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c13], %[a1], %[b3], %[c13]\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : [c00] "+a"(c[0][0]), [c01] "+a"(c[0][1]), [c02] "+a"(c[0][2]), [c03] "+a"(c[0][3]),
+                   [c10] "+a"(c[1][0]), [c11] "+a"(c[1][1]), [c12] "+a"(c[1][2]), [c13] "+a"(c[1][3]),
+                   [an0] "=&v"(an[0]), [an1] "=&v"(an[1]), [bl0] "=&v"(bl[0]), [bh0] "=&v"(bh[0]),
+                   [bl1] "=&v"(bl[1]), [bh1] "=&v"(bh[1]), [bl2] "=&v"(bl[2]), [bh2] "=&v"(bh[2]),
+                   [bl3] "=&v"(bl[3]), [bh3] "=&v"(bh[3])
+                 : [a0] "v"(a[0]), [a1] "v"(a[1]), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]),
+                   [pa] "v"(pa), [pb0] "v"(pb[0]), [pb1] "v"(pb[1]), [pb2] "v"(pb[2]), [pb3] "v"(pb[3]),
+                   [oa0] "n"(OA), [oa1] "n"(OA + 4096), [ob0] "n"(OB), [ob1] "n"(OB + 2048)
+                 : "memory");
+}
+
+// gd_slice that also reads 16 kept-row indices (words 0..15 at pj, the same
+// address in every lane).
+template <int OA, int OB>
+__device__ __forceinline__ void gd_slice_j(f32x16_t (&c)[2][4], const bf16x8_t (&a)[2], const bf16x8_t (&b)[4],
+                                           bf16x8_t (&an)[2], gd_v2i (&bl)[4], gd_v2i (&bh)[4], uint32_t pa,
+                                           const uint32_t (&pb)[4], gd_v4i (&jv)[4], uint32_t pj)
+{
+    asm volatile("s_nop 1\n\t"
+                 "ds_read_b128 %[an0], %[pa] offset:%[oa0]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"
+                 "ds_read_b128 %[an1], %[pa] offset:%[oa1]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"
+                 "ds_read_b64_tr_b16 %[bl0], %[pb0] offset:%[ob0]\n\t"
+                 "ds_read_b64_tr_b16 %[bh0], %[pb0] offset:%[ob1]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c02], %[a0], %[b2], %[c02]\n\t"
+                 "ds_read_b64_tr_b16 %[bl1], %[pb1] offset:%[ob0]\n\t"
+                 "ds_read_b64_tr_b16 %[bh1], %[pb1] offset:%[ob1]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c03], %[a0], %[b3], %[c03]\n\t"
+                 "ds_read_b64_tr_b16 %[bl2], %[pb2] offset:%[ob0]\n\t"
+                 "ds_read_b64_tr_b16 %[bh2], %[pb2] offset:%[ob1]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"
+                 "ds_read_b64_tr_b16 %[bl3], %[pb3] offset:%[ob0]\n\t"
+                 "ds_read_b64_tr_b16 %[bh3], %[pb3] offset:%[ob1]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
+                 "ds_read_b128 %[j0], %[pj]\n\t"
+                 "ds_read_b128 %[j1], %[pj] offset:16\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c12], %[a1], %[b2], %[c12]\n\t"
+                 "ds_read_b128 %[j2], %[pj] offset:32\n\t"
+                 "ds_read_b128 %[j3], %[pj] offset:48\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c13], %[a1], %[b3], %[c13]\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : [c00] "+a"(c[0][0]), [c01] "+a"(c[0][1]), [c02] "+a"(c[0][2]), [c03] "+a"(c[0][3]),
+                   [c10] "+a"(c[1][0]), [c11] "+a"(c[1][1]), [c12] "+a"(c[1][2]), [c13] "+a"(c[1][3]),
+                   [an0] "=&v"(an[0]), [an1] "=&v"(an[1]), [bl0] "=&v"(bl[0]), [bh0] "=&v"(bh[0]),
+                   [bl1] "=&v"(bl[1]), [bh1] "=&v"(bh[1]), [bl2] "=&v"(bl[2]), [bh2] "=&v"(bh[2]),
+                   [bl3] "=&v"(bl[3]), [bh3] "=&v"(bh[3]), [j0] "=&v"(jv[0]), [j1] "=&v"(jv[1]),
+                   [j2] "=&v"(jv[2]), [j3] "=&v"(jv[3])
+                 : [a0] "v"(a[0]), [a1] "v"(a[1]), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]),
+                   [pa] "v"(pa), [pb0] "v"(pb[0]), [pb1] "v"(pb[1]), [pb2] "v"(pb[2]), [pb3] "v"(pb[3]),
+                   [pj] "v"(pj), [oa0] "n"(OA), [oa1] "n"(OA + 4096), [ob0] "n"(OB), [ob1] "n"(OB + 2048)
+                 : "memory");
+}
+
+// The last slice: MFMAs only.
+__device__ __forceinline__ void gd_slice_last(f32x16_t (&c)[2][4], const bf16x8_t (&a)[2], const bf16x8_t (&b)[4])
+{
+    asm volatile("s_nop 1\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c02], %[a0], %[b2], %[c02]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c03], %[a0], %[b3], %[c03]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c12], %[a1], %[b2], %[c12]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c13], %[a1], %[b3], %[c13]\n\t"
+                 "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : [c00] "+a"(c[0][0]), [c01] "+a"(c[0][1]), [c02] "+a"(c[0][2]), [c03] "+a"(c[0][3]),
+                   [c10] "+a"(c[1][0]), [c11] "+a"(c[1][1]), [c12] "+a"(c[1][2]), [c13] "+a"(c[1][3])
+                 : [a0] "v"(a[0]), [a1] "v"(a[1]), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3])
+                 : "memory");
+}
+
+// The first slice's fragments (reads only).
+template <int OA>
+__device__ __forceinline__ void gd_read(bf16x8_t (&an)[2], gd_v2i (&bl)[4], gd_v2i (&bh)[4], uint32_t pa,
+                                        const uint32_t (&pb)[4])
+{
+    asm volatile("ds_read_b128 %[an0], %[pa] offset:%[oa0]\n\t"
+                 "ds_read_b128 %[an1], %[pa] offset:%[oa1]\n\t"
+                 "ds_read_b64_tr_b16 %[bl0], %[pb0]\n\t"
+                 "ds_read_b64_tr_b16 %[bh0], %[pb0] offset:2048\n\t"
+                 "ds_read_b64_tr_b16 %[bl1], %[pb1]\n\t"
+                 "ds_read_b64_tr_b16 %[bh1], %[pb1] offset:2048\n\t"
+                 "ds_read_b64_tr_b16 %[bl2], %[pb2]\n\t"
+                 "ds_read_b64_tr_b16 %[bh2], %[pb2] offset:2048\n\t"
+                 "ds_read_b64_tr_b16 %[bl3], %[pb3]\n\t"
+                 "ds_read_b64_tr_b16 %[bh3], %[pb3] offset:2048\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : [an0] "=&v"(an[0]), [an1] "=&v"(an[1]), [bl0] "=&v"(bl[0]), [bh0] "=&v"(bh[0]),
+                   [bl1] "=&v"(bl[1]), [bh1] "=&v"(bh[1]), [bl2] "=&v"(bl[2]), [bh2] "=&v"(bh[2]),
+                   [bl3] "=&v"(bl[3]), [bh3] "=&v"(bh[3])
+                 : [pa] "v"(pa), [pb0] "v"(pb[0]), [pb1] "v"(pb[1]), [pb2] "v"(pb[2]), [pb3] "v"(pb[3]),
+                   [oa0] "n"(OA), [oa1] "n"(OA + 4096)
+                 : "memory");
+}
+
+__device__ __forceinline__ bf16x8_t gd_cat(gd_v2i lo, gd_v2i hi)
+{
+    const gd_v4i v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (n is one of the counts the pipeline below uses).
+__device__ __forceinline__ void gd_wait_vm(int n)
+{
+    switch (n) {
+    case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
+    case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+template <bool DENSE>
+__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__restrict__ A, int64_t lda, int T, int tile,
+                                                          int mblocks, int nblocks, const uint16_t *__restrict__ wt,
+                                                          int64_t ldw, int M, const int32_t *__restrict__ idx, int k,
+                                                          int ksteps, float *__restrict__ y, int64_t ldy)
+{
+    extern __shared__ __attribute__((aligned(1024))) uint8_t gd_lds[];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / WAVE);
+    // workgroup i runs on XCD i % 8: an XCD takes consecutive row blocks with all their column blocks
+    int lin = blockIdx.x;
+    if ((gridDim.x & 7) == 0)
+        lin = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int nb = lin % nblocks, rb = lin / nblocks;
+    const int tau = rb / mblocks, mm = rb % mblocks;
+    const int row0 = tau * tile + mm * GD_M;
+    const int rowend = min(T, tau * tile + tile);
+    if (row0 >= rowend)
+        return; // the tile's rows end before this block (uniform: before any barrier)
+    const int n0 = nb * GD_N;
+    const int32_t *J = DENSE ? nullptr : idx + (int64_t)tau * k;
+    const int klim = DENSE ? ksteps * GD_K : k;
+
+    // ---- DMA sources of this lane
+    // A instruction i of wave w fills rows 8(4w + i) + lane/8; lane's chunk (lane & 7) holds chunk (lane & 7) ^ (lane >> 3)
+    const uint16_t *pA[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = min(row0 + (4 * w + i) * 8 + (lane >> 3), rowend - 1);
+        pA[i] = A + (int64_t)r * lda + (((lane & 7) ^ (lane >> 3)) * 8);
+    }
+    // B instruction i of wave w fills rows q = 16w + 2i + lane/32; q & 3 = 2(i & 1) + lane/32
+    const int mlast = (M - 1) / 8 * 8;
+    int colB[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int c = (lane & 31) ^ (2 * (2 * p + (lane >> 5)));
+        colB[p] = min(n0 + 8 * c, mlast);
+    }
+    const uint32_t lbase = (uint32_t)(uintptr_t)gd_lds;
+
+    // Rows of a k step: a DMA instruction i of wave w fills rows 16w + 2i (lanes
+    // 0-31) and 16w + 2i + 1 (lanes 32-63); rr[q] is the W^T row of row 16w + q.
+    auto issue = [&](int t, int st, const int (&rr)[16]) {
+        const int kk = t * GD_K;
+        uint8_t *la = gd_lds + st * GD_A_STAGE + w * 4 * 1024;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds(pA[i] + kk, la + i * 1024, 16, 0, 0);
+        uint8_t *lb = gd_lds + GD_B_BASE + st * GD_B_STAGE + w * 8 * 1024;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = (lane >> 5) ? rr[2 * i + 1] : rr[2 * i];
+            __builtin_amdgcn_global_load_lds(wt + (int64_t)row * ldw + colB[i & 1], lb + i * 1024, 16, 0, 0);
+        }
+    };
+    auto dense_rows = [&](int t, int (&rr)[16]) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            rr[q] = min(t * GD_K + 16 * w + q, klim - 1);
+    };
+    // the kept-row indices of k step t go to LDS slot t % 3 of this wave (lane l: row 16w + l % 16)
+    auto issue_idx = [&](int t) {
+        if (!DENSE)
+            __builtin_amdgcn_global_load_lds(J + min(t * GD_K + 16 * w + (lane & 15), klim - 1),
+                                             gd_lds + GD_J_BASE + ((t % 3) * 4 + w) * 256, 4, 0, 0);
+    };
+    constexpr int PER_STEP = DENSE ? 12 : 13; // vector-memory operations issued per k step
+
+    // ---- fragment read addresses
+    const int wm = w >> 1, wn = w & 1;
+    uint32_t pa[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        pa[j] = lbase + (wm * 64 + (lane & 31)) * 128 + (((2 * j + (lane >> 5)) ^ (lane & 7)) * 16);
+    const int g = lane >> 4, i16 = lane & 15, trow = 8 * (g >> 1) + (i16 >> 2);
+    uint32_t pb[1][4];
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) {
+        const int c = (wn * 16 + jn * 4 + 2 * (g & 1) + ((i16 & 3) >> 1)) ^ (2 * (trow & 3));
+        pb[0][jn] = lbase + GD_B_BASE + trow * 512 + c * 16 + 8 * (i16 & 1);
+    }
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][jn][r] = 0.0f;
+
+    // ---- prologue: k steps 0..2 in flight; the indices of step t + 3 travel with step t
+    {
+        int jr[3] = {0, 0, 0};
+        if (!DENSE)
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+                jr[t] = J[min(t * GD_K + 16 * w + (lane & 15), klim - 1)];
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            if (t > 0 && t >= ksteps)
+                break;
+            int rr[16];
+            if (DENSE)
+                dense_rows(t, rr);
+            else
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    rr[q] = __builtin_amdgcn_readlane(jr[t], q);
+            issue(t, t, rr);
+            issue_idx(t + 3);
+        }
+    }
+    // step 0 has landed: the operations issued after it may be outstanding
+    gd_wait_vm((PER_STEP - 12) + PER_STEP * (min(ksteps, 3) - 1));
+    __builtin_amdgcn_s_barrier();
+
+    bf16x8_t a[2], b[4], an[2];
+    gd_v2i bl[4], bh[4];
+    gd_read<0>(an, bl, bh, pa[0], pb[0]);
+    auto next = [&]() {
+        a[0] = an[0];
+        a[1] = an[1];
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn)
+            b[jn] = gd_cat(bl[jn], bh[jn]);
+    };
+    next();
+    const uint32_t pj = lbase + GD_J_BASE + w * 256;
+    // The k steps that have a successor.  Stage addresses are offset at run time
+    // (a few adds per step) so that the loop body is one block of code.
+    int s = 0, st = 0;
+    for (; s + 1 < ksteps; ++s) {
+        const int sn = st == 2 ? 0 : st + 1;
+        uint32_t pl[4], pbl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pl[j] = pa[j] + st * GD_A_STAGE;
+            pbl[j] = pb[0][j] + st * GD_B_STAGE;
+        }
+        gd_slice<0, 1 * 8192>(acc, a, b, an, bl, bh, pl[1], pbl);
+        next();
+        gd_slice<0, 2 * 8192>(acc, a, b, an, bl, bh, pl[2], pbl);
+        next();
+        gd_slice<0, 3 * 8192>(acc, a, b, an, bl, bh, pl[3], pbl);
+        next();
+        // step s + 1 has landed (this wave's loads; the barrier covers the other
+        // waves'), and every wave has finished reading stage st
+        gd_wait_vm((PER_STEP - 12) + (s + 2 < ksteps ? PER_STEP : 0));
+        __builtin_amdgcn_s_barrier();
+        const uint32_t pn = pa[0] + sn * GD_A_STAGE;
+        uint32_t pbn[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            pbn[j] = pb[0][j] + sn * GD_B_STAGE;
+        gd_v4i jv[4];
+        gd_slice_j<0, 0>(acc, a, b, an, bl, bh, pn, pbn, jv, pj + st * 4 * 256);
+        next();
+        if (s + 3 < ksteps) {
+            int rr[16];
+            if (DENSE)
+                dense_rows(s + 3, rr);
+            else
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    rr[q] = jv[q >> 2][q & 3];
+            issue(s + 3, st, rr);
+            issue_idx(s + 6);
+        }
+        st = sn;
+    }
+    {
+        // the last k step
+        uint32_t pl[4], pbl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pl[j] = pa[j] + st * GD_A_STAGE;
+            pbl[j] = pb[0][j] + st * GD_B_STAGE;
+        }
+        gd_slice<0, 1 * 8192>(acc, a, b, an, bl, bh, pl[1], pbl);
+        next();
+        gd_slice<0, 2 * 8192>(acc, a, b, an, bl, bh, pl[2], pbl);
+        next();
+        gd_slice<0, 3 * 8192>(acc, a, b, an, bl, bh, pl[3], pbl);
+        next();
+        gd_slice_last(acc, a, b);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // D layout of a 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) {
+            const int col = n0 + wn * 128 + jn * 32 + (lane & 31);
+            if (col >= M)
+                continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (row < rowend)
+                    y[(int64_t)row * ldy + col] = acc[i][jn][r];
+            }
+        }
+}
+
 size_t gemm_ws_bytes(int64_t T, int64_t k)
 {
     const int64_t kpad = (k + GB_K - 1) / GB_K * GB_K;
@@ -461,24 +902,37 @@ hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const v
                        hipStream_t st)
 {
     const int64_t rows = tile < T ? tile : T;
-    const int mblocks = (int)((rows + GB_M - 1) / GB_M);
     const int64_t ntiles = (T + tile - 1) / tile;
-    dim3 grid((unsigned)((M + GB_N - 1) / GB_N), (unsigned)(ntiles * mblocks));
-    if (dense) {
+    if (dense && K % GD_K != 0) {
+        // partial last k step: the register-staged kernel zero-fills it
+        const int mblocks = (int)((rows + GB_M - 1) / GB_M);
+        dim3 grid((unsigned)((M + GB_N - 1) / GB_N), (unsigned)(ntiles * mblocks));
         gemm_kernel<true><<<grid, GEMM_THREADS, 0, st>>>((const uint16_t *)x, ldx, (int)T, (int)tile, mblocks,
                                                          (const uint16_t *)wt, ldw, (int)M, nullptr, (int)K, (int)K,
                                                          y, ldy);
         return hipGetLastError();
     }
+    const int mblocks = (int)((rows + GD_M - 1) / GD_M);
+    const int nblocks = (int)((M + GD_N - 1) / GD_N);
+    const unsigned grid = (unsigned)(ntiles * mblocks * nblocks);
+    if (dense) {
+        gemm_dma_kernel<true><<<grid, 256, GD_LDS, st>>>((const uint16_t *)x, ldx, (int)T, (int)tile, mblocks, nblocks,
+                                                         (const uint16_t *)wt, ldw, (int)M, nullptr, (int)K,
+                                                         (int)(K / GD_K), y, ldy);
+        return hipGetLastError();
+    }
     const int64_t kpad = (k + GB_K - 1) / GB_K * GB_K;
-    if (K <= GATHER_LDS_MAX_K)
-        gather_kernel<true><<<(unsigned)T, 256, (size_t)(K + 7) / 8 * 16, st>>>(
-            (const uint16_t *)x, ldx, (int)K, (int)tile, idx, (int)k, (int)kpad, (uint16_t *)xg);
+    const GatherPlan g = gather_plan(T, K, tile);
+    const unsigned ggrid = (unsigned)((int64_t)g.ntiles * g.groups_per_tile);
+    if (g.stage)
+        gather_kernel<true><<<ggrid, 256, g.lds, st>>>((const uint16_t *)x, ldx, (int)T, (int)K, (int)tile, idx, (int)k,
+                                                       (int)kpad, g.rows, g.groups_per_tile, (uint16_t *)xg);
     else
-        gather_kernel<false><<<(unsigned)T, 256, 0, st>>>((const uint16_t *)x, ldx, (int)K, (int)tile, idx, (int)k,
-                                                          (int)kpad, (uint16_t *)xg);
-    gemm_kernel<false><<<grid, GEMM_THREADS, 0, st>>>((const uint16_t *)xg, kpad, (int)T, (int)tile, mblocks,
-                                                      (const uint16_t *)wt, ldw, (int)M, idx, (int)k, (int)k, y, ldy);
+        gather_kernel<false><<<ggrid, 256, 0, st>>>((const uint16_t *)x, ldx, (int)T, (int)K, (int)tile, idx, (int)k,
+                                                    (int)kpad, g.rows, g.groups_per_tile, (uint16_t *)xg);
+    gemm_dma_kernel<false><<<grid, 256, GD_LDS, st>>>((const uint16_t *)xg, kpad, (int)T, (int)tile, mblocks, nblocks,
+                                                      (const uint16_t *)wt, ldw, (int)M, idx, (int)k,
+                                                      (int)(kpad / GD_K), y, ldy);
     return hipGetLastError();
 }
 
@@ -486,6 +940,10 @@ void linear_init()
 {
     (void)hipFuncSetAttribute((const void *)gather_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               GATHER_LDS_MAX_K * 2);
+    (void)hipFuncSetAttribute((const void *)gemm_dma_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              GD_LDS);
+    (void)hipFuncSetAttribute((const void *)gemm_dma_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              GD_LDS);
 }
 
 } // namespace rmm
