@@ -275,8 +275,8 @@ hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const v
 constexpr int GATHER_LDS_MAX_K = 32768;
 constexpr int GATHER_LDS_BUDGET = 32768;  // bytes of staged rows per workgroup (one row may exceed it)
 constexpr int GATHER_MAX_ROWS = 8;
-constexpr int GATHER_CH = 4;              // chunks per thread held in registers per pass
-template <bool STAGE>
+constexpr int GATHER_CH_MAX = 4;          // chunks per thread held in registers per pass
+template <bool STAGE, int GATHER_CH>
 __global__ __launch_bounds__(256) void gather_kernel(const uint16_t *__restrict__ x, int64_t ldx, int T, int K, int tile,
                                                      const int32_t *__restrict__ idx, int k, int kpad, int rows,
                                                      int groups_per_tile, uint16_t *__restrict__ xg)
@@ -335,15 +335,18 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t *__restrict_
 }
 
 struct GatherPlan {
-    int rows, groups_per_tile, ntiles;
+    int rows, groups_per_tile, ntiles, ch;
     size_t lds;
     bool stage;
 };
 
-static GatherPlan gather_plan(int64_t T, int64_t K, int64_t tile)
+static GatherPlan gather_plan(int64_t T, int64_t K, int64_t k, int64_t tile)
 {
     GatherPlan g;
     const int64_t rowbytes = (K + 7) / 8 * 16;
+    // chunk groups of 256 per thread: as many as the packed row needs, up to GATHER_CH_MAX per pass
+    const int64_t kpad = (k + 63) / 64 * 64, groups = (kpad / 8 + 255) / 256;
+    g.ch = groups <= 1 ? 1 : groups <= 2 ? 2 : GATHER_CH_MAX;
     g.stage = K <= GATHER_LDS_MAX_K;
     int64_t r = g.stage ? GATHER_LDS_BUDGET / rowbytes : GATHER_MAX_ROWS;
     r = r < 1 ? 1 : r > GATHER_MAX_ROWS ? GATHER_MAX_ROWS : r;
@@ -513,8 +516,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__re
 // ============================================================================ MFMA GEMM, LDS DMA
 // The same product for k steps that are whole (packed activations, or a dense
 // K that is a multiple of 64).  Workgroup tile 128 x 256, k step 64, 4 waves of
-// 64 x 128 (2 x 4 v_mfma_f32_32x32x16_bf16 per 16-deep slice), one workgroup
-// per CU (144 KiB of LDS).
+// 128 x 64 (4 x 2 v_mfma_f32_32x32x16_bf16 per 16-deep slice: the waves share
+// every A fragment and read only their own B columns, which take the slower
+// transposing LDS read), one workgroup per CU (147 KiB of LDS).
 //
 // Both operands go from global memory straight into LDS (global_load_lds_dwordx4:
 // lane l's 16 bytes land at the wave's LDS base + 16 l), three k steps ahead,
@@ -539,128 +543,103 @@ constexpr int GD_LDS = GD_J_BASE + 3 * 4 * 256;           // 147 KiB
 typedef int gd_v2i __attribute__((ext_vector_type(2)));
 typedef int gd_v4i __attribute__((ext_vector_type(4)));
 
-// One 16-deep slice: the 8 MFMAs on fragments a, b, with the next slice's
-// fragments read from LDS in between (A rows at pa + OA and + OA + 4096, B
-// halves at pb[jn] + OB and + OB + 2048).  The block waits for its own reads.
+// One 16-deep slice: the 8 MFMAs on fragments a (4 x 32 rows) and b (2 x 32
+// columns), with the next slice's fragments read from LDS in between (A rows
+// at pa + OA + 4096 i, B halves at pb[jn] + OB and + OB + 2048).  The block
+// waits for its own reads.
+#define GD_SLICE_OUTS                                                                                             \
+    [c00] "+a"(c[0][0]), [c01] "+a"(c[0][1]), [c10] "+a"(c[1][0]), [c11] "+a"(c[1][1]), [c20] "+a"(c[2][0]),     \
+        [c21] "+a"(c[2][1]), [c30] "+a"(c[3][0]), [c31] "+a"(c[3][1]), [an0] "=&v"(an[0]), [an1] "=&v"(an[1]),    \
+        [an2] "=&v"(an[2]), [an3] "=&v"(an[3]), [bl0] "=&v"(bl[0]), [bh0] "=&v"(bh[0]), [bl1] "=&v"(bl[1]),       \
+        [bh1] "=&v"(bh[1])
+#define GD_SLICE_INS                                                                                              \
+    [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [b0] "v"(b[0]), [b1] "v"(b[1]), [pa] "v"(pa), \
+        [pb0] "v"(pb[0]), [pb1] "v"(pb[1]), [oa0] "n"(OA), [oa1] "n"(OA + 4096), [oa2] "n"(OA + 8192),           \
+        [oa3] "n"(OA + 12288), [ob0] "n"(OB), [ob1] "n"(OB + 2048)
+#define GD_SLICE_BODY                                                                                             \
+    "s_nop 1\n\t"                                                                                                 \
+    "ds_read_b128 %[an0], %[pa] offset:%[oa0]\n\t"                                                                \
+    "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"                                                   \
+    "ds_read_b128 %[an1], %[pa] offset:%[oa1]\n\t"                                                                \
+    "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"                                                   \
+    "ds_read_b128 %[an2], %[pa] offset:%[oa2]\n\t"                                                                \
+    "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"                                                   \
+    "ds_read_b128 %[an3], %[pa] offset:%[oa3]\n\t"                                                                \
+    "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"                                                   \
+    "ds_read_b64_tr_b16 %[bl0], %[pb0] offset:%[ob0]\n\t"                                                         \
+    "ds_read_b64_tr_b16 %[bh0], %[pb0] offset:%[ob1]\n\t"                                                         \
+    "v_mfma_f32_32x32x16_bf16 %[c20], %[a2], %[b0], %[c20]\n\t"                                                   \
+    "ds_read_b64_tr_b16 %[bl1], %[pb1] offset:%[ob0]\n\t"                                                         \
+    "ds_read_b64_tr_b16 %[bh1], %[pb1] offset:%[ob1]\n\t"                                                         \
+    "v_mfma_f32_32x32x16_bf16 %[c21], %[a2], %[b1], %[c21]\n\t"
+
 template <int OA, int OB>
-__device__ __forceinline__ void gd_slice(f32x16_t (&c)[2][4], const bf16x8_t (&a)[2], const bf16x8_t (&b)[4],
-                                         bf16x8_t (&an)[2], gd_v2i (&bl)[4], gd_v2i (&bh)[4], uint32_t pa,
-                                         const uint32_t (&pb)[4])
+__device__ __forceinline__ void gd_slice(f32x16_t (&c)[4][2], const bf16x8_t (&a)[4], const bf16x8_t (&b)[2],
+                                         bf16x8_t (&an)[4], gd_v2i (&bl)[2], gd_v2i (&bh)[2], uint32_t pa,
+                                         const uint32_t (&pb)[2])
 {
-    asm volatile("s_nop 1\n\t"
-                 "ds_read_b128 %[an0], %[pa] offset:%[oa0]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"
-                 "ds_read_b128 %[an1], %[pa] offset:%[oa1]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"
-                 "ds_read_b64_tr_b16 %[bl0], %[pb0] offset:%[ob0]\n\t"
-                 "ds_read_b64_tr_b16 %[bh0], %[pb0] offset:%[ob1]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c02], %[a0], %[b2], %[c02]\n\t"
-                 "ds_read_b64_tr_b16 %[bl1], %[pb1] offset:%[ob0]\n\t"
-                 "ds_read_b64_tr_b16 %[bh1], %[pb1] offset:%[ob1]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c03], %[a0], %[b3], %[c03]\n\t"
-                 "ds_read_b64_tr_b16 %[bl2], %[pb2] offset:%[ob0]\n\t"
-                 "ds_read_b64_tr_b16 %[bh2], %[pb2] offset:%[ob1]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"
-                 "ds_read_b64_tr_b16 %[bl3], %[pb3] offset:%[ob0]\n\t"
-                 "ds_read_b64_tr_b16 %[bh3], %[pb3] offset:%[ob1]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c12], %[a1], %[b2], %[c12]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c13], %[a1], %[b3], %[c13]\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : [c00] "+a"(c[0][0]), [c01] "+a"(c[0][1]), [c02] "+a"(c[0][2]), [c03] "+a"(c[0][3]),
-                   [c10] "+a"(c[1][0]), [c11] "+a"(c[1][1]), [c12] "+a"(c[1][2]), [c13] "+a"(c[1][3]),
-                   [an0] "=&v"(an[0]), [an1] "=&v"(an[1]), [bl0] "=&v"(bl[0]), [bh0] "=&v"(bh[0]),
-                   [bl1] "=&v"(bl[1]), [bh1] "=&v"(bh[1]), [bl2] "=&v"(bl[2]), [bh2] "=&v"(bh[2]),
-                   [bl3] "=&v"(bl[3]), [bh3] "=&v"(bh[3])
-                 : [a0] "v"(a[0]), [a1] "v"(a[1]), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]),
-                   [pa] "v"(pa), [pb0] "v"(pb[0]), [pb1] "v"(pb[1]), [pb2] "v"(pb[2]), [pb3] "v"(pb[3]),
-                   [oa0] "n"(OA), [oa1] "n"(OA + 4096), [ob0] "n"(OB), [ob1] "n"(OB + 2048)
+    asm volatile(GD_SLICE_BODY "v_mfma_f32_32x32x16_bf16 %[c30], %[a3], %[b0], %[c30]\n\t"
+                               "v_mfma_f32_32x32x16_bf16 %[c31], %[a3], %[b1], %[c31]\n\t"
+                               "s_waitcnt lgkmcnt(0)"
+                 : GD_SLICE_OUTS
+                 : GD_SLICE_INS
                  : "memory");
 }
 
 // gd_slice that also reads 16 kept-row indices (words 0..15 at pj, the same
 // address in every lane).
 template <int OA, int OB>
-__device__ __forceinline__ void gd_slice_j(f32x16_t (&c)[2][4], const bf16x8_t (&a)[2], const bf16x8_t (&b)[4],
-                                           bf16x8_t (&an)[2], gd_v2i (&bl)[4], gd_v2i (&bh)[4], uint32_t pa,
-                                           const uint32_t (&pb)[4], gd_v4i (&jv)[4], uint32_t pj)
+__device__ __forceinline__ void gd_slice_j(f32x16_t (&c)[4][2], const bf16x8_t (&a)[4], const bf16x8_t (&b)[2],
+                                           bf16x8_t (&an)[4], gd_v2i (&bl)[2], gd_v2i (&bh)[2], uint32_t pa,
+                                           const uint32_t (&pb)[2], gd_v4i (&jv)[4], uint32_t pj)
 {
-    asm volatile("s_nop 1\n\t"
-                 "ds_read_b128 %[an0], %[pa] offset:%[oa0]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"
-                 "ds_read_b128 %[an1], %[pa] offset:%[oa1]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"
-                 "ds_read_b64_tr_b16 %[bl0], %[pb0] offset:%[ob0]\n\t"
-                 "ds_read_b64_tr_b16 %[bh0], %[pb0] offset:%[ob1]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c02], %[a0], %[b2], %[c02]\n\t"
-                 "ds_read_b64_tr_b16 %[bl1], %[pb1] offset:%[ob0]\n\t"
-                 "ds_read_b64_tr_b16 %[bh1], %[pb1] offset:%[ob1]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c03], %[a0], %[b3], %[c03]\n\t"
-                 "ds_read_b64_tr_b16 %[bl2], %[pb2] offset:%[ob0]\n\t"
-                 "ds_read_b64_tr_b16 %[bh2], %[pb2] offset:%[ob1]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"
-                 "ds_read_b64_tr_b16 %[bl3], %[pb3] offset:%[ob0]\n\t"
-                 "ds_read_b64_tr_b16 %[bh3], %[pb3] offset:%[ob1]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
-                 "ds_read_b128 %[j0], %[pj]\n\t"
-                 "ds_read_b128 %[j1], %[pj] offset:16\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c12], %[a1], %[b2], %[c12]\n\t"
-                 "ds_read_b128 %[j2], %[pj] offset:32\n\t"
-                 "ds_read_b128 %[j3], %[pj] offset:48\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c13], %[a1], %[b3], %[c13]\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : [c00] "+a"(c[0][0]), [c01] "+a"(c[0][1]), [c02] "+a"(c[0][2]), [c03] "+a"(c[0][3]),
-                   [c10] "+a"(c[1][0]), [c11] "+a"(c[1][1]), [c12] "+a"(c[1][2]), [c13] "+a"(c[1][3]),
-                   [an0] "=&v"(an[0]), [an1] "=&v"(an[1]), [bl0] "=&v"(bl[0]), [bh0] "=&v"(bh[0]),
-                   [bl1] "=&v"(bl[1]), [bh1] "=&v"(bh[1]), [bl2] "=&v"(bl[2]), [bh2] "=&v"(bh[2]),
-                   [bl3] "=&v"(bl[3]), [bh3] "=&v"(bh[3]), [j0] "=&v"(jv[0]), [j1] "=&v"(jv[1]),
-                   [j2] "=&v"(jv[2]), [j3] "=&v"(jv[3])
-                 : [a0] "v"(a[0]), [a1] "v"(a[1]), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]),
-                   [pa] "v"(pa), [pb0] "v"(pb[0]), [pb1] "v"(pb[1]), [pb2] "v"(pb[2]), [pb3] "v"(pb[3]),
-                   [pj] "v"(pj), [oa0] "n"(OA), [oa1] "n"(OA + 4096), [ob0] "n"(OB), [ob1] "n"(OB + 2048)
+    asm volatile(GD_SLICE_BODY "ds_read_b128 %[j0], %[pj]\n\t"
+                               "ds_read_b128 %[j1], %[pj] offset:16\n\t"
+                               "v_mfma_f32_32x32x16_bf16 %[c30], %[a3], %[b0], %[c30]\n\t"
+                               "ds_read_b128 %[j2], %[pj] offset:32\n\t"
+                               "ds_read_b128 %[j3], %[pj] offset:48\n\t"
+                               "v_mfma_f32_32x32x16_bf16 %[c31], %[a3], %[b1], %[c31]\n\t"
+                               "s_waitcnt lgkmcnt(0)"
+                 : GD_SLICE_OUTS, [j0] "=&v"(jv[0]), [j1] "=&v"(jv[1]), [j2] "=&v"(jv[2]), [j3] "=&v"(jv[3])
+                 : GD_SLICE_INS, [pj] "v"(pj)
                  : "memory");
 }
 
 // The last slice: MFMAs only.
-__device__ __forceinline__ void gd_slice_last(f32x16_t (&c)[2][4], const bf16x8_t (&a)[2], const bf16x8_t (&b)[4])
+__device__ __forceinline__ void gd_slice_last(f32x16_t (&c)[4][2], const bf16x8_t (&a)[4], const bf16x8_t (&b)[2])
 {
     asm volatile("s_nop 1\n\t"
                  "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"
                  "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c02], %[a0], %[b2], %[c02]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c03], %[a0], %[b3], %[c03]\n\t"
                  "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"
                  "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c12], %[a1], %[b2], %[c12]\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %[c13], %[a1], %[b3], %[c13]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c20], %[a2], %[b0], %[c20]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c21], %[a2], %[b1], %[c21]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c30], %[a3], %[b0], %[c30]\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %[c31], %[a3], %[b1], %[c31]\n\t"
                  "s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : [c00] "+a"(c[0][0]), [c01] "+a"(c[0][1]), [c02] "+a"(c[0][2]), [c03] "+a"(c[0][3]),
-                   [c10] "+a"(c[1][0]), [c11] "+a"(c[1][1]), [c12] "+a"(c[1][2]), [c13] "+a"(c[1][3])
-                 : [a0] "v"(a[0]), [a1] "v"(a[1]), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3])
+                 : [c00] "+a"(c[0][0]), [c01] "+a"(c[0][1]), [c10] "+a"(c[1][0]), [c11] "+a"(c[1][1]),
+                   [c20] "+a"(c[2][0]), [c21] "+a"(c[2][1]), [c30] "+a"(c[3][0]), [c31] "+a"(c[3][1])
+                 : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [b0] "v"(b[0]), [b1] "v"(b[1])
                  : "memory");
 }
 
 // The first slice's fragments (reads only).
-template <int OA>
-__device__ __forceinline__ void gd_read(bf16x8_t (&an)[2], gd_v2i (&bl)[4], gd_v2i (&bh)[4], uint32_t pa,
-                                        const uint32_t (&pb)[4])
+__device__ __forceinline__ void gd_read(bf16x8_t (&an)[4], gd_v2i (&bl)[2], gd_v2i (&bh)[2], uint32_t pa,
+                                        const uint32_t (&pb)[2])
 {
-    asm volatile("ds_read_b128 %[an0], %[pa] offset:%[oa0]\n\t"
-                 "ds_read_b128 %[an1], %[pa] offset:%[oa1]\n\t"
+    asm volatile("ds_read_b128 %[an0], %[pa]\n\t"
+                 "ds_read_b128 %[an1], %[pa] offset:4096\n\t"
+                 "ds_read_b128 %[an2], %[pa] offset:8192\n\t"
+                 "ds_read_b128 %[an3], %[pa] offset:12288\n\t"
                  "ds_read_b64_tr_b16 %[bl0], %[pb0]\n\t"
                  "ds_read_b64_tr_b16 %[bh0], %[pb0] offset:2048\n\t"
                  "ds_read_b64_tr_b16 %[bl1], %[pb1]\n\t"
                  "ds_read_b64_tr_b16 %[bh1], %[pb1] offset:2048\n\t"
-                 "ds_read_b64_tr_b16 %[bl2], %[pb2]\n\t"
-                 "ds_read_b64_tr_b16 %[bh2], %[pb2] offset:2048\n\t"
-                 "ds_read_b64_tr_b16 %[bl3], %[pb3]\n\t"
-                 "ds_read_b64_tr_b16 %[bh3], %[pb3] offset:2048\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : [an0] "=&v"(an[0]), [an1] "=&v"(an[1]), [bl0] "=&v"(bl[0]), [bh0] "=&v"(bh[0]),
-                   [bl1] "=&v"(bl[1]), [bh1] "=&v"(bh[1]), [bl2] "=&v"(bl[2]), [bh2] "=&v"(bh[2]),
-                   [bl3] "=&v"(bl[3]), [bh3] "=&v"(bh[3])
-                 : [pa] "v"(pa), [pb0] "v"(pb[0]), [pb1] "v"(pb[1]), [pb2] "v"(pb[2]), [pb3] "v"(pb[3]),
-                   [oa0] "n"(OA), [oa1] "n"(OA + 4096)
+                 : [an0] "=&v"(an[0]), [an1] "=&v"(an[1]), [an2] "=&v"(an[2]), [an3] "=&v"(an[3]),
+                   [bl0] "=&v"(bl[0]), [bh0] "=&v"(bh[0]), [bl1] "=&v"(bl[1]), [bh1] "=&v"(bh[1])
+                 : [pa] "v"(pa), [pb0] "v"(pb[0]), [pb1] "v"(pb[1])
                  : "memory");
 }
 
@@ -693,11 +672,16 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
     extern __shared__ __attribute__((aligned(1024))) uint8_t gd_lds[];
     const int lane = threadIdx.x & (WAVE - 1);
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / WAVE);
-    // workgroup i runs on XCD i % 8: an XCD takes consecutive row blocks with all their column blocks
+    // Workgroup i runs on XCD i % 8, which gets a contiguous run of lin.  With
+    // kept rows the run covers whole row blocks with all their column blocks
+    // (the two row blocks of a tile share its kept W^T rows, all column blocks
+    // share the activations); dense, it covers whole column blocks with all
+    // their row blocks (W^T is the larger operand, read once per XCD).
     int lin = blockIdx.x;
     if ((gridDim.x & 7) == 0)
         lin = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    const int nb = lin % nblocks, rb = lin / nblocks;
+    const int nrb = (int)(gridDim.x / nblocks);
+    const int nb = DENSE ? lin / nrb : lin % nblocks, rb = DENSE ? lin % nrb : lin / nblocks;
     const int tau = rb / mblocks, mm = rb % mblocks;
     const int row0 = tau * tile + mm * GD_M;
     const int rowend = min(T, tau * tile + tile);
@@ -753,25 +737,24 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
     };
     constexpr int PER_STEP = DENSE ? 12 : 13; // vector-memory operations issued per k step
 
-    // ---- fragment read addresses
-    const int wm = w >> 1, wn = w & 1;
+    // ---- fragment read addresses: wave w computes all 128 rows x columns 64w .. 64w + 63
     uint32_t pa[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        pa[j] = lbase + (wm * 64 + (lane & 31)) * 128 + (((2 * j + (lane >> 5)) ^ (lane & 7)) * 16);
+        pa[j] = lbase + (lane & 31) * 128 + (((2 * j + (lane >> 5)) ^ (lane & 7)) * 16);
     const int g = lane >> 4, i16 = lane & 15, trow = 8 * (g >> 1) + (i16 >> 2);
-    uint32_t pb[1][4];
+    uint32_t pb[1][2];
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-        const int c = (wn * 16 + jn * 4 + 2 * (g & 1) + ((i16 & 3) >> 1)) ^ (2 * (trow & 3));
+    for (int jn = 0; jn < 2; ++jn) {
+        const int c = (w * 8 + jn * 4 + 2 * (g & 1) + ((i16 & 3) >> 1)) ^ (2 * (trow & 3));
         pb[0][jn] = lbase + GD_B_BASE + trow * 512 + c * 16 + 8 * (i16 & 1);
     }
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn)
+        for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 acc[i][jn][r] = 0.0f;
@@ -802,14 +785,15 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
     gd_wait_vm((PER_STEP - 12) + PER_STEP * (min(ksteps, 3) - 1));
     __builtin_amdgcn_s_barrier();
 
-    bf16x8_t a[2], b[4], an[2];
-    gd_v2i bl[4], bh[4];
-    gd_read<0>(an, bl, bh, pa[0], pb[0]);
+    bf16x8_t a[4], b[2], an[4];
+    gd_v2i bl[2], bh[2];
+    gd_read(an, bl, bh, pa[0], pb[0]);
     auto next = [&]() {
-        a[0] = an[0];
-        a[1] = an[1];
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn)
+        for (int i = 0; i < 4; ++i)
+            a[i] = an[i];
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn)
             b[jn] = gd_cat(bl[jn], bh[jn]);
     };
     next();
@@ -819,12 +803,13 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
     int s = 0, st = 0;
     for (; s + 1 < ksteps; ++s) {
         const int sn = st == 2 ? 0 : st + 1;
-        uint32_t pl[4], pbl[4];
+        uint32_t pl[4], pbl[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j)
             pl[j] = pa[j] + st * GD_A_STAGE;
-            pbl[j] = pb[0][j] + st * GD_B_STAGE;
-        }
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn)
+            pbl[jn] = pb[0][jn] + st * GD_B_STAGE;
         gd_slice<0, 1 * 8192>(acc, a, b, an, bl, bh, pl[1], pbl);
         next();
         gd_slice<0, 2 * 8192>(acc, a, b, an, bl, bh, pl[2], pbl);
@@ -836,10 +821,10 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
         gd_wait_vm((PER_STEP - 12) + (s + 2 < ksteps ? PER_STEP : 0));
         __builtin_amdgcn_s_barrier();
         const uint32_t pn = pa[0] + sn * GD_A_STAGE;
-        uint32_t pbn[4];
+        uint32_t pbn[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            pbn[j] = pb[0][j] + sn * GD_B_STAGE;
+        for (int jn = 0; jn < 2; ++jn)
+            pbn[jn] = pb[0][jn] + sn * GD_B_STAGE;
         gd_v4i jv[4];
         gd_slice_j<0, 0>(acc, a, b, an, bl, bh, pn, pbn, jv, pj + st * 4 * 256);
         next();
@@ -858,12 +843,13 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
     }
     {
         // the last k step
-        uint32_t pl[4], pbl[4];
+        uint32_t pl[4], pbl[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j)
             pl[j] = pa[j] + st * GD_A_STAGE;
-            pbl[j] = pb[0][j] + st * GD_B_STAGE;
-        }
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn)
+            pbl[jn] = pb[0][jn] + st * GD_B_STAGE;
         gd_slice<0, 1 * 8192>(acc, a, b, an, bl, bh, pl[1], pbl);
         next();
         gd_slice<0, 2 * 8192>(acc, a, b, an, bl, bh, pl[2], pbl);
@@ -876,15 +862,15 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
 
     // D layout of a 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn) {
-            const int col = n0 + wn * 128 + jn * 32 + (lane & 31);
+        for (int jn = 0; jn < 2; ++jn) {
+            const int col = n0 + w * 64 + jn * 32 + (lane & 31);
             if (col >= M)
                 continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (row < rowend)
                     y[(int64_t)row * ldy + col] = acc[i][jn][r];
             }
@@ -922,14 +908,23 @@ hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const v
         return hipGetLastError();
     }
     const int64_t kpad = (k + GB_K - 1) / GB_K * GB_K;
-    const GatherPlan g = gather_plan(T, K, tile);
+    const GatherPlan g = gather_plan(T, K, k, tile);
     const unsigned ggrid = (unsigned)((int64_t)g.ntiles * g.groups_per_tile);
-    if (g.stage)
-        gather_kernel<true><<<ggrid, 256, g.lds, st>>>((const uint16_t *)x, ldx, (int)T, (int)K, (int)tile, idx, (int)k,
-                                                       (int)kpad, g.rows, g.groups_per_tile, (uint16_t *)xg);
-    else
-        gather_kernel<false><<<ggrid, 256, 0, st>>>((const uint16_t *)x, ldx, (int)T, (int)K, (int)tile, idx, (int)k,
-                                                    (int)kpad, g.rows, g.groups_per_tile, (uint16_t *)xg);
+#define RMM_GATHER(STG, CH)                                                                                          \
+    gather_kernel<STG, CH><<<ggrid, 256, STG ? g.lds : 0, st>>>((const uint16_t *)x, ldx, (int)T, (int)K, (int)tile, \
+                                                               idx, (int)k, (int)kpad, g.rows, g.groups_per_tile,   \
+                                                               (uint16_t *)xg)
+    if (g.stage) {
+        if (g.ch == 1)
+            RMM_GATHER(true, 1);
+        else if (g.ch == 2)
+            RMM_GATHER(true, 2);
+        else
+            RMM_GATHER(true, 4);
+    } else {
+        RMM_GATHER(false, 4);
+    }
+#undef RMM_GATHER
     gemm_dma_kernel<false><<<grid, 256, GD_LDS, st>>>((const uint16_t *)xg, kpad, (int)T, (int)tile, mblocks, nblocks,
                                                       (const uint16_t *)wt, ldw, (int)M, idx, (int)k,
                                                       (int)(kpad / GD_K), y, ldy);
@@ -938,7 +933,11 @@ hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const v
 
 void linear_init()
 {
-    (void)hipFuncSetAttribute((const void *)gather_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void *)gather_kernel<true, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              GATHER_LDS_MAX_K * 2);
+    (void)hipFuncSetAttribute((const void *)gather_kernel<true, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              GATHER_LDS_MAX_K * 2);
+    (void)hipFuncSetAttribute((const void *)gather_kernel<true, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               GATHER_LDS_MAX_K * 2);
     (void)hipFuncSetAttribute((const void *)gemm_dma_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               GD_LDS);
