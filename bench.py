@@ -16,7 +16,7 @@ shapes (microseconds per call), each next to the dense r = 1 kernels; the
 roofline of the dominant kernel (the reduced GEMV) measured with HIP events on
 the launch stream; and the CPU oracle timed on this host as a baseline.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--headline-only]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--headline-only] [--section S]
 """
 from __future__ import annotations
 
@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MALL_BYTES = 256 * 2**20
+SECTIONS = ("batched", "blocks", "layer", "prefill", "attention", "paged")
 
 
 def log(*a):
@@ -45,6 +46,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-sweep", action="store_true", help="headline shape only (all four r)")
     p.add_argument("--headline-only", action="store_true", help="only r = 0.5 of the decode shape (profiling)")
+    p.add_argument("--section", choices=SECTIONS,
+                   help="run only this sweep section after the headline (profiling)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibrate-copy", action="store_true",
@@ -146,6 +149,10 @@ def load_traffic(kernel: str, sha: str):
 
 def main():
     args = parse()
+
+    def want(section):
+        return not args.no_sweep and not args.headline_only and args.section in (None, section)
+
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported (multi-GPU sharding is "
               f"a design, not a build)", file=sys.stderr)
@@ -231,7 +238,7 @@ def main():
     del xs, ws_, cs_
 
     # ------------------------------------------------------------------ batched decode (per-token vs shared selection)
-    if not args.no_sweep and not args.headline_only:
+    if want("batched"):
         log("[bench] batched decode: generating inputs")
         bB = 16
         bc = W.linear_random(bB, K, M, 1, "bf16", seed=3, xsigma=1.0, wsigma=0.02)
@@ -273,7 +280,7 @@ def main():
         del wqs
 
     # ------------------------------------------------------------------ block-granular variant (blog demo shape)
-    if not args.no_sweep and not args.headline_only:
+    if want("blocks"):
         log("[bench] ffn block demo: generating inputs")
         bd = W.ffn_block_demo()
         Kb, Mb = bd.K, bd.M
@@ -312,7 +319,7 @@ def main():
         del xbs, wbs, cbs
 
     # ------------------------------------------------------------------ decode layer: QKV, o_proj, gated FFN
-    if not args.no_sweep and not args.headline_only:
+    if want("layer"):
         log("[bench] decode layer: generating inputs")
         Hh, Mi, Dq = 4096, 14336, 6144   # hidden, FFN intermediate, q+k+v outputs (32 q heads, 8 kv heads, D 128)
         fc = W.ffn_case(1, Hh, Mi, 1, seed=5)
@@ -386,7 +393,7 @@ def main():
         del L, hb, pm
 
     # ------------------------------------------------------------------ prefill (MFMA)
-    if not args.no_sweep and not args.headline_only:
+    if want("prefill"):
         log("[bench] prefill: generating inputs")
         pc = W.linear_prefill()
         T, K2, M2, tile = pc.T, pc.K, pc.M, pc.tile
@@ -427,7 +434,7 @@ def main():
         del xps, wps, cps, yp
 
     # ------------------------------------------------------------------ attention decode
-    if not args.no_sweep and not args.headline_only:
+    if want("attention"):
         for name, mk, pairs in (("attn_gqa_32k", W.attn_32k, ((0.25, 0.25), (0.5, 0.5), (1.0, 1.0))),
                                 ("attn_gqa_128k_b4", W.attn_128k, ((0.5, 0.25),))):
             log(f"[bench] {name}: generating inputs")
@@ -476,7 +483,7 @@ def main():
             del qs, ks_, vs_, kns, q0, k0, v0
 
     # ------------------------------------------------------------------ paged, ragged decode batch
-    if not args.no_sweep and not args.headline_only:
+    if want("paged"):
         lengths = [65536, 40000, 32768, 16384, 8192, 4096, 2048, 1000]
         log(f"[bench] paged ragged batch: generating inputs ({len(lengths)} sequences, {sum(lengths)} positions)")
         pc = W.attn_paged(lengths, page=256, Hq=32, Hkv=8, seed=11, n_hot=64, spare_pages=1)
