@@ -89,6 +89,23 @@ def test_ragged_and_edge_shapes(T, K, M, tile, dtype):
         run_case(cs, r)
 
 
+@pytest.mark.parametrize("k", [64, 100, 150, 250, 300])
+def test_mfma_pipeline_depths(k):
+    # the MFMA path keeps three 64-deep k steps in flight: 1, 2, 3, 4 and 5 steps exercise the
+    # prologue and tail special cases; 200 rows make a partial row block, 520 columns a partial
+    # column block
+    cs = W.linear_random(200, 320, 520, 200, "bf16", seed=k)
+    run_case(cs, k / 320)
+
+
+@pytest.mark.parametrize("K", [64, 128, 192, 256])
+def test_dense_mfma_pipeline_depths(K):
+    cs = W.linear_random(160, K, 264, 160, "bf16", seed=K)
+    y = rmm.linear_dense(dev_padded(cs.x), dev_padded(cs.wt))
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), oracle.dense_linear(cs.x, cs.wt)) <= TOL
+
+
 @pytest.mark.parametrize("K,dense", [(40000, False), (40000, True), (32776, False)])
 def test_linear_beyond_selector_k(K, dense):
     # K above the selector's limit: the index list comes from the caller (here the
