@@ -515,22 +515,26 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__re
 
 // ============================================================================ MFMA GEMM, LDS DMA
 // The same product for k steps that are whole (packed activations, or a dense
-// K that is a multiple of 64).  Workgroup tile 128 x 256, k step 64, 4 waves of
-// 128 x 64 (4 x 2 v_mfma_f32_32x32x16_bf16 per 16-deep slice: the waves share
-// every A fragment and read only their own B columns, which take the slower
-// transposing LDS read), one workgroup per CU (147 KiB of LDS).
+// K that is a multiple of 64).  Workgroup tile 128 x 256, k step 64, one
+// workgroup per CU (147 KiB of LDS), 8 waves: 4 compute waves of 128 x 64
+// (4 x 2 v_mfma_f32_32x32x16_bf16 per 16-deep slice: they share every A
+// fragment and read only their own B columns, which take the slower
+// transposing LDS read) and 4 load waves.
 //
 // Both operands go from global memory straight into LDS (global_load_lds_dwordx4:
 // lane l's 16 bytes land at the wave's LDS base + 16 l), three k steps ahead,
-// so no registers hold tiles in flight.  The compiler drains every outstanding
-// LDS DMA before an LDS read it schedules itself, which would leave one stage
-// in flight; the fragment reads are therefore inline asm, each block of 10
-// reads interleaved with the 8 MFMAs of the previous slice and closed by its
-// own lgkmcnt(0), and the DMA waits (vmcnt) are explicit.
+// so no registers hold tiles in flight; the kept-row indices of a step travel
+// the same way three steps before its rows.  The load waves issue them and wait
+// for them: a wave stalled on a full load queue leaves its SIMD to the compute
+// wave that shares it.  The compiler drains every outstanding LDS DMA before an
+// LDS read it schedules itself, so all LDS reads are inline asm: the compute
+// waves' fragment reads come in blocks of 8 interleaved with the 8 MFMAs of the
+// previous slice, each block closed by its own lgkmcnt(0); the DMA waits
+// (vmcnt) are explicit.
 //
 // LDS per stage.  A: 128 rows x 128 bytes; the 16-byte chunk c of row r sits
 // at chunk c ^ (r & 7).  B (kept W^T rows): 64 rows x 512 bytes; chunk c of
-// row q sits at chunk c ^ 2(q & 3).  Each spreads a fragment read over all
+// row q sits at chunk c ^ 4(q & 3).  Each spreads a fragment read over the
 // banks; the DMA stores a chunk anywhere in its 1 KiB by the choice of the
 // lane's source address.
 constexpr int GD_M = 128, GD_N = 256, GD_K = 64;
@@ -583,25 +587,6 @@ __device__ __forceinline__ void gd_slice(f32x16_t (&c)[4][2], const bf16x8_t (&a
                                "s_waitcnt lgkmcnt(0)"
                  : GD_SLICE_OUTS
                  : GD_SLICE_INS
-                 : "memory");
-}
-
-// gd_slice that also reads 16 kept-row indices (words 0..15 at pj, the same
-// address in every lane).
-template <int OA, int OB>
-__device__ __forceinline__ void gd_slice_j(f32x16_t (&c)[4][2], const bf16x8_t (&a)[4], const bf16x8_t (&b)[2],
-                                           bf16x8_t (&an)[4], gd_v2i (&bl)[2], gd_v2i (&bh)[2], uint32_t pa,
-                                           const uint32_t (&pb)[2], gd_v4i (&jv)[4], uint32_t pj)
-{
-    asm volatile(GD_SLICE_BODY "ds_read_b128 %[j0], %[pj]\n\t"
-                               "ds_read_b128 %[j1], %[pj] offset:16\n\t"
-                               "v_mfma_f32_32x32x16_bf16 %[c30], %[a3], %[b0], %[c30]\n\t"
-                               "ds_read_b128 %[j2], %[pj] offset:32\n\t"
-                               "ds_read_b128 %[j3], %[pj] offset:48\n\t"
-                               "v_mfma_f32_32x32x16_bf16 %[c31], %[a3], %[b1], %[c31]\n\t"
-                               "s_waitcnt lgkmcnt(0)"
-                 : GD_SLICE_OUTS, [j0] "=&v"(jv[0]), [j1] "=&v"(jv[1]), [j2] "=&v"(jv[2]), [j3] "=&v"(jv[3])
-                 : GD_SLICE_INS, [pj] "v"(pj)
                  : "memory");
 }
 
@@ -663,15 +648,37 @@ __device__ __forceinline__ void gd_wait_vm(int n)
     }
 }
 
+// The 16 kept-row indices of a k step from this wave's LDS slot (words 0..15 at
+// pj, the same address in every lane).
+__device__ __forceinline__ void gd_read_idx(gd_v4i (&jv)[4], uint32_t pj)
+{
+    asm volatile("ds_read_b128 %[j0], %[pj]\n\t"
+                 "ds_read_b128 %[j1], %[pj] offset:16\n\t"
+                 "ds_read_b128 %[j2], %[pj] offset:32\n\t"
+                 "ds_read_b128 %[j3], %[pj] offset:48\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : [j0] "=&v"(jv[0]), [j1] "=&v"(jv[1]), [j2] "=&v"(jv[2]), [j3] "=&v"(jv[3])
+                 : [pj] "v"(pj)
+                 : "memory");
+}
+
+// 8 waves: waves 0-3 compute (LDS fragment reads and MFMAs only), waves 4-7
+// issue the loads and wait for them.  A consumer and a producer share each
+// SIMD, so a producer stalled on a full load queue leaves the SIMD to the
+// consumer's MFMAs.  One barrier per k step joins the two halves: the
+// producers arrive once step s + 1 has landed, the consumers once they have
+// read all of step s; after it the consumers read step s + 1 and the producers
+// refill step s's stage with step s + 3.
 template <bool DENSE>
-__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__restrict__ A, int64_t lda, int T, int tile,
-                                                          int mblocks, int nblocks, const uint16_t *__restrict__ wt,
-                                                          int64_t ldw, int M, const int32_t *__restrict__ idx, int k,
-                                                          int ksteps, float *__restrict__ y, int64_t ldy)
+__global__ __launch_bounds__(512) void gemm_dma_kernel(const uint16_t *__restrict__ A, int64_t lda, int T, int tile,
+                                                       int mblocks, int nblocks, const uint16_t *__restrict__ wt,
+                                                       int64_t ldw, int M, const int32_t *__restrict__ idx, int k,
+                                                       int ksteps, float *__restrict__ y, int64_t ldy)
 {
     extern __shared__ __attribute__((aligned(1024))) uint8_t gd_lds[];
     const int lane = threadIdx.x & (WAVE - 1);
-    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x / WAVE);
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x / WAVE);
+    const int w = wv & 3; // index within the wave's role
     // Workgroup i runs on XCD i % 8, which gets a contiguous run of lin.  With
     // kept rows the run covers whole row blocks with all their column blocks
     // (the two row blocks of a tile share its kept W^T rows, all column blocks
@@ -688,66 +695,118 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
     if (row0 >= rowend)
         return; // the tile's rows end before this block (uniform: before any barrier)
     const int n0 = nb * GD_N;
-    const int32_t *J = DENSE ? nullptr : idx + (int64_t)tau * k;
-    const int klim = DENSE ? ksteps * GD_K : k;
-
-    // ---- DMA sources of this lane
-    // A instruction i of wave w fills rows 8(4w + i) + lane/8; lane's chunk (lane & 7) holds chunk (lane & 7) ^ (lane >> 3)
-    const uint16_t *pA[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = min(row0 + (4 * w + i) * 8 + (lane >> 3), rowend - 1);
-        pA[i] = A + (int64_t)r * lda + (((lane & 7) ^ (lane >> 3)) * 8);
-    }
-    // B instruction i of wave w fills rows q = 16w + 2i + lane/32; q & 3 = 2(i & 1) + lane/32
-    const int mlast = (M - 1) / 8 * 8;
-    int colB[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int c = (lane & 31) ^ (2 * (2 * p + (lane >> 5)));
-        colB[p] = min(n0 + 8 * c, mlast);
-    }
     const uint32_t lbase = (uint32_t)(uintptr_t)gd_lds;
 
-    // Rows of a k step: a DMA instruction i of wave w fills rows 16w + 2i (lanes
-    // 0-31) and 16w + 2i + 1 (lanes 32-63); rr[q] is the W^T row of row 16w + q.
-    auto issue = [&](int t, int st, const int (&rr)[16]) {
-        const int kk = t * GD_K;
-        uint8_t *la = gd_lds + st * GD_A_STAGE + w * 4 * 1024;
+    if (wv >= 4) {
+        // ================================================================ producer
+        const int32_t *J = DENSE ? nullptr : idx + (int64_t)tau * k;
+        const int klim = DENSE ? ksteps * GD_K : k;
+        // A instruction i of wave w fills rows 8(4w + i) + lane/8; lane's chunk (lane & 7) holds chunk (lane & 7) ^ (lane >> 3)
+        const uint16_t *pA[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(pA[i] + kk, la + i * 1024, 16, 0, 0);
-        uint8_t *lb = gd_lds + GD_B_BASE + st * GD_B_STAGE + w * 8 * 1024;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = (lane >> 5) ? rr[2 * i + 1] : rr[2 * i];
-            __builtin_amdgcn_global_load_lds(wt + (int64_t)row * ldw + colB[i & 1], lb + i * 1024, 16, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            const int r = min(row0 + (4 * w + i) * 8 + (lane >> 3), rowend - 1);
+            pA[i] = A + (int64_t)r * lda + (((lane & 7) ^ (lane >> 3)) * 8);
         }
-    };
-    auto dense_rows = [&](int t, int (&rr)[16]) {
+        // B instruction i of wave w fills rows q = 16w + 2i + lane/32; q & 3 = 2(i & 1) + lane/32
+        const int mlast = (M - 1) / 8 * 8;
+        int colB[2];
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-            rr[q] = min(t * GD_K + 16 * w + q, klim - 1);
-    };
-    // the kept-row indices of k step t go to LDS slot t % 3 of this wave (lane l: row 16w + l % 16)
-    auto issue_idx = [&](int t) {
-        if (!DENSE)
-            __builtin_amdgcn_global_load_lds(J + min(t * GD_K + 16 * w + (lane & 15), klim - 1),
-                                             gd_lds + GD_J_BASE + ((t % 3) * 4 + w) * 256, 4, 0, 0);
-    };
-    constexpr int PER_STEP = DENSE ? 12 : 13; // vector-memory operations issued per k step
+        for (int p = 0; p < 2; ++p) {
+            const int c = (lane & 31) ^ (4 * (2 * p + (lane >> 5)));
+            colB[p] = min(n0 + 8 * c, mlast);
+        }
+        // Rows of a k step: a DMA instruction i of wave w fills rows 16w + 2i (lanes
+        // 0-31) and 16w + 2i + 1 (lanes 32-63); rr[q] is the W^T row of row 16w + q.
+        auto issue = [&](int t, int st, const int (&rr)[16]) {
+            const int kk = t * GD_K;
+            uint8_t *la = gd_lds + st * GD_A_STAGE + w * 4 * 1024;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds(pA[i] + kk, la + i * 1024, 16, 0, 0);
+            uint8_t *lb = gd_lds + GD_B_BASE + st * GD_B_STAGE + w * 8 * 1024;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = (lane >> 5) ? rr[2 * i + 1] : rr[2 * i];
+                __builtin_amdgcn_global_load_lds(wt + (int64_t)row * ldw + colB[i & 1], lb + i * 1024, 16, 0, 0);
+            }
+        };
+        auto dense_rows = [&](int t, int (&rr)[16]) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                rr[q] = min(t * GD_K + 16 * w + q, klim - 1);
+        };
+        // the kept-row indices of k step t go to LDS slot t % 3 of this wave (lane l: row 16w + l % 16)
+        auto issue_idx = [&](int t) {
+            if (!DENSE)
+                __builtin_amdgcn_global_load_lds(J + min(t * GD_K + 16 * w + (lane & 15), klim - 1),
+                                                 gd_lds + GD_J_BASE + ((t % 3) * 4 + w) * 256, 4, 0, 0);
+        };
+        constexpr int PER_STEP = DENSE ? 12 : 13; // vector-memory operations issued per k step
 
-    // ---- fragment read addresses: wave w computes all 128 rows x columns 64w .. 64w + 63
+        // prologue: k steps 0..2 in flight; the indices of step t + 3 travel with step t
+        {
+            int jr[3] = {0, 0, 0};
+            if (!DENSE)
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+                    jr[t] = J[min(t * GD_K + 16 * w + (lane & 15), klim - 1)];
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                if (t > 0 && t >= ksteps)
+                    break;
+                int rr[16];
+                if (DENSE)
+                    dense_rows(t, rr);
+                else
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        rr[q] = __builtin_amdgcn_readlane(jr[t], q);
+                issue(t, t, rr);
+                issue_idx(t + 3);
+            }
+        }
+        // step 0 has landed: the operations issued after it may be outstanding
+        gd_wait_vm((PER_STEP - 12) + PER_STEP * (min(ksteps, 3) - 1));
+        __builtin_amdgcn_s_barrier();
+        const uint32_t pj = lbase + GD_J_BASE + w * 256;
+        int st = 0;
+        for (int s = 0; s + 1 < ksteps; ++s) {
+            // step s + 1 has landed (this wave's loads; the barrier covers the other producers')
+            gd_wait_vm((PER_STEP - 12) + (s + 2 < ksteps ? PER_STEP : 0));
+            __builtin_amdgcn_s_barrier();
+            if (s + 3 < ksteps) {
+                int rr[16];
+                if (DENSE) {
+                    dense_rows(s + 3, rr);
+                } else {
+                    gd_v4i jv[4];
+                    gd_read_idx(jv, pj + st * 4 * 256);
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        rr[q] = jv[q >> 2][q & 3];
+                }
+                issue(s + 3, st, rr);
+                issue_idx(s + 6);
+            }
+            st = st == 2 ? 0 : st + 1;
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // no load may land after the wave ends
+        return;
+    }
+
+    // ==================================================================== consumer
+    // fragment read addresses: wave w computes all 128 rows x columns 64w .. 64w + 63
     uint32_t pa[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         pa[j] = lbase + (lane & 31) * 128 + (((2 * j + (lane >> 5)) ^ (lane & 7)) * 16);
     const int g = lane >> 4, i16 = lane & 15, trow = 8 * (g >> 1) + (i16 >> 2);
-    uint32_t pb[1][2];
+    uint32_t pb[2];
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn) {
-        const int c = (w * 8 + jn * 4 + 2 * (g & 1) + ((i16 & 3) >> 1)) ^ (2 * (trow & 3));
-        pb[0][jn] = lbase + GD_B_BASE + trow * 512 + c * 16 + 8 * (i16 & 1);
+        const int c = (w * 8 + jn * 4 + 2 * (g & 1) + ((i16 & 3) >> 1)) ^ (4 * (trow & 3));
+        pb[jn] = lbase + GD_B_BASE + trow * 512 + c * 16 + 8 * (i16 & 1);
     }
 
     f32x16_t acc[4][2];
@@ -759,35 +818,10 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
             for (int r = 0; r < 16; ++r)
                 acc[i][jn][r] = 0.0f;
 
-    // ---- prologue: k steps 0..2 in flight; the indices of step t + 3 travel with step t
-    {
-        int jr[3] = {0, 0, 0};
-        if (!DENSE)
-#pragma unroll
-            for (int t = 0; t < 3; ++t)
-                jr[t] = J[min(t * GD_K + 16 * w + (lane & 15), klim - 1)];
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            if (t > 0 && t >= ksteps)
-                break;
-            int rr[16];
-            if (DENSE)
-                dense_rows(t, rr);
-            else
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    rr[q] = __builtin_amdgcn_readlane(jr[t], q);
-            issue(t, t, rr);
-            issue_idx(t + 3);
-        }
-    }
-    // step 0 has landed: the operations issued after it may be outstanding
-    gd_wait_vm((PER_STEP - 12) + PER_STEP * (min(ksteps, 3) - 1));
-    __builtin_amdgcn_s_barrier();
-
+    __builtin_amdgcn_s_barrier(); // step 0 has landed
     bf16x8_t a[4], b[2], an[4];
     gd_v2i bl[2], bh[2];
-    gd_read(an, bl, bh, pa[0], pb[0]);
+    gd_read(an, bl, bh, pa[0], pb);
     auto next = [&]() {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -797,7 +831,6 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
             b[jn] = gd_cat(bl[jn], bh[jn]);
     };
     next();
-    const uint32_t pj = lbase + GD_J_BASE + w * 256;
     // The k steps that have a successor.  Stage addresses are offset at run time
     // (a few adds per step) so that the loop body is one block of code.
     int s = 0, st = 0;
@@ -809,36 +842,22 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
             pl[j] = pa[j] + st * GD_A_STAGE;
 #pragma unroll
         for (int jn = 0; jn < 2; ++jn)
-            pbl[jn] = pb[0][jn] + st * GD_B_STAGE;
+            pbl[jn] = pb[jn] + st * GD_B_STAGE;
         gd_slice<0, 1 * 8192>(acc, a, b, an, bl, bh, pl[1], pbl);
         next();
         gd_slice<0, 2 * 8192>(acc, a, b, an, bl, bh, pl[2], pbl);
         next();
         gd_slice<0, 3 * 8192>(acc, a, b, an, bl, bh, pl[3], pbl);
         next();
-        // step s + 1 has landed (this wave's loads; the barrier covers the other
-        // waves'), and every wave has finished reading stage st
-        gd_wait_vm((PER_STEP - 12) + (s + 2 < ksteps ? PER_STEP : 0));
+        // all of stage st is read (the producers may refill it); step s + 1 has landed after this
         __builtin_amdgcn_s_barrier();
         const uint32_t pn = pa[0] + sn * GD_A_STAGE;
         uint32_t pbn[2];
 #pragma unroll
         for (int jn = 0; jn < 2; ++jn)
-            pbn[jn] = pb[0][jn] + sn * GD_B_STAGE;
-        gd_v4i jv[4];
-        gd_slice_j<0, 0>(acc, a, b, an, bl, bh, pn, pbn, jv, pj + st * 4 * 256);
+            pbn[jn] = pb[jn] + sn * GD_B_STAGE;
+        gd_slice<0, 0>(acc, a, b, an, bl, bh, pn, pbn);
         next();
-        if (s + 3 < ksteps) {
-            int rr[16];
-            if (DENSE)
-                dense_rows(s + 3, rr);
-            else
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    rr[q] = jv[q >> 2][q & 3];
-            issue(s + 3, st, rr);
-            issue_idx(s + 6);
-        }
         st = sn;
     }
     {
@@ -849,7 +868,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
             pl[j] = pa[j] + st * GD_A_STAGE;
 #pragma unroll
         for (int jn = 0; jn < 2; ++jn)
-            pbl[jn] = pb[0][jn] + st * GD_B_STAGE;
+            pbl[jn] = pb[jn] + st * GD_B_STAGE;
         gd_slice<0, 1 * 8192>(acc, a, b, an, bl, bh, pl[1], pbl);
         next();
         gd_slice<0, 2 * 8192>(acc, a, b, an, bl, bh, pl[2], pbl);
@@ -858,7 +877,6 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(const uint16_t *__rest
         next();
         gd_slice_last(acc, a, b);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // D layout of a 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
@@ -902,7 +920,7 @@ hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const v
     const int nblocks = (int)((M + GD_N - 1) / GD_N);
     const unsigned grid = (unsigned)(ntiles * mblocks * nblocks);
     if (dense) {
-        gemm_dma_kernel<true><<<grid, 256, GD_LDS, st>>>((const uint16_t *)x, ldx, (int)T, (int)tile, mblocks, nblocks,
+        gemm_dma_kernel<true><<<grid, 512, GD_LDS, st>>>((const uint16_t *)x, ldx, (int)T, (int)tile, mblocks, nblocks,
                                                          (const uint16_t *)wt, ldw, (int)M, nullptr, (int)K,
                                                          (int)(K / GD_K), y, ldy);
         return hipGetLastError();
@@ -925,7 +943,7 @@ hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const v
         RMM_GATHER(false, 4);
     }
 #undef RMM_GATHER
-    gemm_dma_kernel<false><<<grid, 256, GD_LDS, st>>>((const uint16_t *)xg, kpad, (int)T, (int)tile, mblocks, nblocks,
+    gemm_dma_kernel<false><<<grid, 512, GD_LDS, st>>>((const uint16_t *)xg, kpad, (int)T, (int)tile, mblocks, nblocks,
                                                       (const uint16_t *)wt, ldw, (int)M, idx, (int)k,
                                                       (int)(kpad / GD_K), y, ldy);
     return hipGetLastError();
