@@ -42,25 +42,18 @@ __global__ __launch_bounds__(COLMAX_THREADS) void colmax_kernel(const TE *__rest
     for (int e = 0; e < VEC; ++e)
         m[e] = 0.0f;
     if (col < K) {
-        int t = r0 + w;
-        // four rows in flight per wave
-        for (; t + 3 * 4 < r1; t += 16) {
-            uint4 u[4];
+        // wave w takes rows r0 + w + 4q; all of them are in flight at once (a
+        // chunk holds COLMAX_ROWS rows, so q < COLMAX_ROWS / 4).  Rows past the
+        // chunk's end repeat its last row, which leaves the maximum unchanged.
+        constexpr int NQ = COLMAX_ROWS / 4;
+        uint4 u[NQ];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                u[q] = Vec16<TE>::raw(x + (int64_t)(t + 4 * q) * ldx + col);
+        for (int q = 0; q < NQ; ++q)
+            u[q] = Vec16<TE>::raw(x + (int64_t)min(r0 + w + 4 * q, r1 - 1) * ldx + col);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float v[VEC];
-                Vec16<TE>::unpack(u[q], v);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    m[e] = fmaxf(m[e], fabsf(v[e]));
-            }
-        }
-        for (; t < r1; t += 4) {
+        for (int q = 0; q < NQ; ++q) {
             float v[VEC];
-            Vec16<TE>::unpack(Vec16<TE>::raw(x + (int64_t)t * ldx + col), v);
+            Vec16<TE>::unpack(u[q], v);
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 m[e] = fmaxf(m[e], fabsf(v[e]));
