@@ -290,7 +290,7 @@ __device__ __forceinline__ uint32_t key_bin(uint32_t kk)
 }
 
 template <int GS>
-__global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int Sp, int nqk_all,
+__global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int Sp, int nqk_all, int nsub,
                                                        const float *__restrict__ logit,
                                                        const float2 *__restrict__ pstat, double *__restrict__ lse_ws,
                                                        float *__restrict__ lse_out, const float *__restrict__ vn,
@@ -303,22 +303,28 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS;
     const int Sb = seq_len(s, m, b);
-    if (blockIdx.x * ATTN_KEY_CHUNK >= Sb)
+    // the workgroup takes nsub consecutive chunks of ATTN_KEY_CHUNK positions
+    // (long sequences: fewer workgroups, fewer statistics merges and fewer
+    // global histogram atomics)
+    const int c0 = blockIdx.x * nsub;
+    if (c0 * ATTN_KEY_CHUNK >= Sb)
         return;
     const int nqk = (Sb + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK; // this sequence's QK chunks
     for (int i = tid; i < ATTN_HIST_BINS; i += 256)
         lh[i] = 0;
     // this thread's logits are loaded first so their latency overlaps the statistics merge
-    const int sp = blockIdx.x * ATTN_KEY_CHUNK + threadIdx.x * 8;
-    f32x4_t a[GS][2];
-    if (sp < Sb) {
+    f32x4_t a[GS][2], an[GS][2];
+    auto load_logits = [&](f32x4_t (&dst)[GS][2], int sp) {
+        if (sp < Sb) {
 #pragma unroll
-        for (int hh = 0; hh < GS; ++hh) {
-            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(logit + ((int64_t)b * s.Hq + h0 + hh) * Sp + sp);
-            a[hh][0] = src[0];
-            a[hh][1] = src[1];
+            for (int hh = 0; hh < GS; ++hh) {
+                const f32x4_t *src = reinterpret_cast<const f32x4_t *>(logit + ((int64_t)b * s.Hq + h0 + hh) * Sp + sp);
+                dst[hh][0] = src[0];
+                dst[hh][1] = src[1];
+            }
         }
-    }
+    };
+    load_logits(a, c0 * ATTN_KEY_CHUNK + threadIdx.x * 8);
     // merge the per-chunk softmax statistics of the group's heads into lse (double, fixed order)
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh) {
@@ -362,7 +368,12 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int
     for (int hh = 0; hh < GS; ++hh)
         lse[hh] = lse_s[hh];
     __syncthreads();
-    if (sp < Sb) {
+    for (int sub = 0; sub < nsub; ++sub) {
+        const int sp = (c0 + sub) * ATTN_KEY_CHUNK + threadIdx.x * 8;
+        if (sp >= Sb)
+            break; // (per thread: later chunks start further on)
+        if (sub + 1 < nsub)
+            load_logits(an, sp + ATTN_KEY_CHUNK); // the next chunk's logits load while this one is keyed
         uint32_t kk[8];
         const double sc = (double)s.scale;
         // value-row norms of the 8 positions (one page or row: pitches and pages are multiples of 8)
@@ -390,6 +401,11 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int
         uint4 *dst = reinterpret_cast<uint4 *>(keys + (int64_t)grp * Sp + sp);
         dst[0] = uint4{kk[0], kk[1], kk[2], kk[3]};
         dst[1] = uint4{kk[4], kk[5], kk[6], kk[7]};
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh) {
+            a[hh][0] = an[hh][0];
+            a[hh][1] = an[hh][1];
+        }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < ATTN_HIST_BINS; i += 256)
@@ -860,6 +876,15 @@ size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base)
     return (size_t)(p - base);
 }
 
+// Key chunks per workgroup: one up to 32K positions, more for longer sequences
+// (at 128K x 4 sequences, 2048 workgroups of one chunk spent most of their time
+// in global histogram atomics).
+static int key_chunks_per_wg(int64_t S)
+{
+    const int64_t n = S / 32768;
+    return n < 1 ? 1 : n > 4 ? 4 : (int)n;
+}
+
 template <int GS>
 static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt,
                            const uint16_t *v, const float *kn, const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
@@ -874,8 +899,10 @@ static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q
     uint2 *info = reinterpret_cast<uint2 *>(align256((char *)(sel + G)));
     attn_qk_kernel<GS><<<dim3(nqk, G), QK_THREADS, 0, st>>>(s, m, Sp, q, kt, kn, ws.logit, ws.pstat, dim_idx,
                                                              ws.hist);
-    attn_key_kernel<GS><<<dim3((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK, G), 256, 0, st>>>(
-        s, m, Sp, nqk, ws.logit, ws.pstat, ws.lse, lse, vn, ws.keys, ws.hist);
+    const int nkc = (int)((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK);
+    const int nsub = key_chunks_per_wg(s.S);
+    attn_key_kernel<GS><<<dim3((nkc + nsub - 1) / nsub, G), 256, 0, st>>>(
+        s, m, Sp, nqk, nsub, ws.logit, ws.pstat, ws.lse, lse, vn, ws.keys, ws.hist);
     attn_select_kernel<<<G, 1024, 0, st>>>(s, m, Sp, P, npv, ws.keys, ws.hist, sel, info, pos_idx);
     attn_pv_kernel<GS><<<dim3(npv, G), 256, 0, st>>>(s, m, Sp, P, v, ws.logit, ws.lse, ws.keys, sel, info, pos_idx,
                                                      ws.pvpart);
