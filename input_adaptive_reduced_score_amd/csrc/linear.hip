@@ -360,19 +360,19 @@ static GatherPlan gather_plan(int64_t T, int64_t K, int64_t k, int64_t tile)
     return g;
 }
 
-// ============================================================================ MFMA GEMM
-// C[t][n] = sum_i A[t][i] * W^T[row(i)][n], A = packed kept activations
-// (or x itself when dense), row(i) = idx[tile(t)][i] (or i when dense).
-// Workgroup tile 128 x 128, k step 64, 4 waves of 64 x 64 (2 x 2 MFMA 32x32x16).
+// ============================================================================ MFMA GEMM, register-staged
+// The dense product y = x @ W^T when K is not a multiple of 64: the last k
+// step is partial and the operands are zero-filled past K on their way through
+// registers (the LDS-DMA kernel below needs whole k steps).  Workgroup tile
+// 128 x 128, k step 64, 4 waves of 64 x 64 (2 x 2 MFMA 32x32x16).
 constexpr int GB_M = 128, GB_N = 128, GB_K = 64;
 constexpr int GEMM_THREADS = 256;
 constexpr int LPITCH = GB_K + 8; // bf16 per LDS row (pad against bank conflicts)
 
-template <bool DENSE>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__restrict__ A, int64_t lda, int T,
                                                             int tile, int mblocks, const uint16_t *__restrict__ wt,
-                                                            int64_t ldw, int M, const int32_t *__restrict__ idx,
-                                                            int k, int klim, float *__restrict__ y, int64_t ldy)
+                                                            int64_t ldw, int M, int klim, float *__restrict__ y,
+                                                            int64_t ldy)
 {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][GB_M * LPITCH];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GB_N * LPITCH];
@@ -384,18 +384,16 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__re
     if (row0 >= rowend)
         return;
     const int n0 = nb * GB_N;
-    const int32_t *J = DENSE ? nullptr : idx + (int64_t)tau * k;
     const int wm = w >> 1, wn = w & 1;
 
     // A loader: 4 chunks of 8 bf16 per thread: row ar + 32p, k offset 8*ac
     const int ar = tid >> 3, ac = tid & 7;
     // B loader: lane = k row within the step, chunks w + 4p of 8 columns
     uint4 ra[4], rb[4];
-    // the W^T row index of this lane for a step, loaded one step before its rows are
+    // the W^T row of this lane for a step
     auto jrow = [&](int kk) {
-        int kr = kk + lane;
-        kr = kr < klim ? kr : klim - 1; // padded steps reuse a valid row (times zero A)
-        return DENSE ? kr : J[kr];
+        const int kr = kk + lane;
+        return kr < klim ? kr : klim - 1; // rows past K repeat the last one (times zero A)
     };
     auto load_stage = [&](int kk, int j) {
 #pragma unroll
@@ -405,7 +403,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__re
             uint4 v = {0u, 0u, 0u, 0u};
             if (row0 + r < rowend) {
                 const uint16_t *src = A + (int64_t)(row0 + r) * lda + kc;
-                if (!DENSE || kc + 8 <= klim) {
+                if (kc + 8 <= klim) {
                     v = *reinterpret_cast<const uint4 *>(src);
                 } else if (kc < klim) {
                     uint32_t h[8];
@@ -911,9 +909,8 @@ hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const v
         // partial last k step: the register-staged kernel zero-fills it
         const int mblocks = (int)((rows + GB_M - 1) / GB_M);
         dim3 grid((unsigned)((M + GB_N - 1) / GB_N), (unsigned)(ntiles * mblocks));
-        gemm_kernel<true><<<grid, GEMM_THREADS, 0, st>>>((const uint16_t *)x, ldx, (int)T, (int)tile, mblocks,
-                                                         (const uint16_t *)wt, ldw, (int)M, nullptr, (int)K, (int)K,
-                                                         y, ldy);
+        gemm_kernel<<<grid, GEMM_THREADS, 0, st>>>((const uint16_t *)x, ldx, (int)T, (int)tile, mblocks,
+                                                   (const uint16_t *)wt, ldw, (int)M, (int)K, y, ldy);
         return hipGetLastError();
     }
     const int mblocks = (int)((rows + GD_M - 1) / GD_M);
