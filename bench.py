@@ -534,7 +534,7 @@ def main():
         log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s retained ({n} steps in {el:.1f} s)")
 
     k_head = head["k"]
-    sha = src_hash(["input_adaptive_reduced_score_amd/csrc/linear.hip", "input_adaptive_reduced_score_amd/csrc/device.h",
+    sha = src_hash(["input_adaptive_reduced_score_amd/csrc/gemv.hip", "input_adaptive_reduced_score_amd/csrc/device.h",
                     "input_adaptive_reduced_score_amd/csrc/kernels.h"])
     roofline = {"kernel": "reduced decode product launch: gemv_kernel<bf16,NT=1> + split-K gemv_reduce_kernel",
                 "bound": "hbm",

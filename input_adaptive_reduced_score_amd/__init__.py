@@ -21,7 +21,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "librmm.so")
-SOURCES = ["select.hip", "linear.hip", "ffn.hip", "attn.hip", "api.hip"]
+SOURCES = ["select.hip", "gemv.hip", "linear.hip", "ffn.hip", "attn.hip", "api.hip"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

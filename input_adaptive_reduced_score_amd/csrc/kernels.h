@@ -57,11 +57,13 @@ hipError_t launch_select_blocks(const void *x, bool bf16, int64_t T, int64_t K, 
 #define SELECT_BLOCKS_MAX_NB 1024
 void select_init();
 
-// linear.hip
+// gemv.hip
 size_t gemv_ws_bytes(int64_t T, int64_t M, int64_t k, int64_t tile, bool bf16);
 hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const void *wt, int64_t ldw, int64_t M,
                        const int32_t *idx, int64_t k, int64_t tile, bool dense, float *y, int64_t ldy, float *part,
                        uint32_t *cnt, hipStream_t st);
+
+// linear.hip
 size_t gemm_ws_bytes(int64_t T, int64_t k);
 hipError_t launch_gemm(const void *x, int64_t T, int64_t K, int64_t ldx, const void *wt, int64_t ldw, int64_t M,
                        const int32_t *idx, int64_t k, int64_t tile, bool dense, float *y, int64_t ldy, void *xg,
