@@ -155,10 +155,17 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, KvMap 
     int64_t kpitch = 0;
     const int64_t koff = act ? kt_off(s, m, b, g, sp, kpitch) : 0;
 
-    // q of the group's heads, staged once (all threads) while wave 0 selects
+    // q of the group's heads, staged once (one 16-byte load per thread; q is
+    // 16-byte aligned and D = 128) while wave 0 selects
     __shared__ float qall[GS][D];
-    for (int i = tid; i < GS * D; i += QK_THREADS)
-        qall[i / D][i % D] = bf16_to_f32(qb[i]);
+    static_assert(GS * D / 8 <= QK_THREADS, "one 16-byte vector of q per thread");
+    if (tid < GS * D / 8) {
+        float v[8];
+        Vec16<uint16_t>::unpack(*reinterpret_cast<const uint4 *>(qb + tid * 8), v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            qall[(tid * 8 + e) / D][(tid * 8 + e) % D] = v[e];
+    }
     // 1. head_dim selection (wave 0): sigma_j = fl32(max_h |q_h[j]| * kn[j])
     if (w == 0) {
         uint32_t key[2];
@@ -195,11 +202,16 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, KvMap 
     if (act) {
         const uint16_t *kbase = kt + koff;
         for (int ib = i0; ib < i1; ib += QK_U) {
+            // the rows' indices first, then every load (past the wave's last
+            // dim they repeat it, unused): all loads in flight before the first wait
+            int jr[QK_U];
+#pragma unroll
+            for (int qq = 0; qq < QK_U; ++qq)
+                jr[qq] = jd[min(ib + qq, i1 - 1)];
             uint4 u[QK_U];
 #pragma unroll
             for (int qq = 0; qq < QK_U; ++qq)
-                if (ib + qq < i1)
-                    u[qq] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)jd[ib + qq] * kpitch);
+                u[qq] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)jr[qq] * kpitch);
 #pragma unroll
             for (int qq = 0; qq < QK_U; ++qq) {
                 if (ib + qq < i1) {
