@@ -186,6 +186,11 @@ def main():
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
+    def rel_l2(a, b):
+        """||a - b|| / ||b|| in double on the GPU: the quality side column (reduced against dense)."""
+        a, b = a.double(), b.double()
+        return float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
+
     sweep = []
 
     # ------------------------------------------------------------------ decode down_proj
@@ -224,9 +229,11 @@ def main():
                "step_GBps": A.decode_step_bytes(K, M, k) / t_step / 1e9,
                "gemv_GBps": A.gemv_launch_bytes(k, M) / t_gemv / 1e9}
         rec["gemv_frac_hbm"] = rec["gemv_GBps"] / A.HBM_PEAK_GBS
+        rec["rel_l2_vs_dense"] = rel_l2(rmm.linear(xs[0], ws_[0], idxb[0], 1), rmm.linear_dense(xs[0], ws_[0]))
         sweep.append(rec)
         log(f"[bench] decode r={r}: step {rec['step_us']:.2f} us ({rec['step_GBps']:.0f} GB/s), gemv "
-            f"{rec['gemv_us']:.2f} us ({rec['gemv_GBps']:.0f} GB/s), select {rec['select_us']:.2f} us")
+            f"{rec['gemv_us']:.2f} us ({rec['gemv_GBps']:.0f} GB/s), select {rec['select_us']:.2f} us, "
+            f"rel-L2 vs dense {rec['rel_l2_vs_dense']:.3f}")
         if r == 0.5:
             head = rec
     if not args.headline_only:
@@ -420,9 +427,11 @@ def main():
             rec = {"workload": "prefill", "r": r, "k": k, "step_us": t_step * 1e6, "linear_us": t_lin * 1e6,
                    "retained_flops": fl, "step_TFLOPs": fl / t_step / 1e12, "linear_TFLOPs": fl / t_lin / 1e12}
             rec["linear_frac_mfma"] = rec["linear_TFLOPs"] / A.BF16_MFMA_PEAK_TFLOPS
+            rec["rel_l2_vs_dense"] = rel_l2(rmm.linear(xps[0], wps[0], idxp[0], tile), rmm.linear_dense(xps[0], wps[0]))
             sweep.append(rec)
             log(f"[bench] prefill r={r}: step {rec['step_us']:.1f} us, linear (gather+MFMA) {rec['linear_us']:.1f} "
-                f"us = {rec['linear_TFLOPs']:.0f} TFLOP/s ({100 * rec['linear_frac_mfma']:.1f}% of bf16 peak)")
+                f"us = {rec['linear_TFLOPs']:.0f} TFLOP/s ({100 * rec['linear_frac_mfma']:.1f}% of bf16 peak), "
+                f"rel-L2 vs dense {rec['rel_l2_vs_dense']:.3f}")
         t_dense = event_avg(lambda i: rmm.linear_dense(xps[i % npc], wps[i % npc], out=yp), ps, torch)
         t_blas = eager_event_avg(lambda i: torch.matmul(xps[i % npc], wps[i % npc]), ps, torch)
         fl = A.linear_flops(T, K2, M2)
@@ -460,6 +469,8 @@ def main():
                 by = A.attn_step_bytes(B, Hq, Hkv, D, S, kd, kss)
                 rec = {"workload": name, "r_dim": rd, "r_pos": rp, "kd": kd, "ks": kss, "call_us": t * 1e6,
                        "retained_bytes": by, "GBps": by / t / 1e9, "frac_hbm": by / t / 1e9 / A.HBM_PEAK_GBS}
+                red = rmm.attn_decode(qs[0], ks_[0], vs_[0], kns[0], rd, rp, scale=ac.scale, want_idx=False)[0]
+                rec["rel_l2_vs_dense"] = rel_l2(red, rmm.attn_decode_dense(qs[0], ks_[0], vs_[0], scale=ac.scale)[0])
                 sweep.append(rec)
                 log(f"[bench] {name} r=({rd},{rp}): {rec['call_us']:.1f} us, {rec['GBps']:.0f} GB/s retained")
             if S <= 32768:
@@ -502,8 +513,12 @@ def main():
                           psteps, 2, torch)
             by = sum(A.attn_step_bytes(1, Hq, Hkv, D, n, rmm.keep_count(D, rd), rmm.keep_count(n, rp))
                      for n in lengths)
+            red = rmm.attn_decode_paged(q0, kps[0], vps[0], kn0, bt0, sl0, rd, rp, scale=pc.scale, S=S,
+                                        want_idx=False)[0]
+            dns = rmm.attn_decode_dense_paged(q0, kps[0], vps[0], bt0, sl0, scale=pc.scale, S=S)[0]
             sweep.append({"workload": "attn_paged_ragged_b8", "lengths": lengths, "page": 256, "r_dim": rd,
-                          "r_pos": rp, "call_us": t * 1e6, "retained_bytes": by, "GBps": by / t / 1e9})
+                          "r_pos": rp, "call_us": t * 1e6, "retained_bytes": by, "GBps": by / t / 1e9,
+                          "rel_l2_vs_dense": rel_l2(red, dns)})
             log(f"[bench] paged ragged batch r=({rd},{rp}): {t * 1e6:.1f} us, {by / t / 1e9:.0f} GB/s retained")
         t = time_loop(lambda i: rmm.attn_decode_dense_paged(q0, kps[i % npc], vps[i % npc], bt0, sl0, scale=pc.scale,
                                                             S=S, out=out), psteps, 2, torch)
