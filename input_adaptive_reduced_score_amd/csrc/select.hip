@@ -145,9 +145,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
                                                              const float *__restrict__ pmax, int Kp, int nrsplit,
                                                              int direct, int cvec, int k, int32_t *__restrict__ idx)
 {
-    static_assert(PER % 8 == 0, "slices per thread come in 8-slice chunks");
+    static_assert(PER == 4 || PER % 8 == 0, "slices per thread: 4, or 8-slice chunks");
     constexpr int NW = SEL_THREADS / WAVE;
-    constexpr int CH = PER / 8; // chunks per thread
+    constexpr int CH = PER / 8; // chunks per thread (PER = 4: one 4-slice run, loaded separately)
     __shared__ uint32_t hist[SEL_HIST_WORDS + WAVE];
     __shared__ uint32_t wmin[NW], wmax[NW], wgt[NW], weq[NW], wtot[NW];
     __shared__ uint2 cand[SEL_CAND_CAP];
@@ -174,40 +174,91 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const TE *__restric
 #pragma unroll
     for (int i = 0; i < PER; ++i)
         a[i] = 0.0f;
-    if (direct) {
-        const int t0 = tau * tile, t1 = min(T, t0 + tile);
-        for (int t = t0; t < t1; ++t) {
-            const TE *xr = x + (int64_t)t * ldx;
+    if constexpr (PER == 4) {
+        // four slices per thread (K <= 4096): one 8-byte (bf16) or 16-byte (fp32) run
+        if (j0 < K) {
+            if (direct) {
+                const int t0 = tau * tile, t1 = min(T, t0 + tile);
+                for (int t = t0; t < t1; ++t) {
+                    const TE *xr = x + (int64_t)t * ldx + j0;
+                    float f[4];
+                    if constexpr (sizeof(TE) == 2) {
+                        const uint2 u = *reinterpret_cast<const uint2 *>(xr);
+                        f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+                    } else {
+                        const uint4 u = *reinterpret_cast<const uint4 *>(xr);
+                        f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+                        f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+                    }
 #pragma unroll
-            for (int m = 0; m < CH; ++m) {
-                const int jc = j0 + 8 * m;
-                if (jc < K) {
-                    float f[8];
-                    load8(xr + jc, K - jc, f);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        a[8 * m + e] = fmaxf(a[8 * m + e], fabsf(f[e]));
+                    for (int e = 0; e < 4; ++e)
+                        a[e] = fmaxf(a[e], fabsf(f[e]));
+                }
+            } else {
+                const float *pm = pmax + (int64_t)tau * nrsplit * Kp + j0;
+                for (int rs = 0; rs < nrsplit; ++rs) {
+                    const uint4 u = *reinterpret_cast<const uint4 *>(pm + (int64_t)rs * Kp);
+                    a[0] = fmaxf(a[0], __uint_as_float(u.x)); a[1] = fmaxf(a[1], __uint_as_float(u.y));
+                    a[2] = fmaxf(a[2], __uint_as_float(u.z)); a[3] = fmaxf(a[3], __uint_as_float(u.w));
                 }
             }
         }
     } else {
-        const float *pm = pmax + (int64_t)tau * nrsplit * Kp;
-        for (int rs = 0; rs < nrsplit; ++rs) {
-#pragma unroll
-            for (int m = 0; m < CH; ++m) {
-                const int jc = j0 + 8 * m;
-                if (jc < K) {
-                    float f[8];
-                    load8(pm + (int64_t)rs * Kp + jc, K - jc, f);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        a[8 * m + e] = fmaxf(a[8 * m + e], f[e]);
+        if (direct) {
+            const int t0 = tau * tile, t1 = min(T, t0 + tile);
+            for (int t = t0; t < t1; ++t) {
+                const TE *xr = x + (int64_t)t * ldx;
+    #pragma unroll
+                for (int m = 0; m < CH; ++m) {
+                    const int jc = j0 + 8 * m;
+                    if (jc < K) {
+                        float f[8];
+                        load8(xr + jc, K - jc, f);
+    #pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            a[8 * m + e] = fmaxf(a[8 * m + e], fabsf(f[e]));
+                    }
+                }
+            }
+        } else {
+            const float *pm = pmax + (int64_t)tau * nrsplit * Kp;
+            for (int rs = 0; rs < nrsplit; ++rs) {
+    #pragma unroll
+                for (int m = 0; m < CH; ++m) {
+                    const int jc = j0 + 8 * m;
+                    if (jc < K) {
+                        float f[8];
+                        load8(pm + (int64_t)rs * Kp + jc, K - jc, f);
+    #pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            a[8 * m + e] = fmaxf(a[8 * m + e], f[e]);
+                    }
                 }
             }
         }
     }
     uint32_t uk[PER];
     uint32_t mn = 0xffffffffu, mx = 0u;
+    if constexpr (PER == 4) {
+        const int avail = K - j0; // <= 0 past the end
+        float cw[4];
+        if (cvec && avail >= 4) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(c + j0);
+            cw[0] = __uint_as_float(u.x); cw[1] = __uint_as_float(u.y);
+            cw[2] = __uint_as_float(u.z); cw[3] = __uint_as_float(u.w);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                cw[e] = e < avail ? c[j0 + e] : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t key = e < avail ? nonneg_key(__fmul_rn(a[e], cw[e])) : 0u;
+            uk[e] = key;
+            mn = min(mn, key == 0u ? 0xffffffffu : key);
+            mx = max(mx, key);
+        }
+    }
 #pragma unroll
     for (int m = 0; m < CH; ++m) {
         const int jc = j0 + 8 * m;
@@ -542,7 +593,7 @@ hipError_t launch_select_blocks(const void *x, bool bf16, int64_t T, int64_t K, 
 
 static int per_for(int64_t K)
 {
-    return K <= 8 * SEL_THREADS ? 8 : K <= 16 * SEL_THREADS ? 16 : 32;
+    return K <= 4 * SEL_THREADS ? 4 : K <= 8 * SEL_THREADS ? 8 : K <= 16 * SEL_THREADS ? 16 : 32;
 }
 
 static int64_t pad8(int64_t n) { return (n + 7) / 8 * 8; }
@@ -580,6 +631,9 @@ hipError_t launch_select(const void *x, bool bf16, int64_t T, int64_t K, int64_t
                 idx);                                                                                              \
     } while (0)
     switch (per_for(K)) {
+    case 4:
+        RMM_SEL_LAUNCH(4);
+        break;
     case 8:
         RMM_SEL_LAUNCH(8);
         break;
@@ -607,6 +661,8 @@ size_t select_ws_bytes(int64_t T, int64_t K, int64_t tile)
 void select_init()
 {
     const int lds = SELECT_MAX_K * 4;
+    (void)hipFuncSetAttribute((const void *)select_kernel<uint16_t, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipFuncSetAttribute((const void *)select_kernel<float, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     (void)hipFuncSetAttribute((const void *)select_kernel<uint16_t, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     (void)hipFuncSetAttribute((const void *)select_kernel<float, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     (void)hipFuncSetAttribute((const void *)select_kernel<uint16_t, 16>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
