@@ -46,8 +46,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-sweep", action="store_true", help="headline shape only (all four r)")
     p.add_argument("--headline-only", action="store_true", help="only r = 0.5 of the decode shape (profiling)")
-    p.add_argument("--section", choices=SECTIONS,
-                   help="run only this sweep section after the headline (profiling)")
+    p.add_argument("--section", choices=SECTIONS, action="append",
+                   help="run only this sweep section after the headline (profiling); may be repeated")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibrate-copy", action="store_true",
@@ -151,7 +151,7 @@ def main():
     args = parse()
 
     def want(section):
-        return not args.no_sweep and not args.headline_only and args.section in (None, section)
+        return not args.no_sweep and not args.headline_only and (args.section is None or section in args.section)
 
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported (multi-GPU sharding is "

@@ -825,24 +825,42 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, KvMap m, int 
     }
 }
 
-// out[b, h0 + hh, :] = sum over PV chunks (in order) of the chunk partials.
+// out[b, h0 + hh, :] = sum over the PV chunks of the chunk partials, in a fixed
+// order.  Workgroup = 64 consecutive outputs of one group (GS*D/64 workgroups
+// per group, so the partials are read by many CUs at once); wave w sums the
+// w-th quarter of the chunks in chunk order, then wave 0 adds the four wave
+// sums in wave order.
+constexpr int PVR_WAVES = 4;
 template <int GS>
-__global__ __launch_bounds__(256) void attn_pv_reduce_kernel(AttnShape s, int npv, const float *__restrict__ part,
-                                                             float *__restrict__ out)
+__global__ __launch_bounds__(PVR_WAVES * WAVE) void attn_pv_reduce_kernel(AttnShape s, int npv,
+                                                                         const float *__restrict__ part,
+                                                                         float *__restrict__ out)
 {
-    const int grp = blockIdx.x, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS;
-    const float *pb = part + (int64_t)grp * npv * GS * D;
-    for (int i = threadIdx.x; i < GS * D; i += 256) {
-        float vals[PV_MAX_CHUNKS];
+    constexpr int PIECES = GS * D / WAVE;
+    constexpr int MAXQ = (PV_MAX_CHUNKS + PVR_WAVES - 1) / PVR_WAVES;
+    __shared__ float red[PVR_WAVES][WAVE];
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+    const int grp = blockIdx.x / PIECES, i = (blockIdx.x % PIECES) * WAVE + lane;
+    const float *pb = part + (int64_t)grp * npv * GS * D + i;
+    const int c0 = npv * w / PVR_WAVES, c1 = npv * (w + 1) / PVR_WAVES;
+    float vals[MAXQ];
 #pragma unroll
-        for (int cc = 0; cc < PV_MAX_CHUNKS; ++cc)
-            vals[cc] = cc < npv ? pb[(int64_t)cc * GS * D + i] : 0.0f;
-        float a = 0.0f;
+    for (int q = 0; q < MAXQ; ++q)
+        vals[q] = c0 + q < c1 ? pb[(int64_t)(c0 + q) * GS * D] : 0.0f;
+    float a = 0.0f;
 #pragma unroll
-        for (int cc = 0; cc < PV_MAX_CHUNKS; ++cc)
-            a += vals[cc];
-        out[((int64_t)b * s.Hq + h0 + i / D) * D + i % D] = a;
-    }
+    for (int q = 0; q < MAXQ; ++q)
+        a += vals[q];
+    red[w][lane] = a;
+    __syncthreads();
+    if (w != 0)
+        return;
+    float sum = red[0][lane];
+#pragma unroll
+    for (int q = 1; q < PVR_WAVES; ++q)
+        sum += red[q][lane];
+    const int b = grp / s.Hsel, h0 = (grp % s.Hsel) * s.GS;
+    out[((int64_t)b * s.Hq + h0 + i / D) * D + i % D] = sum;
 }
 
 // ------------------------------------------------------------------ host side
@@ -918,7 +936,7 @@ static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q
     attn_select_kernel<<<G, 1024, 0, st>>>(s, m, Sp, P, npv, ws.keys, ws.hist, sel, info, pos_idx);
     attn_pv_kernel<GS><<<dim3(npv, G), 256, 0, st>>>(s, m, Sp, P, v, ws.logit, ws.lse, ws.keys, sel, info, pos_idx,
                                                      ws.pvpart);
-    attn_pv_reduce_kernel<GS><<<G, 256, 0, st>>>(s, npv, ws.pvpart, out);
+    attn_pv_reduce_kernel<GS><<<G * (GS * D / WAVE), PVR_WAVES * WAVE, 0, st>>>(s, npv, ws.pvpart, out);
     return hipGetLastError();
 }
 
@@ -1108,8 +1126,10 @@ __global__ __launch_bounds__(256) void attn_dense_kernel(AttnShape s, KvMap m, i
 }
 
 // Rescales every span's partial to the largest running max and sums them in
-// span order.  One workgroup per (group, head), one thread per dim; the span
-// statistics are staged in LDS and the partials are loaded DN_MAX_SPANS deep.
+// span order.  One workgroup per (group, head), one thread per dim.  The
+// partials (DN_MAX_SPANS deep) are loaded first, so they are in flight with the
+// span statistics; wave 0 holds one span per lane, finds the largest max and
+// sums the rescaled denominators with a fixed wave reduction.
 template <int G>
 __global__ __launch_bounds__(D) void attn_dense_reduce_kernel(AttnShape s, int nspan, const float *__restrict__ part,
                                                               const float2 *__restrict__ stat,
@@ -1119,33 +1139,29 @@ __global__ __launch_bounds__(D) void attn_dense_reduce_kernel(AttnShape s, int n
     __shared__ float Ms, dens;
     const int grp = blockIdx.x, hh = blockIdx.y, b = grp / s.Hkv, g = grp % s.Hkv, h0 = g * G;
     const int dd = threadIdx.x;
-    const float2 *st = stat + (int64_t)grp * nspan * G + hh;
-    const float2 mine = dd < nspan ? st[(int64_t)dd * G] : make_float2(-INFINITY, 0.0f);
-    if (dd < WAVE) {
-        // nspan <= DN_MAX_SPANS = 64: wave 0 holds one span per lane
-        const float M = wave_max(mine.x);
-        const float f = dd < nspan ? expf(mine.x - M) : 0.0f;
-        fs[dd] = f;
-        if (dd == 0)
-            Ms = M;
-    }
-    __syncthreads();
-    if (dd == 0) {
-        float den = 0.0f;
-        for (int cc = 0; cc < nspan; ++cc)
-            den += fs[cc] * st[(int64_t)cc * G].y;
-        dens = den;
-    }
     const float *pp = part + (int64_t)grp * nspan * G * D + hh * D + dd;
     float v[DN_MAX_SPANS];
 #pragma unroll
     for (int cc = 0; cc < DN_MAX_SPANS; ++cc)
         v[cc] = cc < nspan ? pp[(int64_t)cc * G * D] : 0.0f;
+    const float2 *st = stat + (int64_t)grp * nspan * G + hh;
+    if (dd < WAVE) {
+        // nspan <= DN_MAX_SPANS = 64
+        const float2 mine = dd < nspan ? st[(int64_t)dd * G] : make_float2(-INFINITY, 0.0f);
+        const float M = wave_max(mine.x);
+        const float f = dd < nspan ? expf(mine.x - M) : 0.0f;
+        fs[dd] = f;
+        const float den = wave_sum(f * mine.y);
+        if (dd == 0) {
+            Ms = M;
+            dens = den;
+        }
+    }
+    __syncthreads();
     float num = 0.0f;
 #pragma unroll
     for (int cc = 0; cc < DN_MAX_SPANS; ++cc)
         num += fs[cc] * v[cc];
-    __syncthreads();
     out[((int64_t)b * s.Hq + h0 + hh) * D + dd] = num / dens;
     if (lse_out && dd == 0)
         lse_out[(int64_t)b * s.Hq + h0 + hh] = Ms + logf(dens);
