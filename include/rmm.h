@@ -182,7 +182,8 @@ rmm_status_t rmm_gate_up(const void *x, int64_t T, int64_t H, int64_t ldx,
  *   pos_idx optional out (NULL ok), int32 [B][Hsel][k_s] ascending
  *   lse     optional out (NULL ok), fp32 [B][Hq] = log sum_s exp(l_h[s])
  *   Hsel = Hkv (PER_KV_GROUP) or Hq (PER_Q_HEAD).
- * Limits: D == 128, Hq/Hkv in {1,2,4,8}, S <= 2^24, ldk a multiple of 8.
+ * Limits: D == 128, Hq/Hkv in {1,2,4,8}, S <= 2^24, ldk a multiple of 8,
+ *   B * Hsel <= 512 and B * Hkv <= 512 (else RMM_EUNSUPPORTED).
  * Deterministic. */
 size_t rmm_attn_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,
                                       double r_dim, double r_pos, rmm_sel_mode_t mode);

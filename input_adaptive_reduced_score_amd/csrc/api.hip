@@ -250,13 +250,12 @@ static rmm_status_t linear_common(const void *x, rmm_dtype_t xt, int64_t T, int6
         return fail(RMM_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     init_once();
     char *scratch = (char *)ws + RMM_WS_HEADER_BYTES;
-    uint32_t *cnt = (uint32_t *)ws;
     const int64_t tl = dense ? T : tile;
     hipError_t e;
     if (use_mfma(T, tl, xt))
         e = rmm::launch_gemm(x, T, K, ldx, wt, ldw, M, idx, k, tl, dense, y, ldy, scratch, stream);
     else
-        e = rmm::launch_gemv(x, xt == RMM_BF16, T, ldx, wt, ldw, M, idx, k, tl, dense, y, ldy, (float *)scratch, cnt,
+        e = rmm::launch_gemv(x, xt == RMM_BF16, T, ldx, wt, ldw, M, idx, k, tl, dense, y, ldy, (float *)scratch,
                              stream);
     return launch_status(e, dense ? "linear_dense" : "linear");
 }
@@ -479,7 +478,7 @@ size_t rmm_attn_decode_dense_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, 
     const int64_t S8 = (S + 7) / 8 * 8;
     if (attn_shape(B, Hq, Hkv, D, S, S8, S8, 1.0f, 1.0, 1.0, 0, &s) != RMM_OK)
         return 0;
-    return rmm::attn_dense_ws_layout(B, Hq, S, nullptr, nullptr, nullptr, nullptr);
+    return rmm::attn_dense_ws_layout(B, Hq, S, nullptr, nullptr, nullptr);
 }
 
 rmm_status_t rmm_attn_decode_dense(const void *q, const void *kt, const void *v, int64_t B, int64_t Hq, int64_t Hkv,
@@ -494,17 +493,16 @@ rmm_status_t rmm_attn_decode_dense(const void *q, const void *kt, const void *v,
         return st;
     if (!aligned16(q) || !aligned16(kt) || !aligned16(v) || ((uintptr_t)out & 3u))
         return fail(RMM_EUNSUPPORTED, "q, kt and v must be 16-byte aligned, out 4-byte aligned");
-    const size_t need = rmm::attn_dense_ws_layout(B, Hq, S, nullptr, nullptr, nullptr, nullptr);
+    const size_t need = rmm::attn_dense_ws_layout(B, Hq, S, nullptr, nullptr, nullptr);
     if (!ws || ws_bytes < need)
         return fail(RMM_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     init_once();
     float *part;
     float2 *stat;
-    uint32_t *cnt;
-    rmm::attn_dense_ws_layout(B, Hq, S, (char *)ws, &part, &stat, &cnt);
+    rmm::attn_dense_ws_layout(B, Hq, S, (char *)ws, &part, &stat);
     const rmm::KvMap m{nullptr, nullptr, 0, 0, 1.0};
     return launch_status(rmm::launch_attn_dense(s, m, (const uint16_t *)q, (const uint16_t *)kt, (const uint16_t *)v,
-                                                out, lse, part, stat, cnt, stream),
+                                                out, lse, part, stat, stream),
                          "attn_decode_dense");
 }
 
@@ -526,16 +524,15 @@ rmm_status_t rmm_attn_decode_dense_paged(const void *q, const void *k_pages, con
         return st;
     if (!aligned16(q) || ((uintptr_t)out & 3u))
         return fail(RMM_EUNSUPPORTED, "q must be 16-byte aligned, out 4-byte aligned");
-    const size_t need = rmm::attn_dense_ws_layout(B, Hq, S, nullptr, nullptr, nullptr, nullptr);
+    const size_t need = rmm::attn_dense_ws_layout(B, Hq, S, nullptr, nullptr, nullptr);
     if (!ws || ws_bytes < need)
         return fail(RMM_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     init_once();
     float *part;
     float2 *stat;
-    uint32_t *cnt;
-    rmm::attn_dense_ws_layout(B, Hq, S, (char *)ws, &part, &stat, &cnt);
+    rmm::attn_dense_ws_layout(B, Hq, S, (char *)ws, &part, &stat);
     return launch_status(rmm::launch_attn_dense(s, m, (const uint16_t *)q, (const uint16_t *)k_pages,
-                                                (const uint16_t *)v_pages, out, lse, part, stat, cnt, stream),
+                                                (const uint16_t *)v_pages, out, lse, part, stat, stream),
                          "attn_decode_dense_paged");
 }
 

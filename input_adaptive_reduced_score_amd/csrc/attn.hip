@@ -7,19 +7,22 @@
 // dimension: head_dim for Q K^T, key positions for P V).  GEMM notes section 1:
 // scores = Q K^T, out = softmax(scores) V.
 //
-// Pipeline per (batch element, selection group), four launches on one stream:
+// Pipeline per (batch element, selection group), five launches on one stream:
 //  qk    : head_dim selection (one wave, bitwise search over ballots), then
 //          unscaled logits over the kept dims for 8 positions per lane from
-//          dim-major keys (a kept dim is one contiguous row), per-chunk
-//          softmax statistics; the last workgroup of the group merges them into
-//          lse (double) and clears the group's key histogram.
-//  keys  : position score max_h (scale*a_h[s] - lse_h) in double, stored as a
-//          fixed-point log-probability key; 4096-bin histogram of the top bits.
-//  select: one workgroup per group: threshold bin from the histogram, two
-//          radix passes over the keys, then kept/tie counts per PV chunk.
+//          dim-major keys (a kept dim is one contiguous row), and per-chunk
+//          softmax statistics (max, sum of exponentials); the first chunk's
+//          workgroup clears the group's key histogram.
+//  keys  : every workgroup merges the chunk statistics into lse (double), then
+//          scores its positions by max_h (scale*a_h[s] - lse_h), stores each as
+//          a fixed-point log-probability key and adds the top bits to a
+//          4096-bin histogram.
+//  select: one workgroup per group: threshold bin from the histogram, exact
+//          ranking of the crossing bin's keys, then kept/tie counts per PV chunk.
 //  pv    : each workgroup takes a chunk of positions, keeps the selected ones
-//          (order-preserving), streams their V rows and accumulates p*V; the
-//          last workgroup sums the chunk partials in a fixed order.
+//          (order-preserving), streams their V rows and accumulates p*V into
+//          a per-chunk partial.
+//  reduce: the chunk partials are summed in a fixed order.
 #include "device.h"
 #include "kernels.h"
 #include "radix.h"
@@ -886,7 +889,6 @@ size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base)
     pv_chunks(s.S, &P, &npv);
     char *p = base + RMM_WS_HEADER_BYTES_INTERNAL;
     AttnWs w;
-    w.cnt = (uint32_t *)base;
     w.logit = (float *)p;
     p = align256(p + (size_t)(s.B * s.Hq * Sp) * 4);
     w.pstat = (float2 *)p;
@@ -961,7 +963,7 @@ hipError_t launch_attn(const AttnShape &s, const KvMap &m, const uint16_t *q, co
 // ------------------------------------------------------------------ dense flash decode (r = 1 baseline)
 // One workgroup per (span of positions, KV head): QK over all D dims (waves
 // split the dims), online softmax over 512-position sub-chunks, P V; partial
-// (max, sum, o) per span; the last workgroup rescales and sums in a fixed order.
+// (max, sum, o) per span; a second launch rescales and sums them in a fixed order.
 constexpr int DN_SUB = 512;
 constexpr int DN_MAX_SPANS = 64;
 
@@ -1178,14 +1180,11 @@ static void dense_spans(int64_t S, int *span, int *nspan)
     *nspan = (int)((S + per - 1) / per);
 }
 
-size_t attn_dense_ws_layout(int64_t B, int64_t Hq, int64_t S, char *base, float **part, float2 **stat,
-                            uint32_t **cnt)
+size_t attn_dense_ws_layout(int64_t B, int64_t Hq, int64_t S, char *base, float **part, float2 **stat)
 {
     int span, nspan;
     dense_spans(S, &span, &nspan);
     char *p = base + RMM_WS_HEADER_BYTES_INTERNAL;
-    if (cnt)
-        *cnt = (uint32_t *)base;
     if (part)
         *part = (float *)p;
     p = align256(p + (size_t)(B * Hq * nspan * D) * 4);
@@ -1196,14 +1195,12 @@ size_t attn_dense_ws_layout(int64_t B, int64_t Hq, int64_t S, char *base, float 
 }
 
 hipError_t launch_attn_dense(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt,
-                             const uint16_t *v, float *out, float *lse, float *part, float2 *stat, uint32_t *cnt,
-                             hipStream_t st)
+                             const uint16_t *v, float *out, float *lse, float *part, float2 *stat, hipStream_t st)
 {
     int span, nspan;
     dense_spans(s.S, &span, &nspan);
     dim3 grid(nspan, (unsigned)(s.B * s.Hkv));
     const unsigned ng = (unsigned)(s.B * s.Hkv);
-    (void)cnt;
 #define RMM_DENSE_CASE(GV)                                                                                         \
     case GV:                                                                                                       \
         attn_dense_kernel<GV><<<grid, 256, 0, st>>>(s, m, span, q, kt, v, part, stat);                             \

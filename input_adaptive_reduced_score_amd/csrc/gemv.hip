@@ -246,9 +246,8 @@ static hipError_t gemv_dispatch(const GemvPlan &p, const void *x, int64_t ldx, i
 
 hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const void *wt, int64_t ldw, int64_t M,
                        const int32_t *idx, int64_t k, int64_t tile, bool dense, float *y, int64_t ldy, float *part,
-                       uint32_t *cnt, hipStream_t st)
+                       hipStream_t st)
 {
-    (void)cnt;
     GemvPlan p = gemv_plan(T, M, k, tile, bf16);
     if (bf16)
         return dense ? gemv_dispatch<uint16_t, true>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, y, ldy, st)

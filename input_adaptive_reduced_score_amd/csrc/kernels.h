@@ -43,7 +43,7 @@
 #ifndef ATTN_PV_ROWS
 #define ATTN_PV_ROWS 128 // kept positions per PV workgroup (target)
 #endif
-#define ATTN_MAX_GROUPS 512 // B * Hsel limit (two counter banks in the workspace header)
+#define ATTN_MAX_GROUPS 512 // B * Hsel and B * Hkv limit of the attention entry points (the range the tests cover)
 #define RMM_WS_HEADER_BYTES_INTERNAL 4096
 
 namespace rmm {
@@ -61,7 +61,7 @@ void select_init();
 size_t gemv_ws_bytes(int64_t T, int64_t M, int64_t k, int64_t tile, bool bf16);
 hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const void *wt, int64_t ldw, int64_t M,
                        const int32_t *idx, int64_t k, int64_t tile, bool dense, float *y, int64_t ldy, float *part,
-                       uint32_t *cnt, hipStream_t st);
+                       hipStream_t st);
 
 // linear.hip
 size_t gemm_ws_bytes(int64_t T, int64_t k);
@@ -94,7 +94,6 @@ struct AttnWs {
     uint32_t *hist;  // [B][Hsel][ATTN_HIST_BINS]
     int32_t *pos;    // [B][Hsel][ks]
     float *pvpart;   // [B][Hsel][npv][GS][D]
-    uint32_t *cnt;   // counter header
 };
 // Where the cache of sequence b keeps position p (contiguous caches, or pages
 // named by a block table) and how long each sequence is.
@@ -109,11 +108,9 @@ size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base);
 hipError_t launch_attn(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt, const uint16_t *v,
                        const float *kn, const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
                        const AttnWs &ws, hipStream_t st);
-size_t attn_dense_ws_layout(int64_t B, int64_t Hq, int64_t S, char *base, float **part, float2 **stat,
-                            uint32_t **cnt);
+size_t attn_dense_ws_layout(int64_t B, int64_t Hq, int64_t S, char *base, float **part, float2 **stat);
 hipError_t launch_attn_dense(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt,
-                             const uint16_t *v, float *out, float *lse, float *part, float2 *stat, uint32_t *cnt,
-                             hipStream_t st);
+                             const uint16_t *v, float *out, float *lse, float *part, float2 *stat, hipStream_t st);
 void attn_init();
 
 } // namespace rmm

@@ -78,6 +78,11 @@ def test_linear_and_attn_argument_errors_host_only():
     bad[12] = 0.0    # r_dim
     assert L.rmm_attn_decode(*bad) == 1
     assert L.rmm_attn_decode(*args) == 3  # no workspace
+    bad = list(args)
+    bad[4] = 65      # B * Hsel = 520 selection groups, above the 512 the entry points take
+    assert L.rmm_attn_decode(*bad) == 2
+    bad[4] = 64      # 512 groups: accepted (fails only for the missing workspace)
+    assert L.rmm_attn_decode(*bad) == 3
     # the value-norm variant: vn inserted after kn, NULL allowed, 16-byte alignment checked
     ex = args[:4] + [None] + args[4:]
     assert L.rmm_attn_decode_ex(*ex) == 3
