@@ -82,6 +82,9 @@ def test_prefill_full_size_sampled_rows():
     (100, 1000, 300, 64, "bf16"),  # MFMA path: tiles of 64 and 36 rows, ragged N
     (300, 200, 136, 128, "bf16"),  # MFMA path, k not a multiple of 64
     (64, 32768, 16, 64, "bf16"),   # maximum K of the selector
+    (13, 301, 72, 4, "f32"),       # four slices per selector thread: partial last run, rows scored in place
+    (40, 302, 72, 32, "f32"),      # the same from column maxima
+    (40, 299, 72, 32, "bf16"),
 ])
 def test_ragged_and_edge_shapes(T, K, M, tile, dtype):
     cs = W.linear_random(T, K, M, tile, dtype, seed=T + K)
