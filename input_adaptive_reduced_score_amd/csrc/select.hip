@@ -18,7 +18,7 @@ namespace rmm {
 
 constexpr int SEL_THREADS = 1024;
 constexpr uint32_t SEL_CAND_CAP = 256; // crossing-digit keys ranked directly
-constexpr uint32_t SEL_RANK_SPLIT = SEL_THREADS / SEL_CAND_CAP; // threads per candidate in the ranking
+constexpr int SEL_RANK_SPLIT = SEL_THREADS / SEL_CAND_CAP; // threads per candidate in the ranking
 constexpr int COLMAX_THREADS = 256;
 
 // Partial column maxima of |x| over row chunks of a tile.
