@@ -103,6 +103,11 @@ def test_gqa_32k_full_size(r):
     run_attn(cs, r, r, 0)
 
 
+@pytest.mark.parametrize("seed", [1, 2])
+def test_gqa_32k_other_seeds(seed):
+    run_attn(W.attn_32k(seed=seed), 0.25, 0.25, 0)
+
+
 def test_gqa_128k_batch4_full_size():
     cs = W.attn_128k()
     run_attn(cs, 0.5, 0.25, 0)

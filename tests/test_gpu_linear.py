@@ -55,6 +55,12 @@ def test_decode_down_proj_full_size(r):
     run_case(cs, r)
 
 
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_decode_down_proj_other_seeds(seed):
+    # the benchmarked shape and ratio on four more seeded draws of the same recipe
+    run_case(W.linear_decode(seed=seed), 0.5)
+
+
 @pytest.mark.parametrize("r", [0.25, 0.5])
 def test_qkv_shared_selection_full_size(r):
     # one kept set over the hidden dimension serves the Q, K and V products at once
@@ -71,6 +77,11 @@ def test_prefill_full_size_sampled_rows():
     rows = [0, 1, 255, 256, 700, 1023, 1024, 1500, 1791, 1792, 2046, 2047]
     for r in (0.5, 0.25):
         run_case(cs, r, rows=rows)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_prefill_other_seeds_sampled_rows(seed):
+    run_case(W.linear_prefill(seed=seed), 0.5, rows=[3, 300, 1100, 2040])
 
 
 @pytest.mark.parametrize("T,K,M,tile,dtype", [
