@@ -169,8 +169,10 @@ rmm_status_t rmm_gate_up(const void *x, int64_t T, int64_t H, int64_t ldx,
  *  2. logits l_h[s] = scale * sum_{j kept} q[b,h,j] * K[b,g,s,j], every s < S;
  *  3. full softmax over all S positions: p_h[s] = exp(l_h[s] - lse_h);
  *  4. key positions: pi_s = max_{h in group} p_h[s]; the k_s = rmm_keep_count(S,
- *     r_pos) best are kept (ranked by max_h (l_h[s] - lse_h) held as a fixed-point
- *     log-probability with 2^-25 resolution clamped at -128; ties: lower index);
+ *     r_pos) best are kept, ranked by the log-probability max_h (l_h[s] - lse_h)
+ *     evaluated in double and held as a 64-bit fixed-point key (steps of at most
+ *     2^-28 nat over [-1056, +1024) nats; every probability below e^-1056, which
+ *     is 0 in double, ties); ties: lower index;
  *  5. out[b,h,:] = sum_{s kept} p_h[s] * V[b,g,s,:]  -- no renormalisation.
  *   q   bf16 [B][Hq][D]
  *   kt  bf16 [B][Hkv][D][ldk]  keys stored dim-major: row j holds dim j of every position
@@ -204,9 +206,10 @@ rmm_status_t rmm_attn_decode(const void *q, const void *kt, const void *v, const
  *       vn[b,g,s] >= 0 for s < S
  *       (vn[b,g,s] = L2 norm of V[b,g,s,:], kept by the cache owner; entries
  *       s >= S are read but ignored)
- * The fixed-point key holds log(pi_s) with 2^-25 resolution over [-120, 8):
- * norms above e^8 (about 2981) saturate.  vn = NULL gives exactly
- * rmm_attn_decode's results; the workspace size is rmm_attn_decode's. */
+ * The ranking key holds log(pi_s) - 8 with the same steps and range as the
+ * unweighted key (log(pi_s) from -1048 to +1032 nats; a zero norm ranks last).
+ * vn = NULL gives exactly rmm_attn_decode's results; the workspace size is
+ * rmm_attn_decode's. */
 rmm_status_t rmm_attn_decode_ex(const void *q, const void *kt, const void *v, const float *kn,
                                 const float *vn,
                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t S,

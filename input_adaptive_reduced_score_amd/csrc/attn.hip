@@ -7,34 +7,29 @@
 // dimension: head_dim for Q K^T, key positions for P V).  GEMM notes section 1:
 // scores = Q K^T, out = softmax(scores) V.
 //
-// Pipeline per (batch element, selection group), five launches on one stream:
+// Pipeline per (batch element, selection group), four launches on one stream
+// (a fifth writes the kept-position lists when they are asked for):
 //  qk    : head_dim selection (one wave, bitwise search over ballots), then
 //          unscaled logits over the kept dims for 8 positions per lane from
 //          dim-major keys (a kept dim is one contiguous row), and per-chunk
 //          softmax statistics (max, sum of exponentials); the first chunk's
-//          workgroup clears the group's key histogram.
+//          workgroup clears the group's score histogram.
 //  keys  : every workgroup merges the chunk statistics into lse (double), then
-//          scores its positions by max_h (scale*a_h[s] - lse_h), stores each as
-//          a fixed-point log-probability key and adds the top bits to a
-//          4096-bin histogram.
-//  select: one workgroup per group: threshold bin from the histogram, exact
-//          ranking of the crossing bin's keys, then kept/tie counts per PV chunk.
-//  pv    : each workgroup takes a chunk of positions, keeps the selected ones
-//          (order-preserving), streams their V rows and accumulates p*V into
-//          a per-chunk partial.
+//          scores its positions by max_h (scale*a_h - lse_h) in double, stores
+//          each position's histogram bin and adds it to the group histogram.
+//  pv    : every workgroup resolves the group's exact threshold from the
+//          histogram and the bins (redundantly, with the same result), keeps
+//          its chunk's positions at or above it (order-preserving), streams
+//          their V rows and accumulates p*V into a per-chunk partial.
 //  reduce: the chunk partials are summed in a fixed order.
 #include "device.h"
 #include "kernels.h"
-#include "radix.h"
 
 namespace rmm {
 
 constexpr int D = ATTN_D;
 constexpr int QK_U = 16;      // kept key rows in flight per lane
 constexpr int QK_THREADS = 256; // 4 waves split the kept dims of one chunk
-constexpr int PV_SUB = 512;   // positions examined per PV pass (2 per thread)
-constexpr int PV_MAX_CHUNKS = 64;
-constexpr int PV_U = 16;      // kept V rows in flight per lane
 
 __device__ __forceinline__ float wave_max(float v)
 {
@@ -277,39 +272,95 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, KvMap 
             hist[(int64_t)grp * ATTN_HIST_BINS + i] = 0;
 }
 
+// ------------------------------------------------------------------ position scores
+// A position's selection score is L' = max over the group's heads of the
+// log-probability scale*a_h[s] - lse_h (the log of max_h p_h[s]), plus
+// log vn[s] - 8 when the score is weighted by the value-row norm (the shift puts
+// log(p * ||V_s||) of typical rows in the same window as log p).  Every kernel
+// evaluates it with this one function, in IEEE double without contraction, so a
+// position gets the same value wherever it is scored.
+template <int GS>
+__device__ __forceinline__ double pos_score(const float (&a)[GS], const double (&lse)[GS], double sc, bool has_vn,
+                                            float vnv)
+{
+#pragma clang fp contract(off)
+    double lp = sc * (double)a[0] - lse[0];
+#pragma unroll
+    for (int hh = 1; hh < GS; ++hh)
+        lp = fmax(lp, sc * (double)a[hh] - lse[hh]);
+    if (has_vn)
+        lp += log((double)vnv) - 8.0;
+    return lp;
+}
+
+// Order key of a score: floor((L' + 1056) * 2^52), clamped to 64 bits and
+// non-decreasing in L'.  Over [-1056, 1024) its step (2^-52 nat) is finer than
+// the doubles it is computed from; every score below -1056 maps to 0 (the
+// probabilities there underflow to 0 in double as well).
+constexpr uint64_t KEY_NAT = 1ull << 52;
+constexpr uint64_t KEY_M32 = 1024ull * KEY_NAT; // L' = -32
+constexpr uint64_t KEY_0 = 1056ull * KEY_NAT;   // L' = 0
+__device__ __forceinline__ uint64_t pos_key(double lp)
+{
+#pragma clang fp contract(off)
+    const double y = (lp + 1056.0) * 4503599627370496.0;
+    if (!(y > 0.0))
+        return 0ull;
+    if (y >= 18446744073709549568.0) // the largest double below 2^64
+        return ~0ull;
+    return (uint64_t)y;
+}
+
+// Histogram bin of a key (ATTN_HIST_BINS = 8192 bins, non-decreasing in the
+// key): [0, 2048) half-nat bins for L' in [-1056, -32); [2048, 6144) bins of
+// 1/128 nat for L' in [-32, 0), where the threshold of a decode softmax usually
+// lies; [6144, 8192) half-nat bins for L' >= 0, the last one open-ended.
+__device__ __forceinline__ uint32_t key_bin(uint64_t k)
+{
+    if (k < KEY_M32)
+        return (uint32_t)(k >> 51);
+    if (k < KEY_0)
+        return 2048u + (uint32_t)((k - KEY_M32) >> 45);
+    const uint64_t t = (k - KEY_0) >> 51;
+    return t < 2047u ? 6144u + (uint32_t)t : 8191u;
+}
+
+// Rank key of a position whose key lies in bin d: the key's offset inside the
+// bin cut to 39 bits (a step of at most 2^-28 nat), then the complemented
+// position in the low 24 bits.  A larger rank key comes earlier in the
+// selection order (score descending, then position ascending), no two positions
+// share one, and every rank key is below 2^63.
+__device__ __forceinline__ uint64_t rank_key(uint64_t k, uint32_t d, int pos)
+{
+    uint64_t base;
+    int sh;
+    if (d < 2048u) {
+        base = (uint64_t)d << 51;
+        sh = 12;
+    } else if (d < 6144u) {
+        base = KEY_M32 + ((uint64_t)(d - 2048u) << 45);
+        sh = 6;
+    } else if (d < 8191u) {
+        base = KEY_0 + ((uint64_t)(d - 6144u) << 51);
+        sh = 12;
+    } else {
+        base = KEY_0 + (2047ull << 51);
+        sh = 24;
+    }
+    return (((k - base) >> sh) << 24) | (uint64_t)(0xffffffu - (uint32_t)pos);
+}
+
 // ------------------------------------------------------------------ keys
-// Position key: max over the group's heads of the log-probability
-// scale*a_h[s] - lse_h (double), plus log ||V_s|| when the score is weighted by
-// the value-row norm, as fixed point floor((L + off) * 2^25), clamped to 32 bits.
-// off = 128 covers L in [-128, 0) (plain probabilities); off = 120 covers
-// [-120, 8) (probability times a norm below e^8).
-__device__ __forceinline__ uint32_t logprob_key(double L, double off)
-{
-    const double t = (L + off) * 33554432.0;
-    if (!(t > 0.0))
-        return 0u;
-    if (t >= 4294967295.0)
-        return 0xffffffffu;
-    return (uint32_t)t;
-}
-
-// Histogram bin of a position key: 4096 bins of 1/128 nat over (L + off) in
-// [96, 128), i.e. log-probabilities in [-32, 0) (or [-24, 8) with value norms);
-// every key below that window falls into bin 0.  Bin d >= 1 holds exactly the
-// keys with kk >> 18 == d + KEY_BIN_BASE.
-constexpr uint32_t KEY_BIN_BASE = 96u << 7; // (96 * 2^25) >> 18
-__device__ __forceinline__ uint32_t key_bin(uint32_t kk)
-{
-    const uint32_t t = kk >> 18;
-    return t > KEY_BIN_BASE ? t - KEY_BIN_BASE : 0u;
-}
-
+// Every workgroup merges the group's chunk statistics into lse (double, fixed
+// order), scores its positions, stores each position's histogram bin (2 bytes)
+// and adds the bins to the group's histogram (LDS, then global atomics; the QK
+// kernel cleared it).
 template <int GS>
 __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int Sp, int nqk_all, int nsub,
                                                        const float *__restrict__ logit,
                                                        const float2 *__restrict__ pstat, double *__restrict__ lse_ws,
                                                        float *__restrict__ lse_out, const float *__restrict__ vn,
-                                                       uint32_t *__restrict__ keys, uint32_t *__restrict__ hist)
+                                                       uint16_t *__restrict__ bins, uint32_t *__restrict__ hist)
 {
     __shared__ uint32_t lh[ATTN_HIST_BINS];
     __shared__ float smax[GS][4];
@@ -382,40 +433,37 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh)
         lse[hh] = lse_s[hh];
-    __syncthreads();
+    const double sc = (double)s.scale;
     for (int sub = 0; sub < nsub; ++sub) {
         const int sp = (c0 + sub) * ATTN_KEY_CHUNK + threadIdx.x * 8;
         if (sp >= Sb)
             break; // (per thread: later chunks start further on)
         if (sub + 1 < nsub)
-            load_logits(an, sp + ATTN_KEY_CHUNK); // the next chunk's logits load while this one is keyed
-        uint32_t kk[8];
-        const double sc = (double)s.scale;
+            load_logits(an, sp + ATTN_KEY_CHUNK); // the next chunk's logits load while this one is scored
         // value-row norms of the 8 positions (one page or row: pitches and pages are multiples of 8)
         f32x4_t nv[2] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};
-        const double off = vn ? 120.0 : 128.0;
         if (vn) {
             const f32x4_t *src = reinterpret_cast<const f32x4_t *>(vn + kv_row(s, m, b, h0 / s.G, sp));
             nv[0] = src[0];
             nv[1] = src[1];
         }
+        uint32_t bn[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            double lp = sc * (double)a[0][e >> 2][e & 3] - lse[0];
+            float av[GS];
 #pragma unroll
-            for (int hh = 1; hh < GS; ++hh)
-                lp = fmax(lp, sc * (double)a[hh][e >> 2][e & 3] - lse[hh]);
-            if (vn)
-                lp += log((double)nv[e >> 2][e & 3]);
-            kk[e] = logprob_key(lp, off);
-            if (sp + e < Sb)
-                atomicAdd(&lh[key_bin(kk[e])], 1u);
-            else
-                kk[e] = 0u; // past the sequence's end: the lowest key, in no bin above 0
+            for (int hh = 0; hh < GS; ++hh)
+                av[hh] = a[hh][e >> 2][e & 3];
+            const uint32_t bb = key_bin(pos_key(pos_score<GS>(av, lse, sc, vn != nullptr, nv[e >> 2][e & 3])));
+            if (sp + e < Sb) {
+                atomicAdd(&lh[bb], 1u);
+                bn[e] = bb;
+            } else {
+                bn[e] = 0u; // past the sequence's end: never read as a position
+            }
         }
-        uint4 *dst = reinterpret_cast<uint4 *>(keys + (int64_t)grp * Sp + sp);
-        dst[0] = uint4{kk[0], kk[1], kk[2], kk[3]};
-        dst[1] = uint4{kk[4], kk[5], kk[6], kk[7]};
+        *reinterpret_cast<uint4 *>(bins + (int64_t)grp * Sp + sp) =
+            make_uint4(bn[0] | bn[1] << 16, bn[2] | bn[3] << 16, bn[4] | bn[5] << 16, bn[6] | bn[7] << 16);
 #pragma unroll
         for (int hh = 0; hh < GS; ++hh) {
             a[hh][0] = an[hh][0];
@@ -428,283 +476,158 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int
             atomicAdd(&hist[(int64_t)grp * ATTN_HIST_BINS + i], lh[i]);
 }
 
-// ------------------------------------------------------------------ select
-// Threshold key thr and tie quota of the group, then per PV chunk c (P
-// positions): info[c] = (kept before the chunk, ties at thr before the chunk).
-// Fast path: the 4096-bin histogram (1/128 nat per bin, key_bin) names the bin
-// d holding the k-th key; one pass over the keys counts, per chunk, the keys in
-// higher bins and gathers the bin's keys (candidates) into LDS.  Up to
-// SEL_RANK_MAX candidates are ranked exactly (key descending, position
-// ascending); up to CAND_CAP the last 18 key bits are resolved by two radix
-// passes over the candidates (ranking costs O(n^2) LDS reads); beyond that the
-// radix passes and a counting pass run over all keys, over all 32 bits when the
-// k-th key lies below the histogram's window (bin 0).
-struct SelInfo {
-    uint32_t thr, quota;
-};
-constexpr int CAND_CAP = 8192;
-constexpr int SEL_RANK_MAX = 256;
-constexpr int SEL_KB = 8; // 16-byte key loads in flight per thread
+// ------------------------------------------------------------------ position selection helpers
+constexpr int PV_THREADS = 512;
+constexpr int PV_WAVES = PV_THREADS / WAVE;
+constexpr int PV_PASS = 2 * PV_THREADS; // positions per PV pass (2 per thread)
+constexpr int PV_MAX_CHUNKS = 64;
+constexpr int PV_U = 16;                // kept V rows in flight per lane
+constexpr int SEL_CAP = 2048;           // candidates of the threshold bin ranked in LDS
+constexpr int SEL_FEW = 64;             // a radix digit with at most this many keys is ranked by one wave
 
-__global__ __launch_bounds__(1024) void attn_select_kernel(AttnShape s, KvMap m, int Sp, int P, int npv,
-                                                           const uint32_t *__restrict__ keys,
-                                                           const uint32_t *__restrict__ hist, SelInfo *__restrict__ sel,
-                                                           uint2 *__restrict__ info, int32_t *__restrict__ pos_out)
+// The krem-th largest (1-based) of a set of distinct keys below 2^63, which
+// each_key(f) visits (every thread calls f(key) for its share of the set): 8-bit
+// radix digits from the top; once the crossing digit holds at most SEL_FEW keys
+// they are gathered and wave 0 ranks them.  Every thread of the block calls it.
+struct RadixLds {
+    uint32_t h[256];
+    uint32_t tmp[64];
+    uint64_t few[SEL_FEW];
+    uint32_t nfew;
+    uint32_t res[3];
+    uint64_t found;
+};
+template <typename EachKey>
+__device__ uint64_t radix_select_u64(EachKey each_key, uint32_t krem, RadixLds &R)
 {
-    __shared__ uint32_t h2[SEL_BINS];
-    __shared__ uint32_t tmp[64];
-    __shared__ uint32_t cgt[PV_MAX_CHUNKS], ceq[PV_MAX_CHUNKS];
-    __shared__ uint32_t ckey[CAND_CAP];
-    __shared__ int cpos[CAND_CAP];
-    __shared__ uint32_t rk_above[1024]; // one slot per thread: (part, candidate)
-    __shared__ uint64_t ck64[SEL_RANK_MAX];
-    __shared__ uint32_t ncand, nquota, res[2];
-    const int grp = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-    const uint32_t *K = keys + (int64_t)grp * Sp;
-    const uint32_t *H = hist + (int64_t)grp * ATTN_HIST_BINS;
-    const int Sb = seq_len(s, m, grp / (int)s.Hsel);
-    const int ksb = seq_keep(s, m, Sb);
-    // a shorter sequence keeps fewer positions: the rest of its index row is -1
-    if (pos_out)
-        for (int i = ksb + tid; i < s.ks; i += 1024)
-            pos_out[(int64_t)grp * s.ks + i] = -1;
-    uint32_t krem = (uint32_t)ksb;
-    // the histogram's loads first, then the first batch of keys (it does not depend on
-    // the threshold bin), so the key loads stay in flight through the histogram phase
-    static_assert(ATTN_HIST_BINS == 4 * 1024, "four histogram bins per thread");
-    uint32_t hc[4];
-    hist_counts<4>(H, hc);
-    const uint4 *k4 = reinterpret_cast<const uint4 *>(K);
-    const int n4 = (int)((Sb + 3) / 4), step = 1024;
-    uint4 u[SEL_KB];
-#pragma unroll
-    for (int q = 0; q < SEL_KB; ++q) { // unconditional loads (an in-range address), zeroed past n4
-        const int ii = tid + q * step;
-        const uint4 t = k4[min(ii, n4 - 1)];
-        const uint32_t keep = 0u - ilt(ii, n4);
-        u[q] = make_uint4(t.x & keep, t.y & keep, t.z & keep, t.w & keep);
-    }
-    uint32_t nbin;
-    const uint32_t d = crossing_from_counts<4>(hc, krem, tmp, &nbin);
-    if (tid < PV_MAX_CHUNKS) {
-        cgt[tid] = 0;
-        ceq[tid] = 0;
-    }
-    if (tid == 0) {
-        ncand = 0;
-        nquota = 0;
-        res[0] = 0;
-        res[1] = 0;
-    }
-    __syncthreads();
-    const uint32_t tD = d + KEY_BIN_BASE; // kk >> 18 of the crossing bin's keys (d >= 1)
-    uint32_t thr, quota;
-    if (d > 0 && nbin <= (uint32_t)CAND_CAP) {
-        for (int i0 = tid; i0 - lane < n4; i0 += SEL_KB * step) {
-            if (i0 != tid) {
-#pragma unroll
-                for (int q = 0; q < SEL_KB; ++q)
-                    u[q] = i0 + q * step < n4 ? k4[i0 + q * step] : make_uint4(0u, 0u, 0u, 0u);
-            }
-            // predicates as integer arithmetic (bins are 14-bit): per element, in bin tD
-            // (a candidate) or above it; candidates also as a bit mask.  Keys past the
-            // sequence's end (up to the 8-position boundary the loads reach) are 0, in
-            // neither; loads past n4 give 0 as well.
-            uint32_t cl = 0, cmask = 0, ngt[SEL_KB];
-#pragma unroll
-            for (int q = 0; q < SEL_KB; ++q) {
-                const uint32_t kk[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
-                ngt[q] = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t top = kk[e] >> 18;
-                    const uint32_t g = (tD - top) >> 31, ge = (tD - 1u - top) >> 31; // top > tD, top >= tD
-                    const uint32_t c = ge - g;
-                    cl += c;
-                    cmask |= c << (4 * q + e);
-                    ngt[q] += g;
-                }
-            }
-            // candidates: per-lane count, wave scan, one slot reservation per wave
-            const uint32_t cincl = wave_incl_sum(cl);
-            const uint32_t wcount = (uint32_t)__builtin_amdgcn_readlane((int)cincl, WAVE - 1);
-            uint32_t base = 0;
-            if (lane == 0 && wcount != 0u)
-                base = atomicAdd(&ncand, wcount);
-            base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-            uint32_t slot = base + cincl - cl;
-            while (cmask) { // rare: the bin holds ~1/100 of the keys
-                const int b = __builtin_ctz(cmask);
-                cmask &= cmask - 1u;
-                const int q = b >> 2, e = b & 3;
-                uint32_t kv = 0; // u[q] selected with compile-time indices (no private-memory copy of u)
-#pragma unroll
-                for (int qq = 0; qq < SEL_KB; ++qq)
-                    if (qq == q)
-                        kv = e == 0 ? u[qq].x : e == 1 ? u[qq].y : e == 2 ? u[qq].z : u[qq].w;
-                if (slot < (uint32_t)CAND_CAP) {
-                    ckey[slot] = kv;
-                    cpos[slot] = 4 * (i0 + q * step) + e;
-                }
-                ++slot;
-            }
-            // keys above the bin, per PV chunk (one wave load covers 256 consecutive positions: one chunk)
-#pragma unroll
-            for (int q = 0; q < SEL_KB; ++q) {
-                const int i = i0 + q * step;
-                const uint32_t wgt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(ngt[q]), WAVE - 1);
-                if (lane == 0 && wgt != 0u)
-                    atomicAdd(&cgt[(4 * (i - lane)) / P], wgt);
-            }
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+    uint64_t prefix = 0, pmask = 0;
+    for (int shift = 56;; shift -= 8) {
+        for (int i = tid; i < 256; i += blockDim.x)
+            R.h[i] = 0;
+        if (tid == 0) {
+            R.res[0] = 0;
+            R.res[1] = 1;
+            R.res[2] = 0;
         }
         __syncthreads();
-        const uint32_t nc = min(nbin, (uint32_t)CAND_CAP);
-        if (nc <= (uint32_t)SEL_RANK_MAX) {
-            // Rank by one 64-bit order key per candidate: the 18 key bits under the bin
-            // (candidates share its top 14), then the complemented position (< 2^24), so
-            // larger means earlier in the total order and no two are equal.  Thread t
-            // counts the candidates above candidate t % 256 among every fourth one.
-            const uint32_t kb = tD << 18;
-            for (int i = tid; i < (int)nc; i += 1024)
-                ck64[i] = ((uint64_t)(ckey[i] - kb) << 24) | (uint64_t)(0xffffffu - (uint32_t)cpos[i]);
-            __syncthreads();
-            constexpr uint32_t RS = SEL_RANK_MAX, split = 1024u / RS;
-            const uint32_t me_i = (uint32_t)tid % RS, part = (uint32_t)tid / RS;
-            if (me_i < nc) {
-                const uint64_t mk = ck64[me_i];
-                // 8 independent comparisons per step keep the LDS reads pipelined; a
-                // difference of two keys below 2^42 has its top bit set iff the other is larger
-                uint32_t ab[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                uint32_t i = part;
-                for (; i + 7 * split < nc; i += 8 * split) {
-#pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        ab[u] += (uint32_t)((mk - ck64[i + u * split]) >> 63);
-                }
-                for (; i < nc; i += split)
-                    ab[0] += (uint32_t)((mk - ck64[i]) >> 63);
-                rk_above[tid] = ((ab[0] + ab[1]) + (ab[2] + ab[3])) + ((ab[4] + ab[5]) + (ab[6] + ab[7]));
+        each_key([&](uint64_t key) {
+            if ((key & pmask) == prefix)
+                atomicAdd(&R.h[(uint32_t)(key >> shift) & 255u], 1u);
+        });
+        __syncthreads();
+        // crossing digit in descending order: thread t < 256 holds digit 255 - t
+        const uint32_t cnt = tid < 256 ? R.h[255 - tid] : 0u;
+        const uint32_t incl = block_incl_scan(cnt, R.tmp);
+        if (tid < 256 && incl - cnt < krem && krem <= incl) {
+            R.res[0] = 255u - (uint32_t)tid;
+            R.res[1] = krem - (incl - cnt);
+            R.res[2] = cnt;
+        }
+        __syncthreads();
+        const uint32_t dig = R.res[0], n = R.res[2];
+        krem = R.res[1];
+        prefix |= (uint64_t)dig << shift;
+        pmask |= 0xffull << shift;
+        __syncthreads();
+        if (n <= (uint32_t)SEL_FEW || shift == 0) {
+            if (tid == 0) {
+                R.nfew = 0;
+                R.found = 0;
             }
             __syncthreads();
-            if ((uint32_t)tid < nc) {
+            each_key([&](uint64_t key) {
+                if ((key & pmask) == prefix) {
+                    const uint32_t sl = atomicAdd(&R.nfew, 1u);
+                    if (sl < (uint32_t)SEL_FEW)
+                        R.few[sl] = key;
+                }
+            });
+            __syncthreads();
+            if (tid < WAVE) {
+                const uint32_t nn = min(R.nfew, (uint32_t)SEL_FEW);
+                const uint64_t me = (uint32_t)lane < nn ? R.few[lane] : 0ull;
                 uint32_t above = 0;
-#pragma unroll
-                for (uint32_t q = 0; q < split; ++q)
-                    above += rk_above[q * RS + tid];
-                if (above + 1u == krem) { // the krem-th candidate: the threshold key and its position
-                    res[0] = ckey[tid];
-                    res[1] = (uint32_t)cpos[tid];
-                }
+                for (uint32_t j = 0; j < nn; ++j)
+                    above += R.few[j] > me ? 1u : 0u;
+                if ((uint32_t)lane < nn && above + 1u == krem)
+                    R.found = me;
             }
             __syncthreads();
-            thr = res[0];
-            // quota: the threshold's rank among its ties, i.e. equal keys at positions <= its own
-            const uint32_t pk = res[1];
-            for (int i = tid; i < (int)nc; i += 1024)
-                if (ckey[i] == thr && (uint32_t)cpos[i] <= pk)
-                    atomicAdd(&nquota, 1u);
-            __syncthreads();
-            quota = nquota;
-        } else {
-            uint32_t prefix = tD << 18, pmask = 0xfffc0000u;
-#pragma clang loop unroll(disable)
-            for (int ps = 0; ps < 2; ++ps) // bits 9..17, then 0..8 (one copy of the pass: smaller code)
-                radix_pass(ckey, (int)nc, prefix, pmask, 9 - 9 * ps, 9, krem, h2, tmp);
-            thr = prefix;
-            quota = krem;
-        }
-        for (int i = tid; i < (int)nc; i += 1024) {
-            if (ckey[i] > thr)
-                atomicAdd(&cgt[cpos[i] / P], 1u);
-            else if (ckey[i] == thr)
-                atomicAdd(&ceq[cpos[i] / P], 1u);
-        }
-    } else {
-        // a crowded bin: the 18 bits under it (9 + 9); a threshold below the histogram's
-        // window (bin 0): all 32 bits (11 + 11 + 10)
-        const bool full = d == 0;
-        uint32_t prefix = full ? 0u : tD << 18, pmask = full ? 0u : 0xfffc0000u;
-        if (full)
-            krem = (uint32_t)ksb;
-        const int npass = full ? 3 : 2;
-#pragma clang loop unroll(disable)
-        for (int ps = 0; ps < npass; ++ps) {
-            const int shift = full ? (ps == 0 ? 21 : ps == 1 ? 10 : 0) : (ps == 0 ? 9 : 0);
-            const int nbits = full ? (ps == 2 ? 10 : 11) : 9;
-            radix_pass_v4(K, Sb, prefix, pmask, shift, nbits, krem, h2, tmp);
-        }
-        thr = prefix;
-        quota = krem;
-        for (int i0 = tid; i0 - lane < n4; i0 += SEL_KB * step) {
-            uint4 u[SEL_KB];
-#pragma unroll
-            for (int q = 0; q < SEL_KB; ++q)
-                u[q] = i0 + q * step < n4 ? k4[i0 + q * step] : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-            for (int q = 0; q < SEL_KB; ++q) {
-                const int i = i0 + q * step;
-                const uint32_t kk[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
-                uint32_t ngt = 0, neq = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool ok = 4 * i + e < Sb;
-                    ngt += ok & (kk[e] > thr);
-                    neq += ok & (kk[e] == thr);
-                }
-                const uint32_t wgt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(ngt), WAVE - 1);
-                const uint32_t weq = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(neq), WAVE - 1);
-                if (lane == 0) {
-                    if (wgt)
-                        atomicAdd(&cgt[(4 * (i - lane)) / P], wgt);
-                    if (weq)
-                        atomicAdd(&ceq[(4 * (i - lane)) / P], weq);
-                }
-            }
-        }
-    }
-    __syncthreads();
-    if (w == 0) {
-        // per chunk: kept and tied positions before it (npv <= 64 chunks: one lane each, DPP scans)
-        const uint32_t cg = lane < npv ? cgt[lane] : 0u, ce = lane < npv ? ceq[lane] : 0u;
-        const uint32_t gex = wave_incl_sum(cg) - cg, eex = wave_incl_sum(ce) - ce;
-        if (lane < npv)
-            info[(int64_t)grp * npv + lane] = make_uint2(gex + min(eex, quota), eex);
-        if (lane == 0) {
-            sel[grp].thr = thr;
-            sel[grp].quota = quota;
+            return R.found;
         }
     }
 }
 
-// ------------------------------------------------------------------ pv
-// One workgroup per (chunk of P positions, group).  4 waves; each wave
-// quarter (16 lanes) holds one 256-byte V row, 8 dims per lane.
+// ------------------------------------------------------------------ pv (with the position selection)
+// One workgroup per (chunk of P positions, group), 8 waves.  Every workgroup of
+// a group first finds the group's threshold itself (the same result in each):
+//  - the 8192-bin histogram of scores gives the bin d holding the ks-th
+//    largest score and its rank krem inside the bin;
+//  - one pass over the 2-byte bins of all positions gathers bin d's positions,
+//    whose rank keys (recomputed from the logits) are radix-selected for the
+//    krem-th largest (past SEL_CAP candidates the radix passes recompute the
+//    rank keys from the logits instead of holding them in LDS).
+// A position is kept iff its bin is above d, or it is in bin d with a rank key
+// at least the threshold's: exactly the ks first positions of the order (score
+// descending, position ascending).  Then the chunk's kept positions (in
+// ascending order) stream their V rows, 32 rows at a time (a 16-lane quarter
+// wave per 256-byte row, 16 rows in flight per lane), into p * V partial sums.
+template <int GS> struct PvLds {
+    union {
+        struct {
+            uint64_t key[SEL_CAP];
+            int32_t pos[SEL_CAP];
+        } sel;
+        struct {
+            int64_t rows[PV_PASS];
+            float pr[GS][PV_PASS];
+        } pv;
+        float red[PV_WAVES][GS][D];
+    } u;
+    RadixLds rad;
+    uint32_t tmp[64];
+    uint32_t ncand;
+    uint32_t bres[3];
+    uint32_t wk[PV_WAVES];
+};
+
 template <int GS>
-__global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, KvMap m, int Sp, int P, const uint16_t *__restrict__ v,
-                                                      const float *__restrict__ logit, const double *__restrict__ lse_ws,
-                                                      const uint32_t *__restrict__ keys, const SelInfo *__restrict__ sel,
-                                                      const uint2 *__restrict__ info, int32_t *__restrict__ pos_out,
-                                                      float *__restrict__ part)
+__global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap m, int Sp, int P,
+                                                             const uint16_t *__restrict__ v,
+                                                             const float *__restrict__ logit,
+                                                             const double *__restrict__ lse_ws,
+                                                             const uint16_t *__restrict__ bins,
+                                                             const uint32_t *__restrict__ hist,
+                                                             const float *__restrict__ vn,
+                                                             int32_t *__restrict__ pstage,
+                                                             uint32_t *__restrict__ pcount, float *__restrict__ part)
 {
-    __shared__ int64_t rows[PV_SUB]; // V row index of each kept position of the pass
-    __shared__ float pr[GS][PV_SUB];
-    __shared__ uint32_t wgt[4], weq[4];
-    __shared__ float red[4][GS][D];
+    __shared__ PvLds<GS> L;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS, g = h0 / s.G;
     const int c = blockIdx.x, npv = gridDim.x;
-    const uint32_t thr = sel[grp].thr, quota = sel[grp].quota;
-    const uint2 inf = info[(int64_t)grp * npv + c];
-    uint32_t kept_before = inf.x, ties_before = inf.y;
+    const int Sb = seq_len(s, m, b), ksb = seq_keep(s, m, Sb);
+    const int p0 = c * P, p1 = min(Sb, p0 + P);
+    const float *Lg = logit + ((int64_t)b * s.Hq + h0) * Sp; // head hh at Lg + hh * Sp
+    const uint16_t *Bn = bins + (int64_t)grp * Sp;
+    const double sc = (double)s.scale;
+    double lsed[GS];
     float lsef[GS];
 #pragma unroll
-    for (int hh = 0; hh < GS; ++hh)
-        lsef[hh] = (float)lse_ws[(int64_t)b * s.Hq + h0 + hh];
-    const uint32_t *K = keys + (int64_t)grp * Sp;
-    const float *L = logit + ((int64_t)b * s.Hq + h0) * Sp;
-    const int Sb = seq_len(s, m, b), ksb = seq_keep(s, m, Sb);
-    const int quarter = lane >> 4, dl = lane & 15, slot = w * 4 + quarter;
+    for (int hh = 0; hh < GS; ++hh) {
+        lsed[hh] = lse_ws[(int64_t)b * s.Hq + h0 + hh];
+        lsef[hh] = (float)lsed[hh];
+    }
+    // rank key of position p (its bin is d): score recomputed from the logits
+    auto rank_of = [&](int p, uint32_t d) -> uint64_t {
+        float av[GS];
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh)
+            av[hh] = Lg[(int64_t)hh * Sp + p];
+        const float vv = vn ? vn[kv_row(s, m, b, g, p)] : 1.0f;
+        return rank_key(pos_key(pos_score<GS>(av, lsed, sc, vn != nullptr, vv)), d, p);
+    };
 
     float acc[GS][8];
 #pragma unroll
@@ -712,98 +635,219 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, KvMap m, int 
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             acc[hh][e] = 0.0f;
+    uint32_t chunk_kept = 0;
 
-    const int p0 = c * P, p1 = min(Sb, p0 + P);
-    for (int sb = p0; sb < p1; sb += PV_SUB) {
-        // thread tid holds positions j0, j0+1 (j0 even and Sp a multiple of 8: j0 < S keeps both in the row;
-        // pages hold a multiple of 8 positions, so both share j0's page)
-        const int j0 = sb + 2 * tid;
-        uint2 kk = make_uint2(0u, 0u);
-        float2 lg[GS];
-        int64_t vrow = 0;
+    if (p0 < p1) { // (uniform over the workgroup) chunks past the sequence's end only write zeros
+        // 1. threshold bin from the histogram: thread t holds bins 8191-16t down to 8176-16t
+        static_assert(ATTN_HIST_BINS == 16 * PV_THREADS, "16 histogram bins per thread");
+        uint32_t hc[16];
+        {
+            const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + (int64_t)grp * ATTN_HIST_BINS +
+                                                              ATTN_HIST_BINS - 16 * (tid + 1));
+            const uint4 q0 = h4[0], q1 = h4[1], q2 = h4[2], q3 = h4[3];
+            const uint32_t asc[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                                      q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
 #pragma unroll
-        for (int hh = 0; hh < GS; ++hh)
-            lg[hh] = make_float2(0.0f, 0.0f);
-        if (j0 < p1) {
-            vrow = kv_row(s, m, b, g, j0);
-            kk = *reinterpret_cast<const uint2 *>(K + j0);
-#pragma unroll
-            for (int hh = 0; hh < GS; ++hh)
-                lg[hh] = *reinterpret_cast<const float2 *>(L + (int64_t)hh * Sp + j0);
+            for (int q = 0; q < 16; ++q)
+                hc[q] = asc[15 - q];
         }
-        const uint32_t va = j0 < p1, vb1 = j0 + 1 < p1;
-        const uint32_t ga = va & (kk.x > thr), gb = vb1 & (kk.y > thr);
-        const uint32_t ea = va & (kk.x == thr), eb = vb1 & (kk.y == thr);
-        // kept before a position = greater before + min(equal before, quota): one scan of each
-        const uint32_t gi = wave_incl_sum(ga + gb), ei = wave_incl_sum(ea + eb);
-        if (lane == WAVE - 1) {
-            wgt[w] = gi;
-            weq[w] = ei;
+        if (tid == 0) {
+            L.bres[0] = 0;
+            L.bres[1] = 1;
+            L.bres[2] = 0;
+            L.ncand = 0;
         }
-        __syncthreads();
-        uint32_t gbw = 0, ebw = 0, gtot = 0, etot = 0;
+        uint32_t tot = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            gbw += i < w ? wgt[i] : 0u;
-            ebw += i < w ? weq[i] : 0u;
-            gtot += wgt[i];
-            etot += weq[i];
-        }
-        const uint32_t gpa = gbw + gi - (ga + gb), epa = ties_before + ebw + ei - (ea + eb); // before position a
-        const uint32_t gpb = gpa + ga, epb = epa + ea;
-        const uint32_t base0 = min(ties_before, quota); // kept ties before this pass
-        const uint32_t keepa = ga | (ea & (epa < quota)), keepb = gb | (eb & (epb < quota));
-        const uint32_t la = gpa + min(epa, quota) - base0, lb = gpb + min(epb, quota) - base0; // pass-local slots
-        const uint32_t nkept = gtot + min(ties_before + etot, quota) - base0;
-        if (keepa && la < PV_SUB) {
-            rows[la] = vrow;
+        for (int q = 0; q < 16; ++q)
+            tot += hc[q];
+        const uint32_t incl = block_incl_scan(tot, L.tmp); // (barriers inside)
+        {
+            const uint32_t top = ATTN_HIST_BINS - 1 - 16 * tid;
+            const uint32_t want = (uint32_t)ksb;
+            uint32_t run = incl - tot;
 #pragma unroll
-            for (int hh = 0; hh < GS; ++hh)
-                pr[hh][la] = expf(fmaf(s.scale, lg[hh].x, -lsef[hh]));
-            if (pos_out && kept_before + la < (uint32_t)ksb)
-                pos_out[(int64_t)grp * s.ks + kept_before + la] = j0;
-        }
-        if (keepb && lb < PV_SUB) {
-            rows[lb] = vrow + 1;
-#pragma unroll
-            for (int hh = 0; hh < GS; ++hh)
-                pr[hh][lb] = expf(fmaf(s.scale, lg[hh].y, -lsef[hh]));
-            if (pos_out && kept_before + lb < (uint32_t)ksb)
-                pos_out[(int64_t)grp * s.ks + kept_before + lb] = j0 + 1;
-        }
-        __syncthreads();
-        // stream kept V rows: slot (wave, quarter) takes rows slot + 16 m, PV_U rows in flight per lane
-        const int nk = (int)min(nkept, (uint32_t)PV_SUB);
-        for (int r0 = slot; r0 < nk; r0 += 16 * PV_U) {
-            uint4 u[PV_U];
-#pragma unroll
-            for (int qq = 0; qq < PV_U; ++qq) {
-                const int r = r0 + 16 * qq;
-                if (r < nk)
-                    u[qq] = *reinterpret_cast<const uint4 *>(v + rows[r] * D + dl * 8);
+            for (int q = 0; q < 16; ++q) {
+                if (run < want && want <= run + hc[q]) {
+                    L.bres[0] = top - q;
+                    L.bres[1] = want - run;
+                    L.bres[2] = hc[q];
+                }
+                run += hc[q];
             }
+        }
+        __syncthreads();
+        const uint32_t d = L.bres[0], krem = L.bres[1], nbin = L.bres[2];
+
+        // 2. rank-key threshold inside bin d
+        const int n8 = (Sb + 7) / 8;
+        const uint4 *B4 = reinterpret_cast<const uint4 *>(Bn);
+        uint64_t thr;
+        if (nbin <= (uint32_t)SEL_CAP) {
+            // gather bin d's positions: per-lane bit masks, one slot reservation per wave
+            for (int i0 = tid; i0 - lane < n8; i0 += 4 * PV_THREADS) {
+                uint4 u[4];
 #pragma unroll
-            for (int qq = 0; qq < PV_U; ++qq) {
-                const int r = r0 + 16 * qq;
-                if (r < nk) {
-                    float vv[8];
-                    Vec16<uint16_t>::unpack(u[qq], vv);
+                for (int q = 0; q < 4; ++q) {
+                    const int i = i0 + q * PV_THREADS;
+                    u[q] = i < n8 ? B4[i] : make_uint4(0u, 0u, 0u, 0u);
+                }
+                uint32_t cm = 0;
 #pragma unroll
-                    for (int hh = 0; hh < GS; ++hh) {
-                        const float pv = pr[hh][r];
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t wd[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+                    const int pb = 8 * (i0 + q * PV_THREADS);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            acc[hh][e] = fmaf(pv, vv[e], acc[hh][e]);
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t bn = (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu;
+                        cm |= (uint32_t)((bn == d) & (pb + e < Sb)) << (8 * q + e);
+                    }
+                }
+                const uint32_t cl = (uint32_t)__popc(cm);
+                const uint32_t cincl = wave_incl_sum(cl);
+                const uint32_t wcount = (uint32_t)__builtin_amdgcn_readlane((int)cincl, WAVE - 1);
+                uint32_t base = 0;
+                if (lane == 0 && wcount != 0u)
+                    base = atomicAdd(&L.ncand, wcount);
+                base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+                uint32_t slot = base + cincl - cl;
+                while (cm) {
+                    const int bit = __builtin_ctz(cm);
+                    cm &= cm - 1u;
+                    if (slot < (uint32_t)SEL_CAP)
+                        L.u.sel.pos[slot] = 8 * (i0 + (bit >> 3) * PV_THREADS) + (bit & 7);
+                    ++slot;
+                }
+            }
+            __syncthreads();
+            const int nc = (int)min(L.ncand, (uint32_t)SEL_CAP);
+            for (int i = tid; i < nc; i += PV_THREADS)
+                L.u.sel.key[i] = rank_of(L.u.sel.pos[i], d);
+            __syncthreads();
+            thr = radix_select_u64(
+                [&](auto f) {
+                    for (int i = tid; i < nc; i += PV_THREADS)
+                        f(L.u.sel.key[i]);
+                },
+                krem, L.rad);
+        } else {
+            // a crowded bin: every radix pass recomputes the rank keys of bin d's positions
+            thr = radix_select_u64(
+                [&](auto f) {
+                    for (int i = tid; i < n8; i += PV_THREADS) {
+                        const uint4 u = B4[i];
+                        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t bn = (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu;
+                            const int p = 8 * i + e;
+                            if (bn == d && p < Sb)
+                                f(rank_of(p, d));
+                        }
+                    }
+                },
+                krem, L.rad);
+        }
+        __syncthreads(); // the selection's LDS is reused below
+
+        // 3. P V over the chunk's kept positions
+        const int quarter = lane >> 4, dl = lane & 15, slot = w * 4 + quarter;
+        constexpr int NSLOT = PV_WAVES * 4;
+        for (int sb = p0; sb < p1; sb += PV_PASS) {
+            // thread tid holds positions j0, j0 + 1 (j0 even and Sp a multiple of 8: j0 < Sb keeps both in
+            // the row; pages hold a multiple of 8 positions, so both share j0's page)
+            const int j0 = sb + 2 * tid;
+            uint32_t bw = 0;
+            float2 lg[GS];
+            int64_t vrow = 0;
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+                lg[hh] = make_float2(0.0f, 0.0f);
+            if (j0 < p1) {
+                vrow = kv_row(s, m, b, g, j0);
+                bw = *reinterpret_cast<const uint32_t *>(Bn + j0);
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    lg[hh] = *reinterpret_cast<const float2 *>(Lg + (int64_t)hh * Sp + j0);
+            }
+            const uint32_t ba = bw & 0xffffu, bb = bw >> 16;
+            uint32_t ka = (uint32_t)(j0 < p1) & (uint32_t)(ba > d);
+            uint32_t kb = (uint32_t)(j0 + 1 < p1) & (uint32_t)(bb > d);
+            if (j0 < p1 && ba == d) {
+                float av[GS];
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    av[hh] = lg[hh].x;
+                const float vv = vn ? vn[vrow] : 1.0f;
+                ka = rank_key(pos_key(pos_score<GS>(av, lsed, sc, vn != nullptr, vv)), d, j0) >= thr;
+            }
+            if (j0 + 1 < p1 && bb == d) {
+                float av[GS];
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    av[hh] = lg[hh].y;
+                const float vv = vn ? vn[vrow + 1] : 1.0f;
+                kb = rank_key(pos_key(pos_score<GS>(av, lsed, sc, vn != nullptr, vv)), d, j0 + 1) >= thr;
+            }
+            const uint32_t ki = wave_incl_sum(ka + kb);
+            if (lane == WAVE - 1)
+                L.wk[w] = ki;
+            __syncthreads();
+            uint32_t before = 0, nkept = 0;
+#pragma unroll
+            for (int i = 0; i < PV_WAVES; ++i) {
+                before += i < w ? L.wk[i] : 0u;
+                nkept += L.wk[i];
+            }
+            const uint32_t sa = before + ki - (ka + kb), sbb = sa + ka; // pass-local slots
+            if (ka) {
+                L.u.pv.rows[sa] = vrow;
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    L.u.pv.pr[hh][sa] = expf(fmaf(s.scale, lg[hh].x, -lsef[hh]));
+                if (pstage)
+                    pstage[(int64_t)grp * Sp + p0 + chunk_kept + sa] = j0;
+            }
+            if (kb) {
+                L.u.pv.rows[sbb] = vrow + 1;
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    L.u.pv.pr[hh][sbb] = expf(fmaf(s.scale, lg[hh].y, -lsef[hh]));
+                if (pstage)
+                    pstage[(int64_t)grp * Sp + p0 + chunk_kept + sbb] = j0 + 1;
+            }
+            __syncthreads();
+            const int nk = (int)nkept;
+            for (int r0 = slot; r0 < nk; r0 += NSLOT * PV_U) {
+                uint4 u[PV_U];
+#pragma unroll
+                for (int qq = 0; qq < PV_U; ++qq) {
+                    const int r = r0 + NSLOT * qq;
+                    if (r < nk)
+                        u[qq] = *reinterpret_cast<const uint4 *>(v + L.u.pv.rows[r] * D + dl * 8);
+                }
+#pragma unroll
+                for (int qq = 0; qq < PV_U; ++qq) {
+                    const int r = r0 + NSLOT * qq;
+                    if (r < nk) {
+                        float vv[8];
+                        Vec16<uint16_t>::unpack(u[qq], vv);
+#pragma unroll
+                        for (int hh = 0; hh < GS; ++hh) {
+                            const float pv = L.u.pv.pr[hh][r];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                acc[hh][e] = fmaf(pv, vv[e], acc[hh][e]);
+                        }
                     }
                 }
             }
+            chunk_kept += nkept;
+            __syncthreads();
         }
-        kept_before += nkept;
-        ties_before += etot;
-        __syncthreads();
     }
 
-    // reduce the four quarters of each wave, then the four waves (fixed order)
+    // reduce the four quarters of each wave, then the waves (fixed order)
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh)
 #pragma unroll
@@ -813,19 +857,25 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnShape s, KvMap m, int 
             x += __shfl_xor(x, 32, WAVE);
             acc[hh][e] = x;
         }
-    if (quarter == 0) {
+    if ((lane >> 4) == 0) {
 #pragma unroll
         for (int hh = 0; hh < GS; ++hh)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                red[w][hh][dl * 8 + e] = acc[hh][e];
+                L.u.red[w][hh][(lane & 15) * 8 + e] = acc[hh][e];
     }
     __syncthreads();
     float *mine = part + ((int64_t)grp * npv + c) * GS * D;
-    for (int i = tid; i < GS * D; i += 256) {
+    for (int i = tid; i < GS * D; i += PV_THREADS) {
         const int hh = i / D, dd = i % D;
-        mine[i] = ((red[0][hh][dd] + red[1][hh][dd]) + red[2][hh][dd]) + red[3][hh][dd];
+        float x = L.u.red[0][hh][dd];
+#pragma unroll
+        for (int ww = 1; ww < PV_WAVES; ++ww)
+            x += L.u.red[ww][hh][dd];
+        mine[i] = x;
     }
+    if (pcount && tid == 0)
+        pcount[(int64_t)grp * npv + c] = chunk_kept;
 }
 
 // out[b, h0 + hh, :] = sum over the PV chunks of the chunk partials, in a fixed
@@ -866,16 +916,54 @@ __global__ __launch_bounds__(PVR_WAVES * WAVE) void attn_pv_reduce_kernel(AttnSh
     out[((int64_t)b * s.Hq + h0 + i / D) * D + i % D] = sum;
 }
 
-// ------------------------------------------------------------------ host side
-static void pv_chunks(int64_t S, int *P, int *npv)
+// Kept-position lists: workgroup (chunk c, group) copies the chunk's staged
+// kept positions (ascending) to the group's list after the kept positions of
+// chunks 0 .. c-1; chunk 0 also fills the entries past a shorter sequence's
+// keep count with -1.
+__global__ __launch_bounds__(256) void attn_pos_kernel(AttnShape s, KvMap m, int Sp, int P,
+                                                       const uint32_t *__restrict__ pcount,
+                                                       const int32_t *__restrict__ pstage,
+                                                       int32_t *__restrict__ pos_out)
 {
-    int64_t n = (S + PV_SUB - 1) / PV_SUB;
-    if (n > PV_MAX_CHUNKS)
-        n = PV_MAX_CHUNKS;
-    int64_t per = (S + n - 1) / n;
-    per = (per + PV_SUB - 1) / PV_SUB * PV_SUB;
+    __shared__ uint32_t off_s;
+    const int grp = blockIdx.y, c = blockIdx.x, npv = gridDim.x;
+    const int tid = threadIdx.x;
+    const int Sb = seq_len(s, m, grp / s.Hsel), ksb = seq_keep(s, m, Sb);
+    const uint32_t *pc = pcount + (int64_t)grp * npv;
+    if (tid < WAVE) { // npv <= PV_MAX_CHUNKS = 64: one chunk per lane
+        const uint32_t x = tid < c ? pc[tid] : 0u;
+        const uint32_t tot = wave_incl_sum(x);
+        if (tid == WAVE - 1)
+            off_s = tot;
+    }
+    __syncthreads();
+    const uint32_t off = off_s, n = c * P < Sb ? pc[c] : 0u;
+    int32_t *dst = pos_out + (int64_t)grp * s.ks;
+    const int32_t *src = pstage + (int64_t)grp * Sp + (int64_t)c * P;
+    for (uint32_t i = tid; i < n; i += 256)
+        if (off + i < (uint32_t)s.ks)
+            dst[off + i] = src[i];
+    if (c == 0)
+        for (int i = ksb + tid; i < s.ks; i += 256)
+            dst[i] = -1;
+}
+
+// ------------------------------------------------------------------ host side
+// PV chunks: whole passes of PV_PASS positions, about ATTN_PV_TARGET_WGS
+// workgroups over all groups, at most PV_MAX_CHUNKS per group.
+static void pv_chunks(int64_t S, int64_t groups, int *P, int *npv)
+{
+    int64_t per = (S * groups + ATTN_PV_TARGET_WGS - 1) / ATTN_PV_TARGET_WGS;
+    per = per < PV_PASS ? PV_PASS : per;
+    per = (per + PV_PASS - 1) / PV_PASS * PV_PASS;
+    int64_t n = (S + per - 1) / per;
+    if (n > PV_MAX_CHUNKS) {
+        per = (S + PV_MAX_CHUNKS - 1) / PV_MAX_CHUNKS;
+        per = (per + PV_PASS - 1) / PV_PASS * PV_PASS;
+        n = (S + per - 1) / per;
+    }
     *P = (int)per;
-    *npv = (int)((S + per - 1) / per);
+    *npv = (int)n;
 }
 
 static inline char *align256(char *p) { return (char *)(((uintptr_t)p + 255) & ~(uintptr_t)255); }
@@ -886,7 +974,7 @@ size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base)
     const int64_t nqk = (s.S + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK;
     const int64_t G = s.B * s.Hsel;
     int P, npv;
-    pv_chunks(s.S, &P, &npv);
+    pv_chunks(s.S, G, &P, &npv);
     char *p = base + RMM_WS_HEADER_BYTES_INTERNAL;
     AttnWs w;
     w.logit = (float *)p;
@@ -895,12 +983,14 @@ size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base)
     p = align256(p + (size_t)(s.B * s.Hq * nqk) * 8);
     w.lse = (double *)p;
     p = align256(p + (size_t)(s.B * s.Hq) * 8);
-    w.keys = (uint32_t *)p;
-    p = align256(p + (size_t)(G * Sp) * 4);
+    w.bins = (uint16_t *)p;
+    p = align256(p + (size_t)(G * Sp) * 2);
     w.hist = (uint32_t *)p;
     p = align256(p + (size_t)(G * ATTN_HIST_BINS) * 4);
-    w.pos = (int32_t *)p; // SelInfo [G] then chunk info [G][npv]
-    p = align256(p + (size_t)G * sizeof(SelInfo) + (size_t)(G * npv) * sizeof(uint2) + 256);
+    w.pcount = (uint32_t *)p;
+    p = align256(p + (size_t)(G * npv) * 4);
+    w.pstage = (int32_t *)p;
+    p = align256(p + (size_t)(G * Sp) * 4);
     w.pvpart = (float *)p;
     p = align256(p + (size_t)(G * npv * s.GS * D) * 4);
     if (ws)
@@ -926,19 +1016,19 @@ static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q
     const int G = (int)(s.B * s.Hsel);
     const int nqk = (int)((s.S + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK);
     int P, npv;
-    pv_chunks(s.S, &P, &npv);
-    SelInfo *sel = reinterpret_cast<SelInfo *>(ws.pos);
-    uint2 *info = reinterpret_cast<uint2 *>(align256((char *)(sel + G)));
+    pv_chunks(s.S, G, &P, &npv);
     attn_qk_kernel<GS><<<dim3(nqk, G), QK_THREADS, 0, st>>>(s, m, Sp, q, kt, kn, ws.logit, ws.pstat, dim_idx,
                                                              ws.hist);
     const int nkc = (int)((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK);
     const int nsub = key_chunks_per_wg(s.S);
     attn_key_kernel<GS><<<dim3((nkc + nsub - 1) / nsub, G), 256, 0, st>>>(
-        s, m, Sp, nqk, nsub, ws.logit, ws.pstat, ws.lse, lse, vn, ws.keys, ws.hist);
-    attn_select_kernel<<<G, 1024, 0, st>>>(s, m, Sp, P, npv, ws.keys, ws.hist, sel, info, pos_idx);
-    attn_pv_kernel<GS><<<dim3(npv, G), 256, 0, st>>>(s, m, Sp, P, v, ws.logit, ws.lse, ws.keys, sel, info, pos_idx,
-                                                     ws.pvpart);
+        s, m, Sp, nqk, nsub, ws.logit, ws.pstat, ws.lse, lse, vn, ws.bins, ws.hist);
+    attn_pv_kernel<GS><<<dim3(npv, G), PV_THREADS, 0, st>>>(s, m, Sp, P, v, ws.logit, ws.lse, ws.bins, ws.hist, vn,
+                                                            pos_idx ? ws.pstage : nullptr,
+                                                            pos_idx ? ws.pcount : nullptr, ws.pvpart);
     attn_pv_reduce_kernel<GS><<<G * (GS * D / WAVE), PVR_WAVES * WAVE, 0, st>>>(s, npv, ws.pvpart, out);
+    if (pos_idx)
+        attn_pos_kernel<<<dim3(npv, G), 256, 0, st>>>(s, m, Sp, P, ws.pcount, ws.pstage, pos_idx);
     return hipGetLastError();
 }
 

@@ -39,9 +39,9 @@
 #define ATTN_D 128
 #define ATTN_QK_CHUNK 512   // positions per QK workgroup
 #define ATTN_KEY_CHUNK 2048 // positions per key/histogram workgroup
-#define ATTN_HIST_BINS 4096 // first radix level over the top 12 key bits
-#ifndef ATTN_PV_ROWS
-#define ATTN_PV_ROWS 128 // kept positions per PV workgroup (target)
+#define ATTN_HIST_BINS 8192 // position-score histogram: half-nat bins outside [-32, 0), 1/128 nat inside
+#ifndef ATTN_PV_TARGET_WGS
+#define ATTN_PV_TARGET_WGS 384 // PV workgroups the chunking aims for (each resolves its group's threshold)
 #endif
 #define ATTN_MAX_GROUPS 512 // B * Hsel and B * Hkv limit of the attention entry points (the range the tests cover)
 #define RMM_WS_HEADER_BYTES_INTERNAL 4096
@@ -87,13 +87,14 @@ struct AttnShape {
     float scale;
 };
 struct AttnWs {
-    float *logit;    // [B][Hq][S] unscaled q.k over kept dims
-    float2 *pstat;   // [B][Hq][nqk] (max, sum exp) per QK chunk
-    double *lse;     // [B][Hq]
-    uint32_t *keys;  // [B][Hsel][S]
-    uint32_t *hist;  // [B][Hsel][ATTN_HIST_BINS]
-    int32_t *pos;    // [B][Hsel][ks]
-    float *pvpart;   // [B][Hsel][npv][GS][D]
+    float *logit;     // [B][Hq][Sp] unscaled q.k over kept dims
+    float2 *pstat;    // [B][Hq][nqk] (max, sum exp) per QK chunk
+    double *lse;      // [B][Hq]
+    uint16_t *bins;   // [B][Hsel][Sp] histogram bin of every position's score
+    uint32_t *hist;   // [B][Hsel][ATTN_HIST_BINS]
+    uint32_t *pcount; // [B][Hsel][npv] kept positions per PV chunk
+    int32_t *pstage;  // [B][Hsel][Sp] kept positions of each PV chunk, staged at the chunk's start
+    float *pvpart;    // [B][Hsel][npv][GS][D]
 };
 // Where the cache of sequence b keeps position p (contiguous caches, or pages
 // named by a block table) and how long each sequence is.

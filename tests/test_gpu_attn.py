@@ -54,6 +54,7 @@ def run_attn(cs, r_dim, r_pos, mode=0, kt=None, v=None, S=None, vn=None):
         assert err <= 1e-5, f"out rel-L2 {err:.3e} with identical position sets"
     lg, lr = lse.cpu().numpy(), ref["lse"]
     assert np.max(np.abs(lg - lr) / np.abs(lr)) <= 1e-6
+    run_attn.last_out = out
     return ndiff, err
 
 
@@ -111,6 +112,34 @@ def test_gqa_32k_other_seeds(seed):
 def test_gqa_128k_batch4_full_size():
     cs = W.attn_128k()
     run_attn(cs, 0.5, 0.25, 0)
+
+
+def test_gqa_32k_per_query_head():
+    # mode 1 at the full 32K shape: 32 selection groups of one query head
+    run_attn(W.attn_32k(), 0.25, 0.25, 1)
+
+
+def test_gqa_128k_batch4_per_query_head():
+    # mode 1 at 128K x 4: 128 selection groups over 131072 positions each
+    run_attn(W.attn_128k(), 0.5, 0.25, 1)
+
+
+@pytest.mark.parametrize("r", [0.25, 0.5])
+def test_gqa_32k_without_optional_outputs(r):
+    # the call as the benchmark times it: dim_idx, pos_idx and lse not requested (NULL).  Its
+    # output must equal, bit for bit, the output of the same call with every output requested,
+    # and that one is checked against the oracle (position sets, out, lse)
+    cs = W.attn_32k()
+    print(f"[case] {cs.name} r={r} NULL optional outputs", flush=True)
+    out0, d0, p0, l0 = rmm.attn_decode(dev(cs.q), dev(cs.kt), dev(cs.v), dev(cs.kn), r, r, scale=cs.scale,
+                                       want_idx=False)
+    torch.cuda.synchronize()
+    assert d0 is None and p0 is None and l0 is None
+    ndiff, err = run_attn(cs, r, r, 0)
+    assert torch.equal(out0, run_attn.last_out)
+    ref = oracle.attn_decode(cs.q, cs.kt, cs.v, cs.kn, cs.scale, r, r, 0)
+    e0 = rel_l2(out0.cpu().numpy(), ref["out"])
+    assert e0 <= (1e-5 if ndiff == 0 else 2e-2), f"NULL-output call: out rel-L2 {e0:.3e}"
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv", [(1, 32768, 32, 8), (2, 1000, 8, 2), (1, 77, 8, 1)])
@@ -177,6 +206,30 @@ def test_value_norm_ragged_spare_capacity(S):
 def test_value_norm_32k_full_size():
     cs = W.attn_32k()
     run_attn(cs, 0.25, 0.25, 0, vn=W.value_row_norms(cs.v))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("scale,r_pos", [(4.0, 0.9), (8.0, 0.5), (8.0, 0.9), (16.0, 0.5), (16.0, 0.9)])
+def test_sharp_softmax_threshold_far_below(mode, scale, r_pos):
+    # sharp softmaxes: the k-th log-probability lies between -96 and -680 nats (measured with the
+    # oracle), and at scale 16 in mode 1 with r_pos 0.9 the k-th probability underflows to 0 in
+    # double, where every zero ties and the lowest positions win.  Positions are still ranked by
+    # their scores wherever the oracle's scores differ.
+    cs = W.attn_case(1, 4000, Hq=4, Hkv=1, seed=21, n_hot=4)
+    cs.scale = scale
+    run_attn(cs, 0.5, r_pos, mode)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("factor", [1e7, 1e-8])
+def test_value_norm_far_outside_the_fine_bins(mode, factor):
+    # value norms scaled so that log(p * ||V_s||) at the k-th position lies far above (x1e7: about
+    # +11) or far below (x1e-8) the 1/128-nat bins of the score histogram; a half-nat bin then
+    # holds hundreds of positions, ranked exactly in LDS
+    cs = W.attn_case(1, 4000, Hq=8, Hkv=2, seed=23, n_hot=4)
+    vn = (W.value_row_norms(cs.v) * factor).astype(np.float32)
+    run_attn(cs, 0.5, 0.25, mode, vn=vn)
+    run_attn(cs, 0.5, 0.9, mode, vn=vn)
 
 
 @pytest.mark.parametrize("mode", [0, 1])

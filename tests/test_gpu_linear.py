@@ -72,16 +72,20 @@ def test_o_proj_full_size(r):
     run_case(W.linear_o_decode(), r)
 
 
+# Rows of every 128-row block of the 2048 prefill tokens: the MFMA kernel's row blocks (and the
+# two blocks of each 256-token tile) are all compared, first and last row of each.
+PREFILL_ROWS = [128 * blk + o for blk in range(16) for o in (0, 127)]
+
+
 def test_prefill_full_size_sampled_rows():
     cs = W.linear_prefill()
-    rows = [0, 1, 255, 256, 700, 1023, 1024, 1500, 1791, 1792, 2046, 2047]
-    for r in (0.5, 0.25):
-        run_case(cs, r, rows=rows)
+    for r in (0.5, 0.25, 0.75, 1.0):
+        run_case(cs, r, rows=PREFILL_ROWS)
 
 
 @pytest.mark.parametrize("seed", [1, 2])
 def test_prefill_other_seeds_sampled_rows(seed):
-    run_case(W.linear_prefill(seed=seed), 0.5, rows=[3, 300, 1100, 2040])
+    run_case(W.linear_prefill(seed=seed), 0.5, rows=[128 * blk + o for blk in range(16) for o in (5, 100)])
 
 
 @pytest.mark.parametrize("T,K,M,tile,dtype", [
