@@ -7,8 +7,8 @@
 // dimension: head_dim for Q K^T, key positions for P V).  GEMM notes section 1:
 // scores = Q K^T, out = softmax(scores) V.
 //
-// Pipeline per (batch element, selection group), four launches on one stream
-// (a fifth writes the kept-position lists when they are asked for):
+// Pipeline per (batch element, selection group), five launches on one stream
+// (a sixth writes the kept-position lists when they are asked for):
 //  qk    : head_dim selection (one wave, bitwise search over ballots), then
 //          unscaled logits over the kept dims for 8 positions per lane from
 //          dim-major keys (a kept dim is one contiguous row), and per-chunk
@@ -17,10 +17,11 @@
 //  keys  : every workgroup merges the chunk statistics into lse (double), then
 //          scores its positions by max_h (scale*a_h - lse_h) in double, stores
 //          each position's histogram bin and adds it to the group histogram.
-//  pv    : every workgroup resolves the group's exact threshold from the
-//          histogram and the bins (redundantly, with the same result), keeps
-//          its chunk's positions at or above it (order-preserving), streams
-//          their V rows and accumulates p*V into a per-chunk partial.
+//  select: one workgroup per group resolves the group's exact threshold from
+//          the histogram and the bins.
+//  pv    : each workgroup keeps its chunk's positions at or above the
+//          threshold (order-preserving), streams their V rows and accumulates
+//          p*V into a per-chunk partial.
 //  reduce: the chunk partials are summed in a fixed order.
 #include "device.h"
 #include "kernels.h"
@@ -477,7 +478,8 @@ __global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int
 }
 
 // ------------------------------------------------------------------ position selection helpers
-constexpr int PV_THREADS = 512;
+constexpr int ASEL_THREADS = 512;       // threshold workgroup (one per group)
+constexpr int PV_THREADS = 256;
 constexpr int PV_WAVES = PV_THREADS / WAVE;
 constexpr int PV_PASS = 2 * PV_THREADS; // positions per PV pass (2 per thread)
 constexpr int PV_MAX_CHUNKS = 64;
@@ -559,66 +561,50 @@ __device__ uint64_t radix_select_u64(EachKey each_key, uint32_t krem, RadixLds &
     }
 }
 
-// ------------------------------------------------------------------ pv (with the position selection)
-// One workgroup per (chunk of P positions, group), 8 waves.  Every workgroup of
-// a group first finds the group's threshold itself (the same result in each):
-//  - the 8192-bin histogram of scores gives the bin d holding the ks-th
-//    largest score and its rank krem inside the bin;
-//  - one pass over the 2-byte bins of all positions gathers bin d's positions,
-//    whose rank keys (recomputed from the logits) are radix-selected for the
-//    krem-th largest (past SEL_CAP candidates the radix passes recompute the
-//    rank keys from the logits instead of holding them in LDS).
-// A position is kept iff its bin is above d, or it is in bin d with a rank key
-// at least the threshold's: exactly the ks first positions of the order (score
-// descending, position ascending).  Then the chunk's kept positions (in
-// ascending order) stream their V rows, 32 rows at a time (a 16-lane quarter
-// wave per 256-byte row, 16 rows in flight per lane), into p * V partial sums.
-template <int GS> struct PvLds {
-    union {
-        struct {
-            uint64_t key[SEL_CAP];
-            int32_t pos[SEL_CAP];
-        } sel;
-        struct {
-            int64_t rows[PV_PASS];
-            float pr[GS][PV_PASS];
-        } pv;
-        float red[PV_WAVES][GS][D];
-    } u;
+// ------------------------------------------------------------------ select
+// One workgroup per group finds the group's exact threshold: the 8192-bin
+// histogram of scores gives the bin d holding the ks-th largest score and its
+// rank krem inside the bin; one pass over the 2-byte bins of all positions
+// gathers bin d's positions, whose rank keys (recomputed from the logits) are
+// radix-selected for the krem-th largest.  Past SEL_CAP candidates the radix
+// passes recompute the rank keys instead of holding them in LDS.  Output per
+// group: (d, threshold rank key).  A position is kept iff its bin is above d,
+// or it is in bin d with a rank key at least the threshold's: exactly the ks
+// first positions of the order (score descending, position ascending).
+struct AttnSel {
+    uint32_t d, pad;
+    uint64_t thr;
+};
+struct SelLds {
+    uint64_t key[SEL_CAP];
+    int32_t pos[SEL_CAP];
     RadixLds rad;
     uint32_t tmp[64];
     uint32_t ncand;
     uint32_t bres[3];
-    uint32_t wk[PV_WAVES];
 };
 
 template <int GS>
-__global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap m, int Sp, int P,
-                                                             const uint16_t *__restrict__ v,
-                                                             const float *__restrict__ logit,
-                                                             const double *__restrict__ lse_ws,
-                                                             const uint16_t *__restrict__ bins,
-                                                             const uint32_t *__restrict__ hist,
-                                                             const float *__restrict__ vn,
-                                                             int32_t *__restrict__ pstage,
-                                                             uint32_t *__restrict__ pcount, float *__restrict__ part)
+__global__ __launch_bounds__(ASEL_THREADS) void attn_select_kernel(AttnShape s, KvMap m, int Sp,
+                                                                   const float *__restrict__ logit,
+                                                                   const double *__restrict__ lse_ws,
+                                                                   const uint16_t *__restrict__ bins,
+                                                                   const uint32_t *__restrict__ hist,
+                                                                   const float *__restrict__ vn,
+                                                                   AttnSel *__restrict__ sel)
 {
-    __shared__ PvLds<GS> L;
-    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-    const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS, g = h0 / s.G;
-    const int c = blockIdx.x, npv = gridDim.x;
+    __shared__ SelLds L;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+    const int grp = blockIdx.x, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS, g = h0 / s.G;
     const int Sb = seq_len(s, m, b), ksb = seq_keep(s, m, Sb);
-    const int p0 = c * P, p1 = min(Sb, p0 + P);
     const float *Lg = logit + ((int64_t)b * s.Hq + h0) * Sp; // head hh at Lg + hh * Sp
-    const uint16_t *Bn = bins + (int64_t)grp * Sp;
+    const uint4 *B4 = reinterpret_cast<const uint4 *>(bins + (int64_t)grp * Sp);
+    const int n8 = (Sb + 7) / 8; // 8-position groups of bins
     const double sc = (double)s.scale;
     double lsed[GS];
-    float lsef[GS];
 #pragma unroll
-    for (int hh = 0; hh < GS; ++hh) {
+    for (int hh = 0; hh < GS; ++hh)
         lsed[hh] = lse_ws[(int64_t)b * s.Hq + h0 + hh];
-        lsef[hh] = (float)lsed[hh];
-    }
     // rank key of position p (its bin is d): score recomputed from the logits
     auto rank_of = [&](int p, uint32_t d) -> uint64_t {
         float av[GS];
@@ -629,6 +615,167 @@ __global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap 
         return rank_key(pos_key(pos_score<GS>(av, lsed, sc, vn != nullptr, vv)), d, p);
     };
 
+    // the histogram's loads, then the first batch of bins (it does not depend on the
+    // threshold bin), so both are in flight together
+    static_assert(ATTN_HIST_BINS == 16 * ASEL_THREADS, "16 histogram bins per thread");
+    constexpr int UB = 4; // 16-byte loads of bins in flight per thread
+    uint4 q[4];
+    {
+        const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + (int64_t)grp * ATTN_HIST_BINS + ATTN_HIST_BINS -
+                                                          16 * (tid + 1));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            q[i] = h4[i];
+    }
+    uint4 u[UB];
+#pragma unroll
+    for (int j = 0; j < UB; ++j) {
+        const int i = tid + j * ASEL_THREADS;
+        u[j] = i < n8 ? B4[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // threshold bin: thread t holds bins 8191-16t down to 8176-16t
+    uint32_t hc[16];
+    {
+        const uint32_t asc[16] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w,
+                                  q[2].x, q[2].y, q[2].z, q[2].w, q[3].x, q[3].y, q[3].z, q[3].w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            hc[i] = asc[15 - i];
+    }
+    if (tid == 0) {
+        L.bres[0] = 0;
+        L.bres[1] = 1;
+        L.bres[2] = 0;
+        L.ncand = 0;
+    }
+    uint32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        tot += hc[i];
+    const uint32_t incl = block_incl_scan(tot, L.tmp); // (barriers inside)
+    {
+        const uint32_t top = ATTN_HIST_BINS - 1 - 16 * tid, want = (uint32_t)ksb;
+        uint32_t run = incl - tot;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (run < want && want <= run + hc[i]) {
+                L.bres[0] = top - i;
+                L.bres[1] = want - run;
+                L.bres[2] = hc[i];
+            }
+            run += hc[i];
+        }
+    }
+    __syncthreads();
+    const uint32_t d = L.bres[0], krem = L.bres[1], nbin = L.bres[2];
+
+    uint64_t thr;
+    if (nbin <= (uint32_t)SEL_CAP) {
+        // gather bin d's positions: per-lane bit masks, one slot reservation per wave
+        for (int i0 = tid; i0 - lane < n8; i0 += UB * ASEL_THREADS) {
+            if (i0 != tid) {
+#pragma unroll
+                for (int j = 0; j < UB; ++j) {
+                    const int i = i0 + j * ASEL_THREADS;
+                    u[j] = i < n8 ? B4[i] : make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
+            uint32_t cm = 0;
+#pragma unroll
+            for (int j = 0; j < UB; ++j) {
+                const uint32_t wd[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+                const int pb = 8 * (i0 + j * ASEL_THREADS);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t bn = (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu;
+                    cm |= (uint32_t)((bn == d) & (pb + e < Sb)) << (8 * j + e);
+                }
+            }
+            const uint32_t cl = (uint32_t)__popc(cm);
+            const uint32_t cincl = wave_incl_sum(cl);
+            const uint32_t wcount = (uint32_t)__builtin_amdgcn_readlane((int)cincl, WAVE - 1);
+            uint32_t base = 0;
+            if (lane == 0 && wcount != 0u)
+                base = atomicAdd(&L.ncand, wcount);
+            base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+            uint32_t slot = base + cincl - cl;
+            while (cm) {
+                const int bit = __builtin_ctz(cm);
+                cm &= cm - 1u;
+                if (slot < (uint32_t)SEL_CAP)
+                    L.pos[slot] = 8 * (i0 + (bit >> 3) * ASEL_THREADS) + (bit & 7);
+                ++slot;
+            }
+        }
+        __syncthreads();
+        const int nc = (int)min(L.ncand, (uint32_t)SEL_CAP);
+        for (int i = tid; i < nc; i += ASEL_THREADS)
+            L.key[i] = rank_of(L.pos[i], d);
+        __syncthreads();
+        thr = radix_select_u64(
+            [&](auto f) {
+                for (int i = tid; i < nc; i += ASEL_THREADS)
+                    f(L.key[i]);
+            },
+            krem, L.rad);
+    } else {
+        // a crowded bin: every radix pass recomputes the rank keys of bin d's positions
+        thr = radix_select_u64(
+            [&](auto f) {
+                for (int i = tid; i < n8; i += ASEL_THREADS) {
+                    const uint4 w4 = B4[i];
+                    const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t bn = (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu;
+                        const int p = 8 * i + e;
+                        if (bn == d && p < Sb)
+                            f(rank_of(p, d));
+                    }
+                }
+            },
+            krem, L.rad);
+    }
+    if (tid == 0) {
+        AttnSel r;
+        r.d = d;
+        r.pad = 0;
+        r.thr = thr;
+        sel[grp] = r;
+    }
+}
+
+// ------------------------------------------------------------------ pv
+// One workgroup per (chunk of P positions, group), 4 waves.  The group's
+// threshold and the first pass's bins and logits are loaded together; each
+// pass examines PV_PASS positions (2 per thread), keeps those at or above the
+// threshold (bin above d, or bin d with a rank key at least the threshold's,
+// recomputed from the logits already loaded), stages their V rows and
+// probabilities in LDS in position order, and streams the rows, 16 in flight
+// per lane (a 16-lane quarter wave per 256-byte row), into p * V partial sums.
+template <int GS>
+__global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap m, int Sp, int P,
+                                                             const uint16_t *__restrict__ v,
+                                                             const float *__restrict__ logit,
+                                                             const double *__restrict__ lse_ws,
+                                                             const uint16_t *__restrict__ bins,
+                                                             const float *__restrict__ vn,
+                                                             const AttnSel *__restrict__ sel,
+                                                             int32_t *__restrict__ pstage,
+                                                             uint32_t *__restrict__ pcount, float *__restrict__ part)
+{
+    __shared__ int64_t rows[PV_PASS]; // V row index of each kept position of the pass
+    __shared__ float pr[GS][PV_PASS];
+    __shared__ uint32_t wk[PV_WAVES];
+    __shared__ float red[PV_WAVES][GS][D];
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS, g = h0 / s.G;
+    const int c = blockIdx.x, npv = gridDim.x;
+    const int Sb = seq_len(s, m, b);
+    const int p0 = c * P, p1 = min(Sb, p0 + P);
+    const float *Lg = logit + ((int64_t)b * s.Hq + h0) * Sp;
+    const uint16_t *Bn = bins + (int64_t)grp * Sp;
+    const double sc = (double)s.scale;
     float acc[GS][8];
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh)
@@ -636,130 +783,12 @@ __global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap 
         for (int e = 0; e < 8; ++e)
             acc[hh][e] = 0.0f;
     uint32_t chunk_kept = 0;
-
-    if (p0 < p1) { // (uniform over the workgroup) chunks past the sequence's end only write zeros
-        // 1. threshold bin from the histogram: thread t holds bins 8191-16t down to 8176-16t
-        static_assert(ATTN_HIST_BINS == 16 * PV_THREADS, "16 histogram bins per thread");
-        uint32_t hc[16];
-        {
-            const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + (int64_t)grp * ATTN_HIST_BINS +
-                                                              ATTN_HIST_BINS - 16 * (tid + 1));
-            const uint4 q0 = h4[0], q1 = h4[1], q2 = h4[2], q3 = h4[3];
-            const uint32_t asc[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
-                                      q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-                hc[q] = asc[15 - q];
-        }
-        if (tid == 0) {
-            L.bres[0] = 0;
-            L.bres[1] = 1;
-            L.bres[2] = 0;
-            L.ncand = 0;
-        }
-        uint32_t tot = 0;
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            tot += hc[q];
-        const uint32_t incl = block_incl_scan(tot, L.tmp); // (barriers inside)
-        {
-            const uint32_t top = ATTN_HIST_BINS - 1 - 16 * tid;
-            const uint32_t want = (uint32_t)ksb;
-            uint32_t run = incl - tot;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                if (run < want && want <= run + hc[q]) {
-                    L.bres[0] = top - q;
-                    L.bres[1] = want - run;
-                    L.bres[2] = hc[q];
-                }
-                run += hc[q];
-            }
-        }
-        __syncthreads();
-        const uint32_t d = L.bres[0], krem = L.bres[1], nbin = L.bres[2];
-
-        // 2. rank-key threshold inside bin d
-        const int n8 = (Sb + 7) / 8;
-        const uint4 *B4 = reinterpret_cast<const uint4 *>(Bn);
-        uint64_t thr;
-        if (nbin <= (uint32_t)SEL_CAP) {
-            // gather bin d's positions: per-lane bit masks, one slot reservation per wave
-            for (int i0 = tid; i0 - lane < n8; i0 += 4 * PV_THREADS) {
-                uint4 u[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int i = i0 + q * PV_THREADS;
-                    u[q] = i < n8 ? B4[i] : make_uint4(0u, 0u, 0u, 0u);
-                }
-                uint32_t cm = 0;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t wd[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
-                    const int pb = 8 * (i0 + q * PV_THREADS);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t bn = (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu;
-                        cm |= (uint32_t)((bn == d) & (pb + e < Sb)) << (8 * q + e);
-                    }
-                }
-                const uint32_t cl = (uint32_t)__popc(cm);
-                const uint32_t cincl = wave_incl_sum(cl);
-                const uint32_t wcount = (uint32_t)__builtin_amdgcn_readlane((int)cincl, WAVE - 1);
-                uint32_t base = 0;
-                if (lane == 0 && wcount != 0u)
-                    base = atomicAdd(&L.ncand, wcount);
-                base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-                uint32_t slot = base + cincl - cl;
-                while (cm) {
-                    const int bit = __builtin_ctz(cm);
-                    cm &= cm - 1u;
-                    if (slot < (uint32_t)SEL_CAP)
-                        L.u.sel.pos[slot] = 8 * (i0 + (bit >> 3) * PV_THREADS) + (bit & 7);
-                    ++slot;
-                }
-            }
-            __syncthreads();
-            const int nc = (int)min(L.ncand, (uint32_t)SEL_CAP);
-            for (int i = tid; i < nc; i += PV_THREADS)
-                L.u.sel.key[i] = rank_of(L.u.sel.pos[i], d);
-            __syncthreads();
-            thr = radix_select_u64(
-                [&](auto f) {
-                    for (int i = tid; i < nc; i += PV_THREADS)
-                        f(L.u.sel.key[i]);
-                },
-                krem, L.rad);
-        } else {
-            // a crowded bin: every radix pass recomputes the rank keys of bin d's positions
-            thr = radix_select_u64(
-                [&](auto f) {
-                    for (int i = tid; i < n8; i += PV_THREADS) {
-                        const uint4 u = B4[i];
-                        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const uint32_t bn = (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu;
-                            const int p = 8 * i + e;
-                            if (bn == d && p < Sb)
-                                f(rank_of(p, d));
-                        }
-                    }
-                },
-                krem, L.rad);
-        }
-        __syncthreads(); // the selection's LDS is reused below
-
-        // 3. P V over the chunk's kept positions
-        const int quarter = lane >> 4, dl = lane & 15, slot = w * 4 + quarter;
-        constexpr int NSLOT = PV_WAVES * 4;
-        for (int sb = p0; sb < p1; sb += PV_PASS) {
-            // thread tid holds positions j0, j0 + 1 (j0 even and Sp a multiple of 8: j0 < Sb keeps both in
-            // the row; pages hold a multiple of 8 positions, so both share j0's page)
+    if (p0 < p1) { // (uniform over the workgroup) chunks past the sequence's end write zeros
+        // this thread's positions of the first pass, loaded with the threshold
+        auto load_pass = [&](int sb, uint32_t &bw, float2 (&lg)[GS], int64_t &vrow) {
             const int j0 = sb + 2 * tid;
-            uint32_t bw = 0;
-            float2 lg[GS];
-            int64_t vrow = 0;
+            bw = 0;
+            vrow = 0;
 #pragma unroll
             for (int hh = 0; hh < GS; ++hh)
                 lg[hh] = make_float2(0.0f, 0.0f);
@@ -770,6 +799,29 @@ __global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap 
                 for (int hh = 0; hh < GS; ++hh)
                     lg[hh] = *reinterpret_cast<const float2 *>(Lg + (int64_t)hh * Sp + j0);
             }
+        };
+        uint32_t bw;
+        float2 lg[GS];
+        int64_t vrow;
+        load_pass(p0, bw, lg, vrow);
+        const AttnSel st = sel[grp];
+        double lsed[GS];
+        float lsef[GS];
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh) {
+            lsed[hh] = lse_ws[(int64_t)b * s.Hq + h0 + hh];
+            lsef[hh] = (float)lsed[hh];
+        }
+        const uint32_t d = st.d;
+        const uint64_t thr = st.thr;
+        const int quarter = lane >> 4, dl = lane & 15, slot = w * 4 + quarter;
+        constexpr int NSLOT = PV_WAVES * 4;
+        for (int sb = p0; sb < p1; sb += PV_PASS) {
+            if (sb != p0)
+                load_pass(sb, bw, lg, vrow);
+            // thread tid holds positions j0, j0 + 1 (j0 even and Sp a multiple of 8: j0 < Sb keeps both in
+            // the row; pages hold a multiple of 8 positions, so both share j0's page)
+            const int j0 = sb + 2 * tid;
             const uint32_t ba = bw & 0xffffu, bb = bw >> 16;
             uint32_t ka = (uint32_t)(j0 < p1) & (uint32_t)(ba > d);
             uint32_t kb = (uint32_t)(j0 + 1 < p1) & (uint32_t)(bb > d);
@@ -791,28 +843,28 @@ __global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap 
             }
             const uint32_t ki = wave_incl_sum(ka + kb);
             if (lane == WAVE - 1)
-                L.wk[w] = ki;
+                wk[w] = ki;
             __syncthreads();
             uint32_t before = 0, nkept = 0;
 #pragma unroll
             for (int i = 0; i < PV_WAVES; ++i) {
-                before += i < w ? L.wk[i] : 0u;
-                nkept += L.wk[i];
+                before += i < w ? wk[i] : 0u;
+                nkept += wk[i];
             }
             const uint32_t sa = before + ki - (ka + kb), sbb = sa + ka; // pass-local slots
             if (ka) {
-                L.u.pv.rows[sa] = vrow;
+                rows[sa] = vrow;
 #pragma unroll
                 for (int hh = 0; hh < GS; ++hh)
-                    L.u.pv.pr[hh][sa] = expf(fmaf(s.scale, lg[hh].x, -lsef[hh]));
+                    pr[hh][sa] = expf(fmaf(s.scale, lg[hh].x, -lsef[hh]));
                 if (pstage)
                     pstage[(int64_t)grp * Sp + p0 + chunk_kept + sa] = j0;
             }
             if (kb) {
-                L.u.pv.rows[sbb] = vrow + 1;
+                rows[sbb] = vrow + 1;
 #pragma unroll
                 for (int hh = 0; hh < GS; ++hh)
-                    L.u.pv.pr[hh][sbb] = expf(fmaf(s.scale, lg[hh].y, -lsef[hh]));
+                    pr[hh][sbb] = expf(fmaf(s.scale, lg[hh].y, -lsef[hh]));
                 if (pstage)
                     pstage[(int64_t)grp * Sp + p0 + chunk_kept + sbb] = j0 + 1;
             }
@@ -824,7 +876,7 @@ __global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap 
                 for (int qq = 0; qq < PV_U; ++qq) {
                     const int r = r0 + NSLOT * qq;
                     if (r < nk)
-                        u[qq] = *reinterpret_cast<const uint4 *>(v + L.u.pv.rows[r] * D + dl * 8);
+                        u[qq] = *reinterpret_cast<const uint4 *>(v + rows[r] * D + dl * 8);
                 }
 #pragma unroll
                 for (int qq = 0; qq < PV_U; ++qq) {
@@ -834,7 +886,7 @@ __global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap 
                         Vec16<uint16_t>::unpack(u[qq], vv);
 #pragma unroll
                         for (int hh = 0; hh < GS; ++hh) {
-                            const float pv = L.u.pv.pr[hh][r];
+                            const float pv = pr[hh][r];
 #pragma unroll
                             for (int e = 0; e < 8; ++e)
                                 acc[hh][e] = fmaf(pv, vv[e], acc[hh][e]);
@@ -862,16 +914,16 @@ __global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap 
         for (int hh = 0; hh < GS; ++hh)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                L.u.red[w][hh][(lane & 15) * 8 + e] = acc[hh][e];
+                red[w][hh][(lane & 15) * 8 + e] = acc[hh][e];
     }
     __syncthreads();
     float *mine = part + ((int64_t)grp * npv + c) * GS * D;
     for (int i = tid; i < GS * D; i += PV_THREADS) {
         const int hh = i / D, dd = i % D;
-        float x = L.u.red[0][hh][dd];
+        float x = red[0][hh][dd];
 #pragma unroll
         for (int ww = 1; ww < PV_WAVES; ++ww)
-            x += L.u.red[ww][hh][dd];
+            x += red[ww][hh][dd];
         mine[i] = x;
     }
     if (pcount && tid == 0)
@@ -949,21 +1001,16 @@ __global__ __launch_bounds__(256) void attn_pos_kernel(AttnShape s, KvMap m, int
 }
 
 // ------------------------------------------------------------------ host side
-// PV chunks: whole passes of PV_PASS positions, about ATTN_PV_TARGET_WGS
-// workgroups over all groups, at most PV_MAX_CHUNKS per group.
-static void pv_chunks(int64_t S, int64_t groups, int *P, int *npv)
+// PV chunks: at most PV_MAX_CHUNKS per group, each a whole number of passes.
+static void pv_chunks(int64_t S, int *P, int *npv)
 {
-    int64_t per = (S * groups + ATTN_PV_TARGET_WGS - 1) / ATTN_PV_TARGET_WGS;
-    per = per < PV_PASS ? PV_PASS : per;
+    int64_t n = (S + PV_PASS - 1) / PV_PASS;
+    if (n > PV_MAX_CHUNKS)
+        n = PV_MAX_CHUNKS;
+    int64_t per = (S + n - 1) / n;
     per = (per + PV_PASS - 1) / PV_PASS * PV_PASS;
-    int64_t n = (S + per - 1) / per;
-    if (n > PV_MAX_CHUNKS) {
-        per = (S + PV_MAX_CHUNKS - 1) / PV_MAX_CHUNKS;
-        per = (per + PV_PASS - 1) / PV_PASS * PV_PASS;
-        n = (S + per - 1) / per;
-    }
     *P = (int)per;
-    *npv = (int)n;
+    *npv = (int)((S + per - 1) / per);
 }
 
 static inline char *align256(char *p) { return (char *)(((uintptr_t)p + 255) & ~(uintptr_t)255); }
@@ -974,7 +1021,7 @@ size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base)
     const int64_t nqk = (s.S + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK;
     const int64_t G = s.B * s.Hsel;
     int P, npv;
-    pv_chunks(s.S, G, &P, &npv);
+    pv_chunks(s.S, &P, &npv);
     char *p = base + RMM_WS_HEADER_BYTES_INTERNAL;
     AttnWs w;
     w.logit = (float *)p;
@@ -989,6 +1036,8 @@ size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base)
     p = align256(p + (size_t)(G * ATTN_HIST_BINS) * 4);
     w.pcount = (uint32_t *)p;
     p = align256(p + (size_t)(G * npv) * 4);
+    w.sel = p;
+    p = align256(p + (size_t)G * sizeof(AttnSel));
     w.pstage = (int32_t *)p;
     p = align256(p + (size_t)(G * Sp) * 4);
     w.pvpart = (float *)p;
@@ -1016,14 +1065,16 @@ static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q
     const int G = (int)(s.B * s.Hsel);
     const int nqk = (int)((s.S + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK);
     int P, npv;
-    pv_chunks(s.S, G, &P, &npv);
+    pv_chunks(s.S, &P, &npv);
+    AttnSel *sel = reinterpret_cast<AttnSel *>(ws.sel);
     attn_qk_kernel<GS><<<dim3(nqk, G), QK_THREADS, 0, st>>>(s, m, Sp, q, kt, kn, ws.logit, ws.pstat, dim_idx,
                                                              ws.hist);
     const int nkc = (int)((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK);
     const int nsub = key_chunks_per_wg(s.S);
     attn_key_kernel<GS><<<dim3((nkc + nsub - 1) / nsub, G), 256, 0, st>>>(
         s, m, Sp, nqk, nsub, ws.logit, ws.pstat, ws.lse, lse, vn, ws.bins, ws.hist);
-    attn_pv_kernel<GS><<<dim3(npv, G), PV_THREADS, 0, st>>>(s, m, Sp, P, v, ws.logit, ws.lse, ws.bins, ws.hist, vn,
+    attn_select_kernel<GS><<<G, ASEL_THREADS, 0, st>>>(s, m, Sp, ws.logit, ws.lse, ws.bins, ws.hist, vn, sel);
+    attn_pv_kernel<GS><<<dim3(npv, G), PV_THREADS, 0, st>>>(s, m, Sp, P, v, ws.logit, ws.lse, ws.bins, vn, sel,
                                                             pos_idx ? ws.pstage : nullptr,
                                                             pos_idx ? ws.pcount : nullptr, ws.pvpart);
     attn_pv_reduce_kernel<GS><<<G * (GS * D / WAVE), PVR_WAVES * WAVE, 0, st>>>(s, npv, ws.pvpart, out);

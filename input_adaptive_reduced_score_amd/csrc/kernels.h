@@ -40,9 +40,6 @@
 #define ATTN_QK_CHUNK 512   // positions per QK workgroup
 #define ATTN_KEY_CHUNK 2048 // positions per key/histogram workgroup
 #define ATTN_HIST_BINS 8192 // position-score histogram: half-nat bins outside [-32, 0), 1/128 nat inside
-#ifndef ATTN_PV_TARGET_WGS
-#define ATTN_PV_TARGET_WGS 384 // PV workgroups the chunking aims for (each resolves its group's threshold)
-#endif
 #define ATTN_MAX_GROUPS 512 // B * Hsel and B * Hkv limit of the attention entry points (the range the tests cover)
 #define RMM_WS_HEADER_BYTES_INTERNAL 4096
 
@@ -93,6 +90,7 @@ struct AttnWs {
     uint16_t *bins;   // [B][Hsel][Sp] histogram bin of every position's score
     uint32_t *hist;   // [B][Hsel][ATTN_HIST_BINS]
     uint32_t *pcount; // [B][Hsel][npv] kept positions per PV chunk
+    void *sel;        // [B][Hsel] threshold of each group (bin, rank key)
     int32_t *pstage;  // [B][Hsel][Sp] kept positions of each PV chunk, staged at the chunk's start
     float *pvpart;    // [B][Hsel][npv][GS][D]
 };
