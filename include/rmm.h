@@ -128,6 +128,25 @@ rmm_status_t rmm_linear(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int
                         const int32_t *idx, int64_t k, int64_t tile,
                         float *y, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* rmm_linear for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and results as rmm_linear with the same arguments, with no
+ * workspace argument.  Its scratch is a device array of
+ * RMM_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, kept until the
+ * process ends; the call allocates and frees nothing.  All calls on one GPU
+ * share that array, so calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  The array needs
+ * no initialisation: every call writes the scratch it reads.
+ * Errors: as rmm_linear; RMM_EUNSUPPORTED when the product needs more scratch
+ * than the array holds (rmm_linear_workspace_size above it: e.g. more than 8
+ * tokens per tile times M = 32768 on the streaming path, or T * k above
+ * 8 Mi elements on the MFMA path). */
+#define RMM_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+rmm_status_t rmm_linear_noalloc(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int64_t ldx,
+                                const void *wt, rmm_dtype_t wt_t, int64_t M, int64_t ldw,
+                                const int32_t *idx, int64_t k, int64_t tile,
+                                float *y, int64_t ldy, hipStream_t stream);
+
 /* Dense product y = x @ wt over all K slices, by the same kernels without the
  * index list (the r = 1 baseline; blog section 8 asks for a full path next to
  * the compact one).  Same arguments and rules as rmm_linear. */

@@ -92,6 +92,8 @@ def lib():
                 "rmm_select_blocks": (i32, [vp, i32, i64, i64, i64, i64, i64, dbl, vp, vp, sz, vp]),
                 "rmm_linear_workspace_size": (sz, [i64, i64, i64, i64, i64, i32]),
                 "rmm_linear": (i32, [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, i64, i64, vp, i64, vp, sz, vp]),
+                "rmm_linear_noalloc": (i32, [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, i64, i64, vp, i64,
+                                             vp]),
                 "rmm_linear_dense_workspace_size": (sz, [i64, i64, i64, i32]),
                 "rmm_linear_dense": (i32, [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, i64, vp, sz, vp]),
                 "rmm_attn_decode_workspace_size": (sz, [i64, i64, i64, i64, i64, dbl, dbl, i32]),
@@ -121,7 +123,7 @@ def lib():
 
 EXPORTS = ("rmm_keep_count", "rmm_select_workspace_size", "rmm_select", "rmm_block_keep_count",
            "rmm_select_blocks_workspace_size", "rmm_select_blocks", "rmm_linear_workspace_size", "rmm_linear",
-           "rmm_linear_dense_workspace_size", "rmm_linear_dense", "rmm_attn_decode_workspace_size",
+           "rmm_linear_noalloc", "rmm_linear_dense_workspace_size", "rmm_linear_dense", "rmm_attn_decode_workspace_size",
            "rmm_gate_up_workspace_size", "rmm_gate_up",
            "rmm_attn_decode", "rmm_attn_decode_ex", "rmm_attn_decode_paged", "rmm_attn_decode_dense_paged", "rmm_attn_decode_dense_workspace_size", "rmm_attn_decode_dense", "rmm_status_string",
            "rmm_last_error")
@@ -241,6 +243,22 @@ def linear(x: torch.Tensor, wt: torch.Tensor, idx: torch.Tensor, tile: int, out:
     w = ws if ws is not None else _WS.get(need, x.device)
     _check(L.rmm_linear(_ptr(x), _dtype(x), T, K, _ld(x), _ptr(wt), _dtype(wt), M, _ld(wt), _ptr(idx), k, tile,
                         _ptr(out), _ld(out), _ptr(w), w.numel() * w.element_size(), _stream()))
+    return out
+
+
+def linear_noalloc(x: torch.Tensor, wt: torch.Tensor, idx: torch.Tensor, tile: int,
+                   out: torch.Tensor | None = None):
+    """rmm_linear without a workspace: the library's own device scratch array is used (calls on one
+    GPU must not overlap).  Same arguments and results as linear()."""
+    L = lib()
+    _dev(x, "x")
+    T, K = x.shape
+    k = idx.shape[1]
+    M = wt.shape[1]
+    if out is None:
+        out = torch.empty((T, M), dtype=torch.float32, device=x.device)
+    _check(L.rmm_linear_noalloc(_ptr(x), _dtype(x), T, K, _ld(x), _ptr(wt), _dtype(wt), M, _ld(wt), _ptr(idx), k,
+                                tile, _ptr(out), _ld(out), _stream()))
     return out
 
 

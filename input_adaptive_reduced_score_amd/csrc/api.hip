@@ -276,6 +276,65 @@ rmm_status_t rmm_linear(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int
     return linear_common(x, xt, T, K, ldx, wt, M, ldw, idx, k, tile, false, y, ldy, ws, ws_bytes, stream);
 }
 
+// ------------------------------------------------------------------ linear without a caller workspace
+// For callers that cannot allocate device memory: the split-K partials (or the
+// packed activations of the MFMA path) live in a file-scope device array of
+// RMM_NOALLOC_SCRATCH_BYTES, one copy per GPU, held until the process ends.
+// Host code never passes the array's name to a kernel: each device's address
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is used.
+static __device__ __align__(256) char scratch[RMM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+rmm_status_t scratch_for_current_device(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(RMM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(RMM_EUNSUPPORTED, "device %d beyond the %d devices the scratch table covers", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(RMM_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return RMM_OK;
+}
+} // namespace
+
+rmm_status_t rmm_linear_noalloc(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int64_t ldx, const void *wt,
+                                rmm_dtype_t wt_t, int64_t M, int64_t ldw, const int32_t *idx, int64_t k, int64_t tile,
+                                float *y, int64_t ldy, hipStream_t stream)
+{
+    rmm_status_t st = check_linear(x, xt, T, K, ldx, wt, wt_t, M, ldw, y, ldy);
+    if (st != RMM_OK)
+        return st;
+    if (!idx)
+        return fail(RMM_EINVAL, "null idx");
+    if (k < 1 || k > K)
+        return fail(RMM_EINVAL, "k = %lld not in [1, K=%lld]", (long long)k, (long long)K);
+    if (tile < 1)
+        return fail(RMM_EINVAL, "tile must be positive");
+    const size_t need = linear_ws(T, K, M, k, tile, xt, false);
+    if (need > (size_t)RMM_NOALLOC_SCRATCH_BYTES)
+        return fail(RMM_EUNSUPPORTED, "this product needs %zu bytes of scratch, above the %d-byte device array",
+                    need, RMM_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((st = scratch_for_current_device(&ws)) != RMM_OK)
+        return st;
+    return linear_common(x, xt, T, K, ldx, wt, M, ldw, idx, k, tile, false, y, ldy, ws,
+                         (size_t)RMM_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 size_t rmm_linear_dense_workspace_size(int64_t T, int64_t K, int64_t M, rmm_dtype_t xt)
 {
     if (T < 1 || K < 1 || M < 1)
