@@ -214,25 +214,37 @@ def main():
             rmm.select(xs[i], cs_[i], 1, r, idx=idxb[i])
 
         def step(i):
+            # the decode step in one launch (+ the split-K sum): selection and reduced product,
+            # the kept index list written as well
+            j = i % ncp
+            rmm.select_linear(xs[j], cs_[j], r, ws_[j], out=yb, idx=idxb[j])
+
+        def step2(i):
+            # the same step as two calls: rmm_select, then rmm_linear on its list
             j = i % ncp
             rmm.select(xs[j], cs_[j], 1, r, idx=idxb[j])
             rmm.linear(xs[j], ws_[j], idxb[j], 1, out=yb)
 
         t_step = time_loop(step, steps, warmup, torch)
+        t_launch = event_avg(step, steps, torch)
+        t_step2 = time_loop(step2, steps, warmup, torch)
         t_eager = eager_loop(step, min(steps, 50), torch)
         t_gemv = event_avg(lambda i: rmm.linear(xs[i % ncp], ws_[i % ncp], idxb[i % ncp], 1, out=yb), steps, torch)
         t_sel = event_avg(lambda i: rmm.select(xs[i % ncp], cs_[i % ncp], 1, r, idx=idxb[i % ncp]), steps, torch)
+        by = A.decode_step_bytes(K, M, k)
         rec = {"workload": "decode_down_proj", "r": r, "k": k,
-               "step_us": t_step * 1e6, "eager_step_us": t_eager * 1e6, "select_us": t_sel * 1e6,
-               "gemv_us": t_gemv * 1e6,
-               "retained_bytes": A.decode_step_bytes(K, M, k),
-               "step_GBps": A.decode_step_bytes(K, M, k) / t_step / 1e9,
+               "step_us": t_step * 1e6, "fused_launch_us": t_launch * 1e6, "eager_step_us": t_eager * 1e6,
+               "two_call_step_us": t_step2 * 1e6, "select_us": t_sel * 1e6, "gemv_us": t_gemv * 1e6,
+               "retained_bytes": by, "step_GBps": by / t_step / 1e9, "fused_launch_GBps": by / t_launch / 1e9,
+               "two_call_step_GBps": by / t_step2 / 1e9,
                "gemv_GBps": A.gemv_launch_bytes(k, M) / t_gemv / 1e9}
+        rec["fused_launch_frac_hbm"] = rec["fused_launch_GBps"] / A.HBM_PEAK_GBS
         rec["gemv_frac_hbm"] = rec["gemv_GBps"] / A.HBM_PEAK_GBS
         rec["rel_l2_vs_dense"] = rel_l2(rmm.linear(xs[0], ws_[0], idxb[0], 1), rmm.linear_dense(xs[0], ws_[0]))
         sweep.append(rec)
-        log(f"[bench] decode r={r}: step {rec['step_us']:.2f} us ({rec['step_GBps']:.0f} GB/s), gemv "
-            f"{rec['gemv_us']:.2f} us ({rec['gemv_GBps']:.0f} GB/s), select {rec['select_us']:.2f} us, "
+        log(f"[bench] decode r={r}: step {rec['step_us']:.2f} us ({rec['step_GBps']:.0f} GB/s; fused launch "
+            f"{rec['fused_launch_us']:.2f} us by events), as two calls {rec['two_call_step_us']:.2f} us (select "
+            f"{rec['select_us']:.2f} us, gemv {rec['gemv_us']:.2f} us = {rec['gemv_GBps']:.0f} GB/s), "
             f"rel-L2 vs dense {rec['rel_l2_vs_dense']:.3f}")
         if r == 0.5:
             head = rec
@@ -242,8 +254,7 @@ def main():
         idxw = rmm.select(xs[0], cs_[0], 1, 0.5)
 
         def wstep(i):
-            rmm.select(xs[0], cs_[0], 1, 0.5, idx=idxw)
-            rmm.linear(xs[0], ws_[0], idxw, 1, out=yb)
+            rmm.select_linear(xs[0], cs_[0], 0.5, ws_[0], out=yb, idx=idxw)
 
         t_warm = time_loop(wstep, steps, warmup, torch)
         sweep.append({"workload": "decode_down_proj_warm_cache", "r": 0.5, "k": k, "step_us": t_warm * 1e6,
@@ -560,16 +571,18 @@ def main():
                          f"bf16) of the single-threaded C oracle, {el:.1f} s"}
         log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s retained ({n} steps in {el:.1f} s)")
 
-    k_head = head["k"]
-    sha = src_hash(["input_adaptive_reduced_score_amd/csrc/gemv.hip", "input_adaptive_reduced_score_amd/csrc/device.h",
+    sha = src_hash(["input_adaptive_reduced_score_amd/csrc/gemv.hip",
+                    "input_adaptive_reduced_score_amd/csrc/select_body.h",
+                    "input_adaptive_reduced_score_amd/csrc/radix.h",
+                    "input_adaptive_reduced_score_amd/csrc/device.h",
                     "input_adaptive_reduced_score_amd/csrc/kernels.h"])
-    roofline = {"kernel": "reduced decode product launch: gemv_kernel<bf16,NT=1> + split-K gemv_reduce_kernel",
+    roofline = {"kernel": "fused decode step: select_gemv_kernel<bf16,16> + split-K gemv_reduce_kernel<1,512>",
                 "bound": "hbm",
-                "achieved": head["gemv_GBps"], "peak": A.HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": head["gemv_GBps"] / A.HBM_PEAK_GBS,
-                "algorithmic_bytes_per_launch": A.gemv_launch_bytes(k_head, M),
-                "avg_launch_us": head["gemv_us"],
-                "traffic": load_traffic("gemv_decode_r0.5", sha), "source_sha": sha}
+                "achieved": head["fused_launch_GBps"], "peak": A.HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": head["fused_launch_GBps"] / A.HBM_PEAK_GBS,
+                "algorithmic_bytes_per_launch": head["retained_bytes"],
+                "avg_launch_us": head["fused_launch_us"],
+                "traffic": load_traffic("select_gemv_decode_r0.5", sha), "source_sha": sha}
     line = {
         "metric": "retained-work HBM GB/s & MFMA TFLOP/s vs r; reduced attn-decode us at S=32K",
         "value": head["step_GBps"],
@@ -583,7 +596,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "decode_down_proj: select + reduced GEMV, X[1,14336] bf16 = silu(a)*b, "
+        "config": {"workload": "decode_down_proj: select + reduced GEMV in one launch (rmm_select_linear, kept "
+                               "list written), X[1,14336] bf16 = silu(a)*b, "
                                "W^T[14336,4096] bf16 ~N(0,0.02), r=0.5 (k=7168), cold-cache input rotation",
                    "r": 0.5, "K": K, "M": M, "T": 1, "accumulate": "fp32", "parallelism": "single GPU"},
         "roofline": roofline,

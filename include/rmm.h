@@ -89,6 +89,33 @@ rmm_status_t rmm_select(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int
                         const float *c, int64_t tile, double r,
                         int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ fused decode step
+ * rmm_select followed by rmm_linear for one token, as one launch plus the
+ * split-K sum (blog sections 5.1-5.3: score, top-k, compact product; paper
+ * abstract).  One workgroup scores and selects; as soon as its first radix
+ * pass has run it tells the workgroups that stream W^T which slices are kept
+ * for certain, and they start on those rows while it resolves the rest, so the
+ * product does not wait for the whole selection.
+ *   x    [K] activations of the token (dtype xt), 16-byte aligned; read in
+ *        16-byte vectors, so its buffer holds K rounded up to a multiple of 8
+ *        (bf16) or 4 (fp32) elements (the padding is read and ignored)
+ *   c    [K] fp32 slice weights, c[j] >= 0
+ *   wt   [K][ldw] W^T (dtype xt); y out, fp32 [M]
+ *   idx  optional out (NULL ok), int32 [k], k = rmm_keep_count(K, r): the kept
+ *        slices in ascending order, exactly as rmm_select(x, xt, 1, K, K, c, 1, r, ...)
+ *        writes them
+ * The kept set is rmm_select's; y is rmm_linear's up to fp32 summation order
+ * (each split adds the rows kept for certain before the others).  Deterministic.
+ * Workspace: rmm_select_linear_workspace_size(K, M, xt) bytes.  Unlike the
+ * other entry points, the first RMM_WS_HEADER_BYTES bytes of this workspace
+ * must be zero before the first call that uses it (a zero-filled allocation);
+ * every call leaves them zero and no other entry point writes them.
+ * Limits: K <= 32768; one token. */
+size_t rmm_select_linear_workspace_size(int64_t K, int64_t M, rmm_dtype_t xt);
+rmm_status_t rmm_select_linear(const void *x, rmm_dtype_t xt, int64_t K, const float *c, double r,
+                               const void *wt, rmm_dtype_t wt_t, int64_t M, int64_t ldw,
+                               int32_t *idx, float *y, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ block-granular selection
  * The blog's block variant (section 5.1: a block's importance is the mean
  * absolute activation over its neurons; 5.2: top-k over blocks, the block mask

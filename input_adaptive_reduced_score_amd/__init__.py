@@ -87,6 +87,8 @@ def lib():
                 "rmm_keep_count": (i64, [i64, dbl]),
                 "rmm_select_workspace_size": (sz, [i64, i64, i64, i32]),
                 "rmm_select": (i32, [vp, i32, i64, i64, i64, vp, i64, dbl, vp, vp, sz, vp]),
+                "rmm_select_linear_workspace_size": (sz, [i64, i64, i32]),
+                "rmm_select_linear": (i32, [vp, i32, i64, vp, dbl, vp, i32, i64, i64, vp, vp, vp, sz, vp]),
                 "rmm_block_keep_count": (i64, [i64, dbl]),
                 "rmm_select_blocks_workspace_size": (sz, [i64, i64, i64, i64, i32]),
                 "rmm_select_blocks": (i32, [vp, i32, i64, i64, i64, i64, i64, dbl, vp, vp, sz, vp]),
@@ -121,7 +123,8 @@ def lib():
     return _lib
 
 
-EXPORTS = ("rmm_keep_count", "rmm_select_workspace_size", "rmm_select", "rmm_block_keep_count",
+EXPORTS = ("rmm_keep_count", "rmm_select_workspace_size", "rmm_select", "rmm_select_linear_workspace_size",
+           "rmm_select_linear", "rmm_block_keep_count",
            "rmm_select_blocks_workspace_size", "rmm_select_blocks", "rmm_linear_workspace_size", "rmm_linear",
            "rmm_linear_noalloc", "rmm_linear_dense_workspace_size", "rmm_linear_dense", "rmm_attn_decode_workspace_size",
            "rmm_gate_up_workspace_size", "rmm_gate_up",
@@ -202,6 +205,32 @@ def select(x: torch.Tensor, c: torch.Tensor, tile: int, r: float, idx: torch.Ten
     _check(L.rmm_select(_ptr(x), _dtype(x), T, K, _ld(x), _ptr(c), tile, float(r), _ptr(idx), _ptr(w),
                         w.numel() * w.element_size(), _stream()))
     return idx
+
+
+def select_linear(x: torch.Tensor, c: torch.Tensor, r: float, wt: torch.Tensor, out: torch.Tensor | None = None,
+                  idx: torch.Tensor | None = None, want_idx: bool = True, ws=None):
+    """One-token decode step in one launch: selection + reduced product.  x [1,K] or [K];
+    returns (y [1,M] fp32, idx [1,k] int32 or None).  The workspace's first WS_HEADER_BYTES
+    bytes must be zero before first use (the default workspaces are zero-filled)."""
+    L = lib()
+    _dev(x, "x")
+    K = x.shape[-1]
+    if x.dim() == 2 and x.shape[0] != 1:
+        raise ValueError("select_linear takes one token")
+    M = wt.shape[1]
+    k = keep_count(K, r)
+    if k < 0:
+        raise RmmError(1, "ratio must be in (0, 1]")
+    if out is None:
+        out = torch.empty((1, M), dtype=torch.float32, device=x.device)
+    if want_idx and idx is None:
+        idx = torch.empty((1, k), dtype=torch.int32, device=x.device)
+    need = L.rmm_select_linear_workspace_size(K, M, _dtype(x))
+    w = ws if ws is not None else _WS.get(need, x.device)
+    _check(L.rmm_select_linear(_ptr(x), _dtype(x), K, _ptr(c), float(r), _ptr(wt), _dtype(wt), M, _ld(wt),
+                               _ptr(idx if want_idx else None), _ptr(out), _ptr(w), w.numel() * w.element_size(),
+                               _stream()))
+    return out, (idx if want_idx else None)
 
 
 def block_keep_count(nb: int, keep: float) -> int:

@@ -176,6 +176,52 @@ rmm_status_t rmm_select(const void *x, rmm_dtype_t xt, int64_t T, int64_t K, int
     return launch_status(rmm::launch_select(x, xt == RMM_BF16, T, K, ldx, c, tile, k, idx, pmax, stream), "select");
 }
 
+// ------------------------------------------------------------------ fused decode step
+size_t rmm_select_linear_workspace_size(int64_t K, int64_t M, rmm_dtype_t xt)
+{
+    if (K < 1 || M < 1 || K > SELECT_MAX_K || M > INT32_MAX || (xt != RMM_F32 && xt != RMM_BF16))
+        return 0;
+    if (!rmm::select_gemv_fits(K, M, xt == RMM_BF16))
+        return 0;
+    return RMM_WS_HEADER_BYTES + round256(rmm::select_gemv_ws_bytes(K, M, xt == RMM_BF16));
+}
+
+rmm_status_t rmm_select_linear(const void *x, rmm_dtype_t xt, int64_t K, const float *c, double r, const void *wt,
+                               rmm_dtype_t wt_t, int64_t M, int64_t ldw, int32_t *idx, float *y, void *ws,
+                               size_t ws_bytes, hipStream_t stream)
+{
+    if (!x || !c || !wt || !y)
+        return fail(RMM_EINVAL, "null pointer (x=%p c=%p wt=%p y=%p)", x, (const void *)c, wt, (void *)y);
+    if (K < 1 || M < 1)
+        return fail(RMM_EINVAL, "sizes must be positive (K=%lld M=%lld)", (long long)K, (long long)M);
+    if (xt != RMM_F32 && xt != RMM_BF16)
+        return fail(RMM_EINVAL, "unknown dtype %d", (int)xt);
+    if (wt_t != xt)
+        return fail(RMM_EINVAL, "x and W^T dtypes differ (%d vs %d)", (int)xt, (int)wt_t);
+    if (ldw < M)
+        return fail(RMM_EINVAL, "ldw (%lld) < M (%lld)", (long long)ldw, (long long)M);
+    const int64_t k = keep_count(K, r);
+    if (k < 0)
+        return fail(RMM_EINVAL, "retention ratio %g not in (0, 1]", r);
+    if (K > SELECT_MAX_K || M > INT32_MAX)
+        return fail(RMM_EUNSUPPORTED, "K = %lld above the selector limit %d or M beyond 2^31", (long long)K,
+                    SELECT_MAX_K);
+    const int ve = vec_elems(xt);
+    if (!aligned16(x) || !aligned16(wt) || ldw % ve || ((uintptr_t)y & 3u) || ((uintptr_t)idx & 3u))
+        return fail(RMM_EUNSUPPORTED, "x and W^T must be 16-byte aligned with ldw a multiple of %d elements, "
+                                      "y and idx 4-byte aligned", ve);
+    if (!rmm::select_gemv_fits(K, M, xt == RMM_BF16))
+        return fail(RMM_EUNSUPPORTED, "no split of K = %lld over the fused launch (at most 1024 slices per split)",
+                    (long long)K);
+    const size_t need = rmm_select_linear_workspace_size(K, M, xt);
+    if (!ws || ws_bytes < need)
+        return fail(RMM_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    init_once();
+    return launch_status(rmm::launch_select_gemv(x, xt == RMM_BF16, K, c, k, wt, ldw, M, idx, y, (char *)ws,
+                                                 (char *)ws + RMM_WS_HEADER_BYTES, stream),
+                         "select_linear");
+}
+
 // ------------------------------------------------------------------ block-granular selection
 int64_t rmm_block_keep_count(int64_t nb, double keep)
 {

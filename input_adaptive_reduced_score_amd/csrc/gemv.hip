@@ -12,6 +12,7 @@
 // are deterministic.  (Many tokens per tile: linear.hip.)
 #include "device.h"
 #include "kernels.h"
+#include "select_body.h"
 
 namespace rmm {
 
@@ -136,8 +137,14 @@ template <int NT, int CW>
 __global__ __launch_bounds__(RED_WAVES * WAVE) void gemv_reduce_kernel(const float *__restrict__ part, int T,
                                                                        int tile, int groups_per_tile, int nslices,
                                                                        int nsplit, int M, float *__restrict__ y,
-                                                                       int64_t ldy)
+                                                                       int64_t ldy, uint64_t *__restrict__ clear1 = nullptr,
+                                                                       uint64_t *__restrict__ clear2 = nullptr)
 {
+    if (clear1 && blockIdx.x == 0 && threadIdx.x == 0) {
+        // the fused launch before this one has finished: its flags return to zero
+        __hip_atomic_store(clear1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(clear2, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     constexpr int CHUNKS = NT * CW / WAVE;
     __shared__ float red[RED_WAVES][WAVE];
     const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
@@ -254,6 +261,257 @@ hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const v
                      : gemv_dispatch<uint16_t, false>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, y, ldy, st);
     return dense ? gemv_dispatch<float, true>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, y, ldy, st)
                  : gemv_dispatch<float, false>(p, x, ldx, T, tile, wt, ldw, M, idx, k, part, y, ldy, st);
+}
+
+// ============================================================================ fused select + GEMV (one token)
+// One launch selects and multiplies.  Workgroup 0 runs the tile's selection
+// (select_body with PUB) and publishes, in two steps, which slices are kept;
+// every workgroup (0 included, after its selection) owns a column slice and a
+// range of R slice indices, 16 waves of up to 64 slices each.  After flag1 a
+// wave streams the rows of its slices above the undecided digit (kept for
+// certain) while workgroup 0 still resolves that digit; after flag2 it streams
+// the digit's kept rows.  Each wave adds its rows in that fixed order, the waves
+// are summed in order, and gemv_reduce_kernel sums the splits in order, so the
+// result is deterministic.  Workgroup 0 is dispatched first and waits on no
+// other workgroup, so the waits end whatever the residency; each wait is
+// bounded all the same, and a wait that runs out poisons the output with NaN.
+constexpr int FUSED_WAVES = SEL_THREADS / WAVE; // 16
+constexpr int FUSED_SPIN = 1 << 20;             // polls (about 1 s) before a wait gives up
+
+// Polls a published word until its ready bit is set; 0 if it never is.
+__device__ __forceinline__ uint64_t wait_sig(const uint64_t *sig)
+{
+    for (int it = 0; it < FUSED_SPIN; ++it) {
+        const uint64_t v = pub_load64(sig);
+        if (v & 1ull)
+            return v;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return 0ull;
+}
+
+template <typename TE, int PER>
+__global__ __launch_bounds__(SEL_THREADS) void select_gemv_kernel(const TE *__restrict__ x, const float *__restrict__ c,
+                                                                  int K, int k, int cvec, const TE *__restrict__ wt,
+                                                                  int64_t ldw, int M, int nslices, SelPub pub,
+                                                                  float *__restrict__ part, int32_t *__restrict__ idx)
+{
+    constexpr int VEC = Vec16<TE>::N;
+    constexpr int CW = WAVE * VEC; // columns per slice
+    constexpr int U = GEMV_UNROLL; // kept rows in flight per wave
+    __shared__ float red[FUSED_WAVES][CW];
+    __shared__ uint64_t sig[2];
+    __shared__ uint32_t wcnt[FUSED_WAVES];
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    if (blockIdx.x == 0)
+        select_body<TE, PER, true>(x, 0, 1, K, 1, c, nullptr, 0, 1, 1, cvec, k, 0, nullptr, pub);
+
+    const int slice = (int)blockIdx.x % nslices, split = (int)blockIdx.x / nslices;
+    // this workgroup's slice range: column slice 0 starts with the selecting workgroup's short range
+    int ws0, ws1;
+    if (slice == 0) {
+        ws0 = split_start0(pub, split, K);
+        ws1 = split_start0(pub, split + 1, K);
+    } else {
+        ws0 = min(split * pub.R, K);
+        ws1 = min(ws0 + pub.R, K);
+    }
+    const int RW = (ws1 - ws0 + FUSED_WAVES - 1) / FUSED_WAVES; // <= 64 slices per wave
+    const int lo = ws0 + w * RW;
+    const int hi = min(lo + RW, ws1);
+    const int n = hi > lo ? hi - lo : 0;
+    const int col = slice * CW + lane * VEC;
+    const bool active = col < M;
+    // this lane's slice: activation and score key (the selecting workgroup's
+    // arithmetic: one fp32 multiply of |x| by the slice weight), loaded before the wait
+    float xj = 0.0f, cj = 0.0f;
+    if (lane < n) {
+        xj = ld_elem(x, lo + lane);
+        cj = c[lo + lane];
+    }
+    const uint32_t key0 = lane < n ? nonneg_key(__fmul_rn(fabsf(xj), cj)) : 0u;
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        acc[e] = 0.0f;
+    // rows of the slices lo + b for the set bits b of a wave-uniform mask, U in flight
+    auto stream = [&](uint64_t m) {
+        while (m) {
+            uint4 u[U];
+            float xs[U];
+            int cnt = 0;
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                if (m) {
+                    const int b = __builtin_ctzll(m);
+                    m &= m - 1ull;
+                    xs[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xj), b));
+                    if (active)
+                        u[q] = Vec16<TE>::raw(wt + (int64_t)(lo + b) * ldw + col);
+                    cnt = q + 1;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                if (q < cnt) {
+                    float v[VEC];
+                    Vec16<TE>::unpack(u[q], v);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        acc[e] = fmaf(xs[q], v[e], acc[e]);
+                }
+            }
+        }
+    };
+
+    // 1. rows above the undecided digit (kept for certain)
+    if (tid == 0)
+        sig[0] = wait_sig(pub.sig1);
+    __syncthreads();
+    const uint64_t s1 = sig[0];
+    const uint32_t mn = (uint32_t)(s1 >> 32), dg = (uint32_t)(s1 >> 11) & 0x1fffffu;
+    const int sh = (int)(s1 >> 6) & 31, nb = (int)(s1 >> 1) & 31;
+    const uint32_t pm = ((1u << nb) - 1u) << sh, pfx = dg << sh;
+    const uint32_t key = key0 == 0u ? 0u : key0 - mn + 1u; // re-based as the selecting workgroup does
+    const uint64_t sure = __ballot(lane < n && (key & pm) > pfx);
+    const bool cand = lane < n && (key & pm) == pfx;
+    stream(sure);
+    // 2. the undecided digit's kept rows
+    if (tid == 0)
+        sig[1] = wait_sig(pub.sig2);
+    __syncthreads();
+    const uint64_t s2 = sig[1];
+    const uint32_t thr = (uint32_t)(s2 >> 32);
+    const int jt = (int)((uint32_t)s2 >> 1);
+    const uint64_t keptc = __ballot(cand && (key > thr || (key == thr && lo + lane <= jt)));
+    stream(keptc);
+    if (!(s1 & s2 & 1ull)) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            acc[e] = __builtin_nanf("");
+    }
+    // kept list (ascending): the waves of column slice 0 write their kept slices
+    if (idx && slice == 0) {
+        const uint64_t kept = sure | keptc;
+        if (lane == 0)
+            wcnt[w] = (uint32_t)__popcll(kept);
+        __syncthreads();
+        uint32_t off = pub_load(pub.offs + split);
+        for (int i = 0; i < w; ++i)
+            off += wcnt[i];
+        const uint32_t at = off + (uint32_t)__popcll(kept & lanemask_lt());
+        if (((kept >> lane) & 1ull) && at < (uint32_t)k)
+            idx[at] = lo + lane;
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        red[w][lane * VEC + e] = acc[e];
+    __syncthreads();
+    for (int i = tid; i < CW; i += SEL_THREADS) {
+        float sum = red[0][i];
+#pragma unroll
+        for (int ww = 1; ww < FUSED_WAVES; ++ww)
+            sum += red[ww][i];
+        part[((int64_t)slice * pub.nsplit + split) * CW + i] = sum;
+    }
+}
+
+struct FusedPlan {
+    int nslices, nsplit, R, R0, R1;
+};
+static FusedPlan fused_plan(int64_t K, int64_t M, bool bf16)
+{
+    FusedPlan p;
+    const int cw = WAVE * (bf16 ? 8 : 4);
+    const int64_t cap = 64 * FUSED_WAVES; // at most 64 slices per wave
+    p.nslices = (int)((M + cw - 1) / cw);
+    int64_t ns = 256 / p.nslices; // one workgroup per CU
+    if (ns > GEMV_MAX_SPLIT)
+        ns = GEMV_MAX_SPLIT;
+    if (ns > K)
+        ns = K;
+    if (ns < 1)
+        ns = 1;
+    // column slice 0: the selecting workgroup (split 0) takes an eighth of a range, since it
+    // starts streaming only after its selection; splits 1 .. nsplit-1 share the rest
+    for (;; ++ns) {
+        p.nsplit = (int)ns;
+        p.R = (int)((K + ns - 1) / ns);
+        if (ns == 1) {
+            p.R0 = (int)K;
+            p.R1 = 1;
+        } else {
+            p.R0 = (p.R + 7) / 8;
+            p.R1 = (int)((K - p.R0 + ns - 2) / (ns - 1));
+        }
+        if ((p.R <= cap && p.R0 <= cap && p.R1 <= cap) || ns >= GEMV_MAX_SPLIT || ns >= K)
+            break;
+    }
+    return p;
+}
+
+static inline size_t al256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t select_gemv_ws_bytes(int64_t K, int64_t M, bool bf16)
+{
+    const FusedPlan p = fused_plan(K, M, bf16);
+    const int cw = WAVE * (bf16 ? 8 : 4);
+    return al256((size_t)(p.nsplit + 1) * 4) + (size_t)p.nslices * p.nsplit * cw * sizeof(float);
+}
+
+bool select_gemv_fits(int64_t K, int64_t M, bool bf16)
+{
+    const FusedPlan p = fused_plan(K, M, bf16);
+    return (int64_t)p.R <= 64 * FUSED_WAVES && (int64_t)p.R0 <= 64 * FUSED_WAVES &&
+           (int64_t)p.R1 <= 64 * FUSED_WAVES && p.nsplit <= GEMV_MAX_SPLIT;
+}
+
+template <typename TE>
+static hipError_t select_gemv_dispatch(const FusedPlan &p, const TE *x, int64_t K, const float *c, int cvec, int64_t k,
+                                       const TE *wt, int64_t ldw, int64_t M, int32_t *idx, float *y, char *hdr,
+                                       char *body, hipStream_t st)
+{
+    constexpr int CW = WAVE * Vec16<TE>::N;
+    SelPub pub;
+    pub.sig1 = reinterpret_cast<uint64_t *>(hdr);
+    pub.sig2 = reinterpret_cast<uint64_t *>(hdr + 128);
+    pub.offs = reinterpret_cast<uint32_t *>(body);
+    pub.R = p.R;
+    pub.R0 = p.R0;
+    pub.R1 = p.R1;
+    pub.nsplit = p.nsplit;
+    float *part = reinterpret_cast<float *>(body + al256((size_t)(p.nsplit + 1) * 4));
+    const dim3 grid((unsigned)(p.nslices * p.nsplit));
+#define RMM_FUSED_CASE(PERV)                                                                                       \
+    case PERV:                                                                                                     \
+        select_gemv_kernel<TE, PERV><<<grid, SEL_THREADS, 0, st>>>(x, c, (int)K, (int)k, cvec, wt, ldw, (int)M,    \
+                                                                   p.nslices, pub, part, idx);                     \
+        break;
+    switch (select_per_for(K)) {
+        RMM_FUSED_CASE(4)
+        RMM_FUSED_CASE(8)
+        RMM_FUSED_CASE(16)
+        RMM_FUSED_CASE(32)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef RMM_FUSED_CASE
+    const dim3 rgrid((unsigned)(p.nslices * (CW / WAVE)));
+    gemv_reduce_kernel<1, CW><<<rgrid, RED_WAVES * WAVE, 0, st>>>(part, 1, 1, 1, p.nslices, p.nsplit, (int)M, y,
+                                                                 (int64_t)M, pub.sig1, pub.sig2);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_gemv(const void *x, bool bf16, int64_t K, const float *c, int64_t k, const void *wt,
+                              int64_t ldw, int64_t M, int32_t *idx, float *y, char *hdr, char *body, hipStream_t st)
+{
+    const FusedPlan p = fused_plan(K, M, bf16);
+    const int cvec = ((uintptr_t)c & 15u) == 0u;
+    if (bf16)
+        return select_gemv_dispatch<uint16_t>(p, (const uint16_t *)x, K, c, cvec, k, (const uint16_t *)wt, ldw, M,
+                                              idx, y, hdr, body, st);
+    return select_gemv_dispatch<float>(p, (const float *)x, K, c, cvec, k, (const float *)wt, ldw, M, idx, y, hdr,
+                                       body, st);
 }
 
 } // namespace rmm

@@ -45,6 +45,37 @@
 
 namespace rmm {
 
+// What the selecting workgroup of a fused select-and-product launch publishes
+// (select_body.h, gemv.hip), as two 64-bit words in the workspace header (zero
+// before the launch, cleared by the launch after it), each carrying a ready bit:
+//   sig1: after the first radix pass, the smallest non-zero key mn (keys are
+//         re-based as u = key - mn + 1, 0 stays 0) and the undecided digit
+//         (digit d of nb bits at bit sh): u above it is kept for certain;
+//   sig2: the threshold u and the slice of the last kept key equal to it;
+// and offs[p] = kept slices before split p's first slice in the column slice the
+// index list is written from (p <= nsplit).  That column slice is cut into a
+// short first range of R0 slices (the selecting workgroup's own share, streamed
+// after its selection) and nsplit - 1 ranges of R1; the others into ranges of R.
+struct SelPub {
+    uint64_t *sig1 = nullptr, *sig2 = nullptr;
+    uint32_t *offs = nullptr;
+    int R = 1, R0 = 1, R1 = 1, nsplit = 0;
+};
+// first slice of split p in the column slice of the index list (p <= nsplit)
+__host__ __device__ __forceinline__ int split_start0(const SelPub &pb, int p, int K)
+{
+    const int q = p == 0 ? 0 : pb.R0 + (p - 1) * pb.R1;
+    return q < K ? q : K;
+}
+__device__ __forceinline__ uint64_t sig1_pack(uint32_t mn, uint32_t d, int sh, int nb)
+{
+    return ((uint64_t)mn << 32) | ((uint64_t)d << 11) | ((uint64_t)sh << 6) | ((uint64_t)nb << 1) | 1ull;
+}
+__device__ __forceinline__ uint64_t sig2_pack(uint32_t thr, int jt)
+{
+    return ((uint64_t)thr << 32) | ((uint64_t)(uint32_t)jt << 1) | 1ull;
+}
+
 // select.hip
 size_t select_ws_bytes(int64_t T, int64_t K, int64_t tile);
 hipError_t launch_select(const void *x, bool bf16, int64_t T, int64_t K, int64_t ldx, const float *c, int64_t tile,
@@ -54,6 +85,13 @@ hipError_t launch_select_blocks(const void *x, bool bf16, int64_t T, int64_t K, 
 #define SELECT_BLOCKS_MAX_NB 1024
 void select_init();
 
+// gemv.hip: the fused select + GEMV for one token (workspace after the header;
+// its two flags live in the header)
+size_t select_gemv_ws_bytes(int64_t K, int64_t M, bool bf16);
+bool select_gemv_fits(int64_t K, int64_t M, bool bf16);
+hipError_t launch_select_gemv(const void *x, bool bf16, int64_t K, const float *c, int64_t k, const void *wt,
+                              int64_t ldw, int64_t M, int32_t *idx, float *y, char *hdr, char *body, hipStream_t st);
+int select_per_for(int64_t K);
 // gemv.hip
 size_t gemv_ws_bytes(int64_t T, int64_t M, int64_t k, int64_t tile, bool bf16);
 hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const void *wt, int64_t ldw, int64_t M,
