@@ -49,22 +49,38 @@ extern "C" {
 
 #define RMM_WS_HEADER_BYTES 4096
 
+/* Each enum below spans the whole int32 range (the _RANGE_ enumerators are not
+ * values to pass), so every integer a caller passes is a value of the type and
+ * is reported as an argument error when it names nothing, instead of being
+ * undefined behaviour in the C++ implementation. */
 typedef enum {
     RMM_OK = 0,
     RMM_EINVAL = 1,        /* bad argument: null pointer, size, ratio, stride */
     RMM_EUNSUPPORTED = 2,  /* valid, but no kernel for this shape / dtype / alignment */
     RMM_EWORKSPACE = 3,    /* workspace missing or smaller than the size query */
-    RMM_EHIP = 4           /* a HIP launch failed */
+    RMM_EHIP = 4,          /* a HIP launch failed */
+    RMM_STATUS_RANGE_MIN_ = INT32_MIN,
+    RMM_STATUS_RANGE_MAX_ = INT32_MAX
 } rmm_status_t;
 
-typedef enum { RMM_F32 = 0, RMM_BF16 = 1 } rmm_dtype_t;
+typedef enum {
+    RMM_F32 = 0,
+    RMM_BF16 = 1,
+    RMM_DTYPE_RANGE_MIN_ = INT32_MIN,
+    RMM_DTYPE_RANGE_MAX_ = INT32_MAX
+} rmm_dtype_t;
 
 /* Selection groups for grouped-query attention.  PER_KV_GROUP: the G = Hq/Hkv
  * query heads sharing one KV head share one head_dim selection and one key
  * position selection (scores take the max over those heads).  PER_Q_HEAD:
  * each query head selects alone (the KV rows of a group are then read once per
  * query head). */
-typedef enum { RMM_SEL_PER_KV_GROUP = 0, RMM_SEL_PER_Q_HEAD = 1 } rmm_sel_mode_t;
+typedef enum {
+    RMM_SEL_PER_KV_GROUP = 0,
+    RMM_SEL_PER_Q_HEAD = 1,
+    RMM_SEL_RANGE_MIN_ = INT32_MIN,
+    RMM_SEL_RANGE_MAX_ = INT32_MAX
+} rmm_sel_mode_t;
 
 /* ------------------------------------------------------------------ keep count
  * Paper abstract ("retention-ratio control"): k = ceil(r*n) slices are kept.

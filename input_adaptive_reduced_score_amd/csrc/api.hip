@@ -130,6 +130,8 @@ const char *rmm_status_string(rmm_status_t s)
         return "RMM_EWORKSPACE: workspace missing or too small";
     case RMM_EHIP:
         return "RMM_EHIP: HIP launch failed";
+    default:
+        break;
     }
     return "unknown rmm_status_t";
 }
