@@ -62,6 +62,31 @@ def n_copies(bytes_per_copy: int, touched_per_step: int) -> int:
     return max(2, min(n, cap, 64))
 
 
+def host_cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_compiler():
+    """The compiler and flags the C oracle is built with."""
+    import subprocess
+
+    import oracle
+
+    try:
+        ver = subprocess.run(["gcc", "-dumpfullversion"], capture_output=True, text=True).stdout.strip()
+    except OSError:
+        ver = "?"
+    return f"gcc {ver} " + " ".join(oracle.CFLAGS)
+
+
 def time_loop(fn, steps, warmup, torch):
     """Seconds per step of `fn(i)`: `warmup` eager steps, then `steps` steps
     captured into one HIP graph and replayed once between two synchronizations
@@ -557,18 +582,28 @@ def main():
         import oracle
 
         k = oracle.keep_count(dc.K, 0.5)
-        n, t0 = 0, time.perf_counter()
-        while True:
-            idx = oracle.select(dc.x, dc.c, 1, 0.5)
-            oracle.linear(dc.x, dc.wt, idx, 1)
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds and n >= 3:
-                break
+        # the oracle is single-threaded: its thread is pinned to one host CPU
+        # (the first this process may use, as `taskset -c` would) while timed
+        allowed = sorted(os.sched_getaffinity(0))
+        pin = allowed[0]
+        os.sched_setaffinity(0, {pin})
+        try:
+            n, t0 = 0, time.perf_counter()
+            while True:
+                idx = oracle.select(dc.x, dc.c, 1, 0.5)
+                oracle.linear(dc.x, dc.wt, idx, 1)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= args.cpu_seconds and n >= 3:
+                    break
+        finally:
+            os.sched_setaffinity(0, set(allowed))
         cpu = {"value": A.decode_step_bytes(dc.K, dc.M, k) * n / el / 1e9, "unit": "GB/s", "cores": 1,
                "kind": "oracle",
                "sample": f"{n} full decode steps (select + reduced product, r=0.5, X[1,14336] x W^T[14336,4096] "
-                         f"bf16) of the single-threaded C oracle, {el:.1f} s"}
+                         f"bf16) of the single-threaded C oracle, {el:.1f} s",
+               "pinned_cpu": pin, "host_cpus": os.cpu_count(), "cpus_allowed": len(allowed),
+               "cpu_model": host_cpu_model(), "compiler": oracle_compiler()}
         log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s retained ({n} steps in {el:.1f} s)")
 
     sha = src_hash(["input_adaptive_reduced_score_amd/csrc/gemv.hip",
