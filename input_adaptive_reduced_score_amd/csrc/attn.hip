@@ -7,21 +7,23 @@
 // dimension: head_dim for Q K^T, key positions for P V).  GEMM notes section 1:
 // scores = Q K^T, out = softmax(scores) V.
 //
-// Pipeline per (batch element, selection group), five launches on one stream
-// (a sixth writes the kept-position lists when they are asked for):
+// Pipeline per (batch element, selection group), three launches on one stream
+// (a fourth writes the kept-position lists when they are asked for):
 //  qk    : head_dim selection (one wave, bitwise search over ballots), then
 //          unscaled logits over the kept dims for 8 positions per lane from
 //          dim-major keys (a kept dim is one contiguous row), and per-chunk
 //          softmax statistics (max, sum of exponentials); the first chunk's
-//          workgroup clears the group's score histogram.
-//  keys  : every workgroup merges the chunk statistics into lse (double), then
-//          scores its positions by max_h (scale*a_h - lse_h) in double, stores
-//          each position's histogram bin and adds it to the group histogram.
-//  select: one workgroup per group resolves the group's exact threshold from
-//          the histogram and the bins.
-//  pv    : each workgroup keeps its chunk's positions at or above the
-//          threshold (order-preserving), streams their V rows and accumulates
-//          p*V into a per-chunk partial.
+//          workgroup clears the group's score histogram and signal words.
+//  fused : one launch of two workgroup roles.  Key workgroups merge the
+//          chunk statistics into lse (double), score their positions by
+//          max_h (scale*a_h - lse_h) in double, store each one's histogram bin
+//          and add them to the group's score histogram; the group's last key
+//          workgroup finds and publishes the bin holding the threshold, then
+//          ranks that bin's positions and publishes the exact threshold.  PV
+//          workgroups score their own chunk's positions the same way and
+//          stream the V rows of those above the threshold bin into p*V
+//          partial sums while the rank is resolved, then those in the bin at
+//          or above the threshold.
 //  reduce: the chunk partials are summed in a fixed order.
 #include "device.h"
 #include "kernels.h"
@@ -127,6 +129,17 @@ __device__ __forceinline__ void wave_select128(uint32_t key0, uint32_t key1, int
         jd[__popcll(k0) + __popcll(k1 & lt)] = lane + WAVE;
 }
 
+// ------------------------------------------------------------------ signals between the roles
+// Per group, 256 bytes of the workspace.  First cache line: the count of key
+// workgroups done (32-bit, word 0).  Second line, polled: the threshold bin
+// (word 16: d << 40 | krem << 2 | all-of-bin-d-kept << 1 | ready) and the
+// threshold rank key (word 17: thr << 1 | ready).  The QK kernel clears them;
+// the fused kernel writes them with agent-scope stores and atomics, which every
+// XCD sees once they complete.
+constexpr int SIG_WORDS = 32;
+constexpr int SIG_KCNT = 0, SIG_D = 16, SIG_THR = 17;
+constexpr int ATTN_SPIN = 1 << 20; // polls (about a second) before a wait gives up
+
 // ------------------------------------------------------------------ qk
 template <int GS>
 __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, KvMap m, int Sp, const uint16_t *__restrict__ q,
@@ -134,7 +147,7 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, KvMap 
                                                              const float *__restrict__ kn, float *__restrict__ logit,
                                                              float2 *__restrict__ pstat,
                                                              int32_t *__restrict__ dim_idx_out,
-                                                             uint32_t *__restrict__ hist)
+                                                             uint32_t *__restrict__ hist, uint64_t *__restrict__ sig)
 {
     constexpr int NWQ = QK_THREADS / WAVE;
     __shared__ int jd[D];
@@ -267,10 +280,17 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, KvMap 
             pstat[((int64_t)b * s.Hq + h0 + hh) * nchunk + chunk] = make_float2(mx, z);
     }
 
-    // 4. the first chunk's workgroup clears the group's key histogram for the key kernel
-    if (chunk == 0)
+    // 4. the first chunk's workgroup clears the group's score histogram and signal words for the next launch
+    if (chunk == 0) {
         for (int i = tid; i < ATTN_HIST_BINS; i += QK_THREADS)
             hist[(int64_t)grp * ATTN_HIST_BINS + i] = 0;
+        if (tid == 0) {
+            uint64_t *sg = sig + (int64_t)grp * SIG_WORDS;
+            pub_store64(sg + SIG_KCNT, 0ull);
+            pub_store64(sg + SIG_D, 0ull);
+            pub_store64(sg + SIG_THR, 0ull);
+        }
+    }
 }
 
 // ------------------------------------------------------------------ position scores
@@ -351,141 +371,96 @@ __device__ __forceinline__ uint64_t rank_key(uint64_t k, uint32_t d, int pos)
     return (((k - base) >> sh) << 24) | (uint64_t)(0xffffffu - (uint32_t)pos);
 }
 
-// ------------------------------------------------------------------ keys
-// Every workgroup merges the group's chunk statistics into lse (double, fixed
-// order), scores its positions, stores each position's histogram bin (2 bytes)
-// and adds the bins to the group's histogram (LDS, then global atomics; the QK
-// kernel cleared it).
+// ------------------------------------------------------------------ group log-sum-exp
+// lse_h for each of the group's heads: scale*M + log(sum over the QK chunks of
+// z_c * exp(scale*(m_c - M))), M the largest chunk maximum, in double.  Each
+// thread merges its share of the chunk statistics online, then the block merges
+// the threads' pairs in a fixed order, so every workgroup that calls this
+// function (256 threads; barriers inside) holds the same bits.  The caller loads
+// the thread's first statistic of each head early (ld_stats), ahead of its other
+// loads.
+struct LseLds {
+    float smax[8][4];
+    double ssum[8][4];
+};
 template <int GS>
-__global__ __launch_bounds__(256) void attn_key_kernel(AttnShape s, KvMap m, int Sp, int nqk_all, int nsub,
-                                                       const float *__restrict__ logit,
-                                                       const float2 *__restrict__ pstat, double *__restrict__ lse_ws,
-                                                       float *__restrict__ lse_out, const float *__restrict__ vn,
-                                                       uint16_t *__restrict__ bins, uint32_t *__restrict__ hist)
+__device__ __forceinline__ void ld_stats(const AttnShape &s, int b, int h0, int nqk_all, int nqk,
+                                         const float2 *__restrict__ pstat, float2 (&pst)[GS])
 {
-    __shared__ uint32_t lh[ATTN_HIST_BINS];
-    __shared__ float smax[GS][4];
-    __shared__ double ssum[GS][4];
-    __shared__ double lse_s[GS];
-    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-    const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS;
-    const int Sb = seq_len(s, m, b);
-    // the workgroup takes nsub consecutive chunks of ATTN_KEY_CHUNK positions
-    // (long sequences: fewer workgroups, fewer statistics merges and fewer
-    // global histogram atomics)
-    const int c0 = blockIdx.x * nsub;
-    if (c0 * ATTN_KEY_CHUNK >= Sb)
-        return;
-    const int nqk = (Sb + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK; // this sequence's QK chunks
-    for (int i = tid; i < ATTN_HIST_BINS; i += 256)
-        lh[i] = 0;
-    // this thread's logits are loaded first so their latency overlaps the statistics merge
-    f32x4_t a[GS][2], an[GS][2];
-    auto load_logits = [&](f32x4_t (&dst)[GS][2], int sp) {
-        if (sp < Sb) {
-#pragma unroll
-            for (int hh = 0; hh < GS; ++hh) {
-                const f32x4_t *src = reinterpret_cast<const f32x4_t *>(logit + ((int64_t)b * s.Hq + h0 + hh) * Sp + sp);
-                dst[hh][0] = src[0];
-                dst[hh][1] = src[1];
-            }
-        }
-    };
-    load_logits(a, c0 * ATTN_KEY_CHUNK + threadIdx.x * 8);
-    // merge the per-chunk softmax statistics of the group's heads into lse (double, fixed order)
-#pragma unroll
-    for (int hh = 0; hh < GS; ++hh) {
-        const float2 *ps = pstat + ((int64_t)b * s.Hq + h0 + hh) * nqk_all;
-        float mx = -INFINITY;
-        for (int i = tid; i < nqk; i += 256)
-            mx = fmaxf(mx, ps[i].x);
-        mx = wave_max(mx);
-        if (lane == 0)
-            smax[hh][w] = mx;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int hh = 0; hh < GS; ++hh) {
-        const float M = fmaxf(fmaxf(smax[hh][0], smax[hh][1]), fmaxf(smax[hh][2], smax[hh][3]));
-        const float2 *ps = pstat + ((int64_t)b * s.Hq + h0 + hh) * nqk_all;
-        double z = 0.0;
-        for (int i = tid; i < nqk; i += 256) {
-            const float2 st = ps[i];
-            z += (double)st.y * exp((double)s.scale * ((double)st.x - (double)M));
-        }
-        z = wave_sum(z);
-        if (lane == 0)
-            ssum[hh][w] = z;
-    }
-    __syncthreads();
-    if (tid < GS) {
-        const float M = fmaxf(fmaxf(smax[tid][0], smax[tid][1]), fmaxf(smax[tid][2], smax[tid][3]));
-        const double z = ((ssum[tid][0] + ssum[tid][1]) + ssum[tid][2]) + ssum[tid][3];
-        const double l = (double)s.scale * (double)M + log(z);
-        lse_s[tid] = l;
-        if (blockIdx.x == 0) {
-            lse_ws[(int64_t)b * s.Hq + h0 + tid] = l;
-            if (lse_out)
-                lse_out[(int64_t)b * s.Hq + h0 + tid] = (float)l;
-        }
-    }
-    __syncthreads();
-    double lse[GS];
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh)
-        lse[hh] = lse_s[hh];
+        pst[hh] = tid < nqk ? pstat[((int64_t)b * s.Hq + h0 + hh) * nqk_all + tid] : make_float2(-INFINITY, 0.0f);
+}
+template <int GS>
+__device__ void group_lse(const AttnShape &s, int b, int h0, int nqk_all, int nqk, const float2 *__restrict__ pstat,
+                          const float2 (&pst)[GS], LseLds &L, double (&lse)[GS])
+{
+#pragma clang fp contract(off)
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const double sc = (double)s.scale;
-    for (int sub = 0; sub < nsub; ++sub) {
-        const int sp = (c0 + sub) * ATTN_KEY_CHUNK + threadIdx.x * 8;
-        if (sp >= Sb)
-            break; // (per thread: later chunks start further on)
-        if (sub + 1 < nsub)
-            load_logits(an, sp + ATTN_KEY_CHUNK); // the next chunk's logits load while this one is scored
-        // value-row norms of the 8 positions (one page or row: pitches and pages are multiples of 8)
-        f32x4_t nv[2] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};
-        if (vn) {
-            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(vn + kv_row(s, m, b, h0 / s.G, sp));
-            nv[0] = src[0];
-            nv[1] = src[1];
-        }
-        uint32_t bn[8];
+    float mt[GS];
+    double zt[GS];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float av[GS];
-#pragma unroll
-            for (int hh = 0; hh < GS; ++hh)
-                av[hh] = a[hh][e >> 2][e & 3];
-            const uint32_t bb = key_bin(pos_key(pos_score<GS>(av, lse, sc, vn != nullptr, nv[e >> 2][e & 3])));
-            if (sp + e < Sb) {
-                atomicAdd(&lh[bb], 1u);
-                bn[e] = bb;
-            } else {
-                bn[e] = 0u; // past the sequence's end: never read as a position
-            }
-        }
-        *reinterpret_cast<uint4 *>(bins + (int64_t)grp * Sp + sp) =
-            make_uint4(bn[0] | bn[1] << 16, bn[2] | bn[3] << 16, bn[4] | bn[5] << 16, bn[6] | bn[7] << 16);
+    for (int hh = 0; hh < GS; ++hh) {
+        mt[hh] = pst[hh].x;
+        zt[hh] = (double)pst[hh].y;
+    }
+    for (int i = tid + 256; i < nqk; i += 256) { // sequences of more than 256 QK chunks
 #pragma unroll
         for (int hh = 0; hh < GS; ++hh) {
-            a[hh][0] = an[hh][0];
-            a[hh][1] = an[hh][1];
+            const float2 st = pstat[((int64_t)b * s.Hq + h0 + hh) * nqk_all + i];
+            if (st.x > mt[hh]) {
+                zt[hh] = zt[hh] * exp(sc * ((double)mt[hh] - (double)st.x)) + (double)st.y;
+                mt[hh] = st.x;
+            } else {
+                zt[hh] += (double)st.y * exp(sc * ((double)st.x - (double)mt[hh]));
+            }
         }
     }
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+        const float mx = wave_max(mt[hh]);
+        if (lane == 0)
+            L.smax[hh][w] = mx;
+    }
     __syncthreads();
-    for (int i = threadIdx.x; i < ATTN_HIST_BINS; i += 256)
-        if (lh[i])
-            atomicAdd(&hist[(int64_t)grp * ATTN_HIST_BINS + i], lh[i]);
+    float M[GS];
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+        M[hh] = fmaxf(fmaxf(L.smax[hh][0], L.smax[hh][1]), fmaxf(L.smax[hh][2], L.smax[hh][3]));
+        const double z = mt[hh] == -INFINITY ? 0.0 : zt[hh] * exp(sc * ((double)mt[hh] - (double)M[hh]));
+        const double zs = wave_sum(z);
+        if (lane == 0)
+            L.ssum[hh][w] = zs;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+        lse[hh] = sc * (double)M[hh] + log(((L.ssum[hh][0] + L.ssum[hh][1]) + L.ssum[hh][2]) + L.ssum[hh][3]);
+}
+
+__device__ __forceinline__ uint64_t wait_ready(const uint64_t *p)
+{
+    for (int it = 0; it < ATTN_SPIN; ++it) {
+        const uint64_t v = pub_load64(p);
+        if (v & 1ull)
+            return v;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return 0ull;
 }
 
 // ------------------------------------------------------------------ position selection helpers
-constexpr int ASEL_THREADS = 512;       // threshold workgroup (one per group)
-constexpr int PV_THREADS = 256;
-constexpr int PV_WAVES = PV_THREADS / WAVE;
-constexpr int PV_PASS = 2 * PV_THREADS; // positions per PV pass (2 per thread)
-constexpr int PV_MAX_CHUNKS = 64;
-constexpr int PV_U = 16;                // kept V rows in flight per lane
-constexpr int SEL_CAP = 2048;           // candidates of the threshold bin ranked in LDS
-constexpr int SEL_FEW = 64;             // a radix digit with at most this many keys is ranked by one wave
+constexpr int PV_WAVES = 4;
+constexpr int PV_THREADS = PV_WAVES * WAVE; // every role of the fused kernel: 256 threads
+constexpr int PV_PASS = 2 * PV_THREADS;     // positions per PV pass (2 per thread)
+constexpr int PV_MAX_CHUNKS = 32;
+constexpr int PV_U = 16;                    // kept V rows in flight per lane
+constexpr int PV_CAND = PV_THREADS;         // threshold-bin positions a PV chunk keeps in LDS for its second phase
+constexpr int SEL_CAP = 2048;               // threshold-bin candidates of a group ranked in LDS
+constexpr int SEL_FEW = 64;                 // a radix digit with at most this many keys is ranked by one wave
+static_assert(PV_MAX_CHUNKS <= PV_THREADS, "one chunk count per thread");
 
 // The krem-th largest (1-based) of a set of distinct keys below 2^63, which
 // each_key(f) visits (every thread calls f(key) for its share of the set): 8-bit
@@ -561,51 +536,65 @@ __device__ uint64_t radix_select_u64(EachKey each_key, uint32_t krem, RadixLds &
     }
 }
 
-// ------------------------------------------------------------------ select
-// One workgroup per group finds the group's exact threshold: the 8192-bin
-// histogram of scores gives the bin d holding the ks-th largest score and its
-// rank krem inside the bin; one pass over the 2-byte bins of all positions
-// gathers bin d's positions, whose rank keys (recomputed from the logits) are
-// radix-selected for the krem-th largest.  Past SEL_CAP candidates the radix
-// passes recompute the rank keys instead of holding them in LDS.  Output per
-// group: (d, threshold rank key).  A position is kept iff its bin is above d,
-// or it is in bin d with a rank key at least the threshold's: exactly the ks
-// first positions of the order (score descending, position ascending).
-struct AttnSel {
-    uint32_t d, pad;
-    uint64_t thr;
-};
-struct SelLds {
-    uint64_t key[SEL_CAP];
-    int32_t pos[SEL_CAP];
+// ------------------------------------------------------------------ key role and threshold
+// A key workgroup takes nsub consecutive chunks of ATTN_KEY_CHUNK positions of
+// one group: it scores them (lse from the chunk statistics), stores each
+// position's 2-byte histogram bin (agent-scope stores) and adds the bins to the
+// group's histogram (LDS, then global atomics; the QK kernel cleared it), then
+// counts itself.  The group's last key workgroup to count (every histogram
+// atomic and bin store of the group has then completed) resolves the
+// threshold: the histogram gives the bin d holding the ks-th largest score and
+// the rank krem of that score inside the bin; d is published at once (with a
+// flag when all of bin d is kept, which makes the threshold rank key 0), so
+// the PV workgroups start on the positions above it.  Then bin d's positions
+// are gathered from the bins, their rank keys are recomputed from the logits,
+// and the krem-th largest is radix-selected and published.  Past SEL_CAP
+// candidates the radix passes recompute the rank keys instead of holding them
+// in LDS.  No key workgroup waits on another.
+//
+// The last workgroup reads the histogram and the bins with plain loads: the
+// atomics are performed in memory and the bins written through to it with
+// agent-scope stores before their workgroups count themselves, and no
+// workgroup reads a group's histogram or bins before that group's last count
+// (each group's bins row is padded to whole 128-byte lines), so no XCD's cache
+// holds an older copy of them.
+constexpr int SEL_UB = 16;  // 16-byte words of bins per thread per pass
+constexpr int BIN_ROW = 64; // positions a group's bins row is padded to (128 bytes)
+struct KeyLds {
+    union {
+        uint32_t lh[ATTN_HIST_BINS];
+        struct {
+            uint64_t key[SEL_CAP];
+            int32_t pos[SEL_CAP];
+        } c;
+    };
     RadixLds rad;
-    uint32_t tmp[64];
     uint32_t ncand;
     uint32_t bres[3];
+    uint32_t last;
 };
+static_assert(ATTN_HIST_BINS == 32 * PV_THREADS, "32 histogram bins per thread");
+
+__device__ __forceinline__ uint32_t bin_of(const uint4 &w, int e)
+{
+    const uint32_t wd = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+    return (e & 1) ? wd >> 16 : wd & 0xffffu;
+}
 
 template <int GS>
-__global__ __launch_bounds__(ASEL_THREADS) void attn_select_kernel(AttnShape s, KvMap m, int Sp,
-                                                                   const float *__restrict__ logit,
-                                                                   const double *__restrict__ lse_ws,
-                                                                   const uint16_t *__restrict__ bins,
-                                                                   const uint32_t *__restrict__ hist,
-                                                                   const float *__restrict__ vn,
-                                                                   AttnSel *__restrict__ sel)
+__device__ void publish_select(const AttnShape &s, const KvMap &m, int Sp, int Spb, int grp,
+                               const float *__restrict__ logit, const double (&lsed)[GS],
+                               const float *__restrict__ vn, const uint16_t *bins, const uint32_t *hg,
+                               uint64_t *sg, KeyLds &L)
 {
-    __shared__ SelLds L;
+    constexpr int T = PV_THREADS;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1);
-    const int grp = blockIdx.x, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS, g = h0 / s.G;
+    const int b = grp / s.Hsel, h0 = (grp % s.Hsel) * s.GS, g = h0 / s.G;
     const int Sb = seq_len(s, m, b), ksb = seq_keep(s, m, Sb);
     const float *Lg = logit + ((int64_t)b * s.Hq + h0) * Sp; // head hh at Lg + hh * Sp
-    const uint4 *B4 = reinterpret_cast<const uint4 *>(bins + (int64_t)grp * Sp);
-    const int n8 = (Sb + 7) / 8; // 8-position groups of bins
+    const uint4 *B16 = reinterpret_cast<const uint4 *>(bins + (int64_t)grp * Spb);
+    const int n8 = (Sb + 7) / 8; // 8-position words of bins
     const double sc = (double)s.scale;
-    double lsed[GS];
-#pragma unroll
-    for (int hh = 0; hh < GS; ++hh)
-        lsed[hh] = lse_ws[(int64_t)b * s.Hq + h0 + hh];
-    // rank key of position p (its bin is d): score recomputed from the logits
     auto rank_of = [&](int p, uint32_t d) -> uint64_t {
         float av[GS];
 #pragma unroll
@@ -614,33 +603,21 @@ __global__ __launch_bounds__(ASEL_THREADS) void attn_select_kernel(AttnShape s, 
         const float vv = vn ? vn[kv_row(s, m, b, g, p)] : 1.0f;
         return rank_key(pos_key(pos_score<GS>(av, lsed, sc, vn != nullptr, vv)), d, p);
     };
-
-    // the histogram's loads, then the first batch of bins (it does not depend on the
-    // threshold bin), so both are in flight together
-    static_assert(ATTN_HIST_BINS == 16 * ASEL_THREADS, "16 histogram bins per thread");
-    constexpr int UB = 4; // 16-byte loads of bins in flight per thread
-    uint4 q[4];
+    // threshold bin: thread t holds bins 8191-32t down to 8160-32t
+    uint32_t hc[32];
     {
-        const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + (int64_t)grp * ATTN_HIST_BINS + ATTN_HIST_BINS -
-                                                          16 * (tid + 1));
+        const uint4 *h4 = reinterpret_cast<const uint4 *>(hg + ATTN_HIST_BINS - 32 * (tid + 1));
+        uint4 q[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
             q[i] = h4[i];
-    }
-    uint4 u[UB];
 #pragma unroll
-    for (int j = 0; j < UB; ++j) {
-        const int i = tid + j * ASEL_THREADS;
-        u[j] = i < n8 ? B4[i] : make_uint4(0u, 0u, 0u, 0u);
-    }
-    // threshold bin: thread t holds bins 8191-16t down to 8176-16t
-    uint32_t hc[16];
-    {
-        const uint32_t asc[16] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w,
-                                  q[2].x, q[2].y, q[2].z, q[2].w, q[3].x, q[3].y, q[3].z, q[3].w};
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            hc[i] = asc[15 - i];
+        for (int i = 0; i < 8; ++i) {
+            hc[31 - 4 * i] = q[i].x;
+            hc[30 - 4 * i] = q[i].y;
+            hc[29 - 4 * i] = q[i].z;
+            hc[28 - 4 * i] = q[i].w;
+        }
     }
     if (tid == 0) {
         L.bres[0] = 0;
@@ -650,14 +627,14 @@ __global__ __launch_bounds__(ASEL_THREADS) void attn_select_kernel(AttnShape s, 
     }
     uint32_t tot = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < 32; ++i)
         tot += hc[i];
-    const uint32_t incl = block_incl_scan(tot, L.tmp); // (barriers inside)
+    const uint32_t incl = block_incl_scan(tot, L.rad.tmp); // (barriers inside)
     {
-        const uint32_t top = ATTN_HIST_BINS - 1 - 16 * tid, want = (uint32_t)ksb;
+        const uint32_t top = ATTN_HIST_BINS - 1 - 32 * tid, want = (uint32_t)ksb;
         uint32_t run = incl - tot;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 32; ++i) {
             if (run < want && want <= run + hc[i]) {
                 L.bres[0] = top - i;
                 L.bres[1] = want - run;
@@ -668,114 +645,227 @@ __global__ __launch_bounds__(ASEL_THREADS) void attn_select_kernel(AttnShape s, 
     }
     __syncthreads();
     const uint32_t d = L.bres[0], krem = L.bres[1], nbin = L.bres[2];
+    if (tid == 0)
+        pub_store64(sg + SIG_D, (uint64_t)d << 40 | (uint64_t)krem << 2 | (krem == nbin ? 2ull : 0ull) | 1ull);
+    if (krem == nbin)
+        return; // all of bin d is kept
 
     uint64_t thr;
     if (nbin <= (uint32_t)SEL_CAP) {
-        // gather bin d's positions: per-lane bit masks, one slot reservation per wave
-        for (int i0 = tid; i0 - lane < n8; i0 += UB * ASEL_THREADS) {
-            if (i0 != tid) {
+        // gather bin d's positions: per-lane bit masks of 4 words, one slot reservation per wave
+        for (int base = 0; base < n8; base += SEL_UB * T) {
+            uint4 u[SEL_UB];
 #pragma unroll
-                for (int j = 0; j < UB; ++j) {
-                    const int i = i0 + j * ASEL_THREADS;
-                    u[j] = i < n8 ? B4[i] : make_uint4(0u, 0u, 0u, 0u);
-                }
+            for (int j = 0; j < SEL_UB; ++j) {
+                const int i = base + tid + j * T;
+                u[j] = i < n8 ? B16[i] : make_uint4(0u, 0u, 0u, 0u);
             }
-            uint32_t cm = 0;
 #pragma unroll
-            for (int j = 0; j < UB; ++j) {
-                const uint32_t wd[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
-                const int pb = 8 * (i0 + j * ASEL_THREADS);
+            for (int j0 = 0; j0 < SEL_UB; j0 += 4) {
+                uint32_t cm = 0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t bn = (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu;
-                    cm |= (uint32_t)((bn == d) & (pb + e < Sb)) << (8 * j + e);
+                for (int j = 0; j < 4; ++j) {
+                    const int i = base + tid + (j0 + j) * T;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        cm |= (uint32_t)((bin_of(u[j0 + j], e) == d) & (8 * i + e < Sb)) << (8 * j + e);
                 }
-            }
-            const uint32_t cl = (uint32_t)__popc(cm);
-            const uint32_t cincl = wave_incl_sum(cl);
-            const uint32_t wcount = (uint32_t)__builtin_amdgcn_readlane((int)cincl, WAVE - 1);
-            uint32_t base = 0;
-            if (lane == 0 && wcount != 0u)
-                base = atomicAdd(&L.ncand, wcount);
-            base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-            uint32_t slot = base + cincl - cl;
-            while (cm) {
-                const int bit = __builtin_ctz(cm);
-                cm &= cm - 1u;
-                if (slot < (uint32_t)SEL_CAP)
-                    L.pos[slot] = 8 * (i0 + (bit >> 3) * ASEL_THREADS) + (bit & 7);
-                ++slot;
+                const uint32_t cl = (uint32_t)__popc(cm);
+                const uint32_t cincl = wave_incl_sum(cl);
+                const uint32_t wcount = (uint32_t)__builtin_amdgcn_readlane((int)cincl, WAVE - 1);
+                uint32_t sbase = 0;
+                if (lane == 0 && wcount != 0u)
+                    sbase = atomicAdd(&L.ncand, wcount);
+                sbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)sbase);
+                uint32_t slot = sbase + cincl - cl;
+                while (cm) {
+                    const int bit = __builtin_ctz(cm);
+                    cm &= cm - 1u;
+                    if (slot < (uint32_t)SEL_CAP)
+                        L.c.pos[slot] = 8 * (base + tid + (j0 + (bit >> 3)) * T) + (bit & 7);
+                    ++slot;
+                }
             }
         }
         __syncthreads();
         const int nc = (int)min(L.ncand, (uint32_t)SEL_CAP);
-        for (int i = tid; i < nc; i += ASEL_THREADS)
-            L.key[i] = rank_of(L.pos[i], d);
+        for (int i = tid; i < nc; i += T)
+            L.c.key[i] = rank_of(L.c.pos[i], d);
         __syncthreads();
         thr = radix_select_u64(
             [&](auto f) {
-                for (int i = tid; i < nc; i += ASEL_THREADS)
-                    f(L.key[i]);
+                for (int i = tid; i < nc; i += T)
+                    f(L.c.key[i]);
             },
             krem, L.rad);
     } else {
         // a crowded bin: every radix pass recomputes the rank keys of bin d's positions
         thr = radix_select_u64(
             [&](auto f) {
-                for (int i = tid; i < n8; i += ASEL_THREADS) {
-                    const uint4 w4 = B4[i];
-                    const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
+                for (int i = tid; i < n8; i += T) {
+                    const uint4 w4 = B16[i];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const uint32_t bn = (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu;
                         const int p = 8 * i + e;
-                        if (bn == d && p < Sb)
+                        if (bin_of(w4, e) == d && p < Sb)
                             f(rank_of(p, d));
                     }
                 }
             },
             krem, L.rad);
     }
-    if (tid == 0) {
-        AttnSel r;
-        r.d = d;
-        r.pad = 0;
-        r.thr = thr;
-        sel[grp] = r;
-    }
+    if (tid == 0)
+        pub_store64(sg + SIG_THR, thr << 1 | 1ull);
 }
 
-// ------------------------------------------------------------------ pv
-// One workgroup per (chunk of P positions, group), 4 waves.  The group's
-// threshold and the first pass's bins and logits are loaded together; each
-// pass examines PV_PASS positions (2 per thread), keeps those at or above the
-// threshold (bin above d, or bin d with a rank key at least the threshold's,
-// recomputed from the logits already loaded), stages their V rows and
-// probabilities in LDS in position order, and streams the rows, 16 in flight
-// per lane (a 16-lane quarter wave per 256-byte row), into p * V partial sums.
 template <int GS>
-__global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap m, int Sp, int P,
-                                                             const uint16_t *__restrict__ v,
-                                                             const float *__restrict__ logit,
-                                                             const double *__restrict__ lse_ws,
-                                                             const uint16_t *__restrict__ bins,
-                                                             const float *__restrict__ vn,
-                                                             const AttnSel *__restrict__ sel,
-                                                             int32_t *__restrict__ pstage,
-                                                             uint32_t *__restrict__ pcount, float *__restrict__ part)
+__device__ void key_role(const AttnShape &s, const KvMap &m, int Sp, int Spb, int nqk_all, int nsub, int nkw, int grp,
+                         int kx, const float *__restrict__ logit, const float2 *__restrict__ pstat,
+                         float *__restrict__ lse_out, const float *__restrict__ vn, uint16_t *bins,
+                         uint32_t *__restrict__ hist, uint64_t *sg, KeyLds &L, LseLds &LL)
 {
-    __shared__ int64_t rows[PV_PASS]; // V row index of each kept position of the pass
-    __shared__ float pr[GS][PV_PASS];
-    __shared__ uint32_t wk[PV_WAVES];
-    __shared__ float red[PV_WAVES][GS][D];
+    const int tid = threadIdx.x;
+    const int b = grp / s.Hsel, h0 = (grp % s.Hsel) * s.GS;
+    const int Sb = seq_len(s, m, b);
+    const int nqk = (Sb + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK; // this sequence's QK chunks
+    const int c0 = kx * nsub;
+    uint32_t *hg = hist + (int64_t)grp * ATTN_HIST_BINS;
+    double lse[GS];
+    float2 pst[GS];
+    ld_stats<GS>(s, b, h0, nqk_all, nqk, pstat, pst);
+    if (c0 * ATTN_KEY_CHUNK < Sb) { // (uniform) workgroups past the sequence's end only count themselves
+        for (int i = tid; i < ATTN_HIST_BINS; i += PV_THREADS)
+            L.lh[i] = 0;
+        // this thread's logits load behind the statistics, so their latency overlaps the merge
+        f32x4_t a[GS][2], an[GS][2];
+        auto load_logits = [&](f32x4_t (&dst)[GS][2], int sp) {
+            if (sp < Sb) {
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh) {
+                    const f32x4_t *src =
+                        reinterpret_cast<const f32x4_t *>(logit + ((int64_t)b * s.Hq + h0 + hh) * Sp + sp);
+                    dst[hh][0] = src[0];
+                    dst[hh][1] = src[1];
+                }
+            }
+        };
+        load_logits(a, c0 * ATTN_KEY_CHUNK + tid * 8);
+        group_lse<GS>(s, b, h0, nqk_all, nqk, pstat, pst, LL, lse); // (its barriers order the clearing of lh)
+        if (kx == 0 && lse_out) {
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+                if (tid == hh)
+                    lse_out[(int64_t)b * s.Hq + h0 + hh] = (float)lse[hh];
+        }
+        const double sc = (double)s.scale;
+        uint64_t *bg = reinterpret_cast<uint64_t *>(bins + (int64_t)grp * Spb);
+        for (int sub = 0; sub < nsub; ++sub) {
+            const int sp = (c0 + sub) * ATTN_KEY_CHUNK + tid * 8;
+            if (sp >= Sb)
+                break; // (per thread: later chunks start further on)
+            if (sub + 1 < nsub)
+                load_logits(an, sp + ATTN_KEY_CHUNK); // the next chunk's logits load while this one is scored
+            // value-row norms of the 8 positions (one page or row: pitches and pages are multiples of 8)
+            f32x4_t nv[2] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};
+            if (vn) {
+                const f32x4_t *src = reinterpret_cast<const f32x4_t *>(vn + kv_row(s, m, b, h0 / s.G, sp));
+                nv[0] = src[0];
+                nv[1] = src[1];
+            }
+            uint32_t bn[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float av[GS];
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    av[hh] = a[hh][e >> 2][e & 3];
+                const uint32_t bb = key_bin(pos_key(pos_score<GS>(av, lse, sc, vn != nullptr, nv[e >> 2][e & 3])));
+                if (sp + e < Sb) {
+                    atomicAdd(&L.lh[bb], 1u);
+                    bn[e] = bb;
+                } else {
+                    bn[e] = 0u; // past the sequence's end: never read as a position
+                }
+            }
+            pub_store64(bg + sp / 4, (uint64_t)(bn[0] | bn[1] << 16) | (uint64_t)(bn[2] | bn[3] << 16) << 32);
+            pub_store64(bg + sp / 4 + 1, (uint64_t)(bn[4] | bn[5] << 16) | (uint64_t)(bn[6] | bn[7] << 16) << 32);
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh) {
+                a[hh][0] = an[hh][0];
+                a[hh][1] = an[hh][1];
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < ATTN_HIST_BINS; i += PV_THREADS)
+            if (L.lh[i])
+                atomicAdd(&hg[i], L.lh[i]);
+    }
+    // every histogram atomic and bin store of the workgroup has completed before it counts itself
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t before = __hip_atomic_fetch_add(reinterpret_cast<uint32_t *>(sg + SIG_KCNT), 1u,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        L.last = before == (uint32_t)(nkw - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!L.last)
+        return;
+    if (c0 * ATTN_KEY_CHUNK >= Sb) // (uniform) a workgroup past the end merges lse only when it is the last
+        group_lse<GS>(s, b, h0, nqk_all, nqk, pstat, pst, LL, lse);
+    publish_select<GS>(s, m, Sp, Spb, grp, logit, lse, vn, bins, hg, sg, L);
+}
+
+// ------------------------------------------------------------------ pv role
+// One workgroup per (chunk of P positions, group).  It loads its first pass's
+// logits and merges the group's lse, stores every position's histogram bin and
+// counts itself; the group's last chunk to count resolves the threshold.  Then
+// it waits for the threshold bin d (its first pass's scores stay in
+// registers).  Phase one: every pass keeps the positions above bin d
+// (order-preserving), stages their V rows and probabilities in LDS and streams
+// the rows, 16 in flight per lane (a 16-lane quarter wave per 256-byte row),
+// into p*V partial sums; the chunk's bin-d positions go to an LDS list with
+// their rank keys.  Phase two (only chunks holding bin-d positions wait for the
+// threshold rank key): the listed positions at or above it are streamed the
+// same way.  The order of the additions does not depend on the optional
+// outputs.
+template <int GS> struct PvLds {
+    int64_t rows[PV_PASS]; // V row index of each kept position of the pass
+    union {
+        float pr[GS][PV_PASS];
+        float red[PV_WAVES][GS][D];
+    };
+    int32_t cpos[PV_CAND];
+    uint64_t crank[PV_CAND];
+    uint32_t wk[PV_WAVES];
+};
+static_assert(PV_PASS == PV_WAVES * D, "the wave partials reuse the probability staging");
+
+template <int GS> struct FusedLds {
+    LseLds ls;
+    uint64_t sigv;
+    union {
+        KeyLds key;
+        PvLds<GS> pv;
+    };
+};
+
+template <int GS>
+__device__ void pv_role(const AttnShape &s, const KvMap &m, int Sp, int nqk_all, int P, int npv, int grp, int c,
+                        const uint16_t *__restrict__ v, const float *__restrict__ logit,
+                        const float2 *__restrict__ pstat, const float *__restrict__ vn, uint64_t *sg,
+                        int32_t *__restrict__ pstage, uint32_t *__restrict__ pcount, float *__restrict__ part,
+                        FusedLds<GS> &LF)
+{
+    PvLds<GS> &L = LF.pv;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-    const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel, h0 = sg * s.GS, g = h0 / s.G;
-    const int c = blockIdx.x, npv = gridDim.x;
+    const int b = grp / s.Hsel, h0 = (grp % s.Hsel) * s.GS, g = h0 / s.G;
     const int Sb = seq_len(s, m, b);
     const int p0 = c * P, p1 = min(Sb, p0 + P);
     const float *Lg = logit + ((int64_t)b * s.Hq + h0) * Sp;
-    const uint16_t *Bn = bins + (int64_t)grp * Sp;
     const double sc = (double)s.scale;
+    const int quarter = lane >> 4, dl = lane & 15, slot = w * 4 + quarter;
+    constexpr int NSLOT = PV_WAVES * 4;
     float acc[GS][8];
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh)
@@ -783,119 +873,219 @@ __global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap 
         for (int e = 0; e < 8; ++e)
             acc[hh][e] = 0.0f;
     uint32_t chunk_kept = 0;
+    bool poison = false;
+
+    // the nk rows staged in L.rows / L.pr, into acc
+    auto stream = [&](int nk) {
+        for (int r0 = slot; r0 < nk; r0 += NSLOT * PV_U) {
+            uint4 uu[PV_U];
+#pragma unroll
+            for (int qq = 0; qq < PV_U; ++qq) {
+                const int r = r0 + NSLOT * qq;
+                if (r < nk)
+                    uu[qq] = *reinterpret_cast<const uint4 *>(v + L.rows[r] * D + dl * 8);
+            }
+#pragma unroll
+            for (int qq = 0; qq < PV_U; ++qq) {
+                const int r = r0 + NSLOT * qq;
+                if (r < nk) {
+                    float vv[8];
+                    Vec16<uint16_t>::unpack(uu[qq], vv);
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh) {
+                        const float pv = L.pr[hh][r];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[hh][e] = fmaf(pv, vv[e], acc[hh][e]);
+                    }
+                }
+            }
+        }
+    };
+    // exclusive slot of this thread's n among the pass (wave scan plus the wave
+    // totals in LDS); returns the block total.  A barrier must separate two calls.
+    auto pass_slots = [&](uint32_t n, uint32_t &excl) -> uint32_t {
+        const uint32_t ki = wave_incl_sum(n);
+        if (lane == WAVE - 1)
+            L.wk[w] = ki;
+        __syncthreads();
+        uint32_t before = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < PV_WAVES; ++i) {
+            before += i < w ? L.wk[i] : 0u;
+            tot += L.wk[i];
+        }
+        excl = before + ki - n;
+        return tot;
+    };
+
     if (p0 < p1) { // (uniform over the workgroup) chunks past the sequence's end write zeros
-        // this thread's positions of the first pass, loaded with the threshold
-        auto load_pass = [&](int sb, uint32_t &bw, float2 (&lg)[GS], int64_t &vrow) {
-            const int j0 = sb + 2 * tid;
-            bw = 0;
+        // this thread's two positions of a pass: j0 even and Sp a multiple of 8, so
+        // j0 < Sb keeps both in the row, and pages hold a multiple of 8 positions,
+        // so both share j0's page
+        int j0 = 0;
+        uint32_t va = 0, vb = 0;
+        int64_t vrow = 0;
+        float2 lg[GS], nv = make_float2(1.0f, 1.0f);
+        double lsed[GS];
+        float lsef[GS];
+        uint64_t ka = 0, kb = 0;
+        auto load_pass = [&](int sb) {
+            j0 = sb + 2 * tid;
+            va = (uint32_t)(j0 < p1);
+            vb = (uint32_t)(j0 + 1 < p1);
             vrow = 0;
 #pragma unroll
             for (int hh = 0; hh < GS; ++hh)
                 lg[hh] = make_float2(0.0f, 0.0f);
-            if (j0 < p1) {
+            nv = make_float2(1.0f, 1.0f);
+            if (va) {
                 vrow = kv_row(s, m, b, g, j0);
-                bw = *reinterpret_cast<const uint32_t *>(Bn + j0);
 #pragma unroll
                 for (int hh = 0; hh < GS; ++hh)
                     lg[hh] = *reinterpret_cast<const float2 *>(Lg + (int64_t)hh * Sp + j0);
+                if (vn)
+                    nv = *reinterpret_cast<const float2 *>(vn + vrow);
             }
         };
-        uint32_t bw;
-        float2 lg[GS];
-        int64_t vrow;
-        load_pass(p0, bw, lg, vrow);
-        const AttnSel st = sel[grp];
-        double lsed[GS];
-        float lsef[GS];
+        auto score_pass = [&]() {
+            float ax[GS], ay[GS];
 #pragma unroll
-        for (int hh = 0; hh < GS; ++hh) {
-            lsed[hh] = lse_ws[(int64_t)b * s.Hq + h0 + hh];
+            for (int hh = 0; hh < GS; ++hh) {
+                ax[hh] = lg[hh].x;
+                ay[hh] = lg[hh].y;
+            }
+            ka = pos_key(pos_score<GS>(ax, lsed, sc, vn != nullptr, nv.x));
+            kb = pos_key(pos_score<GS>(ay, lsed, sc, vn != nullptr, nv.y));
+        };
+        auto stage = [&](uint32_t so, bool second) {
+            L.rows[so] = vrow + (second ? 1 : 0);
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+                L.pr[hh][so] = expf(fmaf(s.scale, second ? lg[hh].y : lg[hh].x, -lsef[hh]));
+        };
+        const int nqk = (Sb + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK;
+        float2 pst[GS];
+        ld_stats<GS>(s, b, h0, nqk_all, nqk, pstat, pst);
+        load_pass(p0);
+        group_lse<GS>(s, b, h0, nqk_all, nqk, pstat, pst, LF.ls, lsed);
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh)
             lsef[hh] = (float)lsed[hh];
-        }
-        const uint32_t d = st.d;
-        const uint64_t thr = st.thr;
-        const int quarter = lane >> 4, dl = lane & 15, slot = w * 4 + quarter;
-        constexpr int NSLOT = PV_WAVES * 4;
-        for (int sb = p0; sb < p1; sb += PV_PASS) {
-            if (sb != p0)
-                load_pass(sb, bw, lg, vrow);
-            // thread tid holds positions j0, j0 + 1 (j0 even and Sp a multiple of 8: j0 < Sb keeps both in
-            // the row; pages hold a multiple of 8 positions, so both share j0's page)
-            const int j0 = sb + 2 * tid;
-            const uint32_t ba = bw & 0xffffu, bb = bw >> 16;
-            uint32_t ka = (uint32_t)(j0 < p1) & (uint32_t)(ba > d);
-            uint32_t kb = (uint32_t)(j0 + 1 < p1) & (uint32_t)(bb > d);
-            if (j0 < p1 && ba == d) {
-                float av[GS];
-#pragma unroll
-                for (int hh = 0; hh < GS; ++hh)
-                    av[hh] = lg[hh].x;
-                const float vv = vn ? vn[vrow] : 1.0f;
-                ka = rank_key(pos_key(pos_score<GS>(av, lsed, sc, vn != nullptr, vv)), d, j0) >= thr;
-            }
-            if (j0 + 1 < p1 && bb == d) {
-                float av[GS];
-#pragma unroll
-                for (int hh = 0; hh < GS; ++hh)
-                    av[hh] = lg[hh].y;
-                const float vv = vn ? vn[vrow + 1] : 1.0f;
-                kb = rank_key(pos_key(pos_score<GS>(av, lsed, sc, vn != nullptr, vv)), d, j0 + 1) >= thr;
-            }
-            const uint32_t ki = wave_incl_sum(ka + kb);
-            if (lane == WAVE - 1)
-                wk[w] = ki;
-            __syncthreads();
-            uint32_t before = 0, nkept = 0;
-#pragma unroll
-            for (int i = 0; i < PV_WAVES; ++i) {
-                before += i < w ? wk[i] : 0u;
-                nkept += wk[i];
-            }
-            const uint32_t sa = before + ki - (ka + kb), sbb = sa + ka; // pass-local slots
-            if (ka) {
-                rows[sa] = vrow;
-#pragma unroll
-                for (int hh = 0; hh < GS; ++hh)
-                    pr[hh][sa] = expf(fmaf(s.scale, lg[hh].x, -lsef[hh]));
-                if (pstage)
-                    pstage[(int64_t)grp * Sp + p0 + chunk_kept + sa] = j0;
-            }
-            if (kb) {
-                rows[sbb] = vrow + 1;
-#pragma unroll
-                for (int hh = 0; hh < GS; ++hh)
-                    pr[hh][sbb] = expf(fmaf(s.scale, lg[hh].y, -lsef[hh]));
-                if (pstage)
-                    pstage[(int64_t)grp * Sp + p0 + chunk_kept + sbb] = j0 + 1;
-            }
-            __syncthreads();
-            const int nk = (int)nkept;
-            for (int r0 = slot; r0 < nk; r0 += NSLOT * PV_U) {
-                uint4 u[PV_U];
-#pragma unroll
-                for (int qq = 0; qq < PV_U; ++qq) {
-                    const int r = r0 + NSLOT * qq;
-                    if (r < nk)
-                        u[qq] = *reinterpret_cast<const uint4 *>(v + rows[r] * D + dl * 8);
+        score_pass();
+        // the threshold bin, from the group's last key workgroup
+        if (tid == 0)
+            LF.sigv = wait_ready(sg + SIG_D);
+        __syncthreads();
+        const uint64_t s1 = LF.sigv;
+        poison = !(s1 & 1ull);
+        const uint32_t d = (uint32_t)(s1 >> 40);
+        const bool all_kept = (s1 & 2ull) != 0ull; // every bin-d position is kept: threshold rank key 0
+        uint64_t thr = 0;
+        uint32_t ncand = 0;
+        // phase one: positions above bin d; the bin-d positions go to the LDS list
+        if (!poison) {
+            for (int sb = p0; sb < p1; sb += PV_PASS) {
+                if (sb != p0) {
+                    load_pass(sb);
+                    score_pass();
                 }
-#pragma unroll
-                for (int qq = 0; qq < PV_U; ++qq) {
-                    const int r = r0 + NSLOT * qq;
-                    if (r < nk) {
-                        float vv[8];
-                        Vec16<uint16_t>::unpack(u[qq], vv);
-#pragma unroll
-                        for (int hh = 0; hh < GS; ++hh) {
-                            const float pv = pr[hh][r];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                acc[hh][e] = fmaf(pv, vv[e], acc[hh][e]);
-                        }
+                const uint32_t ba = key_bin(ka), bb = key_bin(kb);
+                const uint32_t ya = va & (uint32_t)(ba > d), yb = vb & (uint32_t)(bb > d);
+                const uint32_t ca = va & (uint32_t)(ba == d), cb = vb & (uint32_t)(bb == d);
+                const uint32_t n = (ya + yb) | (ca + cb) << 16;
+                uint32_t ex;
+                const uint32_t tot = pass_slots(n, ex);
+                uint32_t so = ex & 0xffffu, co = ncand + (ex >> 16);
+                if (ya)
+                    stage(so++, false);
+                if (yb)
+                    stage(so, true);
+                if (ca) {
+                    if (co < (uint32_t)PV_CAND) {
+                        L.cpos[co] = j0;
+                        L.crank[co] = rank_key(ka, d, j0);
                     }
+                    ++co;
+                }
+                if (cb && co < (uint32_t)PV_CAND) {
+                    L.cpos[co] = j0 + 1;
+                    L.crank[co] = rank_key(kb, d, j0 + 1);
+                }
+                __syncthreads();
+                stream((int)(tot & 0xffffu));
+                chunk_kept += tot & 0xffffu;
+                ncand += tot >> 16;
+                __syncthreads();
+            }
+        }
+        // phase two: the bin-d positions at or above the threshold
+        if (ncand != 0u && !poison && !all_kept) {
+            if (tid == 0)
+                LF.sigv = wait_ready(sg + SIG_THR);
+            __syncthreads();
+            const uint64_t s2 = LF.sigv;
+            poison = !(s2 & 1ull);
+            thr = s2 >> 1;
+        }
+        if (ncand != 0u && !poison) {
+            if (ncand <= (uint32_t)PV_CAND) {
+                const uint32_t keep = (uint32_t)((uint32_t)tid < ncand) & (uint32_t)(L.crank[tid] >= thr);
+                uint32_t ex;
+                const uint32_t tot = pass_slots(keep, ex);
+                if (keep) {
+                    const int p = L.cpos[tid];
+                    L.rows[ex] = kv_row(s, m, b, g, p);
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh)
+                        L.pr[hh][ex] = expf(fmaf(s.scale, Lg[(int64_t)hh * Sp + p], -lsef[hh]));
+                }
+                __syncthreads();
+                stream((int)tot);
+                chunk_kept += tot;
+                __syncthreads();
+            } else {
+                // more bin-d positions than the list holds: the passes are scored again
+                for (int sb = p0; sb < p1; sb += PV_PASS) {
+                    load_pass(sb);
+                    score_pass();
+                    const uint32_t ya = va & (uint32_t)(key_bin(ka) == d) & (uint32_t)(rank_key(ka, d, j0) >= thr);
+                    const uint32_t yb =
+                        vb & (uint32_t)(key_bin(kb) == d) & (uint32_t)(rank_key(kb, d, j0 + 1) >= thr);
+                    uint32_t ex;
+                    const uint32_t tot = pass_slots(ya + yb, ex);
+                    if (ya)
+                        stage(ex++, false);
+                    if (yb)
+                        stage(ex, true);
+                    __syncthreads();
+                    stream((int)tot);
+                    chunk_kept += tot;
+                    __syncthreads();
                 }
             }
-            chunk_kept += nkept;
-            __syncthreads();
+        }
+        // kept positions in ascending order, for the kept-position lists
+        if (pstage && !poison) {
+            uint32_t off = 0;
+            for (int sb = p0; sb < p1; sb += PV_PASS) {
+                load_pass(sb);
+                score_pass();
+                const uint32_t ba = key_bin(ka), bb = key_bin(kb);
+                const uint32_t ya =
+                    va & ((uint32_t)(ba > d) | ((uint32_t)(ba == d) & (uint32_t)(rank_key(ka, d, j0) >= thr)));
+                const uint32_t yb =
+                    vb & ((uint32_t)(bb > d) | ((uint32_t)(bb == d) & (uint32_t)(rank_key(kb, d, j0 + 1) >= thr)));
+                uint32_t ex;
+                const uint32_t tot = pass_slots(ya + yb, ex);
+                int32_t *dst = pstage + (int64_t)grp * Sp + p0 + off + ex;
+                if (ya)
+                    *dst++ = j0;
+                if (yb)
+                    *dst = j0 + 1;
+                off += tot;
+                __syncthreads();
+            }
         }
     }
 
@@ -909,25 +1099,58 @@ __global__ __launch_bounds__(PV_THREADS) void attn_pv_kernel(AttnShape s, KvMap 
             x += __shfl_xor(x, 32, WAVE);
             acc[hh][e] = x;
         }
+    __syncthreads(); // (the partials reuse the probability staging)
     if ((lane >> 4) == 0) {
 #pragma unroll
         for (int hh = 0; hh < GS; ++hh)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                red[w][hh][(lane & 15) * 8 + e] = acc[hh][e];
+                L.red[w][hh][(lane & 15) * 8 + e] = acc[hh][e];
     }
     __syncthreads();
     float *mine = part + ((int64_t)grp * npv + c) * GS * D;
     for (int i = tid; i < GS * D; i += PV_THREADS) {
         const int hh = i / D, dd = i % D;
-        float x = red[0][hh][dd];
+        float x = L.red[0][hh][dd];
 #pragma unroll
         for (int ww = 1; ww < PV_WAVES; ++ww)
-            x += red[ww][hh][dd];
-        mine[i] = x;
+            x += L.red[ww][hh][dd];
+        mine[i] = poison ? __builtin_nanf("") : x;
     }
     if (pcount && tid == 0)
         pcount[(int64_t)grp * npv + c] = chunk_kept;
+}
+
+// ------------------------------------------------------------------ fused key / pv launch
+// Workgroups take their role from their index: [0, nkw*G) key workgroups
+// (group-major), then npv*G PV workgroups (group-major).  Only PV workgroups
+// wait, and only for the words the group's last key workgroup publishes; key
+// workgroups wait on nobody and have lower indices.  The dispatcher starts
+// workgroups in index order on each XCD, so every key workgroup has started
+// before any PV workgroup and the waits end whatever the residency.  Each wait
+// is bounded all the same, and one that runs out poisons the group's output
+// with NaN.
+template <int GS>
+__global__ __launch_bounds__(PV_THREADS) void attn_fused_kernel(
+    AttnShape s, KvMap m, int Sp, int nqk_all, int nsub, int nkw, int P, int npv, const uint16_t *__restrict__ v,
+    const float *__restrict__ logit, const float2 *__restrict__ pstat, float *__restrict__ lse_out,
+    const float *__restrict__ vn, uint16_t *__restrict__ bins, uint32_t *__restrict__ hist,
+    uint64_t *__restrict__ sig, int32_t *__restrict__ pstage, uint32_t *__restrict__ pcount, float *__restrict__ part)
+{
+    __shared__ FusedLds<GS> L;
+    const int G = (int)(s.B * s.Hsel);
+    const int Spb = (Sp + BIN_ROW - 1) / BIN_ROW * BIN_ROW;
+    int bid = (int)blockIdx.x;
+    if (bid < nkw * G) {
+        const int grp = bid / nkw;
+        key_role<GS>(s, m, Sp, Spb, nqk_all, nsub, nkw, grp, bid % nkw, logit, pstat, lse_out, vn, bins, hist,
+                     sig + (int64_t)grp * SIG_WORDS, L.key, L.ls);
+        return;
+    }
+    bid -= nkw * G;
+    const int grp = bid / npv;
+    pv_role<GS>(s, m, Sp, nqk_all, P, npv, grp, bid % npv, v, logit, pstat, vn, sig + (int64_t)grp * SIG_WORDS,
+                pstage, pcount, part, L);
 }
 
 // out[b, h0 + hh, :] = sum over the PV chunks of the chunk partials, in a fixed
@@ -1028,16 +1251,14 @@ size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base)
     p = align256(p + (size_t)(s.B * s.Hq * Sp) * 4);
     w.pstat = (float2 *)p;
     p = align256(p + (size_t)(s.B * s.Hq * nqk) * 8);
-    w.lse = (double *)p;
-    p = align256(p + (size_t)(s.B * s.Hq) * 8);
     w.bins = (uint16_t *)p;
-    p = align256(p + (size_t)(G * Sp) * 2);
+    p = align256(p + (size_t)(G * ((Sp + BIN_ROW - 1) / BIN_ROW * BIN_ROW)) * 2);
     w.hist = (uint32_t *)p;
     p = align256(p + (size_t)(G * ATTN_HIST_BINS) * 4);
     w.pcount = (uint32_t *)p;
     p = align256(p + (size_t)(G * npv) * 4);
-    w.sel = p;
-    p = align256(p + (size_t)G * sizeof(AttnSel));
+    w.sig = (uint64_t *)p;
+    p = align256(p + (size_t)(G * SIG_WORDS) * 8);
     w.pstage = (int32_t *)p;
     p = align256(p + (size_t)(G * Sp) * 4);
     w.pvpart = (float *)p;
@@ -1048,8 +1269,7 @@ size_t attn_ws_layout(const AttnShape &s, AttnWs *ws, char *base)
 }
 
 // Key chunks per workgroup: one up to 32K positions, more for longer sequences
-// (at 128K x 4 sequences, 2048 workgroups of one chunk spent most of their time
-// in global histogram atomics).
+// (fewer workgroups, fewer statistics merges and fewer global histogram atomics).
 static int key_chunks_per_wg(int64_t S)
 {
     const int64_t n = S / 32768;
@@ -1066,17 +1286,14 @@ static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q
     const int nqk = (int)((s.S + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK);
     int P, npv;
     pv_chunks(s.S, &P, &npv);
-    AttnSel *sel = reinterpret_cast<AttnSel *>(ws.sel);
     attn_qk_kernel<GS><<<dim3(nqk, G), QK_THREADS, 0, st>>>(s, m, Sp, q, kt, kn, ws.logit, ws.pstat, dim_idx,
-                                                             ws.hist);
+                                                             ws.hist, ws.sig);
     const int nkc = (int)((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK);
     const int nsub = key_chunks_per_wg(s.S);
-    attn_key_kernel<GS><<<dim3((nkc + nsub - 1) / nsub, G), 256, 0, st>>>(
-        s, m, Sp, nqk, nsub, ws.logit, ws.pstat, ws.lse, lse, vn, ws.bins, ws.hist);
-    attn_select_kernel<GS><<<G, ASEL_THREADS, 0, st>>>(s, m, Sp, ws.logit, ws.lse, ws.bins, ws.hist, vn, sel);
-    attn_pv_kernel<GS><<<dim3(npv, G), PV_THREADS, 0, st>>>(s, m, Sp, P, v, ws.logit, ws.lse, ws.bins, vn, sel,
-                                                            pos_idx ? ws.pstage : nullptr,
-                                                            pos_idx ? ws.pcount : nullptr, ws.pvpart);
+    const int nkw = (nkc + nsub - 1) / nsub;
+    attn_fused_kernel<GS><<<(unsigned)((int64_t)(nkw + npv) * G), PV_THREADS, 0, st>>>(
+        s, m, Sp, nqk, nsub, nkw, P, npv, v, ws.logit, ws.pstat, lse, vn, ws.bins, ws.hist, ws.sig,
+        pos_idx ? ws.pstage : nullptr, pos_idx ? ws.pcount : nullptr, ws.pvpart);
     attn_pv_reduce_kernel<GS><<<G * (GS * D / WAVE), PVR_WAVES * WAVE, 0, st>>>(s, npv, ws.pvpart, out);
     if (pos_idx)
         attn_pos_kernel<<<dim3(npv, G), 256, 0, st>>>(s, m, Sp, P, ws.pcount, ws.pstage, pos_idx);

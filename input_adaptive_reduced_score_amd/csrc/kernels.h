@@ -38,7 +38,7 @@
 
 #define ATTN_D 128
 #define ATTN_QK_CHUNK 512   // positions per QK workgroup
-#define ATTN_KEY_CHUNK 2048 // positions per key/histogram workgroup
+#define ATTN_KEY_CHUNK 2048 // positions per key-workgroup chunk
 #define ATTN_HIST_BINS 8192 // position-score histogram: half-nat bins outside [-32, 0), 1/128 nat inside
 #define ATTN_MAX_GROUPS 512 // B * Hsel and B * Hkv limit of the attention entry points (the range the tests cover)
 #define RMM_WS_HEADER_BYTES_INTERNAL 4096
@@ -124,11 +124,10 @@ struct AttnShape {
 struct AttnWs {
     float *logit;     // [B][Hq][Sp] unscaled q.k over kept dims
     float2 *pstat;    // [B][Hq][nqk] (max, sum exp) per QK chunk
-    double *lse;      // [B][Hq]
-    uint16_t *bins;   // [B][Hsel][Sp] histogram bin of every position's score
+    uint16_t *bins;   // [B][Hsel][Sp rounded up to 64] histogram bin of every position's score
     uint32_t *hist;   // [B][Hsel][ATTN_HIST_BINS]
     uint32_t *pcount; // [B][Hsel][npv] kept positions per PV chunk
-    void *sel;        // [B][Hsel] threshold of each group (bin, rank key)
+    uint64_t *sig;    // [B][Hsel][32] words: workgroup counts, threshold bin, threshold rank key
     int32_t *pstage;  // [B][Hsel][Sp] kept positions of each PV chunk, staged at the chunk's start
     float *pvpart;    // [B][Hsel][npv][GS][D]
 };

@@ -41,24 +41,6 @@ __device__ __forceinline__ int hpad(int b) { return b + (b >> 5); }
 constexpr int SEL_HIST_WORDS = SEL_BINS + SEL_BINS / 32;
 constexpr int SEL_DUMMY = SEL_HIST_WORDS; // + lane: per-lane sink for masked-off histogram atomics
 
-// Agent-scope stores and loads of published words (coherent across XCDs when complete).
-__device__ __forceinline__ void pub_store(uint32_t *p, uint32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t pub_load(const uint32_t *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void pub_store64(uint64_t *p, uint64_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t pub_load64(const uint64_t *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // The whole block finds the digit holding the krem-th largest key, clears the
 // histogram and publishes (digit, rank inside the digit, keys in the digit) in
 // res[0..2].  Thread t owns bins 2047-2t and 2046-2t, so threads in ascending
