@@ -455,6 +455,7 @@ __device__ __forceinline__ uint64_t wait_ready(const uint64_t *p)
 constexpr int PV_WAVES = 4;
 constexpr int PV_THREADS = PV_WAVES * WAVE; // every role of the fused kernel: 256 threads
 constexpr int PV_PASS = 2 * PV_THREADS;     // positions per PV pass (2 per thread)
+constexpr int PV_STAGE = 2 * PV_PASS;       // kept rows staged in LDS before they are streamed
 constexpr int PV_MAX_CHUNKS = 32;
 constexpr int PV_U = 16;                    // kept V rows in flight per lane
 constexpr int PV_CAND = PV_THREADS;         // threshold-bin positions a PV chunk keeps in LDS for its second phase
@@ -830,16 +831,16 @@ __device__ void key_role(const AttnShape &s, const KvMap &m, int Sp, int Spb, in
 // same way.  The order of the additions does not depend on the optional
 // outputs.
 template <int GS> struct PvLds {
-    int64_t rows[PV_PASS]; // V row index of each kept position of the pass
+    int64_t rows[PV_STAGE]; // V row index of each staged kept position
     union {
-        float pr[GS][PV_PASS];
+        float pr[GS][PV_STAGE];
         float red[PV_WAVES][GS][D];
     };
     int32_t cpos[PV_CAND];
     uint64_t crank[PV_CAND];
     uint32_t wk[PV_WAVES];
 };
-static_assert(PV_PASS == PV_WAVES * D, "the wave partials reuse the probability staging");
+static_assert(PV_STAGE >= PV_WAVES * D, "the wave partials reuse the probability staging");
 
 template <int GS> struct FusedLds {
     LseLds ls;
@@ -948,6 +949,39 @@ __device__ void pv_role(const AttnShape &s, const KvMap &m, int Sp, int nqk_all,
                     nv = *reinterpret_cast<const float2 *>(vn + vrow);
             }
         };
+        // the next pass's logits, value norms and row, loaded while this pass's rows stream
+        int j0n = 0;
+        uint32_t van = 0, vbn = 0;
+        int64_t vrown = 0;
+        float2 lgn[GS], nvn = make_float2(1.0f, 1.0f);
+        auto load_next = [&](int sb) {
+            j0n = sb + 2 * tid;
+            van = (uint32_t)(j0n < p1);
+            vbn = (uint32_t)(j0n + 1 < p1);
+            vrown = 0;
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+                lgn[hh] = make_float2(0.0f, 0.0f);
+            nvn = make_float2(1.0f, 1.0f);
+            if (van) {
+                vrown = kv_row(s, m, b, g, j0n);
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    lgn[hh] = *reinterpret_cast<const float2 *>(Lg + (int64_t)hh * Sp + j0n);
+                if (vn)
+                    nvn = *reinterpret_cast<const float2 *>(vn + vrown);
+            }
+        };
+        auto take_next = [&]() {
+            j0 = j0n;
+            va = van;
+            vb = vbn;
+            vrow = vrown;
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+                lg[hh] = lgn[hh];
+            nv = nvn;
+        };
         auto score_pass = [&]() {
             float ax[GS], ay[GS];
 #pragma unroll
@@ -983,11 +1017,14 @@ __device__ void pv_role(const AttnShape &s, const KvMap &m, int Sp, int nqk_all,
         const bool all_kept = (s1 & 2ull) != 0ull; // every bin-d position is kept: threshold rank key 0
         uint64_t thr = 0;
         uint32_t ncand = 0;
-        // phase one: positions above bin d; the bin-d positions go to the LDS list
+        // phase one: positions above bin d, staged over passes in LDS and
+        // streamed when the stage would overflow or the chunk ends; the bin-d
+        // positions go to the LDS list
         if (!poison) {
+            uint32_t nst = 0; // rows staged and not yet streamed
             for (int sb = p0; sb < p1; sb += PV_PASS) {
                 if (sb != p0) {
-                    load_pass(sb);
+                    take_next();
                     score_pass();
                 }
                 const uint32_t ba = key_bin(ka), bb = key_bin(kb);
@@ -996,7 +1033,7 @@ __device__ void pv_role(const AttnShape &s, const KvMap &m, int Sp, int nqk_all,
                 const uint32_t n = (ya + yb) | (ca + cb) << 16;
                 uint32_t ex;
                 const uint32_t tot = pass_slots(n, ex);
-                uint32_t so = ex & 0xffffu, co = ncand + (ex >> 16);
+                uint32_t so = nst + (ex & 0xffffu), co = ncand + (ex >> 16);
                 if (ya)
                     stage(so++, false);
                 if (yb)
@@ -1012,10 +1049,17 @@ __device__ void pv_role(const AttnShape &s, const KvMap &m, int Sp, int nqk_all,
                     L.cpos[co] = j0 + 1;
                     L.crank[co] = rank_key(kb, d, j0 + 1);
                 }
-                __syncthreads();
-                stream((int)(tot & 0xffffu));
+                nst += tot & 0xffffu;
                 chunk_kept += tot & 0xffffu;
                 ncand += tot >> 16;
+                __syncthreads();
+                if (sb + PV_PASS < p1)
+                    load_next(sb + PV_PASS);
+                // (uniform) a further pass could overflow the stage, or this is the last pass
+                if (nst > (uint32_t)(PV_STAGE - PV_PASS) || sb + PV_PASS >= p1) {
+                    stream((int)nst);
+                    nst = 0;
+                }
                 __syncthreads();
             }
         }
