@@ -160,7 +160,8 @@ def src_hash(files):
 
 
 def load_traffic(kernel: str, sha: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    """The committed rocprofv3 record of a launch (HBM bytes from the FETCH_SIZE / WRITE_SIZE runs,
+    traced kernel durations), if the kernel's sources are unchanged since; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -169,14 +170,17 @@ def load_traffic(kernel: str, sha: str):
         return None
     if not rec or rec.get("source_sha") != sha:
         return None
-    return rec.get("bytes_per_launch")
+    return rec
 
 
 def main():
     args = parse()
 
     def want(section):
-        return not args.no_sweep and not args.headline_only and (args.section is None or section in args.section)
+        # sections named with --section run whatever else is limited; otherwise the whole sweep runs
+        if args.section is not None:
+            return section in args.section
+        return not args.no_sweep and not args.headline_only
 
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported (multi-GPU sharding is "
@@ -611,13 +615,18 @@ def main():
                     "input_adaptive_reduced_score_amd/csrc/radix.h",
                     "input_adaptive_reduced_score_amd/csrc/device.h",
                     "input_adaptive_reduced_score_amd/csrc/kernels.h"])
+    prof = load_traffic("select_gemv_decode_r0.5", sha)
     roofline = {"kernel": "fused decode step: select_gemv_kernel<bf16,16> + split-K gemv_reduce_kernel<1,512>",
                 "bound": "hbm",
                 "achieved": head["fused_launch_GBps"], "peak": A.HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": head["fused_launch_GBps"] / A.HBM_PEAK_GBS,
                 "algorithmic_bytes_per_launch": head["retained_bytes"],
                 "avg_launch_us": head["fused_launch_us"],
-                "traffic": load_traffic("select_gemv_decode_r0.5", sha), "source_sha": sha}
+                "traffic": prof["bytes_per_launch"] if prof else None, "source_sha": sha}
+    if prof:
+        # the same launch in the committed rocprofv3 trace (the tracer adds about 1 us per dispatch)
+        roofline["profile_avg_launch_us"] = prof["profile_launch_avg_us"]
+        roofline["profile_frac"] = head["retained_bytes"] / prof["profile_launch_avg_us"] / 1e3 / A.HBM_PEAK_GBS
     line = {
         "metric": "retained-work HBM GB/s & MFMA TFLOP/s vs r; reduced attn-decode us at S=32K",
         "value": head["step_GBps"],
