@@ -267,16 +267,73 @@ hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const v
 // One launch selects and multiplies.  Workgroup 0 runs the tile's selection
 // (select_body with PUB) and publishes, in two steps, which slices are kept;
 // every workgroup (0 included, after its selection) owns a column slice and a
-// range of R slice indices, 16 waves of up to 64 slices each.  After flag1 a
-// wave streams the rows of its slices above the undecided digit (kept for
-// certain) while workgroup 0 still resolves that digit; after flag2 it streams
-// the digit's kept rows.  Each wave adds its rows in that fixed order, the waves
-// are summed in order, and gemv_reduce_kernel sums the splits in order, so the
-// result is deterministic.  Workgroup 0 is dispatched first and waits on no
-// other workgroup, so the waits end whatever the residency; each wait is
-// bounded all the same, and a wait that runs out poisons the output with NaN.
+// range of R slice indices, 16 waves of up to 64 slices each.  Every other
+// workgroup first estimates the threshold key from a sample of the keys
+// (estimate_edge) and streams the rows of its slices at or above it while
+// workgroup 0 still selects.  Once both flags are out a wave streams, in one
+// pass, the kept rows it has not taken yet and takes back (adds with the
+// opposite sign) those it took that are not kept.  The kept set is the
+// selection's in every case; the estimate only moves work earlier.  Each wave
+// adds its rows in that fixed order, the waves are summed in order, and
+// gemv_reduce_kernel sums the splits in order, so the result is
+// deterministic.  Workgroup 0 is dispatched first and waits on no other
+// workgroup, so the waits end whatever the residency; each wait is bounded all
+// the same, and a wait that runs out poisons the output with NaN.
 constexpr int FUSED_WAVES = SEL_THREADS / WAVE; // 16
 constexpr int FUSED_SPIN = 1 << 20;             // polls (about 1 s) before a wait gives up
+constexpr int EST_SAMPLE = 4096;                // slices the early threshold estimate is taken from
+constexpr int EST_BITS = 11;                    // its histogram: the top 11 bits of the 31-bit key
+constexpr int EST_BINS = 1 << EST_BITS;
+
+// The early estimate, taken by every workgroup but the selecting one from the
+// same sample, so that all agree without a hand-off: the keys of the first
+// EST_SAMPLE slices (the selector's arithmetic), an LDS histogram of their top
+// EST_BITS bits (8 bins per octave), and E = the upper edge of the bin holding
+// the sample key of rank 0.9 * k * n / K from the top.  Keys at or above E are
+// kept for all but a sample that misleads; the caller streams those rows
+// before the selection is known and corrects the rest after it.  h holds
+// EST_BINS + FUSED_WAVES + 1 words of LDS.  Contains barriers: every thread of
+// the workgroup calls it.
+template <typename TE>
+__device__ uint32_t estimate_edge(const TE *__restrict__ x, const float *__restrict__ c, int K, int k, uint32_t *h)
+{
+    const int tid = threadIdx.x;
+    const int ns = min(K, EST_SAMPLE);
+    uint32_t kk[EST_SAMPLE / SEL_THREADS];
+#pragma unroll
+    for (int j = 0; j < EST_SAMPLE / SEL_THREADS; ++j) {
+        const int i = tid + j * SEL_THREADS;
+        kk[j] = i < ns ? nonneg_key(__fmul_rn(fabsf(ld_elem(x, i)), c[i])) : 0u;
+    }
+    for (int i = tid; i < EST_BINS; i += SEL_THREADS)
+        h[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EST_SAMPLE / SEL_THREADS; ++j)
+        if (tid + j * SEL_THREADS < ns)
+            atomicAdd(&h[kk[j] >> (31 - EST_BITS)], 1u);
+    __syncthreads();
+    // thread t holds bins B-1-BPT*t down to B-BPT-BPT*t (B bins); exactly one
+    // bin holds the target rank, since 1 <= want <= ns
+    constexpr int BPT = EST_BINS / SEL_THREADS;
+    const uint32_t want = max(1u, (uint32_t)(0.9 * (double)k * (double)ns / (double)K));
+    uint32_t hc[BPT], tot = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        hc[i] = h[EST_BINS - 1 - BPT * tid - i];
+        tot += hc[i];
+    }
+    const uint32_t incl = block_incl_scan(tot, h + EST_BINS); // (barriers inside)
+    uint32_t run = incl - tot;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        if (run < want && want <= run + hc[i])
+            h[EST_BINS + FUSED_WAVES] = (uint32_t)(EST_BINS - BPT * tid - i) << (31 - EST_BITS);
+        run += hc[i];
+    }
+    __syncthreads();
+    return h[EST_BINS + FUSED_WAVES];
+}
 
 // Polls a published word until its ready bit is set; 0 if it never is.
 __device__ __forceinline__ uint64_t wait_sig(const uint64_t *sig)
@@ -299,7 +356,11 @@ __global__ __launch_bounds__(SEL_THREADS) void select_gemv_kernel(const TE *__re
     constexpr int VEC = Vec16<TE>::N;
     constexpr int CW = WAVE * VEC; // columns per slice
     constexpr int U = GEMV_UNROLL; // kept rows in flight per wave
-    __shared__ float red[FUSED_WAVES][CW];
+    __shared__ union {
+        float red[FUSED_WAVES][CW];             // the waves' partial sums
+        uint32_t est[EST_BINS + FUSED_WAVES + 1]; // the early estimate's histogram
+    } lds;
+    float(&red)[FUSED_WAVES][CW] = lds.red;
     __shared__ uint64_t sig[2];
     __shared__ uint32_t wcnt[FUSED_WAVES];
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
@@ -334,8 +395,11 @@ __global__ __launch_bounds__(SEL_THREADS) void select_gemv_kernel(const TE *__re
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
         acc[e] = 0.0f;
-    // rows of the slices lo + b for the set bits b of a wave-uniform mask, U in flight
-    auto stream = [&](uint64_t m) {
+    // rows of the slices lo + b for the set bits b of two disjoint wave-uniform
+    // masks, ascending, U in flight: added for `plus`, taken back (added with
+    // the opposite sign) for `minus`
+    auto stream = [&](uint64_t plus, uint64_t minus) {
+        uint64_t m = plus | minus;
         while (m) {
             uint4 u[U];
             float xs[U];
@@ -345,7 +409,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_gemv_kernel(const TE *__re
                 if (m) {
                     const int b = __builtin_ctzll(m);
                     m &= m - 1ull;
-                    xs[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xj), b));
+                    const float xb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xj), b));
+                    xs[q] = ((minus >> b) & 1ull) ? -xb : xb;
                     if (active)
                         u[q] = Vec16<TE>::raw(wt + (int64_t)(lo + b) * ldw + col);
                     cnt = q + 1;
@@ -364,27 +429,33 @@ __global__ __launch_bounds__(SEL_THREADS) void select_gemv_kernel(const TE *__re
         }
     };
 
-    // 1. rows above the undecided digit (kept for certain)
-    if (tid == 0)
+    // 0. rows at or above the early estimate (every workgroup but the selecting one)
+    uint64_t spec = 0;
+    if (blockIdx.x != 0) {
+        const uint32_t est = estimate_edge<TE>(x, c, K, k, lds.est);
+        spec = __ballot(lane < n && key0 >= est);
+        stream(spec, 0ull);
+    }
+    // 1. the selection: the undecided digit and the slices above it (flag1), the
+    // threshold within the digit (flag2)
+    if (tid == 0) {
         sig[0] = wait_sig(pub.sig1);
+        sig[1] = wait_sig(pub.sig2);
+    }
     __syncthreads();
-    const uint64_t s1 = sig[0];
+    const uint64_t s1 = sig[0], s2 = sig[1];
     const uint32_t mn = (uint32_t)(s1 >> 32), dg = (uint32_t)(s1 >> 11) & 0x1fffffu;
     const int sh = (int)(s1 >> 6) & 31, nb = (int)(s1 >> 1) & 31;
     const uint32_t pm = ((1u << nb) - 1u) << sh, pfx = dg << sh;
     const uint32_t key = key0 == 0u ? 0u : key0 - mn + 1u; // re-based as the selecting workgroup does
-    const uint64_t sure = __ballot(lane < n && (key & pm) > pfx);
-    const bool cand = lane < n && (key & pm) == pfx;
-    stream(sure);
-    // 2. the undecided digit's kept rows
-    if (tid == 0)
-        sig[1] = wait_sig(pub.sig2);
-    __syncthreads();
-    const uint64_t s2 = sig[1];
     const uint32_t thr = (uint32_t)(s2 >> 32);
     const int jt = (int)((uint32_t)s2 >> 1);
+    const bool cand = lane < n && (key & pm) == pfx;
+    const uint64_t sure = __ballot(lane < n && (key & pm) > pfx);
     const uint64_t keptc = __ballot(cand && (key > thr || (key == thr && lo + lane <= jt)));
-    stream(keptc);
+    const uint64_t kept = sure | keptc;
+    // 2. the kept rows not taken early, and those taken early that are not kept, in one pass
+    stream(kept & ~spec, spec & ~kept);
     if (!(s1 & s2 & 1ull)) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
@@ -392,7 +463,6 @@ __global__ __launch_bounds__(SEL_THREADS) void select_gemv_kernel(const TE *__re
     }
     // kept list (ascending): the waves of column slice 0 write their kept slices
     if (idx && slice == 0) {
-        const uint64_t kept = sure | keptc;
         if (lane == 0)
             wcnt[w] = (uint32_t)__popcll(kept);
         __syncthreads();

@@ -91,6 +91,16 @@ def test_all_equal_scores():
     assert np.array_equal(idx.cpu().numpy()[0], np.arange(2500))
 
 
+@pytest.mark.parametrize("scale", [1.0 / 64, 64.0])
+def test_early_estimate_misled_by_its_sample(scale):
+    # the early threshold estimate samples the first 4096 slices; here they score far below the
+    # rest (most rows streamed early are then taken back) or far above it (few are streamed early)
+    cs = W.linear_random(1, 14336, 4096, 1, "bf16", seed=12)
+    cs.c[:4096] *= np.float32(scale)
+    for r in (0.25, 0.5, 0.75):
+        run_fused(cs, r)
+
+
 def test_without_index_list_and_repeated_calls():
     # the benchmark's call: no index list; repeated calls and calls of other shapes in between give
     # bit-identical results (the launch's flags are cleared after every call)
