@@ -526,6 +526,28 @@ def main():
                 sweep.append(rec)
                 log(f"[bench] {name} r=({rd},{rp}): {rec['call_us']:.1f} us, {rec['GBps']:.0f} GB/s retained")
             if S <= 32768:
+                # per-query-head selection: each KV row read once for the union of its heads' sets
+                for rd, rp in ((0.25, 0.25), (0.5, 0.5)):
+                    kd, kss = rmm.keep_count(D, rd), rmm.keep_count(S, rp)
+                    t = time_loop(lambda i: rmm.attn_decode(qs[i % nac], ks_[i % nac], vs_[i % nac], kns[i % nac],
+                                                            rd, rp, scale=ac.scale, out=out, mode=1,
+                                                            want_idx=False), asteps, 3, torch)
+                    _, di, pi, _ = rmm.attn_decode(qs[0], ks_[0], vs_[0], kns[0], rd, rp, scale=ac.scale, mode=1)
+                    G = Hq // Hkv
+                    di = di.cpu().numpy().reshape(B, Hkv, G, kd)
+                    pi = pi.cpu().numpy().reshape(B, Hkv, G, kss)
+                    du = sum(np.unique(di[b_, g_]).size for b_ in range(B) for g_ in range(Hkv))
+                    pu = sum(np.unique(pi[b_, g_][pi[b_, g_] >= 0]).size for b_ in range(B) for g_ in range(Hkv))
+                    by = A.attn_union_step_bytes(B, Hq, Hkv, D, S, du, pu)
+                    per_head = B * Hq * (kd * S + kss * D) * 2
+                    sweep.append({"workload": name + "_per_q_head", "mode": 1, "r_dim": rd, "r_pos": rp, "kd": kd,
+                                  "ks": kss, "call_us": t * 1e6, "retained_bytes": by, "GBps": by / t / 1e9,
+                                  "frac_hbm": by / t / 1e9 / A.HBM_PEAK_GBS,
+                                  "union_dims_frac": du / (B * Hkv * D), "union_pos_frac": pu / (B * Hkv * S),
+                                  "kv_bytes_union": du * S * 2 + pu * D * 2, "kv_bytes_per_head_reads": per_head})
+                    log(f"[bench] {name} per-query-head r=({rd},{rp}): {t * 1e6:.1f} us, {by / t / 1e9:.0f} GB/s "
+                        f"retained (union: {100 * du / (B * Hkv * D):.0f}% of dims, "
+                        f"{100 * pu / (B * Hkv * S):.0f}% of positions)")
                 # position score weighted by the value-row norm: one more fp32 read per position
                 vns = [torch.from_numpy(W.value_row_norms(ac.v)).to(dev) for _ in range(nac)]
                 rd, rp = 0.25, 0.25

@@ -73,8 +73,10 @@ typedef enum {
 /* Selection groups for grouped-query attention.  PER_KV_GROUP: the G = Hq/Hkv
  * query heads sharing one KV head share one head_dim selection and one key
  * position selection (scores take the max over those heads).  PER_Q_HEAD:
- * each query head selects alone (the KV rows of a group are then read once per
- * query head). */
+ * each query head selects alone (blog section 3.3: reduce inside each head);
+ * with G > 1 a KV head's K^T dim rows and V position rows are read once for the
+ * union of its query heads' sets, and each head adds only its own kept dims and
+ * positions. */
 typedef enum {
     RMM_SEL_PER_KV_GROUP = 0,
     RMM_SEL_PER_Q_HEAD = 1,

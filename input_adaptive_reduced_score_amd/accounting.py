@@ -44,6 +44,16 @@ def attn_step_bytes(B: int, Hq: int, Hkv: int, D: int, S: int, kd: int, ks: int,
     return kept_k + kept_v + logits + idx + small
 
 
+def attn_union_step_bytes(B: int, Hq: int, Hkv: int, D: int, S: int, dims_union: int, pos_union: int) -> int:
+    """Reduced decode attention with per-query-head selection, read as the union
+    over each KV head's query heads: dims_union and pos_union are the sizes of the
+    union of the heads' kept dims and kept positions, summed over the B*Hkv KV
+    heads.  Each union K^T row (S positions) and V row (D dims) is read once;
+    plus the fp32 logits written and read back, q, kn and out."""
+    small = B * Hq * D * 2 + B * Hkv * D * 4 + B * Hq * D * 4
+    return dims_union * S * 2 + pos_union * D * 2 + 2 * B * Hq * S * 4 + small
+
+
 def attn_dense_bytes(B: int, Hq: int, Hkv: int, D: int, S: int) -> int:
     return B * Hkv * S * D * 2 * 2 + B * Hq * D * (2 + 4)
 

@@ -104,7 +104,7 @@ __device__ __forceinline__ int64_t kt_off(const AttnShape &s, const KvMap &m, in
 
 // Keeps the kd largest of 128 keys held two per lane (j = lane, lane + 64),
 // ties to the lower index, and writes the kept indices in ascending order.
-__device__ __forceinline__ void wave_select128(uint32_t key0, uint32_t key1, int kd, int *jd)
+__device__ __forceinline__ void wave_select128(uint32_t key0, uint32_t key1, int kd, int *jd, uint64_t *kmask = nullptr)
 {
     const int lane = threadIdx.x & (WAVE - 1);
     // largest v with #(key >= v) >= kd: the kd-th largest key
@@ -123,6 +123,10 @@ __device__ __forceinline__ void wave_select128(uint32_t key0, uint32_t key1, int
     const bool keep0 = key0 > v || (key0 == v && r0 < quota);
     const bool keep1 = key1 > v || (key1 == v && r1 < quota);
     const uint64_t k0 = __ballot(keep0), k1 = __ballot(keep1);
+    if (kmask && lane == 0) {
+        kmask[0] = k0;
+        kmask[1] = k1;
+    }
     if (keep0)
         jd[__popcll(k0 & lt)] = lane;
     if (keep1)
@@ -141,7 +145,12 @@ constexpr int SIG_KCNT = 0, SIG_D = 16, SIG_THR = 17;
 constexpr int ATTN_SPIN = 1 << 20; // polls (about a second) before a wait gives up
 
 // ------------------------------------------------------------------ qk
-template <int GS>
+// One workgroup per (chunk of ATTN_QK_CHUNK positions, group).  PH = false: the
+// group is a selection group whose GS heads share one kept dim set.  PH = true
+// (per-query-head selection with G > 1): the group is a KV head, each of its GS
+// = G query heads selects its own dims, the union of the heads' dims is read
+// once, and a head's logits add only its own dims (q is zero on the others).
+template <int GS, bool PH>
 __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, KvMap m, int Sp, const uint16_t *__restrict__ q,
                                                              const uint16_t *__restrict__ kt,
                                                              const float *__restrict__ kn, float *__restrict__ logit,
@@ -150,12 +159,15 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, KvMap 
                                                              uint32_t *__restrict__ hist, uint64_t *__restrict__ sig)
 {
     constexpr int NWQ = QK_THREADS / WAVE;
-    __shared__ int jd[D];
+    __shared__ int jd[D]; // the dims read, ascending
     __shared__ float qs[GS][D];
     __shared__ float part[NWQ][GS][ATTN_QK_CHUNK];
+    __shared__ int jh[PH ? GS : 1][D];          // PH: each head's kept dims
+    __shared__ uint64_t hm[PH ? GS : 1][2];     // PH: each head's kept dims as two 64-bit masks
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-    const int grp = blockIdx.y, b = grp / s.Hsel, sg = grp % s.Hsel;
-    const int h0 = sg * s.GS, g = h0 / s.G;
+    const int grp = blockIdx.y;
+    const int b = PH ? grp / (int)s.Hkv : grp / s.Hsel;
+    const int h0 = PH ? (grp % (int)s.Hkv) * s.G : (grp % s.Hsel) * s.GS, g = h0 / s.G;
     const int chunk = blockIdx.x, nchunk = gridDim.x;
     const int Sb = seq_len(s, m, b);
     if (chunk * ATTN_QK_CHUNK >= Sb)
@@ -178,33 +190,73 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, KvMap 
         for (int e = 0; e < 8; ++e)
             qall[(tid * 8 + e) / D][(tid * 8 + e) % D] = v[e];
     }
-    // 1. head_dim selection (wave 0): sigma_j = fl32(max_h |q_h[j]| * kn[j])
-    if (w == 0) {
-        uint32_t key[2];
+    int nsel = s.kd; // dims read
+    if constexpr (!PH) {
+        // 1. head_dim selection (wave 0): sigma_j = fl32(max_h |q_h[j]| * kn[j])
+        if (w == 0) {
+            uint32_t key[2];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int j = lane + WAVE * half;
-            float a = 0.0f;
+            for (int half = 0; half < 2; ++half) {
+                const int j = lane + WAVE * half;
+                float a = 0.0f;
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    a = fmaxf(a, fabsf(bf16_to_f32(qb[hh * D + j])));
+                key[half] = nonneg_key(__fmul_rn(a, kn[((int64_t)b * s.Hkv + g) * D + j]));
+            }
+            wave_select128(key[0], key[1], s.kd, jd);
+        }
+        __syncthreads();
+        for (int i = tid; i < s.kd; i += QK_THREADS) {
+            const int j = jd[i];
 #pragma unroll
             for (int hh = 0; hh < GS; ++hh)
-                a = fmaxf(a, fabsf(bf16_to_f32(qb[hh * D + j])));
-            key[half] = nonneg_key(__fmul_rn(a, kn[((int64_t)b * s.Hkv + g) * D + j]));
+                qs[hh][i] = qall[hh][j];
+            if (chunk == 0 && dim_idx_out)
+                dim_idx_out[(int64_t)grp * s.kd + i] = j;
         }
-        wave_select128(key[0], key[1], s.kd, jd);
-    }
-    __syncthreads();
-    for (int i = tid; i < s.kd; i += QK_THREADS) {
-        const int j = jd[i];
+    } else {
+        // 1. each head's selection (wave w takes heads w, w + 4, ...):
+        // sigma_j = fl32(|q_h[j]| * kn[j])
+        for (int hh = w; hh < GS; hh += NWQ) {
+            uint32_t key[2];
 #pragma unroll
-        for (int hh = 0; hh < GS; ++hh)
-            qs[hh][i] = qall[hh][j];
+            for (int half = 0; half < 2; ++half) {
+                const int j = lane + WAVE * half;
+                key[half] = nonneg_key(
+                    __fmul_rn(fabsf(bf16_to_f32(qb[hh * D + j])), kn[((int64_t)b * s.Hkv + g) * D + j]));
+            }
+            wave_select128(key[0], key[1], s.kd, jh[hh], hm[hh]);
+        }
+        __syncthreads();
+        // the union of the heads' dims, ascending; q of a head is zero on the dims it dropped
+        uint64_t u0 = 0, u1 = 0;
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh) {
+            u0 |= hm[hh][0];
+            u1 |= hm[hh][1];
+        }
+        nsel = __popcll(u0) + __popcll(u1);
+        if (tid < D) {
+            const int j = tid, hf = j / WAVE, bit = j % WAVE;
+            const uint64_t um = hf ? u1 : u0;
+            if ((um >> bit) & 1ull) {
+                const uint64_t below = bit ? (um & (~0ull >> (WAVE - bit))) : 0ull;
+                const int i = (hf ? __popcll(u0) : 0) + __popcll(below);
+                jd[i] = j;
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    qs[hh][i] = ((hm[hh][hf] >> bit) & 1ull) ? qall[hh][j] : 0.0f;
+            }
+        }
         if (chunk == 0 && dim_idx_out)
-            dim_idx_out[(int64_t)grp * s.kd + i] = j;
+            for (int i = tid; i < GS * s.kd; i += QK_THREADS)
+                dim_idx_out[((int64_t)b * s.Hq + h0 + i / s.kd) * s.kd + i % s.kd] = jh[i / s.kd][i % s.kd];
     }
     __syncthreads();
 
     // 2. partial dot products: wave w takes kept dims [i0, i1) (ascending), 8 positions per lane
-    const int i0 = s.kd * w / NWQ, i1 = s.kd * (w + 1) / NWQ;
+    const int i0 = nsel * w / NWQ, i1 = nsel * (w + 1) / NWQ;
     float acc[GS][8];
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh)
@@ -280,15 +332,18 @@ __global__ __launch_bounds__(QK_THREADS) void attn_qk_kernel(AttnShape s, KvMap 
             pstat[((int64_t)b * s.Hq + h0 + hh) * nchunk + chunk] = make_float2(mx, z);
     }
 
-    // 4. the first chunk's workgroup clears the group's score histogram and signal words for the next launch
+    // 4. the first chunk's workgroup clears the score histograms and signal words
+    // of the group's selection groups (PH: one per head) for the next launch
     if (chunk == 0) {
-        for (int i = tid; i < ATTN_HIST_BINS; i += QK_THREADS)
-            hist[(int64_t)grp * ATTN_HIST_BINS + i] = 0;
-        if (tid == 0) {
-            uint64_t *sg = sig + (int64_t)grp * SIG_WORDS;
-            pub_store64(sg + SIG_KCNT, 0ull);
-            pub_store64(sg + SIG_D, 0ull);
-            pub_store64(sg + SIG_THR, 0ull);
+        const int nsg = PH ? GS : 1;
+        const int64_t sg0 = PH ? (int64_t)b * s.Hq + h0 : grp;
+        for (int i = tid; i < nsg * ATTN_HIST_BINS; i += QK_THREADS)
+            hist[sg0 * ATTN_HIST_BINS + i] = 0;
+        if (tid < nsg) {
+            uint64_t *sw = sig + (sg0 + tid) * SIG_WORDS;
+            pub_store64(sw + SIG_KCNT, 0ull);
+            pub_store64(sw + SIG_D, 0ull);
+            pub_store64(sw + SIG_THR, 0ull);
         }
     }
 }
@@ -1197,6 +1252,241 @@ __global__ __launch_bounds__(PV_THREADS) void attn_fused_kernel(
                 pstage, pcount, part, L);
 }
 
+// ------------------------------------------------------------------ per-query-head PV over the union of rows
+// Per-query-head selection with G > 1: after the key launch has published every
+// head's threshold, one workgroup per (chunk of P positions, KV head) decides
+// for each position and each of the G heads whether that head keeps it (the
+// head's own score, bin and rank key, as its key workgroups computed them),
+// and streams every position some head keeps once, each head adding p_h * V
+// for the positions it keeps (0 for the others).  Partials per (KV head,
+// chunk, head) as the grouped path writes them; the kept positions per head go
+// to the staging lists.
+template <int GS>
+__global__ __launch_bounds__(PV_THREADS) void attn_pv_union_kernel(AttnShape s, KvMap m, int Sp, int nqk_all, int P,
+                                                                   const uint16_t *__restrict__ v,
+                                                                   const float *__restrict__ logit,
+                                                                   const float2 *__restrict__ pstat,
+                                                                   const float *__restrict__ vn,
+                                                                   const uint64_t *__restrict__ sig,
+                                                                   int32_t *__restrict__ pstage,
+                                                                   uint32_t *__restrict__ pcount,
+                                                                   float *__restrict__ part)
+{
+    __shared__ LseLds LL;
+    __shared__ PvLds<GS> L;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    const int grp = blockIdx.y, c = blockIdx.x, npv = gridDim.x;
+    const int b = grp / (int)s.Hkv, g = grp % (int)s.Hkv, h0 = g * s.G;
+    const int Sb = seq_len(s, m, b);
+    const int p0 = c * P, p1 = min(Sb, p0 + P);
+    const float *Lg = logit + ((int64_t)b * s.Hq + h0) * Sp;
+    const double sc = (double)s.scale;
+    const int quarter = lane >> 4, dl = lane & 15, slot = w * 4 + quarter;
+    constexpr int NSLOT = PV_WAVES * 4;
+    float acc[GS][8];
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[hh][e] = 0.0f;
+    bool poison = false;
+    uint32_t kept_h[GS];
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+        kept_h[hh] = 0;
+
+    auto stream = [&](int nk) {
+        for (int r0 = slot; r0 < nk; r0 += NSLOT * PV_U) {
+            uint4 uu[PV_U];
+#pragma unroll
+            for (int qq = 0; qq < PV_U; ++qq) {
+                const int r = r0 + NSLOT * qq;
+                if (r < nk)
+                    uu[qq] = *reinterpret_cast<const uint4 *>(v + L.rows[r] * D + dl * 8);
+            }
+#pragma unroll
+            for (int qq = 0; qq < PV_U; ++qq) {
+                const int r = r0 + NSLOT * qq;
+                if (r < nk) {
+                    float vv[8];
+                    Vec16<uint16_t>::unpack(uu[qq], vv);
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh) {
+                        const float pv = L.pr[hh][r];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[hh][e] = fmaf(pv, vv[e], acc[hh][e]);
+                    }
+                }
+            }
+        }
+    };
+    // exclusive slot of this thread's n (wave scan plus the wave totals in LDS);
+    // returns the block total.  A barrier must separate two calls.
+    auto pass_slots = [&](uint32_t n, uint32_t &excl) -> uint32_t {
+        const uint32_t ki = wave_incl_sum(n);
+        if (lane == WAVE - 1)
+            L.wk[w] = ki;
+        __syncthreads();
+        uint32_t before = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < PV_WAVES; ++i) {
+            before += i < w ? L.wk[i] : 0u;
+            tot += L.wk[i];
+        }
+        excl = before + ki - n;
+        return tot;
+    };
+
+    if (p0 < p1) { // (uniform) chunks past the sequence's end write zeros
+        // every head's threshold: bin d, all-of-bin-d flag, rank key (the key launch has finished)
+        uint32_t dh[GS];
+        uint64_t th[GS];
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh) {
+            const uint64_t *sw = sig + ((int64_t)b * s.Hq + h0 + hh) * SIG_WORDS;
+            const uint64_t w1 = sw[SIG_D], w2 = sw[SIG_THR];
+            const bool all = (w1 & 2ull) != 0ull;
+            poison |= !(w1 & 1ull) || (!all && !(w2 & 1ull));
+            dh[hh] = (uint32_t)(w1 >> 40);
+            th[hh] = all ? 0ull : w2 >> 1;
+        }
+        const int nqk = (Sb + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK;
+        float2 pst[GS];
+        double lsed[GS];
+        float lsef[GS];
+        ld_stats<GS>(s, b, h0, nqk_all, nqk, pstat, pst);
+        group_lse<GS>(s, b, h0, nqk_all, nqk, pstat, pst, LL, lsed);
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh)
+            lsef[hh] = (float)lsed[hh];
+        if (!poison) {
+            uint32_t nst = 0;
+            uint32_t off[GS]; // kept positions of each head staged so far (pstage)
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+                off[hh] = 0;
+            for (int sb = p0; sb < p1; sb += PV_PASS) {
+                // this thread's two positions (j0 even, Sp a multiple of 8, pages hold a multiple of 8)
+                const int j0 = sb + 2 * tid;
+                const bool va = j0 < p1, vb = j0 + 1 < p1;
+                float2 lg[GS];
+                float2 nv = make_float2(1.0f, 1.0f);
+                int64_t vrow = 0;
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    lg[hh] = make_float2(0.0f, 0.0f);
+                if (va) {
+                    vrow = kv_row(s, m, b, g, j0);
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh)
+                        lg[hh] = *reinterpret_cast<const float2 *>(Lg + (int64_t)hh * Sp + j0);
+                    if (vn)
+                        nv = *reinterpret_cast<const float2 *>(vn + vrow);
+                }
+                // which heads keep each position: the head's own score key against its threshold
+                uint32_t ma = 0, mb = 0;
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh) {
+                    const float ax[1] = {lg[hh].x}, ay[1] = {lg[hh].y};
+                    const double lh[1] = {lsed[hh]};
+                    const uint64_t ka = pos_key(pos_score<1>(ax, lh, sc, vn != nullptr, nv.x));
+                    const uint64_t kb = pos_key(pos_score<1>(ay, lh, sc, vn != nullptr, nv.y));
+                    const uint32_t ba = key_bin(ka), bb = key_bin(kb);
+                    const bool keepa = va && (ba > dh[hh] || (ba == dh[hh] && rank_key(ka, dh[hh], j0) >= th[hh]));
+                    const bool keepb =
+                        vb && (bb > dh[hh] || (bb == dh[hh] && rank_key(kb, dh[hh], j0 + 1) >= th[hh]));
+                    ma |= (uint32_t)keepa << hh;
+                    mb |= (uint32_t)keepb << hh;
+                }
+                uint32_t ex;
+                const uint32_t tot = pass_slots((uint32_t)(ma != 0u) + (uint32_t)(mb != 0u), ex);
+                uint32_t so = nst + ex;
+                if (ma) {
+                    L.rows[so] = vrow;
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh)
+                        L.pr[hh][so] = ((ma >> hh) & 1u) ? expf(fmaf(s.scale, lg[hh].x, -lsef[hh])) : 0.0f;
+                    ++so;
+                }
+                if (mb) {
+                    L.rows[so] = vrow + 1;
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh)
+                        L.pr[hh][so] = ((mb >> hh) & 1u) ? expf(fmaf(s.scale, lg[hh].y, -lsef[hh])) : 0.0f;
+                }
+                nst += tot;
+                __syncthreads();
+                // each head's kept positions, ascending, for the kept-position lists
+                if (pstage) {
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh) {
+                        const uint32_t ka = (ma >> hh) & 1u, kb = (mb >> hh) & 1u;
+                        uint32_t e2;
+                        const uint32_t t2 = pass_slots(ka + kb, e2);
+                        int32_t *dst = pstage + ((int64_t)b * s.Hq + h0 + hh) * Sp + p0 + off[hh] + e2;
+                        if (ka)
+                            *dst++ = j0;
+                        if (kb)
+                            *dst = j0 + 1;
+                        off[hh] += t2;
+                        __syncthreads();
+                    }
+                }
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    kept_h[hh] += ((ma >> hh) & 1u) + ((mb >> hh) & 1u);
+                // (uniform) a further pass could overflow the stage, or this is the last pass
+                if (nst > (uint32_t)(PV_STAGE - PV_PASS) || sb + PV_PASS >= p1) {
+                    stream((int)nst);
+                    nst = 0;
+                }
+                __syncthreads();
+            }
+        }
+        if (pcount) {
+            // this chunk's kept count per head (block sums of the threads' counts)
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh) {
+                uint32_t e3;
+                const uint32_t t3 = pass_slots(kept_h[hh], e3);
+                if (tid == 0)
+                    pcount[((int64_t)b * s.Hq + h0 + hh) * npv + c] = poison ? 0u : t3;
+                __syncthreads();
+            }
+        }
+    }
+
+    // reduce the four quarters of each wave, then the waves (fixed order)
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = acc[hh][e];
+            x += __shfl_xor(x, 16, WAVE);
+            x += __shfl_xor(x, 32, WAVE);
+            acc[hh][e] = x;
+        }
+    __syncthreads(); // (the partials reuse the probability staging)
+    if ((lane >> 4) == 0) {
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                L.red[w][hh][(lane & 15) * 8 + e] = acc[hh][e];
+    }
+    __syncthreads();
+    float *mine = part + ((int64_t)grp * npv + c) * GS * D;
+    for (int i = tid; i < GS * D; i += PV_THREADS) {
+        const int hh = i / D, dd = i % D;
+        float x = L.red[0][hh][dd];
+#pragma unroll
+        for (int ww = 1; ww < PV_WAVES; ++ww)
+            x += L.red[ww][hh][dd];
+        mine[i] = poison ? __builtin_nanf("") : x;
+    }
+}
+
 // out[b, h0 + hh, :] = sum over the PV chunks of the chunk partials, in a fixed
 // order.  Workgroup = 64 consecutive outputs of one group (GS*D/64 workgroups
 // per group, so the partials are read by many CUs at once); wave w sums the
@@ -1330,8 +1620,8 @@ static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q
     const int nqk = (int)((s.S + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK);
     int P, npv;
     pv_chunks(s.S, &P, &npv);
-    attn_qk_kernel<GS><<<dim3(nqk, G), QK_THREADS, 0, st>>>(s, m, Sp, q, kt, kn, ws.logit, ws.pstat, dim_idx,
-                                                             ws.hist, ws.sig);
+    attn_qk_kernel<GS, false><<<dim3(nqk, G), QK_THREADS, 0, st>>>(s, m, Sp, q, kt, kn, ws.logit, ws.pstat,
+                                                                    dim_idx, ws.hist, ws.sig);
     const int nkc = (int)((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK);
     const int nsub = key_chunks_per_wg(s.S);
     const int nkw = (nkc + nsub - 1) / nsub;
@@ -1344,10 +1634,57 @@ static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q
     return hipGetLastError();
 }
 
+// Per-query-head selection with G > 1 query heads per KV head: QK over the
+// union of the heads' kept dims (one launch per KV head and chunk), the key
+// role per head (the fused kernel with no PV workgroups), PV over the union of
+// the heads' kept positions, the fixed-order reduce per KV head.
+template <int G>
+static hipError_t attn_run_union(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt,
+                                 const uint16_t *v, const float *kn, const float *vn, float *out, int32_t *dim_idx,
+                                 int32_t *pos_idx, float *lse, const AttnWs &ws, hipStream_t st)
+{
+    const int Sp = (int)((s.S + 7) / 8 * 8);
+    const int Gsel = (int)(s.B * s.Hsel); // one selection group per query head
+    const int Gkv = (int)(s.B * s.Hkv);
+    const int nqk = (int)((s.S + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK);
+    int P, npv;
+    pv_chunks(s.S, &P, &npv);
+    attn_qk_kernel<G, true><<<dim3(nqk, Gkv), QK_THREADS, 0, st>>>(s, m, Sp, q, kt, kn, ws.logit, ws.pstat,
+                                                                    dim_idx, ws.hist, ws.sig);
+    const int nkc = (int)((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK);
+    const int nsub = key_chunks_per_wg(s.S);
+    const int nkw = (nkc + nsub - 1) / nsub;
+    attn_fused_kernel<1><<<(unsigned)((int64_t)nkw * Gsel), PV_THREADS, 0, st>>>(
+        s, m, Sp, nqk, nsub, nkw, P, npv, v, ws.logit, ws.pstat, lse, vn, ws.bins, ws.hist, ws.sig, nullptr, nullptr,
+        ws.pvpart);
+    attn_pv_union_kernel<G><<<dim3(npv, Gkv), PV_THREADS, 0, st>>>(s, m, Sp, nqk, P, v, ws.logit, ws.pstat, vn,
+                                                                   ws.sig, pos_idx ? ws.pstage : nullptr,
+                                                                   pos_idx ? ws.pcount : nullptr, ws.pvpart);
+    AttnShape su = s; // the partials are laid out per KV head with its G heads
+    su.GS = G;
+    su.Hsel = (int)s.Hkv;
+    attn_pv_reduce_kernel<G><<<Gkv * (G * D / WAVE), PVR_WAVES * WAVE, 0, st>>>(su, npv, ws.pvpart, out);
+    if (pos_idx)
+        attn_pos_kernel<<<dim3(npv, Gsel), 256, 0, st>>>(s, m, Sp, P, ws.pcount, ws.pstage, pos_idx);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt, const uint16_t *v,
                        const float *kn, const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
                        const AttnWs &ws, hipStream_t st)
 {
+    if (s.GS == 1 && s.G > 1) {
+        switch (s.G) {
+        case 2:
+            return attn_run_union<2>(s, m, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
+        case 4:
+            return attn_run_union<4>(s, m, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
+        case 8:
+            return attn_run_union<8>(s, m, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);
+        default:
+            return hipErrorInvalidValue;
+        }
+    }
     switch (s.GS) {
     case 1:
         return attn_run<1>(s, m, q, kt, v, kn, vn, out, dim_idx, pos_idx, lse, ws, st);

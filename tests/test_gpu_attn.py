@@ -72,20 +72,22 @@ def test_group_sizes(Hq, Hkv):
     run_attn(cs, 0.5, 0.25, 1)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("S", [1, 7, 8, 513, 4095, 9999])
-def test_ragged_lengths(S):
+def test_ragged_lengths(S, mode):
     cs = W.attn_case(1, S, Hq=4, Hkv=1, seed=S, n_hot=min(4, S))
-    run_attn(cs, 0.5, 0.3, 0)
+    run_attn(cs, 0.5, 0.3, mode)
 
 
-def test_cache_with_spare_capacity():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_cache_with_spare_capacity(mode):
     # ldk/ldv larger than S: the kernels must read positions < S only
     cs = W.attn_case(1, 1000, Hq=8, Hkv=2, seed=3, n_hot=4)
     kt = np.full((1, 2, 128, 1032), 0x7f80, np.uint16)  # +inf beyond S
     kt[..., :1000] = cs.kt
     v = np.full((1, 2, 1100, 128), 0x7f80, np.uint16)
     v[:, :, :1000] = cs.v
-    run_attn(cs, 0.5, 0.5, 0, kt=kt, v=v, S=1000)
+    run_attn(cs, 0.5, 0.5, mode, kt=kt, v=v, S=1000)
 
 
 def test_all_equal_logits_take_lowest_positions():

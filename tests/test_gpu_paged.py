@@ -84,9 +84,10 @@ def test_value_norm_weighted_paged():
     check_paged(pc, 0.5, 0.25, 1, use_vn=True)
 
 
-def test_long_mixed_batch_gqa():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_long_mixed_batch_gqa(mode):
     pc = W.attn_paged([40000, 9000, 1, 16384], page=256, Hq=32, Hkv=8, seed=6, n_hot=16)
-    check_paged(pc, 0.25, 0.25, 0)
+    check_paged(pc, 0.25, 0.25, mode)
 
 
 def test_one_page_per_sequence_equals_contiguous_cache():
