@@ -268,7 +268,7 @@ hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const v
 // (select_body with PUB) and publishes, in two steps, which slices are kept;
 // every workgroup (0 included, after its selection) owns a column slice and a
 // range of R slice indices, 16 waves of up to 64 slices each.  Every other
-// workgroup first estimates the threshold key from a sample of the keys
+// workgroup first estimates the threshold key from its own slices' keys
 // (estimate_edge) and streams the rows of its slices at or above it while
 // workgroup 0 still selects.  Once both flags are out a wave streams, in one
 // pass, the kept rows it has not taken yet and takes back (adds with the
@@ -281,40 +281,31 @@ hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const v
 // the same, and a wait that runs out poisons the output with NaN.
 constexpr int FUSED_WAVES = SEL_THREADS / WAVE; // 16
 constexpr int FUSED_SPIN = 1 << 20;             // polls (about 1 s) before a wait gives up
-constexpr int EST_SAMPLE = 4096;                // slices the early threshold estimate is taken from
 constexpr int EST_BITS = 11;                    // its histogram: the top 11 bits of the 31-bit key
 constexpr int EST_BINS = 1 << EST_BITS;
 
-// The early estimate, taken by every workgroup but the selecting one from the
-// same sample, so that all agree without a hand-off: the keys of the first
-// EST_SAMPLE slices (the selector's arithmetic), an LDS histogram of their top
-// EST_BITS bits (8 bins per octave), and E = the upper edge of the bin holding
-// the sample key of rank 0.9 * k * n / K from the top.  Keys at or above E are
-// kept for all but a sample that misleads; the caller streams those rows
-// before the selection is known and corrects the rest after it.  h holds
+// The early estimate, taken by each workgroup but the selecting one from the
+// keys of its own slices (which its waves hold for the selection anyway), so no
+// further load and no hand-off: an LDS histogram of their top EST_BITS bits (8
+// bins per octave), and E = the upper edge of the bin holding the key of rank
+// 0.9 * k * ns / K from the top, ns the workgroup's slice count.  Keys at or
+// above E are kept for all but a range that misleads; the caller streams those
+// rows before the selection is known and corrects the rest after it.  h holds
 // EST_BINS + FUSED_WAVES + 1 words of LDS.  Contains barriers: every thread of
 // the workgroup calls it.
-template <typename TE>
-__device__ uint32_t estimate_edge(const TE *__restrict__ x, const float *__restrict__ c, int K, int k, uint32_t *h)
+__device__ uint32_t estimate_edge(uint32_t key, bool valid, int ns, int K, int k, uint32_t *h)
 {
     const int tid = threadIdx.x;
-    const int ns = min(K, EST_SAMPLE);
-    uint32_t kk[EST_SAMPLE / SEL_THREADS];
-#pragma unroll
-    for (int j = 0; j < EST_SAMPLE / SEL_THREADS; ++j) {
-        const int i = tid + j * SEL_THREADS;
-        kk[j] = i < ns ? nonneg_key(__fmul_rn(fabsf(ld_elem(x, i)), c[i])) : 0u;
-    }
     for (int i = tid; i < EST_BINS; i += SEL_THREADS)
         h[i] = 0;
+    if (tid == 0)
+        h[EST_BINS + FUSED_WAVES] = 0xffffffffu; // no slices: nothing early
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < EST_SAMPLE / SEL_THREADS; ++j)
-        if (tid + j * SEL_THREADS < ns)
-            atomicAdd(&h[kk[j] >> (31 - EST_BITS)], 1u);
+    if (valid)
+        atomicAdd(&h[key >> (31 - EST_BITS)], 1u);
     __syncthreads();
     // thread t holds bins B-1-BPT*t down to B-BPT-BPT*t (B bins); exactly one
-    // bin holds the target rank, since 1 <= want <= ns
+    // bin holds the target rank when 1 <= want <= ns
     constexpr int BPT = EST_BINS / SEL_THREADS;
     const uint32_t want = max(1u, (uint32_t)(0.9 * (double)k * (double)ns / (double)K));
     uint32_t hc[BPT], tot = 0;
@@ -432,7 +423,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_gemv_kernel(const TE *__re
     // 0. rows at or above the early estimate (every workgroup but the selecting one)
     uint64_t spec = 0;
     if (blockIdx.x != 0) {
-        const uint32_t est = estimate_edge<TE>(x, c, K, k, lds.est);
+        const uint32_t est = estimate_edge(key0, lane < n, ws1 - ws0, K, k, lds.est);
         spec = __ballot(lane < n && key0 >= est);
         stream(spec, 0ull);
     }

@@ -93,8 +93,9 @@ def test_all_equal_scores():
 
 @pytest.mark.parametrize("scale", [1.0 / 64, 64.0])
 def test_early_estimate_misled_by_its_sample(scale):
-    # the early threshold estimate samples the first 4096 slices; here they score far below the
-    # rest (most rows streamed early are then taken back) or far above it (few are streamed early)
+    # each workgroup estimates the threshold from its own slices' keys; here the first 4096
+    # slices score far below (above) the rest, so the workgroups holding them (the others)
+    # stream rows early that the selection drops, and take them back
     cs = W.linear_random(1, 14336, 4096, 1, "bf16", seed=12)
     cs.c[:4096] *= np.float32(scale)
     for r in (0.25, 0.5, 0.75):
