@@ -281,6 +281,7 @@ hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const v
 // the same, and a wait that runs out poisons the output with NaN.
 constexpr int FUSED_WAVES = SEL_THREADS / WAVE; // 16
 constexpr int FUSED_SPIN = 1 << 20;             // polls (about 1 s) before a wait gives up
+constexpr double EST_FRAC = 0.9;               // the estimate aims at this fraction of the kept count
 constexpr int EST_BITS = 11;                    // its histogram: the top 11 bits of the 31-bit key
 constexpr int EST_BINS = 1 << EST_BITS;
 
@@ -288,7 +289,7 @@ constexpr int EST_BINS = 1 << EST_BITS;
 // keys of its own slices (which its waves hold for the selection anyway), so no
 // further load and no hand-off: an LDS histogram of their top EST_BITS bits (8
 // bins per octave), and E = the upper edge of the bin holding the key of rank
-// 0.9 * k * ns / K from the top, ns the workgroup's slice count.  Keys at or
+// EST_FRAC * k * ns / K from the top, ns the workgroup's slice count.  Keys at or
 // above E are kept for all but a range that misleads; the caller streams those
 // rows before the selection is known and corrects the rest after it.  h holds
 // EST_BINS + FUSED_WAVES + 1 words of LDS.  Contains barriers: every thread of
@@ -307,7 +308,7 @@ __device__ uint32_t estimate_edge(uint32_t key, bool valid, int ns, int K, int k
     // thread t holds bins B-1-BPT*t down to B-BPT-BPT*t (B bins); exactly one
     // bin holds the target rank when 1 <= want <= ns
     constexpr int BPT = EST_BINS / SEL_THREADS;
-    const uint32_t want = max(1u, (uint32_t)(0.9 * (double)k * (double)ns / (double)K));
+    const uint32_t want = max(1u, (uint32_t)(EST_FRAC * (double)k * (double)ns / (double)K));
     uint32_t hc[BPT], tot = 0;
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
