@@ -243,8 +243,12 @@ def main():
             rmm.select(xs[i], cs_[i], 1, r, idx=idxb[i])
 
         def step(i):
-            # the decode step in one launch (+ the split-K sum): selection and reduced product,
-            # the kept index list written as well
+            # the decode step in one launch (+ the split-K sum): selection and reduced product
+            j = i % ncp
+            rmm.select_linear(xs[j], cs_[j], r, ws_[j], out=yb, want_idx=False)
+
+        def step_list(i):
+            # the same step writing the kept index list as well
             j = i % ncp
             rmm.select_linear(xs[j], cs_[j], r, ws_[j], out=yb, idx=idxb[j])
 
@@ -256,23 +260,26 @@ def main():
 
         t_step = time_loop(step, steps, warmup, torch)
         t_launch = event_avg(step, steps, torch)
+        t_list = time_loop(step_list, steps, warmup, torch)
         t_step2 = time_loop(step2, steps, warmup, torch)
         t_eager = eager_loop(step, min(steps, 50), torch)
         t_gemv = event_avg(lambda i: rmm.linear(xs[i % ncp], ws_[i % ncp], idxb[i % ncp], 1, out=yb), steps, torch)
         t_sel = event_avg(lambda i: rmm.select(xs[i % ncp], cs_[i % ncp], 1, r, idx=idxb[i % ncp]), steps, torch)
-        by = A.decode_step_bytes(K, M, k)
+        by = A.decode_step_bytes(K, M, k, kept_list=False)
         rec = {"workload": "decode_down_proj", "r": r, "k": k,
                "step_us": t_step * 1e6, "fused_launch_us": t_launch * 1e6, "eager_step_us": t_eager * 1e6,
+               "step_with_kept_list_us": t_list * 1e6,
                "two_call_step_us": t_step2 * 1e6, "select_us": t_sel * 1e6, "gemv_us": t_gemv * 1e6,
                "retained_bytes": by, "step_GBps": by / t_step / 1e9, "fused_launch_GBps": by / t_launch / 1e9,
-               "two_call_step_GBps": by / t_step2 / 1e9,
+               "two_call_step_GBps": A.decode_step_bytes(K, M, k) / t_step2 / 1e9,
                "gemv_GBps": A.gemv_launch_bytes(k, M) / t_gemv / 1e9}
         rec["fused_launch_frac_hbm"] = rec["fused_launch_GBps"] / A.HBM_PEAK_GBS
         rec["gemv_frac_hbm"] = rec["gemv_GBps"] / A.HBM_PEAK_GBS
         rec["rel_l2_vs_dense"] = rel_l2(rmm.linear(xs[0], ws_[0], idxb[0], 1), rmm.linear_dense(xs[0], ws_[0]))
         sweep.append(rec)
         log(f"[bench] decode r={r}: step {rec['step_us']:.2f} us ({rec['step_GBps']:.0f} GB/s; fused launch "
-            f"{rec['fused_launch_us']:.2f} us by events), as two calls {rec['two_call_step_us']:.2f} us (select "
+            f"{rec['fused_launch_us']:.2f} us by events; {t_list * 1e6:.2f} us writing the kept list), as two calls "
+            f"{rec['two_call_step_us']:.2f} us (select "
             f"{rec['select_us']:.2f} us, gemv {rec['gemv_us']:.2f} us = {rec['gemv_GBps']:.0f} GB/s), "
             f"rel-L2 vs dense {rec['rel_l2_vs_dense']:.3f}")
         if r == 0.5:
@@ -280,14 +287,13 @@ def main():
     if not args.headline_only:
         # the same step with one input copy (warm: W^T stays in the 256 MB Infinity Cache), labelled as such
         k = rmm.keep_count(K, 0.5)
-        idxw = rmm.select(xs[0], cs_[0], 1, 0.5)
 
         def wstep(i):
-            rmm.select_linear(xs[0], cs_[0], 0.5, ws_[0], out=yb, idx=idxw)
+            rmm.select_linear(xs[0], cs_[0], 0.5, ws_[0], out=yb, want_idx=False)
 
         t_warm = time_loop(wstep, steps, warmup, torch)
         sweep.append({"workload": "decode_down_proj_warm_cache", "r": 0.5, "k": k, "step_us": t_warm * 1e6,
-                      "step_GBps": A.decode_step_bytes(K, M, k) / t_warm / 1e9})
+                      "step_GBps": A.decode_step_bytes(K, M, k, kept_list=False) / t_warm / 1e9})
         log(f"[bench] decode r=0.5, warm cache (one input copy): step {t_warm * 1e6:.2f} us")
         t_dense = event_avg(lambda i: rmm.linear_dense(xs[i % ncp], ws_[i % ncp], out=yb), steps, torch)
         t_blas = eager_event_avg(lambda i: torch.matmul(xs[i % ncp], ws_[i % ncp]), min(steps, 50), torch)
@@ -662,8 +668,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "decode_down_proj: select + reduced GEMV in one launch (rmm_select_linear, kept "
-                               "list written), X[1,14336] bf16 = silu(a)*b, "
+        "config": {"workload": "decode_down_proj: select + reduced GEMV in one launch (rmm_select_linear, the "
+                               "kept list not asked for), X[1,14336] bf16 = silu(a)*b, "
                                "W^T[14336,4096] bf16 ~N(0,0.02), r=0.5 (k=7168), cold-cache input rotation",
                    "r": 0.5, "K": K, "M": M, "T": 1, "accumulate": "fp32", "parallelism": "single GPU"},
         "roofline": roofline,

@@ -20,10 +20,11 @@ def linear_flops(T: int, k: int, M: int) -> int:
     return gemm_flops(T, M, k)
 
 
-def decode_step_bytes(K: int, M: int, k: int, xbytes: int = 2, wbytes: int = 2) -> int:
+def decode_step_bytes(K: int, M: int, k: int, xbytes: int = 2, wbytes: int = 2, kept_list: bool = True) -> int:
     """select + reduced GEMV for one token: read x and c (scorer), write and read
-    the k indices, read the k kept W^T rows, write y (fp32)."""
-    return K * (xbytes + 4) + 8 * k + wbytes * k * M + 4 * M
+    the k indices (kept_list: the two-call step, or the kept list asked for),
+    read the k kept W^T rows, write y (fp32)."""
+    return K * (xbytes + 4) + (8 * k if kept_list else 0) + wbytes * k * M + 4 * M
 
 
 def gemv_launch_bytes(k: int, M: int, T: int = 1, xbytes: int = 2, wbytes: int = 2) -> int:

@@ -138,12 +138,14 @@ __global__ __launch_bounds__(RED_WAVES * WAVE) void gemv_reduce_kernel(const flo
                                                                        int tile, int groups_per_tile, int nslices,
                                                                        int nsplit, int M, float *__restrict__ y,
                                                                        int64_t ldy, uint64_t *__restrict__ clear1 = nullptr,
-                                                                       uint64_t *__restrict__ clear2 = nullptr)
+                                                                       uint64_t *__restrict__ clear2 = nullptr,
+                                                                       uint64_t *__restrict__ clear3 = nullptr)
 {
     if (clear1 && blockIdx.x == 0 && threadIdx.x == 0) {
         // the fused launch before this one has finished: its flags return to zero
         __hip_atomic_store(clear1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(clear2, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(clear3, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     constexpr int CHUNKS = NT * CW / WAVE;
     __shared__ float red[RED_WAVES][WAVE];
@@ -265,14 +267,16 @@ hipError_t launch_gemv(const void *x, bool bf16, int64_t T, int64_t ldx, const v
 
 // ============================================================================ fused select + GEMV (one token)
 // One launch selects and multiplies.  Workgroup 0 runs the tile's selection
-// (select_body with PUB) and publishes, in two steps, which slices are kept;
+// (select_body with PUB) and publishes, in two steps, which slices are kept
+// (then, for the kept list, each split's offset in it);
 // every workgroup (0 included, after its selection) owns a column slice and a
 // range of R slice indices, 16 waves of up to 64 slices each.  Every other
 // workgroup first estimates the threshold key from its own slices' keys
 // (estimate_edge) and streams the rows of its slices at or above it while
 // workgroup 0 still selects.  Once both flags are out a wave streams, in one
 // pass, the kept rows it has not taken yet and takes back (adds with the
-// opposite sign) those it took that are not kept.  The kept set is the
+// opposite sign) those it took that are not kept; the waves of column slice 0
+// write their kept slices once the offsets are out.  The kept set is the
 // selection's in every case; the estimate only moves work earlier.  Each wave
 // adds its rows in that fixed order, the waves are summed in order, and
 // gemv_reduce_kernel sums the splits in order, so the result is
@@ -353,7 +357,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_gemv_kernel(const TE *__re
         uint32_t est[EST_BINS + FUSED_WAVES + 1]; // the early estimate's histogram
     } lds;
     float(&red)[FUSED_WAVES][CW] = lds.red;
-    __shared__ uint64_t sig[2];
+    __shared__ uint64_t sig[3];
     __shared__ uint32_t wcnt[FUSED_WAVES];
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     if (blockIdx.x == 0)
@@ -454,10 +458,18 @@ __global__ __launch_bounds__(SEL_THREADS) void select_gemv_kernel(const TE *__re
             acc[e] = __builtin_nanf("");
     }
     // kept list (ascending): the waves of column slice 0 write their kept slices
+    // once the per-split offsets are out
     if (idx && slice == 0) {
+        if (tid == 0)
+            sig[2] = wait_sig(pub.sig3);
         if (lane == 0)
             wcnt[w] = (uint32_t)__popcll(kept);
         __syncthreads();
+        if (!(sig[2] & 1ull)) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                acc[e] = __builtin_nanf("");
+        }
         uint32_t off = pub_load(pub.offs + split);
         for (int i = 0; i < w; ++i)
             off += wcnt[i];
@@ -537,7 +549,8 @@ static hipError_t select_gemv_dispatch(const FusedPlan &p, const TE *x, int64_t 
     SelPub pub;
     pub.sig1 = reinterpret_cast<uint64_t *>(hdr);
     pub.sig2 = reinterpret_cast<uint64_t *>(hdr + 128);
-    pub.offs = reinterpret_cast<uint32_t *>(body);
+    pub.sig3 = reinterpret_cast<uint64_t *>(hdr + 256);
+    pub.offs = idx ? reinterpret_cast<uint32_t *>(body) : nullptr; // the offsets serve the kept list only
     pub.R = p.R;
     pub.R0 = p.R0;
     pub.R1 = p.R1;
@@ -560,7 +573,7 @@ static hipError_t select_gemv_dispatch(const FusedPlan &p, const TE *x, int64_t 
 #undef RMM_FUSED_CASE
     const dim3 rgrid((unsigned)(p.nslices * (CW / WAVE)));
     gemv_reduce_kernel<1, CW><<<rgrid, RED_WAVES * WAVE, 0, st>>>(part, 1, 1, 1, p.nslices, p.nsplit, (int)M, y,
-                                                                 (int64_t)M, pub.sig1, pub.sig2);
+                                                                 (int64_t)M, pub.sig1, pub.sig2, pub.sig3);
     return hipGetLastError();
 }
 

@@ -57,7 +57,7 @@ namespace rmm {
 // short first range of R0 slices (the selecting workgroup's own share, streamed
 // after its selection) and nsplit - 1 ranges of R1; the others into ranges of R.
 struct SelPub {
-    uint64_t *sig1 = nullptr, *sig2 = nullptr;
+    uint64_t *sig1 = nullptr, *sig2 = nullptr, *sig3 = nullptr;
     uint32_t *offs = nullptr;
     int R = 1, R0 = 1, R1 = 1, nsplit = 0;
 };

@@ -86,11 +86,12 @@ __device__ __forceinline__ void block_crossing(uint32_t *hist, uint32_t krem, ui
 // writes the tile's kept list to idx.  With PUB it publishes to the other
 // workgroups of a fused select-and-product launch (SelPub): after the first
 // radix pass, the re-basing minimum and the digit whose keys are still
-// undecided (sig1; keys above it are kept for certain), then each split's count
-// of kept slices before it, the exact threshold and the slice of the last kept
-// key equal to it (sig2).  Published words are agent-scope stores (coherent
-// across XCDs without cache write-backs); the offsets are complete before sig2
-// is stored.
+// undecided (sig1; keys above it are kept for certain), then the exact
+// threshold and the slice of the last kept key equal to it (sig2: as soon as
+// the crossing digit's candidates are ranked, else after the compaction), and
+// each split's count of kept slices before it (complete before sig3 is
+// stored; only when pub.offs is given).  Published words are agent-scope stores (coherent across XCDs
+// without cache write-backs).
 template <typename TE, int PER, bool PUB>
 __device__ __forceinline__ void select_body(const TE *__restrict__ x, int64_t ldx, int T, int K, int tile,
                                             const float *__restrict__ c, const float *__restrict__ pmax, int Kp,
@@ -104,7 +105,7 @@ __device__ __forceinline__ void select_body(const TE *__restrict__ x, int64_t ld
     __shared__ uint32_t wmin[NW], wmax[NW], wgt[NW], weq[NW], wtot[NW];
     __shared__ uint2 cand[SEL_CAND_CAP];
     __shared__ uint32_t rk_above[SEL_RANK_SPLIT][SEL_CAND_CAP], rk_tie[SEL_RANK_SPLIT][SEL_CAND_CAP];
-    __shared__ uint32_t res[5], ncand;
+    __shared__ uint32_t res[6], ncand;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int j0 = tid * PER; // first slice of this thread
     const int lim = K - j0;   // registers i < lim hold real slices
@@ -117,6 +118,7 @@ __device__ __forceinline__ void select_body(const TE *__restrict__ x, int64_t ld
         res[2] = 0;
         res[3] = 0;
         res[4] = 0;
+        res[5] = 0;
         ncand = 0;
     }
 
@@ -248,7 +250,7 @@ __device__ __forceinline__ void select_body(const TE *__restrict__ x, int64_t ld
 #pragma unroll
     for (int i = 0; i < PER; ++i)
         uk[i] = uk[i] == 0u ? 0u : uk[i] - mn + 1u;
-    bool published1 = false;
+    bool published1 = false, published2 = false;
 
     // 2. radix passes from the top bit of umax, up to 11 bits each.  After a
     // pass, if few keys share the crossing digit they are gathered and ranked
@@ -375,15 +377,26 @@ __device__ __forceinline__ void select_body(const TE *__restrict__ x, int64_t ld
                 if (above + 1u == krem) {
                     res[3] = cand[tid].x;
                     res[4] = tie_upto;
+                    res[5] = cand[tid].y; // the last kept slice
                 }
             }
             __syncthreads();
             prefix = res[3];
             krem = res[4];
+            if constexpr (PUB) {
+                // the threshold is out before the compaction; the offsets follow (sig3)
+                if (tid == 0)
+                    pub_store64(pub.sig2, sig2_pack(prefix, (int)res[5]));
+                published2 = true;
+            }
             break;
         }
     }
     // (L == 0: every key is zero; prefix 0 and krem = k ties)
+    if constexpr (PUB) {
+        if (published2 && !pub.offs)
+            return; // the threshold is out and no kept list is asked for
+    }
 
     // 3. order-preserving compaction.  Kept: u > prefix, or u == prefix among
     // the first krem such slices.  Output position of a slice = slices kept
@@ -444,23 +457,27 @@ __device__ __forceinline__ void select_body(const TE *__restrict__ x, int64_t ld
             const uint32_t below = bq >= 32 ? kmask : (kmask & ((1u << bq) - 1u));
             pub_store(pub.offs + p, pos + (uint32_t)__popc(below));
         };
-        if (j0 == 0 && K > 0)
+        if (pub.offs && j0 == 0 && K > 0)
             put_off(0);
-        if (pub.nsplit >= 1 && K > pub.R0 && j0 + PER > pub.R0 && j0 < K) {
+        if (pub.offs && pub.nsplit >= 1 && K > pub.R0 && j0 + PER > pub.R0 && j0 < K) {
             const int a = j0 > pub.R0 ? (j0 - pub.R0 + pub.R1 - 1) / pub.R1 : 0; // first p - 1 with start >= j0
             const int b = (min(j0 + PER, K) - 1 - pub.R0) / pub.R1;              // last p - 1 with start < j0 + PER
             for (int p = 1 + a; p <= 1 + b && p <= pub.nsplit; ++p)
                 put_off(p);
         }
-        if (tid == 0) { // first split starting at K: 1 + ceil((K - R0) / R1)
+        if (pub.offs && tid == 0) { // first split starting at K: 1 + ceil((K - R0) / R1)
             const int pend = K > pub.R0 ? 1 + (K - pub.R0 + pub.R1 - 1) / pub.R1 : 1;
             for (int p = pend; p <= pub.nsplit; ++p)
                 pub_store(pub.offs + p, (uint32_t)k);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (tid == 0)
-            pub_store64(pub.sig2, sig2_pack(prefix, jt_s));
+        if (tid == 0) {
+            if (!published2)
+                pub_store64(pub.sig2, sig2_pack(prefix, jt_s));
+            if (pub.offs)
+                pub_store64(pub.sig3, 1ull);
+        }
     } else {
         extern __shared__ int32_t outl[]; // k entries: the kept list before it is written out
         while (kmask) {

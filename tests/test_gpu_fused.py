@@ -40,6 +40,21 @@ def test_decode_down_proj_full_size(r):
     run_fused(W.linear_decode(), r)
 
 
+@pytest.mark.parametrize("r", [0.25, 0.5, 0.75, 1.0])
+def test_decode_down_proj_without_index_list(r):
+    # the benchmark's call: no kept list asked for (the threshold goes out before the selector's
+    # compaction, which then does not run)
+    cs = W.linear_decode()
+    x, wt, c = dev_padded(cs.x), dev_padded(cs.wt), dev(cs.c)
+    print(f"[case] fused {cs.name} r={r} no index list", flush=True)
+    y, idx = rmm.select_linear(x, c, r, wt, want_idx=False)
+    torch.cuda.synchronize()
+    assert idx is None
+    yr = oracle.linear(cs.x, cs.wt, oracle.select(cs.x, cs.c, 1, r), 1)
+    err = rel_l2(y.cpu().numpy(), yr)
+    assert err <= TOL, f"r={r}: rel-L2 {err:.3e}"
+
+
 @pytest.mark.parametrize("seed", [1, 2, 3, 4])
 def test_decode_down_proj_other_seeds(seed):
     run_fused(W.linear_decode(seed=seed), 0.5)
