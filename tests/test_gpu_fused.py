@@ -20,7 +20,9 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
 
-def run_fused(cs, r, want_idx=True):
+def run_fused(cs, r, want_idx=True, both=False):
+    """The fused step against the oracle; both=True also runs it without the index list (the
+    selector then publishes the threshold and skips its compaction) and checks that y is the same."""
     assert cs.T == 1
     x, wt, c = dev_padded(cs.x), dev_padded(cs.wt), dev(cs.c)
     print(f"[case] fused {cs.name} r={r}", flush=True)
@@ -32,6 +34,10 @@ def run_fused(cs, r, want_idx=True):
     yr = oracle.linear(cs.x, cs.wt, idx_ref, 1)
     err = rel_l2(y.cpu().numpy(), yr)
     assert err <= TOL, f"{cs.name} r={r}: rel-L2 {err:.3e}"
+    if both:
+        y2, _ = rmm.select_linear(x, c, r, wt, want_idx=not want_idx)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2), f"{cs.name} r={r}: y depends on whether the index list is asked for"
     return y, idx
 
 
@@ -85,7 +91,7 @@ def test_tiny_fp32():
 def test_ragged_and_edge_shapes(K, M, dtype):
     cs = W.linear_random(1, K, M, 1, dtype, seed=K + M)
     for r in (0.3, 1.0, 1.0 / K):
-        run_fused(cs, r)
+        run_fused(cs, r, both=True)
 
 
 def test_ties_lowest_indices_win():
@@ -95,14 +101,14 @@ def test_ties_lowest_indices_win():
     cs.x[:] = W.f32_to_bf16_bits(rng.integers(-3, 4, size=cs.x.shape).astype(np.float32))
     cs.c[:] = 1.0
     for r in (0.25, 0.5, 0.8):
-        run_fused(cs, r)
+        run_fused(cs, r, both=True)
 
 
 def test_all_equal_scores():
     cs = W.linear_random(1, 5000, 1000, 1, "bf16", seed=10)
     cs.x[:] = W.f32_to_bf16_bits(np.ones(cs.x.shape, np.float32))
     cs.c[:] = 2.0
-    _, idx = run_fused(cs, 0.5)
+    _, idx = run_fused(cs, 0.5, both=True)
     assert np.array_equal(idx.cpu().numpy()[0], np.arange(2500))
 
 
