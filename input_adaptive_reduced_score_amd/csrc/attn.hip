@@ -1252,6 +1252,239 @@ __global__ __launch_bounds__(PV_THREADS) void attn_fused_kernel(
                 pstage, pcount, part, L);
 }
 
+// ------------------------------------------------------------------ PV after the threshold (large launches)
+// When the fused launch holds more workgroups than the device keeps resident,
+// its PV workgroups would only start as key workgroups retire and run two to a
+// CU.  Then the key role runs alone, and this kernel does PV once every
+// group's threshold is out: one workgroup per (chunk of P positions, group),
+// every position decided in one pass from its stored histogram bin (above bin
+// d: kept; bin d: its rank key from the logits against the published one), the
+// kept rows staged and streamed as in the fused kernel, PVU rows in flight per
+// lane (fewer registers, more resident workgroups).
+template <int GS, int PVU>
+__global__ __launch_bounds__(PV_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void attn_pv_split_kernel(AttnShape s, KvMap m, int Sp, int nqk_all, int P,
+                                                                   const uint16_t *__restrict__ v,
+                                                                   const float *__restrict__ logit,
+                                                                   const float2 *__restrict__ pstat,
+                                                                   const float *__restrict__ vn,
+                                                                   const uint16_t *__restrict__ bins,
+                                                                   const uint64_t *__restrict__ sig,
+                                                                   int32_t *__restrict__ pstage,
+                                                                   uint32_t *__restrict__ pcount,
+                                                                   float *__restrict__ part)
+{
+    __shared__ LseLds LL;
+    __shared__ int64_t rows[PV_STAGE];
+    __shared__ union {
+        float pr[GS][PV_STAGE];
+        float red[PV_WAVES][GS][D];
+    } U;
+    __shared__ uint32_t wk[PV_WAVES];
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    const int grp = blockIdx.y, c = blockIdx.x, npv = gridDim.x;
+    const int b = grp / s.Hsel, h0 = (grp % s.Hsel) * s.GS, g = h0 / s.G;
+    const int Sb = seq_len(s, m, b);
+    const int p0 = c * P, p1 = min(Sb, p0 + P);
+    const float *Lg = logit + ((int64_t)b * s.Hq + h0) * Sp;
+    const int Spb = (Sp + BIN_ROW - 1) / BIN_ROW * BIN_ROW;
+    const uint16_t *Bg = bins + (int64_t)grp * Spb;
+    const double sc = (double)s.scale;
+    const int quarter = lane >> 4, dl = lane & 15, slot = w * 4 + quarter;
+    constexpr int NSLOT = PV_WAVES * 4;
+    float acc[GS][8];
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[hh][e] = 0.0f;
+    bool poison = false;
+    uint32_t kept_n = 0;
+
+    auto stream = [&](int nk) {
+        for (int r0 = slot; r0 < nk; r0 += NSLOT * PVU) {
+            uint4 uu[PVU];
+#pragma unroll
+            for (int qq = 0; qq < PVU; ++qq) {
+                const int r = r0 + NSLOT * qq;
+                if (r < nk)
+                    uu[qq] = *reinterpret_cast<const uint4 *>(v + rows[r] * D + dl * 8);
+            }
+#pragma unroll
+            for (int qq = 0; qq < PVU; ++qq) {
+                const int r = r0 + NSLOT * qq;
+                if (r < nk) {
+                    float vv[8];
+                    Vec16<uint16_t>::unpack(uu[qq], vv);
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh) {
+                        const float pv = U.pr[hh][r];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[hh][e] = fmaf(pv, vv[e], acc[hh][e]);
+                    }
+                }
+            }
+        }
+    };
+    // exclusive slot of this thread's n; returns the block total.  A barrier must separate two calls.
+    auto pass_slots = [&](uint32_t n, uint32_t &excl) -> uint32_t {
+        const uint32_t ki = wave_incl_sum(n);
+        if (lane == WAVE - 1)
+            wk[w] = ki;
+        __syncthreads();
+        uint32_t before = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < PV_WAVES; ++i) {
+            before += i < w ? wk[i] : 0u;
+            tot += wk[i];
+        }
+        excl = before + ki - n;
+        return tot;
+    };
+
+    if (p0 < p1) { // (uniform) chunks past the sequence's end write zeros
+        const uint64_t *sw = sig + (int64_t)grp * SIG_WORDS;
+        const uint64_t w1 = sw[SIG_D], w2 = sw[SIG_THR];
+        const bool all = (w1 & 2ull) != 0ull;
+        poison = !(w1 & 1ull) || (!all && !(w2 & 1ull));
+        const uint32_t d = (uint32_t)(w1 >> 40);
+        const uint64_t thr = all ? 0ull : w2 >> 1;
+        const int nqk = (Sb + ATTN_QK_CHUNK - 1) / ATTN_QK_CHUNK;
+        float2 pst[GS];
+        double lsed[GS];
+        float lsef[GS];
+        ld_stats<GS>(s, b, h0, nqk_all, nqk, pstat, pst);
+        // this thread's two positions of a pass: bins, logits, value norms and row,
+        // the next pass's loaded while this one is decided and streamed
+        int j0 = 0;
+        uint32_t bw = 0;
+        float2 lg[GS], nv = make_float2(1.0f, 1.0f);
+        int64_t vrow = 0;
+        auto load = [&](int sb, int &jj, uint32_t &bb, float2 (&ll)[GS], float2 &nn, int64_t &vr) {
+            jj = sb + 2 * tid;
+            bb = 0;
+            vr = 0;
+            nn = make_float2(1.0f, 1.0f);
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+                ll[hh] = make_float2(0.0f, 0.0f);
+            if (jj < p1) {
+                vr = kv_row(s, m, b, g, jj);
+                bb = *reinterpret_cast<const uint32_t *>(Bg + jj);
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    ll[hh] = *reinterpret_cast<const float2 *>(Lg + (int64_t)hh * Sp + jj);
+                if (vn)
+                    nn = *reinterpret_cast<const float2 *>(vn + vr);
+            }
+        };
+        load(p0, j0, bw, lg, nv, vrow);
+        group_lse<GS>(s, b, h0, nqk_all, nqk, pstat, pst, LL, lsed);
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh)
+            lsef[hh] = (float)lsed[hh];
+        if (!poison) {
+            uint32_t nst = 0, off = 0;
+            for (int sb = p0; sb < p1; sb += PV_PASS) {
+                int j0n = 0;
+                uint32_t bwn = 0;
+                float2 lgn[GS], nvn = make_float2(1.0f, 1.0f);
+                int64_t vrown = 0;
+                if (sb + PV_PASS < p1)
+                    load(sb + PV_PASS, j0n, bwn, lgn, nvn, vrown);
+                const bool va = j0 < p1, vb = j0 + 1 < p1;
+                const uint32_t ba = bw & 0xffffu, bb = bw >> 16;
+                bool ka = va && ba > d, kb = vb && bb > d;
+                if (va && ba == d) {
+                    float ax[GS];
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh)
+                        ax[hh] = lg[hh].x;
+                    ka = rank_key(pos_key(pos_score<GS>(ax, lsed, sc, vn != nullptr, nv.x)), d, j0) >= thr;
+                }
+                if (vb && bb == d) {
+                    float ay[GS];
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh)
+                        ay[hh] = lg[hh].y;
+                    kb = rank_key(pos_key(pos_score<GS>(ay, lsed, sc, vn != nullptr, nv.y)), d, j0 + 1) >= thr;
+                }
+                uint32_t ex;
+                const uint32_t tot = pass_slots((uint32_t)ka + (uint32_t)kb, ex);
+                uint32_t so = nst + ex;
+                if (ka) {
+                    rows[so] = vrow;
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh)
+                        U.pr[hh][so] = expf(fmaf(s.scale, lg[hh].x, -lsef[hh]));
+                    ++so;
+                }
+                if (kb) {
+                    rows[so] = vrow + 1;
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh)
+                        U.pr[hh][so] = expf(fmaf(s.scale, lg[hh].y, -lsef[hh]));
+                }
+                if (pstage) {
+                    int32_t *dst = pstage + (int64_t)grp * Sp + p0 + off + ex;
+                    if (ka)
+                        *dst++ = j0;
+                    if (kb)
+                        *dst = j0 + 1;
+                }
+                nst += tot;
+                off += tot;
+                kept_n += tot;
+                __syncthreads();
+                // (uniform) a further pass could overflow the stage, or this is the last pass
+                if (nst > (uint32_t)(PV_STAGE - PV_PASS) || sb + PV_PASS >= p1) {
+                    stream((int)nst);
+                    nst = 0;
+                }
+                __syncthreads();
+                j0 = j0n;
+                bw = bwn;
+                vrow = vrown;
+                nv = nvn;
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    lg[hh] = lgn[hh];
+            }
+        }
+        if (pcount && tid == 0)
+            pcount[(int64_t)grp * npv + c] = poison ? 0u : kept_n;
+    }
+
+    // reduce the four quarters of each wave, then the waves (fixed order)
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = acc[hh][e];
+            x += __shfl_xor(x, 16, WAVE);
+            x += __shfl_xor(x, 32, WAVE);
+            acc[hh][e] = x;
+        }
+    __syncthreads(); // (the partials reuse the probability staging)
+    if ((lane >> 4) == 0) {
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                U.red[w][hh][(lane & 15) * 8 + e] = acc[hh][e];
+    }
+    __syncthreads();
+    float *mine = part + ((int64_t)grp * npv + c) * GS * D;
+    for (int i = tid; i < GS * D; i += PV_THREADS) {
+        const int hh = i / D, dd = i % D;
+        float x = U.red[0][hh][dd];
+#pragma unroll
+        for (int ww = 1; ww < PV_WAVES; ++ww)
+            x += U.red[ww][hh][dd];
+        mine[i] = poison ? __builtin_nanf("") : x;
+    }
+}
+
 // ------------------------------------------------------------------ per-query-head PV over the union of rows
 // Per-query-head selection with G > 1: after the key launch has published every
 // head's threshold, one workgroup per (chunk of P positions, KV head) decides
@@ -1610,6 +1843,26 @@ static int key_chunks_per_wg(int64_t S)
     return n < 1 ? 1 : n > 4 ? 4 : (int)n;
 }
 
+// Workgroups of the fused kernel the current device holds at once (occupancy
+// times compute units), per device.
+template <int GS> static int64_t fused_resident()
+{
+    static int64_t cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    if (cached[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fused_kernel<GS>, PV_THREADS, 0) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cached[dev] = (int64_t)per_cu * cus;
+    }
+    return cached[dev];
+}
+constexpr int ATTN_SPLIT_PVU = 8; // V rows in flight per lane in the split PV kernel
+
 template <int GS>
 static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q, const uint16_t *kt,
                            const uint16_t *v, const float *kn, const float *vn, float *out, int32_t *dim_idx, int32_t *pos_idx, float *lse,
@@ -1625,9 +1878,20 @@ static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q
     const int nkc = (int)((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK);
     const int nsub = key_chunks_per_wg(s.S);
     const int nkw = (nkc + nsub - 1) / nsub;
-    attn_fused_kernel<GS><<<(unsigned)((int64_t)(nkw + npv) * G), PV_THREADS, 0, st>>>(
-        s, m, Sp, nqk, nsub, nkw, P, npv, v, ws.logit, ws.pstat, lse, vn, ws.bins, ws.hist, ws.sig,
-        pos_idx ? ws.pstage : nullptr, pos_idx ? ws.pcount : nullptr, ws.pvpart);
+    int32_t *pst = pos_idx ? ws.pstage : nullptr;
+    uint32_t *pcn = pos_idx ? ws.pcount : nullptr;
+    if ((int64_t)(nkw + npv) * G <= fused_resident<GS>()) {
+        attn_fused_kernel<GS><<<(unsigned)((int64_t)(nkw + npv) * G), PV_THREADS, 0, st>>>(
+            s, m, Sp, nqk, nsub, nkw, P, npv, v, ws.logit, ws.pstat, lse, vn, ws.bins, ws.hist, ws.sig, pst, pcn,
+            ws.pvpart);
+    } else {
+        // more workgroups than stay resident: the key role alone, then PV with the thresholds out
+        attn_fused_kernel<GS><<<(unsigned)((int64_t)nkw * G), PV_THREADS, 0, st>>>(
+            s, m, Sp, nqk, nsub, nkw, P, npv, v, ws.logit, ws.pstat, lse, vn, ws.bins, ws.hist, ws.sig, pst, pcn,
+            ws.pvpart);
+        attn_pv_split_kernel<GS, ATTN_SPLIT_PVU><<<dim3(npv, G), PV_THREADS, 0, st>>>(
+            s, m, Sp, nqk, P, v, ws.logit, ws.pstat, vn, ws.bins, ws.sig, pst, pcn, ws.pvpart);
+    }
     attn_pv_reduce_kernel<GS><<<G * (GS * D / WAVE), PVR_WAVES * WAVE, 0, st>>>(s, npv, ws.pvpart, out);
     if (pos_idx)
         attn_pos_kernel<<<dim3(npv, G), 256, 0, st>>>(s, m, Sp, P, ws.pcount, ws.pstage, pos_idx);
