@@ -86,8 +86,15 @@ def test_value_norm_weighted_paged():
 
 @pytest.mark.parametrize("mode", [0, 1])
 def test_long_mixed_batch_gqa(mode):
+    # (mode 0: more workgroups than stay resident, so the key role runs alone and the split PV kernel follows)
     pc = W.attn_paged([40000, 9000, 1, 16384], page=256, Hq=32, Hkv=8, seed=6, n_hot=16)
     check_paged(pc, 0.25, 0.25, mode)
+
+
+def test_long_mixed_batch_value_norms():
+    # the split PV kernel with the value-norm weighted score
+    pc = W.attn_paged([40000, 9000, 1, 16384], page=256, Hq=32, Hkv=8, seed=7, n_hot=16)
+    check_paged(pc, 0.5, 0.25, 0, use_vn=True)
 
 
 def test_one_page_per_sequence_equals_contiguous_cache():
