@@ -141,7 +141,7 @@ __device__ __forceinline__ void wave_select128(uint32_t key0, uint32_t key1, int
 // the fused kernel writes them with agent-scope stores and atomics, which every
 // XCD sees once they complete.
 constexpr int SIG_WORDS = 32;
-constexpr int SIG_KCNT = 0, SIG_D = 16, SIG_THR = 17;
+constexpr int SIG_KCNT = 0, SIG_D = 16, SIG_THR = 17, SIG_LSE = 18; // SIG_LSE: GS doubles (split launches)
 constexpr int ATTN_SPIN = 1 << 20; // polls (about a second) before a wait gives up
 
 // ------------------------------------------------------------------ qk
@@ -637,13 +637,15 @@ __device__ __forceinline__ uint32_t bin_of(const uint4 &w, int e)
     return (e & 1) ? wd >> 16 : wd & 0xffffu;
 }
 
-template <int GS>
+template <int GS, int NT>
 __device__ void publish_select(const AttnShape &s, const KvMap &m, int Sp, int Spb, int grp,
                                const float *__restrict__ logit, const double (&lsed)[GS],
                                const float *__restrict__ vn, const uint16_t *bins, const uint32_t *hg,
                                uint64_t *sg, KeyLds &L)
 {
-    constexpr int T = PV_THREADS;
+    constexpr int T = NT;                    // threads of the workgroup
+    constexpr int BPT = ATTN_HIST_BINS / NT; // histogram bins per thread
+    static_assert(BPT % 4 == 0 && BPT * NT == ATTN_HIST_BINS, "whole 16-byte words of bins per thread");
     const int tid = threadIdx.x, lane = tid & (WAVE - 1);
     const int b = grp / s.Hsel, h0 = (grp % s.Hsel) * s.GS, g = h0 / s.G;
     const int Sb = seq_len(s, m, b), ksb = seq_keep(s, m, Sb);
@@ -659,20 +661,20 @@ __device__ void publish_select(const AttnShape &s, const KvMap &m, int Sp, int S
         const float vv = vn ? vn[kv_row(s, m, b, g, p)] : 1.0f;
         return rank_key(pos_key(pos_score<GS>(av, lsed, sc, vn != nullptr, vv)), d, p);
     };
-    // threshold bin: thread t holds bins 8191-32t down to 8160-32t
-    uint32_t hc[32];
+    // threshold bin: thread t holds bins 8191-BPT*t down to 8192-BPT*(t+1)
+    uint32_t hc[BPT];
     {
-        const uint4 *h4 = reinterpret_cast<const uint4 *>(hg + ATTN_HIST_BINS - 32 * (tid + 1));
-        uint4 q[8];
+        const uint4 *h4 = reinterpret_cast<const uint4 *>(hg + ATTN_HIST_BINS - BPT * (tid + 1));
+        uint4 q[BPT / 4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < BPT / 4; ++i)
             q[i] = h4[i];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            hc[31 - 4 * i] = q[i].x;
-            hc[30 - 4 * i] = q[i].y;
-            hc[29 - 4 * i] = q[i].z;
-            hc[28 - 4 * i] = q[i].w;
+        for (int i = 0; i < BPT / 4; ++i) {
+            hc[BPT - 1 - 4 * i] = q[i].x;
+            hc[BPT - 2 - 4 * i] = q[i].y;
+            hc[BPT - 3 - 4 * i] = q[i].z;
+            hc[BPT - 4 - 4 * i] = q[i].w;
         }
     }
     if (tid == 0) {
@@ -683,14 +685,14 @@ __device__ void publish_select(const AttnShape &s, const KvMap &m, int Sp, int S
     }
     uint32_t tot = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
+    for (int i = 0; i < BPT; ++i)
         tot += hc[i];
     const uint32_t incl = block_incl_scan(tot, L.rad.tmp); // (barriers inside)
     {
-        const uint32_t top = ATTN_HIST_BINS - 1 - 32 * tid, want = (uint32_t)ksb;
+        const uint32_t top = ATTN_HIST_BINS - 1 - BPT * tid, want = (uint32_t)ksb;
         uint32_t run = incl - tot;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
+        for (int i = 0; i < BPT; ++i) {
             if (run < want && want <= run + hc[i]) {
                 L.bres[0] = top - i;
                 L.bres[1] = want - run;
@@ -776,7 +778,7 @@ __device__ void publish_select(const AttnShape &s, const KvMap &m, int Sp, int S
 
 template <int GS>
 __device__ void key_role(const AttnShape &s, const KvMap &m, int Sp, int Spb, int nqk_all, int nsub, int nkw, int grp,
-                         int kx, const float *__restrict__ logit, const float2 *__restrict__ pstat,
+                         int kx, bool resolve, const float *__restrict__ logit, const float2 *__restrict__ pstat,
                          float *__restrict__ lse_out, const float *__restrict__ vn, uint16_t *bins,
                          uint32_t *__restrict__ hist, uint64_t *sg, KeyLds &L, LseLds &LL)
 {
@@ -869,7 +871,15 @@ __device__ void key_role(const AttnShape &s, const KvMap &m, int Sp, int Spb, in
         return;
     if (c0 * ATTN_KEY_CHUNK >= Sb) // (uniform) a workgroup past the end merges lse only when it is the last
         group_lse<GS>(s, b, h0, nqk_all, nqk, pstat, pst, LL, lse);
-    publish_select<GS>(s, m, Sp, Spb, grp, logit, lse, vn, bins, hg, sg, L);
+    if (!resolve) {
+        // the threshold is resolved by attn_select_kernel after this launch: it takes the lse from here
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh)
+            if (tid == hh)
+                pub_store64(sg + SIG_LSE + hh, (uint64_t)__double_as_longlong(lse[hh]));
+        return;
+    }
+    publish_select<GS, PV_THREADS>(s, m, Sp, Spb, grp, logit, lse, vn, bins, hg, sg, L);
 }
 
 // ------------------------------------------------------------------ pv role
@@ -1234,7 +1244,8 @@ __global__ __launch_bounds__(PV_THREADS) void attn_fused_kernel(
     AttnShape s, KvMap m, int Sp, int nqk_all, int nsub, int nkw, int P, int npv, const uint16_t *__restrict__ v,
     const float *__restrict__ logit, const float2 *__restrict__ pstat, float *__restrict__ lse_out,
     const float *__restrict__ vn, uint16_t *__restrict__ bins, uint32_t *__restrict__ hist,
-    uint64_t *__restrict__ sig, int32_t *__restrict__ pstage, uint32_t *__restrict__ pcount, float *__restrict__ part)
+    uint64_t *__restrict__ sig, int32_t *__restrict__ pstage, uint32_t *__restrict__ pcount, float *__restrict__ part,
+    int resolve)
 {
     __shared__ FusedLds<GS> L;
     const int G = (int)(s.B * s.Hsel);
@@ -1242,7 +1253,8 @@ __global__ __launch_bounds__(PV_THREADS) void attn_fused_kernel(
     int bid = (int)blockIdx.x;
     if (bid < nkw * G) {
         const int grp = bid / nkw;
-        key_role<GS>(s, m, Sp, Spb, nqk_all, nsub, nkw, grp, bid % nkw, logit, pstat, lse_out, vn, bins, hist,
+        key_role<GS>(s, m, Sp, Spb, nqk_all, nsub, nkw, grp, bid % nkw, resolve != 0, logit, pstat, lse_out, vn, bins,
+                     hist,
                      sig + (int64_t)grp * SIG_WORDS, L.key, L.ls);
         return;
     }
@@ -1250,6 +1262,33 @@ __global__ __launch_bounds__(PV_THREADS) void attn_fused_kernel(
     const int grp = bid / npv;
     pv_role<GS>(s, m, Sp, nqk_all, P, npv, grp, bid % npv, v, logit, pstat, vn, sig + (int64_t)grp * SIG_WORDS,
                 pstage, pcount, part, L);
+}
+
+// ------------------------------------------------------------------ threshold of split launches
+// When the key role runs as a launch of its own (see attn_pv_split_kernel),
+// one workgroup of SELK_THREADS per group resolves the group's threshold after
+// it, exactly as the key role's last workgroup does in the fused launch
+// (publish_select, with the lse that workgroup left in the signal words), with
+// four times the threads: the stored bins of up to 128K positions are gathered
+// in one round trip.
+constexpr int SELK_THREADS = 1024;
+template <int GS>
+__global__ __launch_bounds__(SELK_THREADS) void attn_select_kernel(AttnShape s, KvMap m, int Sp,
+                                                                   const float *__restrict__ logit,
+                                                                   const float *__restrict__ vn,
+                                                                   const uint16_t *__restrict__ bins,
+                                                                   const uint32_t *__restrict__ hist, uint64_t *sig)
+{
+    __shared__ KeyLds L;
+    const int grp = blockIdx.x;
+    const int Spb = (Sp + BIN_ROW - 1) / BIN_ROW * BIN_ROW;
+    uint64_t *sg = sig + (int64_t)grp * SIG_WORDS;
+    double lse[GS];
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+        lse[hh] = __longlong_as_double((long long)pub_load64(sg + SIG_LSE + hh));
+    publish_select<GS, SELK_THREADS>(s, m, Sp, Spb, grp, logit, lse, vn, bins, hist + (int64_t)grp * ATTN_HIST_BINS,
+                                     sg, L);
 }
 
 // ------------------------------------------------------------------ PV after the threshold (large launches)
@@ -1883,12 +1922,13 @@ static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q
     if ((int64_t)(nkw + npv) * G <= fused_resident<GS>()) {
         attn_fused_kernel<GS><<<(unsigned)((int64_t)(nkw + npv) * G), PV_THREADS, 0, st>>>(
             s, m, Sp, nqk, nsub, nkw, P, npv, v, ws.logit, ws.pstat, lse, vn, ws.bins, ws.hist, ws.sig, pst, pcn,
-            ws.pvpart);
+            ws.pvpart, 1);
     } else {
-        // more workgroups than stay resident: the key role alone, then PV with the thresholds out
+        // more workgroups than stay resident: the key role alone, the thresholds, then PV
         attn_fused_kernel<GS><<<(unsigned)((int64_t)nkw * G), PV_THREADS, 0, st>>>(
             s, m, Sp, nqk, nsub, nkw, P, npv, v, ws.logit, ws.pstat, lse, vn, ws.bins, ws.hist, ws.sig, pst, pcn,
-            ws.pvpart);
+            ws.pvpart, 0);
+        attn_select_kernel<GS><<<G, SELK_THREADS, 0, st>>>(s, m, Sp, ws.logit, vn, ws.bins, ws.hist, ws.sig);
         attn_pv_split_kernel<GS, ATTN_SPLIT_PVU><<<dim3(npv, G), PV_THREADS, 0, st>>>(
             s, m, Sp, nqk, P, v, ws.logit, ws.pstat, vn, ws.bins, ws.sig, pst, pcn, ws.pvpart);
     }
@@ -1920,7 +1960,7 @@ static hipError_t attn_run_union(const AttnShape &s, const KvMap &m, const uint1
     const int nkw = (nkc + nsub - 1) / nsub;
     attn_fused_kernel<1><<<(unsigned)((int64_t)nkw * Gsel), PV_THREADS, 0, st>>>(
         s, m, Sp, nqk, nsub, nkw, P, npv, v, ws.logit, ws.pstat, lse, vn, ws.bins, ws.hist, ws.sig, nullptr, nullptr,
-        ws.pvpart);
+        ws.pvpart, 1);
     attn_pv_union_kernel<G><<<dim3(npv, Gkv), PV_THREADS, 0, st>>>(s, m, Sp, nqk, P, v, ws.logit, ws.pstat, vn,
                                                                    ws.sig, pos_idx ? ws.pstage : nullptr,
                                                                    pos_idx ? ws.pcount : nullptr, ws.pvpart);
