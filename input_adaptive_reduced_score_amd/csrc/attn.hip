@@ -616,12 +616,12 @@ __device__ uint64_t radix_select_u64(EachKey each_key, uint32_t krem, RadixLds &
 // holds an older copy of them.
 constexpr int SEL_UB = 16;  // 16-byte words of bins per thread per pass
 constexpr int BIN_ROW = 64; // positions a group's bins row is padded to (128 bytes)
-struct KeyLds {
+template <int CAP> struct KeyLdsT {
     union {
         uint32_t lh[ATTN_HIST_BINS];
         struct {
-            uint64_t key[SEL_CAP];
-            int32_t pos[SEL_CAP];
+            uint64_t key[CAP];
+            int32_t pos[CAP];
         } c;
     };
     RadixLds rad;
@@ -629,6 +629,7 @@ struct KeyLds {
     uint32_t bres[3];
     uint32_t last;
 };
+using KeyLds = KeyLdsT<SEL_CAP>;
 static_assert(ATTN_HIST_BINS == 32 * PV_THREADS, "32 histogram bins per thread");
 
 __device__ __forceinline__ uint32_t bin_of(const uint4 &w, int e)
@@ -637,11 +638,11 @@ __device__ __forceinline__ uint32_t bin_of(const uint4 &w, int e)
     return (e & 1) ? wd >> 16 : wd & 0xffffu;
 }
 
-template <int GS, int NT>
+template <int GS, int NT, int CAP>
 __device__ void publish_select(const AttnShape &s, const KvMap &m, int Sp, int Spb, int grp,
                                const float *__restrict__ logit, const double (&lsed)[GS],
                                const float *__restrict__ vn, const uint16_t *bins, const uint32_t *hg,
-                               uint64_t *sg, KeyLds &L)
+                               uint64_t *sg, KeyLdsT<CAP> &L)
 {
     constexpr int T = NT;                    // threads of the workgroup
     constexpr int BPT = ATTN_HIST_BINS / NT; // histogram bins per thread
@@ -709,7 +710,7 @@ __device__ void publish_select(const AttnShape &s, const KvMap &m, int Sp, int S
         return; // all of bin d is kept
 
     uint64_t thr;
-    if (nbin <= (uint32_t)SEL_CAP) {
+    if (nbin <= (uint32_t)CAP) {
         // gather bin d's positions: per-lane bit masks of 4 words, one slot reservation per wave
         for (int base = 0; base < n8; base += SEL_UB * T) {
             uint4 u[SEL_UB];
@@ -739,16 +740,37 @@ __device__ void publish_select(const AttnShape &s, const KvMap &m, int Sp, int S
                 while (cm) {
                     const int bit = __builtin_ctz(cm);
                     cm &= cm - 1u;
-                    if (slot < (uint32_t)SEL_CAP)
+                    if (slot < (uint32_t)CAP)
                         L.c.pos[slot] = 8 * (base + tid + (j0 + (bit >> 3)) * T) + (bit & 7);
                     ++slot;
                 }
             }
         }
         __syncthreads();
-        const int nc = (int)min(L.ncand, (uint32_t)SEL_CAP);
-        for (int i = tid; i < nc; i += T)
-            L.c.key[i] = rank_of(L.c.pos[i], d);
+        const int nc = (int)min(L.ncand, (uint32_t)CAP);
+        // the candidates' rank keys, the logits of RB candidates per thread in flight together
+        // (one at a time in the fused launch, whose registers the key role shares with PV)
+        constexpr int RB = NT >= 1024 ? 4 : 1;
+        for (int i0 = tid; i0 < nc; i0 += T * RB) {
+            int pp[RB];
+            float av[RB][GS], vv[RB];
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+                const int i = i0 + u * T;
+                pp[u] = i < nc ? L.c.pos[i] : -1;
+                vv[u] = 1.0f;
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh)
+                    av[u][hh] = pp[u] >= 0 ? Lg[(int64_t)hh * Sp + pp[u]] : 0.0f;
+                if (vn && pp[u] >= 0)
+                    vv[u] = vn[kv_row(s, m, b, g, pp[u])];
+            }
+#pragma unroll
+            for (int u = 0; u < RB; ++u)
+                if (pp[u] >= 0)
+                    L.c.key[i0 + u * T] =
+                        rank_key(pos_key(pos_score<GS>(av[u], lsed, sc, vn != nullptr, vv[u])), d, pp[u]);
+        }
         __syncthreads();
         thr = radix_select_u64(
             [&](auto f) {
@@ -879,7 +901,7 @@ __device__ void key_role(const AttnShape &s, const KvMap &m, int Sp, int Spb, in
                 pub_store64(sg + SIG_LSE + hh, (uint64_t)__double_as_longlong(lse[hh]));
         return;
     }
-    publish_select<GS, PV_THREADS>(s, m, Sp, Spb, grp, logit, lse, vn, bins, hg, sg, L);
+    publish_select<GS, PV_THREADS, SEL_CAP>(s, m, Sp, Spb, grp, logit, lse, vn, bins, hg, sg, L);
 }
 
 // ------------------------------------------------------------------ pv role
@@ -1269,9 +1291,10 @@ __global__ __launch_bounds__(PV_THREADS) void attn_fused_kernel(
 // one workgroup of SELK_THREADS per group resolves the group's threshold after
 // it, exactly as the key role's last workgroup does in the fused launch
 // (publish_select, with the lse that workgroup left in the signal words), with
-// four times the threads: the stored bins of up to 128K positions are gathered
-// in one round trip.
+// four times the threads and four times the candidates in LDS: the stored bins
+// of up to 128K positions are gathered in one round trip.
 constexpr int SELK_THREADS = 1024;
+constexpr int SELK_CAP = 8192; // threshold-bin candidates held in LDS (96 KB)
 template <int GS>
 __global__ __launch_bounds__(SELK_THREADS) void attn_select_kernel(AttnShape s, KvMap m, int Sp,
                                                                    const float *__restrict__ logit,
@@ -1279,7 +1302,7 @@ __global__ __launch_bounds__(SELK_THREADS) void attn_select_kernel(AttnShape s, 
                                                                    const uint16_t *__restrict__ bins,
                                                                    const uint32_t *__restrict__ hist, uint64_t *sig)
 {
-    __shared__ KeyLds L;
+    __shared__ KeyLdsT<SELK_CAP> L;
     const int grp = blockIdx.x;
     const int Spb = (Sp + BIN_ROW - 1) / BIN_ROW * BIN_ROW;
     uint64_t *sg = sig + (int64_t)grp * SIG_WORDS;
@@ -1287,8 +1310,8 @@ __global__ __launch_bounds__(SELK_THREADS) void attn_select_kernel(AttnShape s, 
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh)
         lse[hh] = __longlong_as_double((long long)pub_load64(sg + SIG_LSE + hh));
-    publish_select<GS, SELK_THREADS>(s, m, Sp, Spb, grp, logit, lse, vn, bins, hist + (int64_t)grp * ATTN_HIST_BINS,
-                                     sg, L);
+    publish_select<GS, SELK_THREADS, SELK_CAP>(s, m, Sp, Spb, grp, logit, lse, vn, bins,
+                                               hist + (int64_t)grp * ATTN_HIST_BINS, sg, L);
 }
 
 // ------------------------------------------------------------------ PV after the threshold (large launches)
