@@ -719,15 +719,27 @@ __device__ void publish_select(const AttnShape &s, const KvMap &m, int Sp, int S
                 const int i = base + tid + j * T;
                 u[j] = i < n8 ? B16[i] : make_uint4(0u, 0u, 0u, 0u);
             }
+            // the positions of bin d, two per 32-bit word at a time: a 16-bit half h of
+            // word ^ (d, d) is zero iff bit 15 of ((h & 0x7fff) + 0x7fff) | h is clear (no
+            // carry crosses the halves)
+            const uint32_t dd = d | d << 16;
+            auto eq2 = [&](uint32_t wd) -> uint32_t { // bit 0: low half is d, bit 1: high half
+                const uint32_t a = wd ^ dd;
+                const uint32_t nz = (((a & 0x7fff7fffu) + 0x7fff7fffu) | a) & 0x80008000u;
+                const uint32_t z = ~nz & 0x80008000u;
+                return (z >> 15 & 1u) | z >> 30;
+            };
 #pragma unroll
             for (int j0 = 0; j0 < SEL_UB; j0 += 4) {
                 uint32_t cm = 0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int i = base + tid + (j0 + j) * T;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        cm |= (uint32_t)((bin_of(u[j0 + j], e) == d) & (8 * i + e < Sb)) << (8 * j + e);
+                    const uint4 &wv = u[j0 + j];
+                    uint32_t m8 = eq2(wv.x) | eq2(wv.y) << 2 | eq2(wv.z) << 4 | eq2(wv.w) << 6;
+                    const int left = Sb - 8 * i; // positions of the word inside the sequence
+                    m8 &= left >= 8 ? 0xffu : left > 0 ? (1u << left) - 1u : 0u;
+                    cm |= m8 << (8 * j);
                 }
                 const uint32_t cl = (uint32_t)__popc(cm);
                 const uint32_t cincl = wave_incl_sum(cl);
