@@ -87,6 +87,7 @@ def test_tiny_fp32():
 @pytest.mark.parametrize("K,M,dtype", [
     (1, 8, "bf16"), (7, 520, "bf16"), (100, 64, "f32"), (1003, 4100, "bf16"), (4096, 1024, "f32"),
     (16385, 512, "bf16"), (32768, 4096, "bf16"), (14336, 16384, "bf16"), (3000, 8, "f32"),
+    (4096, 6144, "bf16"), (4096, 4096, "bf16"),  # the decode layer's QKV (12 column slices) and o_proj
 ])
 def test_ragged_and_edge_shapes(K, M, dtype):
     cs = W.linear_random(1, K, M, 1, dtype, seed=K + M)
