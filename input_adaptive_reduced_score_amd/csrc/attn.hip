@@ -25,6 +25,12 @@
 //          partial sums while the rank is resolved, then those in the bin at
 //          or above the threshold.
 //  reduce: the chunk partials are summed in a fixed order.
+// When the fused launch would hold more workgroups than the device keeps
+// resident (long or many sequences), the key role runs as a launch of its own,
+// attn_select_kernel resolves each group's threshold, and attn_pv_split_kernel
+// does PV with the thresholds known.  Per-query-head selection with several
+// query heads per KV head reads each KV row once for the union of the heads'
+// sets (attn_qk_kernel<G, true>, the key role per head, attn_pv_union_kernel).
 #include "device.h"
 #include "kernels.h"
 
