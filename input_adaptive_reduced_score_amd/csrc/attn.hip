@@ -1279,7 +1279,7 @@ __device__ void pv_role(const AttnShape &s, const KvMap &m, int Sp, int nqk_all,
 // before any PV workgroup and the waits end whatever the residency.  Each wait
 // is bounded all the same, and one that runs out poisons the group's output
 // with NaN.
-template <int GS>
+template <int GS, bool KEY_ONLY = false>
 __global__ __launch_bounds__(PV_THREADS) void attn_fused_kernel(
     AttnShape s, KvMap m, int Sp, int nqk_all, int nsub, int nkw, int P, int npv, const uint16_t *__restrict__ v,
     const float *__restrict__ logit, const float2 *__restrict__ pstat, float *__restrict__ lse_out,
@@ -1298,10 +1298,12 @@ __global__ __launch_bounds__(PV_THREADS) void attn_fused_kernel(
                      sig + (int64_t)grp * SIG_WORDS, L.key, L.ls);
         return;
     }
-    bid -= nkw * G;
-    const int grp = bid / npv;
-    pv_role<GS>(s, m, Sp, nqk_all, P, npv, grp, bid % npv, v, logit, pstat, vn, sig + (int64_t)grp * SIG_WORDS,
-                pstage, pcount, part, L);
+    if constexpr (!KEY_ONLY) { // (the key-only instance leaves out the PV role and its registers)
+        bid -= nkw * G;
+        const int grp = bid / npv;
+        pv_role<GS>(s, m, Sp, nqk_all, P, npv, grp, bid % npv, v, logit, pstat, vn, sig + (int64_t)grp * SIG_WORDS,
+                    pstage, pcount, part, L);
+    }
 }
 
 // ------------------------------------------------------------------ threshold of split launches
@@ -1966,7 +1968,7 @@ static hipError_t attn_run(const AttnShape &s, const KvMap &m, const uint16_t *q
             ws.pvpart, 1);
     } else {
         // more workgroups than stay resident: the key role alone, the thresholds, then PV
-        attn_fused_kernel<GS><<<(unsigned)((int64_t)nkw * G), PV_THREADS, 0, st>>>(
+        attn_fused_kernel<GS, true><<<(unsigned)((int64_t)nkw * G), PV_THREADS, 0, st>>>(
             s, m, Sp, nqk, nsub, nkw, P, npv, v, ws.logit, ws.pstat, lse, vn, ws.bins, ws.hist, ws.sig, pst, pcn,
             ws.pvpart, 0);
         attn_select_kernel<GS><<<G, SELK_THREADS, 0, st>>>(s, m, Sp, ws.logit, vn, ws.bins, ws.hist, ws.sig);
@@ -1999,7 +2001,7 @@ static hipError_t attn_run_union(const AttnShape &s, const KvMap &m, const uint1
     const int nkc = (int)((s.S + ATTN_KEY_CHUNK - 1) / ATTN_KEY_CHUNK);
     const int nsub = key_chunks_per_wg(s.S);
     const int nkw = (nkc + nsub - 1) / nsub;
-    attn_fused_kernel<1><<<(unsigned)((int64_t)nkw * Gsel), PV_THREADS, 0, st>>>(
+    attn_fused_kernel<1, true><<<(unsigned)((int64_t)nkw * Gsel), PV_THREADS, 0, st>>>(
         s, m, Sp, nqk, nsub, nkw, P, npv, v, ws.logit, ws.pstat, lse, vn, ws.bins, ws.hist, ws.sig, nullptr, nullptr,
         ws.pvpart, 1);
     attn_pv_union_kernel<G><<<dim3(npv, Gkv), PV_THREADS, 0, st>>>(s, m, Sp, nqk, P, v, ws.logit, ws.pstat, vn,
