@@ -40,19 +40,53 @@ constexpr int D = ATTN_D;
 constexpr int QK_U = 16;      // kept key rows in flight per lane
 constexpr int QK_THREADS = 256; // 4 waves split the kept dims of one chunk
 
+// Wave reductions on DPP moves (VALU only, no LDS round trip per step): the
+// row-scan pattern of wave_scan_dpp, whose last lane then holds the result in a
+// fixed order of operations, read back into every lane.  Doubles move as two
+// 32-bit halves.
+template <int CTRL, int RMASK> __device__ __forceinline__ float dpp_f32(float ident, float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(ident), __float_as_int(v), CTRL, RMASK, 0xf, false));
+}
+template <int CTRL, int RMASK> __device__ __forceinline__ double dpp_f64(double v) // identity 0.0
+{
+    const int64_t u = __double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, RMASK, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, RMASK, 0xf, false);
+    return __longlong_as_double((int64_t)((uint64_t)hi << 32 | lo));
+}
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v = fmaxf(v, __shfl_xor(v, off, WAVE));
-    return v;
+    v = fmaxf(v, dpp_f32<RMM_DPP_ROW_SHR(1), 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<RMM_DPP_ROW_SHR(2), 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<RMM_DPP_ROW_SHR(4), 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<RMM_DPP_ROW_SHR(8), 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<RMM_DPP_ROW_BCAST15, 0xa>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<RMM_DPP_ROW_BCAST31, 0xc>(-INFINITY, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), WAVE - 1));
 }
 template <typename F> __device__ __forceinline__ F wave_sum(F v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v += __shfl_xor(v, off, WAVE);
-    return v;
+    if constexpr (sizeof(F) == 8) {
+        v += dpp_f64<RMM_DPP_ROW_SHR(1), 0xf>(v);
+        v += dpp_f64<RMM_DPP_ROW_SHR(2), 0xf>(v);
+        v += dpp_f64<RMM_DPP_ROW_SHR(4), 0xf>(v);
+        v += dpp_f64<RMM_DPP_ROW_SHR(8), 0xf>(v);
+        v += dpp_f64<RMM_DPP_ROW_BCAST15, 0xa>(v);
+        v += dpp_f64<RMM_DPP_ROW_BCAST31, 0xc>(v);
+        const int64_t u = __double_as_longlong(v);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, WAVE - 1);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), WAVE - 1);
+        return __longlong_as_double((int64_t)((uint64_t)hi << 32 | lo));
+    } else {
+        v += dpp_f32<RMM_DPP_ROW_SHR(1), 0xf>(0.0f, v);
+        v += dpp_f32<RMM_DPP_ROW_SHR(2), 0xf>(0.0f, v);
+        v += dpp_f32<RMM_DPP_ROW_SHR(4), 0xf>(0.0f, v);
+        v += dpp_f32<RMM_DPP_ROW_SHR(8), 0xf>(0.0f, v);
+        v += dpp_f32<RMM_DPP_ROW_BCAST15, 0xa>(0.0f, v);
+        v += dpp_f32<RMM_DPP_ROW_BCAST31, 0xc>(0.0f, v);
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), WAVE - 1));
+    }
 }
 
 // ---- cache addressing (contiguous or paged) and per-sequence lengths
@@ -449,9 +483,14 @@ __device__ __forceinline__ void ld_stats(const AttnShape &s, int b, int h0, int 
                                          const float2 *__restrict__ pstat, float2 (&pst)[GS])
 {
     const int tid = threadIdx.x;
+    // Every thread loads, at a clamped index (nqk_all >= 1); group_lse replaces
+    // the statistic of threads past the sequence's chunks by the empty one.  A
+    // select here, or a load under a per-thread branch, would be waited for at
+    // once: one round trip per head before the logits are even requested.
+    const int i = max(0, min(tid, nqk - 1));
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh)
-        pst[hh] = tid < nqk ? pstat[((int64_t)b * s.Hq + h0 + hh) * nqk_all + tid] : make_float2(-INFINITY, 0.0f);
+        pst[hh] = pstat[((int64_t)b * s.Hq + h0 + hh) * nqk_all + i];
 }
 template <int GS>
 __device__ void group_lse(const AttnShape &s, int b, int h0, int nqk_all, int nqk, const float2 *__restrict__ pstat,
@@ -462,10 +501,14 @@ __device__ void group_lse(const AttnShape &s, int b, int h0, int nqk_all, int nq
     const double sc = (double)s.scale;
     float mt[GS];
     double zt[GS];
+    // threads past the sequence's chunks take the empty statistic (-inf, 0),
+    // blended in with a mask the optimizer cannot turn back into a branch
+    int okm = tid < nqk ? -1 : 0;
+    asm volatile("" : "+v"(okm));
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh) {
-        mt[hh] = pst[hh].x;
-        zt[hh] = (double)pst[hh].y;
+        mt[hh] = __int_as_float((__float_as_int(pst[hh].x) & okm) | (int)(0xff800000u & ~(uint32_t)okm));
+        zt[hh] = (double)__int_as_float(__float_as_int(pst[hh].y) & okm);
     }
     for (int i = tid + 256; i < nqk; i += 256) { // sequences of more than 256 QK chunks
 #pragma unroll

@@ -284,11 +284,15 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const uint16_t *__re
 // (vmcnt) are explicit.
 //
 // LDS per stage.  A: 128 rows x 128 bytes; the 16-byte chunk c of row r sits
-// at chunk c ^ (r & 7).  B (kept W^T rows): 64 rows x 512 bytes; chunk c of
+// at chunk c ^ gd_aswz(r) = c ^ ((r >> 1) & 7): the LDS has 64 banks, so a
+// 128-byte row pair spans them all and the 16 rows of a 16-lane quarter of a
+// 16-byte read must differ in (r & 1, chunk); with c ^ (r & 7) rows r and
+// r + 8 collided.  B (kept W^T rows): 64 rows x 512 bytes; chunk c of
 // row q sits at chunk c ^ 4(q & 3).  Each spreads a fragment read over the
 // banks; the DMA stores a chunk anywhere in its 1 KiB by the choice of the
 // lane's source address.
 constexpr int GD_M = 128, GD_N = 256, GD_K = 64;
+__device__ __forceinline__ int gd_aswz(int r) { return (r >> 1) & 7; }
 constexpr int GD_A_STAGE = GD_M * GD_K * 2;            // 16 KiB
 constexpr int GD_B_STAGE = GD_K * GD_N * 2;            // 32 KiB
 constexpr int GD_B_BASE = 3 * GD_A_STAGE;              // A stages first, then B stages
@@ -452,12 +456,12 @@ __global__ __launch_bounds__(512) void gemm_dma_kernel(const uint16_t *__restric
         // ================================================================ producer
         const int32_t *J = DENSE ? nullptr : idx + (int64_t)tau * k;
         const int klim = DENSE ? ksteps * GD_K : k;
-        // A instruction i of wave w fills rows 8(4w + i) + lane/8; lane's chunk (lane & 7) holds chunk (lane & 7) ^ (lane >> 3)
+        // A instruction i of wave w fills rows r = 8(4w + i) + lane/8; lane's chunk (lane & 7) holds chunk (lane & 7) ^ gd_aswz(r)
         const uint16_t *pA[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = min(row0 + (4 * w + i) * 8 + (lane >> 3), rowend - 1);
-            pA[i] = A + (int64_t)r * lda + (((lane & 7) ^ (lane >> 3)) * 8);
+            pA[i] = A + (int64_t)r * lda + (((lane & 7) ^ gd_aswz((4 * w + i) * 8 + (lane >> 3))) * 8);
         }
         // B instruction i of wave w fills rows q = 16w + 2i + lane/32; q & 3 = 2(i & 1) + lane/32
         const int mlast = (M - 1) / 8 * 8;
@@ -551,7 +555,7 @@ __global__ __launch_bounds__(512) void gemm_dma_kernel(const uint16_t *__restric
     uint32_t pa[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        pa[j] = lbase + (lane & 31) * 128 + (((2 * j + (lane >> 5)) ^ (lane & 7)) * 16);
+        pa[j] = lbase + (lane & 31) * 128 + (((2 * j + (lane >> 5)) ^ gd_aswz(lane & 31)) * 16);
     const int g = lane >> 4, i16 = lane & 15, trow = 8 * (g >> 1) + (i16 >> 2);
     uint32_t pb[2];
 #pragma unroll
