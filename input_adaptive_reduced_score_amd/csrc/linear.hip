@@ -19,9 +19,9 @@ namespace rmm {
 // ============================================================================ gather
 // xg[t][i] = x[t][idx[t/tile][i]] for i < k, 0 for k <= i < kpad.
 // A workgroup takes up to `rows` consecutive token rows of one tile (they share
-// the kept list).  Thread t owns 8-column chunks t, t + 256, ... of the packed
-// rows; it loads the indices of its chunks once, with clamped addresses so that
-// every load is issued before the first wait, and reuses them for each row.
+// the kept list).  Thread t owns packed columns t, t + 256, ...; it loads their
+// indices once, with clamped addresses so that every load is issued before the
+// first wait, and reuses them for each row.
 // With STAGE the rows are first staged in LDS with 16-byte loads, all rows in
 // flight together (rows x K elements, K up to GATHER_LDS_MAX_K); without, each
 // element is read from global memory.
@@ -55,33 +55,29 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t *__restrict_
         }
         __syncthreads();
     }
-    const int nch = kpad / 8;
-    for (int c0 = 0; c0 < nch; c0 += 256 * GATHER_CH) {
-        int jv[GATHER_CH][8];
+    // Packed element i of a row is taken by thread i % 256: a wave's 64 reads
+    // address 64 consecutive kept columns, 2/r bytes apart on average (few
+    // lanes per LDS bank), and its 2-byte stores fill 128 contiguous bytes.  A
+    // thread that took 8 consecutive packed elements read 8 kept columns away
+    // from its neighbours' addresses: up to 8 lanes per bank.
+    constexpr int NJ = 8 * GATHER_CH; // packed elements per thread per pass
+    for (int c0 = 0; c0 < kpad; c0 += 256 * NJ) {
+        int jv[NJ];
 #pragma unroll
-        for (int c = 0; c < GATHER_CH; ++c)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                jv[c][e] = J[min((c0 + (int)threadIdx.x + 256 * c) * 8 + e, k - 1)];
+        for (int j = 0; j < NJ; ++j)
+            jv[j] = J[min(c0 + (int)threadIdx.x + 256 * j, k - 1)];
         for (int r = 0; r < nr; ++r) {
             const uint16_t *src = STAGE ? xrow + (int64_t)r * K8 * 8 : x + (int64_t)(t0 + r) * ldx;
+            uint16_t *dst = xg + (int64_t)(t0 + r) * kpad;
+            uint16_t v[NJ];
 #pragma unroll
-            for (int c = 0; c < GATHER_CH; ++c) {
-                const int ch = c0 + (int)threadIdx.x + 256 * c;
-                if (ch >= nch)
-                    break;
-                uint32_t h[8];
+            for (int j = 0; j < NJ; ++j)
+                v[j] = src[jv[j]]; // clamped index: always in bounds
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t v = src[jv[c][e]]; // clamped index: always in bounds
-                    h[e] = ch * 8 + e < k ? v : 0u;
-                }
-                uint4 o;
-                o.x = h[0] | (h[1] << 16);
-                o.y = h[2] | (h[3] << 16);
-                o.z = h[4] | (h[5] << 16);
-                o.w = h[6] | (h[7] << 16);
-                *reinterpret_cast<uint4 *>(xg + (int64_t)(t0 + r) * kpad + ch * 8) = o;
+            for (int j = 0; j < NJ; ++j) {
+                const int i = c0 + (int)threadIdx.x + 256 * j;
+                if (i < kpad) // (whole waves: kpad, c0 and 256 j are multiples of 64)
+                    dst[i] = i < k ? v[j] : (uint16_t)0;
             }
         }
     }
