@@ -26,7 +26,7 @@ namespace rmm {
 // flight together (rows x K elements, K up to GATHER_LDS_MAX_K); without, each
 // element is read from global memory.
 constexpr int GATHER_LDS_MAX_K = 32768;
-constexpr int GATHER_LDS_BUDGET = 32768;  // bytes of staged rows per workgroup (one row may exceed it)
+constexpr int GATHER_LDS_BUDGET = 16384;  // bytes of staged rows per workgroup (one row may exceed it)
 constexpr int GATHER_MAX_ROWS = 8;
 constexpr int GATHER_CH_MAX = 4;          // chunks per thread held in registers per pass
 template <bool STAGE, int GATHER_CH>
