@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MALL_BYTES = 256 * 2**20
-SECTIONS = ("batched", "blocks", "layer", "prefill", "attention", "paged")
+SECTIONS = ("batched", "blocks", "layer", "prefill", "attention", "context", "paged")
 
 
 def log(*a):
@@ -591,6 +591,35 @@ def main():
             sweep.append({"workload": name + "_dense", "call_us": t * 1e6, "bytes": by, "GBps": by / t / 1e9})
             log(f"[bench] {name} dense flash-decode: {t * 1e6:.1f} us ({by / t / 1e9:.0f} GB/s)")
             del qs, ks_, vs_, kns, q0, k0, v0
+
+    # ------------------------------------------------------------------ context-length sweep
+    # One sequence (B = 1, the GQA decode heads) at lengths from 8K to 256K positions: the reduced call
+    # against dense flash-decode on the same cache, to show where the reduction starts to pay.
+    if want("context"):
+        for S in (8192, 16384, 32768, 65536, 131072, 262144):
+            log(f"[bench] context sweep S={S}: generating inputs")
+            ac = W.attn_case(1, S, seed=21)
+            B, Hq, Hkv, D = ac.B, ac.Hq, ac.Hkv, ac.D
+            q0, k0, v0, kn0 = bf(ac.q), bf(ac.kt), bf(ac.v), torch.from_numpy(ac.kn).to(dev)
+            kvbytes = (k0.numel() + v0.numel()) * 2
+            nac = n_copies(kvbytes, kvbytes // 3)
+            ks_ = [k0 if i == 0 else k0.clone() for i in range(nac)]
+            vs_ = [v0 if i == 0 else v0.clone() for i in range(nac)]
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+            csteps = max(10, steps // 4)
+            t_dense = time_loop(lambda i: rmm.attn_decode_dense(q0, ks_[i % nac], vs_[i % nac], scale=ac.scale,
+                                                                out=out), csteps, 3, torch)
+            for rd, rp in ((0.25, 0.25), (0.5, 0.5)):
+                kd, kss = rmm.keep_count(D, rd), rmm.keep_count(S, rp)
+                t = time_loop(lambda i: rmm.attn_decode(q0, ks_[i % nac], vs_[i % nac], kn0, rd, rp, scale=ac.scale,
+                                                        out=out, want_idx=False), csteps, 3, torch)
+                by = A.attn_step_bytes(B, Hq, Hkv, D, S, kd, kss)
+                sweep.append({"workload": "attn_context_b1", "S": S, "r_dim": rd, "r_pos": rp, "call_us": t * 1e6,
+                              "retained_bytes": by, "GBps": by / t / 1e9, "frac_hbm": by / t / 1e9 / A.HBM_PEAK_GBS,
+                              "dense_us": t_dense * 1e6, "dense_over_reduced": t_dense / t})
+                log(f"[bench] context sweep S={S} r=({rd},{rp}): {t * 1e6:.1f} us against dense "
+                    f"{t_dense * 1e6:.1f} us ({t_dense / t:.2f}x)")
+            del ks_, vs_, q0, k0, v0
 
     # ------------------------------------------------------------------ paged, ragged decode batch
     if want("paged"):

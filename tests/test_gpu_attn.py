@@ -116,6 +116,13 @@ def test_gqa_128k_batch4_full_size():
     run_attn(cs, 0.5, 0.25, 0)
 
 
+@pytest.mark.parametrize("S", [8192, 65536, 262144])
+def test_one_sequence_context_lengths(S):
+    # the lengths of the benchmark's context sweep beyond 32K (one sequence, 8 groups; up to 256K
+    # positions the launches are split as at 128K x 4)
+    run_attn(W.attn_case(1, S, seed=21), 0.25, 0.25, 0)
+
+
 def test_gqa_32k_per_query_head():
     # mode 1 at the full 32K shape: 32 selection groups of one query head
     run_attn(W.attn_32k(), 0.25, 0.25, 1)
